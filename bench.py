@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP32 GEMM hot path on one MI355X.
+
+A step is one C = A.B of the 4096 x 4096 x 4096 workload (A, B, C row-major,
+entries uniform[-1, 1], seed 1) with the operands already resident in HBM.
+W untimed warm-up steps, then exactly K timed steps bracketed by device
+synchronisation; rank 0 prints one JSON line:
+
+  value      TFLOPS = 2*M*N*K * K_steps / wall time
+  roofline   the GEMM kernel's own average duration (HIP events on the
+             stream it is launched on) against the FP32 matrix peak
+  cpu_baseline  the CPU oracle timed on a bounded row sample of the same
+             workload on this host's cores
+
+Other workloads: ``--workload ffn`` etc. (see workloads.WORKLOADS);
+``--all`` also appends a line per workload to the file given by ``--all-out``.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HEADLINE = "sq4096"
+METRIC = "FP32 GEMM TFLOPS (2MNK/t) and % of MI355X FP32 matrix peak at 4096^3"
+
+# FETCH_SIZE / WRITE_SIZE of the GEMM kernel per launch (KiB), read with
+# rocprofv3 --pmc from the current kernels, and the factor that turns the
+# counters into bytes (measured on a plain copy kernel of known size).
+# None until measured for the kernel as it stands.
+TRAFFIC_COUNTERS = None
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=HEADLINE)
+    p.add_argument("--variant", type=int, default=None, help="force a kernel variant")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the baseline")
+    p.add_argument("--all", action="store_true", help="also time every workload")
+    p.add_argument("--all-out", default="gpurun_out/bench_all.jsonl")
+    return p.parse_args()
+
+
+def time_workload(name, steps, warmup, variant=None):
+    import numpy as np
+    import torch
+
+    import dense_gemm_optimisation_fp32_amd as g
+    from dense_gemm_optimisation_fp32_amd import perfmodel as pm
+    from workloads import WORKLOADS, workload_operands
+
+    w = WORKLOADS[name]
+    A, B = workload_operands(w)
+    dev = torch.device("cuda", 0)
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    lda = w.k
+    ldb = w.n if w.layout_b == 0 else w.k
+    dC = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
+    plan = g.get_plan(w.m, w.n, w.k, w.layout_b, lda, ldb, w.n, variant, 0)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    a_ptr, b_ptr, c_ptr = dA.data_ptr(), dB.data_ptr(), dC.data_ptr()
+
+    for _ in range(warmup):
+        plan.run(a_ptr, b_ptr, c_ptr, sh)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` launches, wall clock bracketed by syncs.
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plan.run(a_ptr, b_ptr, c_ptr, sh)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # Per-launch kernel durations with events on the launch stream.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        plan.run(a_ptr, b_ptr, c_ptr, sh)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    durs = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) / 1e3
+    assert torch.isfinite(dC).all().item(), "non-finite output"
+
+    flops = pm.gemm_flops(w.m, w.n, w.k)
+    return {
+        "workload": w,
+        "plan": plan.info,
+        "wall_s": wall,
+        "ms_per_step": wall / steps * 1e3,
+        "tflops": flops * steps / wall / 1e12,
+        "kernel_avg_s": float(durs.mean()),
+        "kernel_median_s": float(np.median(durs)),
+        "kernel_min_s": float(durs.min()),
+        "flops": flops,
+        "bytes": pm.compulsory_bytes(w.m, w.n, w.k),
+    }
+
+
+def cpu_baseline(name, target_s):
+    """The CPU oracle (as it stands) on a bounded sample of the workload: the
+    first R rows of C, with R grown until the run takes about target_s."""
+    import numpy as np
+
+    import oracle
+    from dense_gemm_optimisation_fp32_amd import perfmodel as pm
+    from workloads import WORKLOADS, workload_operands
+
+    w = WORKLOADS[name]
+    A, B = workload_operands(w)
+    rows = 8
+    while True:
+        a = np.ascontiguousarray(A[:rows])
+        t0 = time.perf_counter()
+        oracle.gemm_f64(a, B, rows, w.n, w.k, w.layout_b)
+        t = time.perf_counter() - t0
+        if t >= target_s / 3 or rows >= w.m:
+            break
+        rows = min(w.m, max(rows * 2, int(rows * target_s / 3 / max(t, 1e-3))))
+    return {
+        "value": pm.gemm_flops(rows, w.n, w.k) / t / 1e12,
+        "unit": "TFLOPS",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"first {rows} of {w.m} rows of C for {w.name} ({w.m}x{w.n}x{w.k}), "
+                  f"float64 triple loop, {t:.2f} s",
+    }
+
+
+def roofline(res):
+    from dense_gemm_optimisation_fp32_amd import perfmodel as pm
+
+    w = res["workload"]
+    intensity = pm.arithmetic_intensity(w.m, w.n, w.k)
+    ridge = pm.ridge_point(pm.MI355X_FP32_MATRIX_PEAK, pm.MI355X_HBM_BANDWIDTH)
+    kind = res["plan"]["kind"]
+    if intensity >= ridge:
+        peak = pm.MI355X_FP32_MATRIX_PEAK if kind != 1 else pm.MI355X_FP32_VECTOR_UNPACKED_PEAK
+        achieved = res["flops"] / res["kernel_avg_s"] / 1e12
+        out = {"bound": "mfma" if kind != 1 else "alu", "achieved": round(achieved, 3),
+               "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved / (peak / 1e12), 4)}
+    else:
+        achieved = res["bytes"] / res["kernel_avg_s"] / 1e9
+        out = {"bound": "hbm", "achieved": round(achieved, 1), "peak": pm.MI355X_HBM_BANDWIDTH / 1e9,
+               "unit": "GB/s", "frac": round(achieved / (pm.MI355X_HBM_BANDWIDTH / 1e9), 4)}
+    out["traffic"] = TRAFFIC_COUNTERS.get(w.name) if TRAFFIC_COUNTERS else None
+    out["kernel"] = res["plan"]["name"]
+    out["kernel_avg_us"] = round(res["kernel_avg_s"] * 1e6, 2)
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    from dense_gemm_optimisation_fp32_amd import perfmodel as pm
+
+    res = time_workload(args.workload, args.steps, args.warmup, args.variant)
+    w = res["workload"]
+    line = {
+        "metric": METRIC if w.name == HEADLINE else f"FP32 GEMM TFLOPS (2MNK/t), {w.name}",
+        "value": round(res["tflops"], 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: C=A.B, M={w.m} N={w.n} K={w.k}, A/C row-major, "
+                               f"B {'row' if w.layout_b == 0 else 'column'}-major, {w.dist}, seed {w.seed}",
+                   "m": w.m, "n": w.n, "k": w.k, "layout_b": "row" if w.layout_b == 0 else "col",
+                   "kernel": res["plan"]["name"], "grid": res["plan"]["grid"],
+                   "pct_of_fp32_matrix_peak": round(100 * res["tflops"] / (pm.MI355X_FP32_MATRIX_PEAK / 1e12), 2)},
+        "roofline": roofline(res),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+    if args.all:
+        from workloads import WORKLOADS
+        os.makedirs(os.path.dirname(args.all_out) or ".", exist_ok=True)
+        with open(args.all_out, "a") as f:
+            for name in WORKLOADS:
+                r = time_workload(name, max(5, args.steps // 5), 3, args.variant)
+                rec = {"workload": name, "kernel": r["plan"]["name"], "grid": r["plan"]["grid"],
+                       "tflops": round(r["tflops"], 3), "kernel_avg_us": round(r["kernel_avg_s"] * 1e6, 2),
+                       "kernel_min_us": round(r["kernel_min_s"] * 1e6, 2),
+                       "roofline": roofline(r)}
+                f.write(json.dumps(rec) + "\n")
+                print(json.dumps(rec), file=sys.stderr, flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,105 @@
+// Device-side helpers shared by the GEMM kernels: vector types, raw buffer
+// descriptors with hardware range checking, and the launch argument block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gemmf32 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Word 3 of a gfx9-family raw buffer descriptor: 32-bit data format, no
+// swizzle, no stride.  Loads whose byte offset is at or past num_records
+// return zero and such stores are dropped, so boundary tiles need no branch:
+// an out-of-range element gets the offset kOobOffset instead of its address.
+constexpr int kRawBufferWord3 = 0x00020000;
+// Every operand's byte extent is validated to be below 2^31, so this offset
+// is always out of range.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+// Launch arguments, identical for every kernel family.  Sizes in elements;
+// *_bytes are the operands' byte extents (num_records of the descriptors).
+struct GemmArgs {
+    const float *A;
+    const float *B;
+    float *C;
+    int m, n, k;
+    int lda, ldb, ldc;
+    int tiles_m, tiles_n;  // output tiles along M and N
+    int k_tiles;           // ceil(k / BK)
+    int group_m;           // tile-rows per rasterisation group
+    int num_xcd;           // dispatch round-robins workgroups over this many XCDs
+    uint32_t a_bytes, b_bytes, c_bytes;
+    float *partial;        // split-k partial sums (skinny path), else unused
+    int split_k;           // number of k-splits (skinny path), else 1
+    int k_per_split;       // k values per split (multiple of the k tile)
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             kRawBufferWord3);
+}
+
+__device__ __forceinline__ f32x4 buf_load_x4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
+__device__ __forceinline__ float buf_load_x1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0));
+}
+
+__device__ __forceinline__ void buf_store_x4(f32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)byte_off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store_x1(float v, __amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)byte_off, 0, 0);
+}
+
+// Byte offset of element (row, col) of a row-major operand, or the
+// out-of-range offset when the element is outside the logical matrix.
+__device__ __forceinline__ uint32_t elem_off(bool valid, uint32_t row, uint32_t ld, uint32_t col)
+{
+    return valid ? (row * ld + col) * 4u : kOobOffset;
+}
+
+// Workgroup id -> output tile (tm, tn).
+//
+// Step 1 undoes the hardware's round-robin dispatch of consecutive workgroup
+// ids over the XCDs (each with its own L2): the workgroups that land on one
+// XCD get a contiguous range of logical tile ids, so neighbouring tiles share
+// that XCD's L2.  Step 2 walks the logical ids in groups of `group_m`
+// tile-rows, column by column inside a group, so the tiles resident at one
+// time reuse a few A row-panels and B column-panels instead of one full
+// row of tiles ("GEMM 性能优化", Wave 模型与 L2 命中率: the block order alone
+// changes the L2 hit rate).  Runs once per workgroup.
+__device__ __forceinline__ void raster_tile(int wg, const GemmArgs &a, int &tm, int &tn)
+{
+    const int total = a.tiles_m * a.tiles_n;
+    const int x = wg % a.num_xcd;
+    const int i = wg / a.num_xcd;
+    const int per = total / a.num_xcd;
+    const int rem = total % a.num_xcd;
+    const int logical = x * per + (x < rem ? x : rem) + i;
+
+    const int width = a.group_m * a.tiles_n;
+    const int group = logical / width;
+    const int first_m = group * a.group_m;
+    const int rows_left = a.tiles_m - first_m;
+    const int gsize = rows_left < a.group_m ? rows_left : a.group_m;
+    const int r = logical - group * width;
+    tm = first_m + r % gsize;
+    tn = r / gsize;
+}
+
+}  // namespace gemmf32

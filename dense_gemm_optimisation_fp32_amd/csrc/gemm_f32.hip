@@ -1,0 +1,349 @@
+// Host side of libgemm_f32.so: argument validation, the compiled variant
+// table, shape dispatch, plans and launches.  The C ABI is declared in
+// include/gemm_f32.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+
+#include "gemm_f32.h"
+#include "mfma_gemm.hpp"
+#include "valu_gemm.hpp"
+
+namespace {
+
+using gemmf32::GemmArgs;
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e)
+{
+    g_last_hip_error = static_cast<int>(e);
+    return GEMM_F32_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Variant table
+// ---------------------------------------------------------------------------
+
+struct VariantDesc {
+    const char *name;
+    int kind;
+    int bm, bn, bk;
+    int waves_m, waves_n;
+    int threads;
+    int lds_bytes;
+    int stages;
+    const void *fn[2][2];  // [column-major B][16-byte vector class]
+};
+
+template <class T>
+VariantDesc mfma_variant(const char *name)
+{
+    return VariantDesc{
+        name, GEMM_F32_KIND_MFMA, T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::THREADS, T::LDS_BYTES, 2,
+        {{reinterpret_cast<const void *>(&gemmf32::gemm_mfma_kernel<T, false, false>),
+          reinterpret_cast<const void *>(&gemmf32::gemm_mfma_kernel<T, false, true>)},
+         {reinterpret_cast<const void *>(&gemmf32::gemm_mfma_kernel<T, true, false>),
+          reinterpret_cast<const void *>(&gemmf32::gemm_mfma_kernel<T, true, true>)}}};
+}
+
+VariantDesc valu_variant(const char *name)
+{
+    using T = gemmf32::ValuTile;
+    return VariantDesc{
+        name, GEMM_F32_KIND_VALU, T::BM, T::BN, T::BK, 4, 1, T::THREADS, T::LDS_BYTES, 2,
+        {{reinterpret_cast<const void *>(&gemmf32::gemm_valu_kernel<false, false>),
+          reinterpret_cast<const void *>(&gemmf32::gemm_valu_kernel<false, true>)},
+         {reinterpret_cast<const void *>(&gemmf32::gemm_valu_kernel<true, false>),
+          reinterpret_cast<const void *>(&gemmf32::gemm_valu_kernel<true, true>)}}};
+}
+
+enum VariantId { V_MFMA_256x256 = 0, V_MFMA_128x128 = 1, V_MFMA_256x128 = 2, V_VALU_128x128 = 3, V_COUNT };
+
+const VariantDesc &variant(int v)
+{
+    static const VariantDesc table[V_COUNT] = {
+        mfma_variant<gemmf32::MfmaTile<256, 256, 16, 2, 2>>("mfma_256x256x16_w2x2_32x32x2"),
+        mfma_variant<gemmf32::MfmaTile<128, 128, 16, 2, 2>>("mfma_128x128x16_w2x2_32x32x2"),
+        mfma_variant<gemmf32::MfmaTile<256, 128, 16, 2, 2>>("mfma_256x128x16_w2x2_32x32x2"),
+        valu_variant("valu_128x128x8_t8x8"),
+    };
+    return table[v];
+}
+
+// ---------------------------------------------------------------------------
+// Device facts, queried once per device
+// ---------------------------------------------------------------------------
+
+struct DeviceFacts {
+    int status = -1;  // -1: not queried yet, else a gemm_f32_status
+    int cu_count = 0;
+    int num_xcd = 1;
+    int hip_error = 0;
+};
+
+constexpr int kMaxDevices = 64;
+DeviceFacts g_devices[kMaxDevices];
+std::mutex g_devices_mutex;
+
+int device_facts(int *device_out, DeviceFacts *facts_out)
+{
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e == hipErrorNoDevice || (e == hipSuccess && count == 0)) {
+        (void)hipGetLastError();
+        return GEMM_F32_ERR_NO_DEVICE;
+    }
+    if (e != hipSuccess) return hip_fail(e);
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return GEMM_F32_ERR_UNSUPPORTED_DEVICE;
+
+    std::lock_guard<std::mutex> lock(g_devices_mutex);
+    DeviceFacts &f = g_devices[dev];
+    if (f.status < 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e);
+        if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+            f.status = GEMM_F32_ERR_UNSUPPORTED_DEVICE;
+        } else {
+            f.cu_count = prop.multiProcessorCount;
+            int xcc = 0;
+            if (hipDeviceGetAttribute(&xcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcc < 1) {
+                (void)hipGetLastError();
+                xcc = 1;  // the rasterisation stays a bijection for any count
+            }
+            f.num_xcd = xcc;
+            f.status = GEMM_F32_SUCCESS;
+        }
+    }
+    *device_out = dev;
+    *facts_out = f;
+    return f.status;
+}
+
+// ---------------------------------------------------------------------------
+// Plans
+// ---------------------------------------------------------------------------
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int env_int(const char *name, int fallback)
+{
+    const char *s = std::getenv(name);
+    if (!s || !*s) return fallback;
+    char *end = nullptr;
+    long v = std::strtol(s, &end, 10);
+    if (end == s) return fallback;
+    return static_cast<int>(v);
+}
+
+}  // namespace
+
+struct gemm_f32_plan_impl {
+    int variant;
+    int device;
+    int layout_b;
+    int64_t m, n, k, lda, ldb, ldc;
+    bool shape_vec;      // strides and contiguous extents allow 16-byte accesses
+    GemmArgs args;       // pointers filled at run time
+    unsigned grid;
+    unsigned block;
+};
+
+namespace {
+
+// Shape dispatch: the largest tile that still gives every CU a workgroup.
+int choose_variant(int64_t m, int64_t n, const DeviceFacts &f)
+{
+    const int64_t tiles256 = ceil_div(m, 256) * ceil_div(n, 256);
+    if (tiles256 >= f.cu_count) return V_MFMA_256x256;
+    return V_MFMA_128x128;
+}
+
+int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int64_t k, int layout_b,
+              int64_t lda, int64_t ldb, int64_t ldc)
+{
+    if (!out) return GEMM_F32_ERR_INVALID_VALUE;
+    *out = nullptr;
+    int st = gemm_f32_validate(m, n, k, layout_b, lda, ldb, ldc);
+    if (st != GEMM_F32_SUCCESS) return st;
+    if (forced_variant >= V_COUNT) return GEMM_F32_ERR_INVALID_VALUE;
+
+    int dev = 0;
+    DeviceFacts facts;
+    st = device_facts(&dev, &facts);
+    if (st != GEMM_F32_SUCCESS) return st;
+
+    int v = forced_variant;
+    if (v < 0) {
+        v = env_int("GEMM_F32_VARIANT", -1);
+        if (v < 0 || v >= V_COUNT) v = choose_variant(m, n, facts);
+    }
+    const VariantDesc &d = variant(v);
+
+    gemm_f32_plan p = new (std::nothrow) gemm_f32_plan_impl();
+    if (!p) return GEMM_F32_ERR_ALLOC;
+    p->variant = v;
+    p->device = dev;
+    p->layout_b = layout_b;
+    p->m = m; p->n = n; p->k = k;
+    p->lda = lda; p->ldb = ldb; p->ldc = ldc;
+    const bool b_contig_ok = layout_b == GEMM_F32_ROW_MAJOR ? (n % 4 == 0) : (k % 4 == 0);
+    p->shape_vec = lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0 && k % 4 == 0 && n % 4 == 0 && b_contig_ok;
+
+    GemmArgs &a = p->args;
+    std::memset(&a, 0, sizeof(a));
+    a.m = (int)m; a.n = (int)n; a.k = (int)k;
+    a.lda = (int)lda; a.ldb = (int)ldb; a.ldc = (int)ldc;
+    a.tiles_m = (int)ceil_div(m, d.bm);
+    a.tiles_n = (int)ceil_div(n, d.bn);
+    a.k_tiles = (int)ceil_div(k, d.bk);
+    a.group_m = env_int("GEMM_F32_GROUP_M", 8);
+    if (a.group_m < 1) a.group_m = 1;
+    a.num_xcd = facts.num_xcd;
+    a.a_bytes = (uint32_t)(((m - 1) * lda + k) * 4);
+    a.b_bytes = (uint32_t)((layout_b == GEMM_F32_ROW_MAJOR ? (k - 1) * ldb + n : (n - 1) * ldb + k) * 4);
+    a.c_bytes = (uint32_t)(((m - 1) * ldc + n) * 4);
+    a.split_k = 1;
+    a.k_per_split = (int)k;
+    p->grid = (unsigned)((int64_t)a.tiles_m * a.tiles_n);
+    p->block = (unsigned)d.threads;
+
+    if (env_int("GEMM_F32_LOG", 0))
+        std::fprintf(stderr, "[gemm_f32] m=%lld n=%lld k=%lld layoutB=%d -> %s grid=%u group_m=%d vec=%d\n",
+                     (long long)m, (long long)n, (long long)k, layout_b, d.name, p->grid, a.group_m,
+                     (int)p->shape_vec);
+    *out = p;
+    return GEMM_F32_SUCCESS;
+}
+
+void fill_static_info(int v, gemm_f32_info *info)
+{
+    std::memset(info, 0, sizeof(*info));
+    const VariantDesc &d = variant(v);
+    info->variant = v;
+    info->kind = d.kind;
+    info->bm = d.bm; info->bn = d.bn; info->bk = d.bk;
+    info->waves_m = d.waves_m; info->waves_n = d.waves_n;
+    info->wave_m = d.bm / d.waves_m;
+    info->wave_n = d.bn / d.waves_n;
+    info->threads = d.threads;
+    info->lds_bytes = d.lds_bytes;
+    info->stages = d.stages;
+    info->split_k = 1;
+    std::snprintf(info->name, sizeof(info->name), "%s", d.name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f32_validate(int64_t m, int64_t n, int64_t k, int layout_b, int64_t lda, int64_t ldb, int64_t ldc)
+{
+    if (m < 1 || n < 1 || k < 1) return GEMM_F32_ERR_INVALID_VALUE;
+    if (layout_b != GEMM_F32_ROW_MAJOR && layout_b != GEMM_F32_COL_MAJOR) return GEMM_F32_ERR_INVALID_VALUE;
+    if (lda < k || ldc < n) return GEMM_F32_ERR_INVALID_VALUE;
+    if (layout_b == GEMM_F32_ROW_MAJOR ? ldb < n : ldb < k) return GEMM_F32_ERR_INVALID_VALUE;
+    // Byte extents below 2^31: 32-bit buffer offsets address every element
+    // and the out-of-range offset 2^31 is never a valid element.
+    const int64_t limit = (int64_t)1 << 31;
+    const int64_t cap = limit / 4;  // elements; also bounds each factor against overflow
+    if (m >= cap || n >= cap || k >= cap || lda >= cap || ldb >= cap || ldc >= cap)
+        return GEMM_F32_ERR_INVALID_VALUE;
+    const int64_t a_ext = (m - 1) * lda + k;
+    const int64_t b_ext = layout_b == GEMM_F32_ROW_MAJOR ? (k - 1) * ldb + n : (n - 1) * ldb + k;
+    const int64_t c_ext = (m - 1) * ldc + n;
+    if (a_ext >= cap || b_ext >= cap || c_ext >= cap) return GEMM_F32_ERR_INVALID_VALUE;
+    return GEMM_F32_SUCCESS;
+}
+
+int gemm_f32_create(gemm_f32_plan *out, int64_t m, int64_t n, int64_t k, int layout_b, int64_t lda,
+                    int64_t ldb, int64_t ldc)
+{
+    return make_plan(out, -1, m, n, k, layout_b, lda, ldb, ldc);
+}
+
+int gemm_f32_create_variant(gemm_f32_plan *out, int v, int64_t m, int64_t n, int64_t k, int layout_b,
+                            int64_t lda, int64_t ldb, int64_t ldc)
+{
+    if (v < 0 || v >= V_COUNT) {
+        if (out) *out = nullptr;
+        return GEMM_F32_ERR_INVALID_VALUE;
+    }
+    return make_plan(out, v, m, n, k, layout_b, lda, ldb, ldc);
+}
+
+int gemm_f32_run(gemm_f32_plan p, const float *A, const float *B, float *C, void *stream)
+{
+    if (!p || !A || !B || !C) return GEMM_F32_ERR_INVALID_VALUE;
+    const uintptr_t ua = reinterpret_cast<uintptr_t>(A), ub = reinterpret_cast<uintptr_t>(B),
+                    uc = reinterpret_cast<uintptr_t>(C);
+    if ((ua | ub | uc) & 3u) return GEMM_F32_ERR_INVALID_VALUE;
+    const bool vec = p->shape_vec && ((ua | ub | uc) & 15u) == 0;
+
+    GemmArgs a = p->args;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    const VariantDesc &d = variant(p->variant);
+    const void *fn = d.fn[p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0][vec ? 1 : 0];
+    void *kargs[] = {&a};
+    hipError_t e = hipLaunchKernel(fn, dim3(p->grid), dim3(p->block), kargs, 0,
+                                   reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return GEMM_F32_SUCCESS;
+}
+
+int gemm_f32_destroy(gemm_f32_plan p)
+{
+    delete p;
+    return GEMM_F32_SUCCESS;
+}
+
+int gemm_f32_describe(gemm_f32_plan p, gemm_f32_info *info)
+{
+    if (!p || !info) return GEMM_F32_ERR_INVALID_VALUE;
+    fill_static_info(p->variant, info);
+    info->aligned = p->shape_vec ? 1 : 0;
+    info->tiles_m = p->args.tiles_m;
+    info->tiles_n = p->args.tiles_n;
+    info->k_tiles = p->args.k_tiles;
+    info->grid = p->grid;
+    info->group_m = p->args.group_m;
+    info->split_k = p->args.split_k;
+    return GEMM_F32_SUCCESS;
+}
+
+int gemm_f32_num_variants(void) { return V_COUNT; }
+
+int gemm_f32_variant_info(int v, gemm_f32_info *info)
+{
+    if (!info || v < 0 || v >= V_COUNT) return GEMM_F32_ERR_INVALID_VALUE;
+    fill_static_info(v, info);
+    return GEMM_F32_SUCCESS;
+}
+
+const char *gemm_f32_error_string(int status)
+{
+    switch (status) {
+    case GEMM_F32_SUCCESS: return "success";
+    case GEMM_F32_ERR_INVALID_VALUE: return "invalid value (size, stride, layout, NULL or misaligned pointer)";
+    case GEMM_F32_ERR_NO_DEVICE: return "no HIP device visible";
+    case GEMM_F32_ERR_UNSUPPORTED_DEVICE: return "current device is not gfx950";
+    case GEMM_F32_ERR_HIP: return "HIP runtime call failed (see gemm_f32_last_hip_error)";
+    case GEMM_F32_ERR_ALLOC: return "host allocation failed";
+    default: return "unknown status";
+    }
+}
+
+int gemm_f32_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,148 @@
+/*
+ * gemm_f32.h - C ABI of the MI355X (gfx950) single-precision GEMM library
+ * libgemm_f32.so.
+ *
+ * Operation (pages "GEMM 性能优化", section 指标与目标, and
+ * "PMPP Chapter 06: Performance considerations", section 1, corner-turning
+ * example): for 0 <= i < m and 0 <= j < n
+ *
+ *     C[i*ldc + j] = sum_{0 <= kk < k} A[i*lda + kk] * B(kk, j)
+ *
+ *     B(kk, j) = B[kk*ldb + j]   layout_b == GEMM_F32_ROW_MAJOR
+ *              = B[j*ldb + kk]   layout_b == GEMM_F32_COL_MAJOR (column j contiguous)
+ *
+ * A (m x k) and C (m x n) are always row-major.  C is overwritten (no
+ * alpha/beta, C is never read); the entries of C's row padding
+ * (j >= n) are never written.  Arithmetic is IEEE float32 multiply-add with
+ * float32 accumulation; the order of the k-sum is the library's (blocked
+ * along k, as the block-matrix identity of "GEMM 性能优化" 台阶 1 allows)
+ * and is fixed for a given plan: the same plan on the same inputs gives
+ * bitwise identical results run after run (no atomics).
+ *
+ * Conventions for every entry point:
+ *  - Return value: a gemm_f32_status code.  Nothing here throws, prints or
+ *    aborts.
+ *  - Pointers A, B, C are device pointers (HIP device memory of the current
+ *    device), owned by the caller.  C must not overlap A or B.
+ *  - Sizes and leading dimensions are in elements (floats).
+ *  - Plans hold host state only (no device memory); a plan is immutable after
+ *    creation and may be used from several host threads and streams at once.
+ *  - Execution is asynchronous on the caller's stream; a device-side fault
+ *    is reported by the caller's next synchronisation, not by gemm_f32_run.
+ */
+#ifndef GEMM_F32_H
+#define GEMM_F32_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gemm_f32_plan_impl *gemm_f32_plan; /* opaque, library-owned */
+
+/* Storage order of B (A and C are row-major). */
+enum gemm_f32_layout {
+    GEMM_F32_ROW_MAJOR = 0, /* B(kk, j) = B[kk*ldb + j]; needs ldb >= n */
+    GEMM_F32_COL_MAJOR = 1  /* B(kk, j) = B[j*ldb + kk]; needs ldb >= k */
+};
+
+enum gemm_f32_status {
+    GEMM_F32_SUCCESS = 0,
+    GEMM_F32_ERR_INVALID_VALUE = 1,       /* bad size, stride, layout, NULL or misaligned pointer */
+    GEMM_F32_ERR_NO_DEVICE = 2,           /* no HIP device visible */
+    GEMM_F32_ERR_UNSUPPORTED_DEVICE = 3,  /* current device is not gfx950 */
+    GEMM_F32_ERR_HIP = 4,                 /* a HIP runtime call failed; see gemm_f32_last_hip_error */
+    GEMM_F32_ERR_ALLOC = 5                /* host allocation failed */
+};
+
+/* Kernel families (gemm_f32_info.kind). */
+enum gemm_f32_kind {
+    GEMM_F32_KIND_MFMA = 0,   /* LDS-tiled, wavefront tiles on v_mfma_f32_32x32x2_f32 */
+    GEMM_F32_KIND_VALU = 1,   /* LDS-tiled, per-thread register outer product on the vector ALU */
+    GEMM_F32_KIND_SKINNY = 2  /* few-row (memory-bound) path */
+};
+
+/* What a plan (or a variant) does; filled by gemm_f32_describe / gemm_f32_variant_info. */
+struct gemm_f32_info {
+    int variant;        /* index into the compiled variant table */
+    int kind;           /* enum gemm_f32_kind */
+    int bm, bn, bk;     /* workgroup tile (rows of C, columns of C, k per LDS stage) */
+    int waves_m, waves_n; /* wavefront grid inside the workgroup */
+    int wave_m, wave_n; /* output tile per wavefront */
+    int threads;        /* threads per workgroup */
+    int lds_bytes;      /* LDS per workgroup (all stages) */
+    int stages;         /* LDS buffers along k */
+    int split_k;        /* k-splits (1 = none) */
+    int aligned;        /* plan only: 1 if the 16-byte vector-load class was chosen at create */
+    int64_t tiles_m, tiles_n, k_tiles, grid; /* plan only: tile counts and workgroups launched */
+    int group_m;        /* plan only: tile-rows per rasterisation group */
+    char name[64];      /* human-readable variant name */
+};
+
+/*
+ * gemm_f32_validate: the pure argument check of gemm_f32_create (no HIP call).
+ *   m, n, k >= 1 (a zero dimension is rejected, the pages never define it);
+ *   lda >= k; ldb >= n (row-major B) or ldb >= k (column-major B); ldc >= n;
+ *   layout_b in {0, 1}; every operand's byte extent below 2^31.
+ * Returns GEMM_F32_SUCCESS or GEMM_F32_ERR_INVALID_VALUE.
+ */
+int gemm_f32_validate(int64_t m, int64_t n, int64_t k, int layout_b,
+                      int64_t lda, int64_t ldb, int64_t ldc);
+
+/*
+ * gemm_f32_create: build a plan for C = A.B of the given shape, B layout and
+ * leading dimensions, choosing the kernel variant by shape class.
+ *   out: receives the plan (set to NULL on failure); must be non-NULL.
+ * Errors: GEMM_F32_ERR_INVALID_VALUE (see gemm_f32_validate, or out == NULL),
+ *         GEMM_F32_ERR_NO_DEVICE, GEMM_F32_ERR_UNSUPPORTED_DEVICE,
+ *         GEMM_F32_ERR_HIP, GEMM_F32_ERR_ALLOC.
+ * The environment variable GEMM_F32_VARIANT=<index> forces a variant.
+ */
+int gemm_f32_create(gemm_f32_plan *out, int64_t m, int64_t n, int64_t k, int layout_b,
+                    int64_t lda, int64_t ldb, int64_t ldc);
+
+/*
+ * gemm_f32_create_variant: as gemm_f32_create with an explicit variant index
+ * in [0, gemm_f32_num_variants()).  Used by the tile/occupancy sweep.
+ * Errors: as gemm_f32_create; an out-of-range variant is INVALID_VALUE.
+ */
+int gemm_f32_create_variant(gemm_f32_plan *out, int variant, int64_t m, int64_t n, int64_t k,
+                            int layout_b, int64_t lda, int64_t ldb, int64_t ldc);
+
+/*
+ * gemm_f32_run: enqueue C = A.B on `stream` (a hipStream_t; NULL = the null
+ * stream).  A, B, C: device pointers, 4-byte aligned, non-NULL.  When every
+ * pointer is 16-byte aligned and every leading dimension and contiguous extent
+ * is a multiple of 4, 16-byte vector loads/stores are used; otherwise a
+ * per-element path runs (misalignment is not an error).
+ * Errors: GEMM_F32_ERR_INVALID_VALUE (NULL plan/pointer, pointer not 4-byte
+ *         aligned), GEMM_F32_ERR_HIP (launch failed).  Never synchronises.
+ */
+int gemm_f32_run(gemm_f32_plan plan, const float *A, const float *B, float *C, void *stream);
+
+/* gemm_f32_destroy: release a plan.  NULL is a no-op returning SUCCESS. */
+int gemm_f32_destroy(gemm_f32_plan plan);
+
+/* gemm_f32_describe: copy the plan's choices into *info (both non-NULL). */
+int gemm_f32_describe(gemm_f32_plan plan, struct gemm_f32_info *info);
+
+/* gemm_f32_num_variants: number of entries in the compiled variant table. */
+int gemm_f32_num_variants(void);
+
+/* gemm_f32_variant_info: static description of variant `variant` (no device
+ * needed; the plan-only fields are zero).  INVALID_VALUE if out of range. */
+int gemm_f32_variant_info(int variant, struct gemm_f32_info *info);
+
+/* gemm_f32_error_string: static text for a status code (never NULL). */
+const char *gemm_f32_error_string(int status);
+
+/* gemm_f32_last_hip_error: the hipError_t behind the calling thread's most
+ * recent GEMM_F32_ERR_HIP (0 if none). */
+int gemm_f32_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F32_H */

@@ -1,0 +1,178 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI.
+
+Acceptance per element: |C - C_ref| <= 1e-5 * S + 1e-6 with
+S = sum_k |a_ik * b_kj| (both from the oracle, in float64), and bit-exact
+equality on integer-valued inputs, where every summation order is exact.
+
+Small shapes span several tiles and ragged tails and are compared element by
+element with the full oracle for every compiled variant.  The full workload
+shapes run in the plan the benchmark times and are compared on sampled
+elements the oracle computes one by one, plus a closed-form integer product
+checked on every element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_helpers import run_gemm, variants
+from workloads import (COL_MAJOR, ROW_MAJOR, WORKLOADS, mod_pattern_operands, permutation,
+                       random_operands, sample_indices, workload_operands)
+
+pytestmark = pytest.mark.gpu
+
+REL, ABS = 1e-5, 1e-6
+
+SMALL_SHAPES = [
+    (256, 256, 256),     # the small square workload
+    (300, 520, 77),      # ragged in every dimension
+    (513, 257, 1000),    # one row/column past a tile edge, k tail
+    (1, 1, 1),
+    (1, 300, 17),
+    (37, 1, 5),
+    (129, 131, 33),
+    (64, 64, 4096),      # long k
+]
+
+
+def check_close(C, Cref, S, what):
+    ok, ratio = oracle.within_tolerance(C, Cref, S, REL, ABS)
+    assert ok, f"{what}: max error ratio {ratio:.3g} (> 1 fails), finite={np.isfinite(C).all()}"
+    return ratio
+
+
+def closed_form(rows, cols, k):
+    count = k - (k + 1) // 3
+    return (((np.asarray(rows) % 7) - 3) * ((np.asarray(cols) % 5) - 2) * count).astype(np.float32)
+
+
+@pytest.mark.parametrize("variant", variants())
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+@pytest.mark.parametrize("shape", SMALL_SHAPES)
+def test_small_shapes_vs_oracle(variant, layout_b, shape):
+    m, n, k = shape
+    print(f"\n[case] variant={variant} layout_b={layout_b} shape={shape}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=1000 + m + n + k)
+    C, info = run_gemm(A, B, m, n, k, layout_b, variant=variant)
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    check_close(C, Cref, S, f"{info['name']} {shape} layout {layout_b}")
+
+
+@pytest.mark.parametrize("variant", variants())
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+@pytest.mark.parametrize("shape", [(300, 520, 77), (256, 256, 256), (129, 131, 33)])
+def test_small_shapes_integer_bitexact(variant, layout_b, shape):
+    m, n, k = shape
+    print(f"\n[case] integer variant={variant} layout_b={layout_b} shape={shape}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=2000 + m)
+    C, _ = run_gemm(A, B, m, n, k, layout_b, variant=variant)
+    Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    assert np.array_equal(C.astype(np.float64), Cref)
+
+
+@pytest.mark.parametrize("variant", variants())
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+def test_padded_strides_nan_padding_and_c_padding(variant, layout_b):
+    """lda/ldb/ldc above the minimum: operand padding holds NaN (it must never
+    reach C) and C's padding holds a sentinel (it must never be written)."""
+    m, n, k = 200, 190, 70
+    lda, ldb, ldc = k + 5, (n if layout_b == ROW_MAJOR else k) + 3, n + 7
+    print(f"\n[case] padded variant={variant} layout_b={layout_b}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "uniform", seed=33, lda=lda, ldb=ldb)
+    C, _ = run_gemm(A, B, m, n, k, layout_b, lda, ldb, ldc, variant=variant, c_fill=-7.25)
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b, lda, ldb)
+    check_close(C[:, :n], Cref, S, "padded")
+    assert np.all(C[:-1, n:] == np.float32(-7.25)), "C row padding was written"
+
+
+@pytest.mark.parametrize("variant", variants())
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+def test_aligned_strides_with_misaligned_pointers(variant, layout_b):
+    """Strides allow 16-byte accesses but the pointers are only 4-byte aligned:
+    the per-element class must run and agree."""
+    m, n, k = 160, 136, 96
+    print(f"\n[case] misaligned variant={variant} layout_b={layout_b}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=34)
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    for offs in [(1, 0, 0), (0, 3, 0), (0, 0, 2), (1, 1, 1)]:
+        C, _ = run_gemm(A, B, m, n, k, layout_b, variant=variant, offsets=offs)
+        check_close(C, Cref, S, f"offsets {offs}")
+
+
+@pytest.mark.parametrize("variant", variants())
+def test_identity_and_permutation_bitwise(variant):
+    m, n, k = 96, 80, 128
+    print(f"\n[case] identity/permutation variant={variant}", flush=True)
+    A, B = random_operands(m, n, k, ROW_MAJOR, "normal1", seed=35)
+    eye = np.eye(k, dtype=np.float32)
+    C, _ = run_gemm(A, eye, m, k, k, ROW_MAJOR, variant=variant)
+    assert np.array_equal(C, A)
+    C, _ = run_gemm(eye, B, k, n, k, ROW_MAJOR, variant=variant)
+    assert np.array_equal(C, B)
+    p = permutation(k, 36)
+    P = np.zeros((k, k), dtype=np.float32)
+    P[p, np.arange(k)] = 1.0                           # (A.P)[i][j] = A[i][p[j]]
+    C, _ = run_gemm(A, np.ascontiguousarray(P.T), m, k, k, COL_MAJOR, variant=variant)
+    assert np.array_equal(C, A[:, p])
+
+
+@pytest.mark.parametrize("variant", variants())
+def test_run_to_run_bitwise_determinism(variant):
+    m, n, k = 384, 320, 512
+    print(f"\n[case] determinism variant={variant}", flush=True)
+    A, B = random_operands(m, n, k, ROW_MAJOR, "normal1", seed=37)
+    _, _, outs = run_gemm(A, B, m, n, k, ROW_MAJOR, variant=variant, repeat=3)
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+# ---------------------------------------------------------------------------
+# Full workload shapes, in the plan the benchmark times (gemm_f32_create).
+# ---------------------------------------------------------------------------
+
+FULL = ["sq256", "sq4096", "sq4096t", "ragged", "ffn", "skinny"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload_sampled_vs_oracle(name):
+    w = WORKLOADS[name]
+    print(f"\n[case] workload {name} random inputs", flush=True)
+    A, B = workload_operands(w)
+    C, info = run_gemm(A, B, w.m, w.n, w.k, w.layout_b)
+    assert np.isfinite(C).all()
+    rows, cols = sample_indices(w.m, w.n, 3000, seed=41)
+    c, s = oracle.gemm_f64_sampled(A, B, w.m, w.n, w.k, w.layout_b, rows, cols)
+    check_close(C[rows, cols], c, s, f"{name} via {info['name']}")
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload_integer_sampled_bitexact(name):
+    w = WORKLOADS[name]
+    print(f"\n[case] workload {name} integer inputs", flush=True)
+    A, B = workload_operands(w, integer=True)
+    C, _ = run_gemm(A, B, w.m, w.n, w.k, w.layout_b)
+    rows, cols = sample_indices(w.m, w.n, 3000, seed=42)
+    c, _ = oracle.gemm_f64_sampled(A, B, w.m, w.n, w.k, w.layout_b, rows, cols)
+    assert np.array_equal(C[rows, cols].astype(np.float64), c)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload_closed_form_every_element(name):
+    w = WORKLOADS[name]
+    print(f"\n[case] workload {name} closed form", flush=True)
+    A, B = mod_pattern_operands(w.m, w.n, w.k, w.layout_b)
+    C, _ = run_gemm(A, B, w.m, w.n, w.k, w.layout_b)
+    expect = closed_form(np.arange(w.m)[:, None], np.arange(w.n)[None, :], w.k)
+    bad = np.argwhere(C != expect)
+    assert bad.size == 0, f"{len(bad)} wrong elements, first {bad[:5].tolist()}"
+
+
+def test_binding_matmul_matches_oracle_both_layouts():
+    m, n, k = 250, 270, 190
+    A, B = random_operands(m, n, k, ROW_MAJOR, "normal1", seed=43)
+    import dense_gemm_optimisation_fp32_amd as g
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(B).cuda()
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, ROW_MAJOR)
+    check_close(g.matmul(dA, dB).cpu().numpy(), Cref, S, "matmul row-major B")
+    dBt = dB.t().contiguous().t()                      # same values, column-major storage
+    check_close(g.matmul(dA, dBt).cpu().numpy(), Cref, S, "matmul column-major B")
