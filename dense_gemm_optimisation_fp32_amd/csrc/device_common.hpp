@@ -38,6 +38,7 @@ struct GemmArgs {
     float *partial;        // split-k partial sums (skinny path), else unused
     int split_k;           // number of k-splits (skinny path), else 1
     int k_per_split;       // k values per split (multiple of the k tile)
+    int masked_loads;      // 1: check every element in every slab (tiny ldb)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)

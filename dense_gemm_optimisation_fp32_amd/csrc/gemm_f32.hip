@@ -11,6 +11,7 @@
 #include <new>
 
 #include "gemm_f32.h"
+#include "mfma_dma_gemm.hpp"
 #include "mfma_gemm.hpp"
 #include "valu_gemm.hpp"
 
@@ -38,7 +39,7 @@ struct VariantDesc {
     int threads;
     int lds_bytes;
     int stages;
-    const void *fn[2][2];  // [column-major B][16-byte vector class]
+    const void *fn[2];  // [column-major B]
 };
 
 template <class T>
@@ -46,10 +47,17 @@ VariantDesc mfma_variant(const char *name)
 {
     return VariantDesc{
         name, GEMM_F32_KIND_MFMA, T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::THREADS, T::LDS_BYTES, 2,
-        {{reinterpret_cast<const void *>(&gemmf32::gemm_mfma_kernel<T, false, false>),
-          reinterpret_cast<const void *>(&gemmf32::gemm_mfma_kernel<T, false, true>)},
-         {reinterpret_cast<const void *>(&gemmf32::gemm_mfma_kernel<T, true, false>),
-          reinterpret_cast<const void *>(&gemmf32::gemm_mfma_kernel<T, true, true>)}}};
+        {reinterpret_cast<const void *>(&gemmf32::gemm_mfma_kernel<T, false>),
+         reinterpret_cast<const void *>(&gemmf32::gemm_mfma_kernel<T, true>)}};
+}
+
+template <class T>
+VariantDesc dma_variant(const char *name)
+{
+    return VariantDesc{
+        name, GEMM_F32_KIND_MFMA, T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::THREADS, T::LDS_BYTES, T::STAGES,
+        {reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_kernel<T, false>),
+         reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_kernel<T, true>)}};
 }
 
 VariantDesc valu_variant(const char *name)
@@ -57,21 +65,45 @@ VariantDesc valu_variant(const char *name)
     using T = gemmf32::ValuTile;
     return VariantDesc{
         name, GEMM_F32_KIND_VALU, T::BM, T::BN, T::BK, 4, 1, T::THREADS, T::LDS_BYTES, 2,
-        {{reinterpret_cast<const void *>(&gemmf32::gemm_valu_kernel<false, false>),
-          reinterpret_cast<const void *>(&gemmf32::gemm_valu_kernel<false, true>)},
-         {reinterpret_cast<const void *>(&gemmf32::gemm_valu_kernel<true, false>),
-          reinterpret_cast<const void *>(&gemmf32::gemm_valu_kernel<true, true>)}}};
+        {reinterpret_cast<const void *>(&gemmf32::gemm_valu_kernel<false>),
+         reinterpret_cast<const void *>(&gemmf32::gemm_valu_kernel<true>)}};
 }
 
-enum VariantId { V_MFMA_256x256 = 0, V_MFMA_128x128 = 1, V_MFMA_256x128 = 2, V_VALU_128x128 = 3, V_COUNT };
+enum VariantId {
+    V_MFMA_256x256x16 = 0,
+    V_MFMA_128x128x16,
+    V_MFMA_256x128x16,
+    V_VALU_128x128x8,
+    V_MFMA_256x128x32,
+    V_MFMA_128x128x32,
+    V_DMA_256x256x16_S2,
+    V_DMA_256x256x16_S3,
+    V_DMA_256x256x16_S4,
+    V_DMA_256x256x32_S2,
+    V_DMA_128x128x16_S3,
+    V_DMA_128x128x32_S3,
+    V_DMA_256x128x16_S3,
+    V_COUNT
+};
 
 const VariantDesc &variant(int v)
 {
+    using gemmf32::DmaTile;
+    using gemmf32::MfmaTile;
     static const VariantDesc table[V_COUNT] = {
-        mfma_variant<gemmf32::MfmaTile<256, 256, 16, 2, 2>>("mfma_256x256x16_w2x2_32x32x2"),
-        mfma_variant<gemmf32::MfmaTile<128, 128, 16, 2, 2>>("mfma_128x128x16_w2x2_32x32x2"),
-        mfma_variant<gemmf32::MfmaTile<256, 128, 16, 2, 2>>("mfma_256x128x16_w2x2_32x32x2"),
+        mfma_variant<MfmaTile<256, 256, 16, 2, 2>>("mfma_256x256x16_w2x2_32x32x2"),
+        mfma_variant<MfmaTile<128, 128, 16, 2, 2>>("mfma_128x128x16_w2x2_32x32x2"),
+        mfma_variant<MfmaTile<256, 128, 16, 2, 2>>("mfma_256x128x16_w2x2_32x32x2"),
         valu_variant("valu_128x128x8_t8x8"),
+        mfma_variant<MfmaTile<256, 128, 32, 2, 2>>("mfma_256x128x32_w2x2_32x32x2"),
+        mfma_variant<MfmaTile<128, 128, 32, 2, 2>>("mfma_128x128x32_w2x2_32x32x2"),
+        dma_variant<DmaTile<256, 256, 16, 2, 2, 2>>("dma_256x256x16_w2x2_s2"),
+        dma_variant<DmaTile<256, 256, 16, 2, 2, 3>>("dma_256x256x16_w2x2_s3"),
+        dma_variant<DmaTile<256, 256, 16, 2, 2, 4>>("dma_256x256x16_w2x2_s4"),
+        dma_variant<DmaTile<256, 256, 32, 2, 2, 2>>("dma_256x256x32_w2x2_s2"),
+        dma_variant<DmaTile<128, 128, 16, 2, 2, 3>>("dma_128x128x16_w2x2_s3"),
+        dma_variant<DmaTile<128, 128, 32, 2, 2, 3>>("dma_128x128x32_w2x2_s3"),
+        dma_variant<DmaTile<256, 128, 16, 2, 2, 3>>("dma_256x128x16_w2x2_s3"),
     };
     return table[v];
 }
@@ -152,7 +184,7 @@ struct gemm_f32_plan_impl {
     int device;
     int layout_b;
     int64_t m, n, k, lda, ldb, ldc;
-    bool shape_vec;      // strides and contiguous extents allow 16-byte accesses
+    bool strides4;       // every leading dimension is a multiple of 4 (informational)
     GemmArgs args;       // pointers filled at run time
     unsigned grid;
     unsigned block;
@@ -164,8 +196,8 @@ namespace {
 int choose_variant(int64_t m, int64_t n, const DeviceFacts &f)
 {
     const int64_t tiles256 = ceil_div(m, 256) * ceil_div(n, 256);
-    if (tiles256 >= f.cu_count) return V_MFMA_256x256;
-    return V_MFMA_128x128;
+    if (tiles256 >= f.cu_count) return V_MFMA_256x256x16;
+    return V_MFMA_128x128x16;
 }
 
 int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int64_t k, int layout_b,
@@ -196,8 +228,7 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     p->layout_b = layout_b;
     p->m = m; p->n = n; p->k = k;
     p->lda = lda; p->ldb = ldb; p->ldc = ldc;
-    const bool b_contig_ok = layout_b == GEMM_F32_ROW_MAJOR ? (n % 4 == 0) : (k % 4 == 0);
-    p->shape_vec = lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0 && k % 4 == 0 && n % 4 == 0 && b_contig_ok;
+    p->strides4 = lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0;
 
     GemmArgs &a = p->args;
     std::memset(&a, 0, sizeof(a));
@@ -214,13 +245,15 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     a.c_bytes = (uint32_t)(((m - 1) * ldc + n) * 4);
     a.split_k = 1;
     a.k_per_split = (int)k;
+    // The whole-chunk loads of row-major B may run up to 3 elements past the
+    // last valid column of a k-row; that stays inside B when ldb >= 4.
+    a.masked_loads = (layout_b == GEMM_F32_ROW_MAJOR && ldb < 4) ? 1 : 0;
     p->grid = (unsigned)((int64_t)a.tiles_m * a.tiles_n);
     p->block = (unsigned)d.threads;
 
     if (env_int("GEMM_F32_LOG", 0))
-        std::fprintf(stderr, "[gemm_f32] m=%lld n=%lld k=%lld layoutB=%d -> %s grid=%u group_m=%d vec=%d\n",
-                     (long long)m, (long long)n, (long long)k, layout_b, d.name, p->grid, a.group_m,
-                     (int)p->shape_vec);
+        std::fprintf(stderr, "[gemm_f32] m=%lld n=%lld k=%lld layoutB=%d -> %s grid=%u group_m=%d\n",
+                     (long long)m, (long long)n, (long long)k, layout_b, d.name, p->grid, a.group_m);
     *out = p;
     return GEMM_F32_SUCCESS;
 }
@@ -287,14 +320,13 @@ int gemm_f32_run(gemm_f32_plan p, const float *A, const float *B, float *C, void
     const uintptr_t ua = reinterpret_cast<uintptr_t>(A), ub = reinterpret_cast<uintptr_t>(B),
                     uc = reinterpret_cast<uintptr_t>(C);
     if ((ua | ub | uc) & 3u) return GEMM_F32_ERR_INVALID_VALUE;
-    const bool vec = p->shape_vec && ((ua | ub | uc) & 15u) == 0;
 
     GemmArgs a = p->args;
     a.A = A;
     a.B = B;
     a.C = C;
     const VariantDesc &d = variant(p->variant);
-    const void *fn = d.fn[p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0][vec ? 1 : 0];
+    const void *fn = d.fn[p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0];
     void *kargs[] = {&a};
     hipError_t e = hipLaunchKernel(fn, dim3(p->grid), dim3(p->block), kargs, 0,
                                    reinterpret_cast<hipStream_t>(stream));
@@ -312,7 +344,7 @@ int gemm_f32_describe(gemm_f32_plan p, gemm_f32_info *info)
 {
     if (!p || !info) return GEMM_F32_ERR_INVALID_VALUE;
     fill_static_info(p->variant, info);
-    info->aligned = p->shape_vec ? 1 : 0;
+    info->aligned = p->strides4 ? 1 : 0;
     info->tiles_m = p->args.tiles_m;
     info->tiles_n = p->args.tiles_n;
     info->k_tiles = p->args.k_tiles;

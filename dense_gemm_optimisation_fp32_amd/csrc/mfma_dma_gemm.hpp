@@ -1,0 +1,330 @@
+// FP32 GEMM on the gfx950 matrix cores with direct global -> LDS loads.
+//
+// Same wavefront tiles, k order and MFMA (v_mfma_f32_32x32x2_f32) as
+// mfma_gemm.hpp, but the operands travel from HBM straight into LDS with
+// buffer_load_dwordx4 ... lds (the gfx950 analogue of the asynchronous copy of
+// "GEMM 性能优化", 台阶 7): no staging registers and no LDS write
+// instructions, so the matrix cores are not interrupted by the copy, and a
+// ring of STAGES LDS buffers lets the loads of slab kt+STAGES-1 fly while slab
+// kt is computed (the N-stage generalisation of 台阶 6's double buffer).
+//
+// The DMA writes lane i's 16 bytes at the wavefront's LDS base + 16*i, so a
+// layout is chosen by choosing which global chunk each lane fetches:
+//   * A:  As[r][c ^ swz_a(r)], k-contiguous rows of BK (as in mfma_gemm.hpp).
+//   * B row-major: Bs[kr][nc], n-contiguous k-rows of BN; the fragment read of
+//     a k-step is one 16-byte read covering the NB interleaved columns
+//     (C column NB*j + nb of the wavefront tile for lane column j).
+//   * B column-major: Bs[n][c ^ swz_a(n)], k-contiguous like A -- the tile is
+//     copied in its HBM orientation and the corner turn happens in the
+//     fragment read, which fetches four consecutive k of one column per lane
+//     ("PMPP Chapter 06", section 1: the unfavourable access pattern moves to
+//     on-chip memory).  Columns are block-major here (C column nb*32 + j).
+//
+// Range checking is per 4-byte element: a chunk that straddles an operand's
+// byte extent keeps its in-range elements and reads zeros past the end, rows
+// of A (columns of column-major B) past m (n) get the out-of-range offset and
+// read as zero, and columns of row-major B past n only feed columns of C that
+// are never stored.  What remains is the k tail: elements k >= K of the last
+// slab that lie inside the operand (row padding, or the start of the next
+// row).  After that slab's copy lands, each lane zeroes those elements of the
+// chunks it fetched (A and column-major B; row-major B's k-rows >= K are past
+// its extent and already zero).
+#pragma once
+
+#include "mfma_gemm.hpp"
+
+namespace gemmf32 {
+
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_>
+struct DmaTile : MfmaTile<BM_, BN_, BK_, WAVES_M_, WAVES_N_> {
+    using Base = MfmaTile<BM_, BN_, BK_, WAVES_M_, WAVES_N_>;
+    static constexpr int STAGES = STAGES_;
+    static constexpr int PIECES = Base::A_PER_T + Base::B_PER_T;   // 16-byte copies per lane per slab
+    static constexpr int LDS_BYTES = STAGES * (Base::A_CHUNKS + Base::B_CHUNKS) * 16;
+    static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
+    static_assert(LDS_BYTES <= 160 * 1024, "fits the 160 KB LDS of a CU");
+    static_assert((STAGES - 2) * PIECES <= 63, "outstanding copies fit the vmcnt counter");
+};
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// One 16-byte global -> LDS copy for wavefront-uniform LDS chunk `wave_chunk`
+// (lane i lands at wave_chunk + i).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 *wave_chunk)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)wave_chunk, 16, (int)byte_off, 0, 0, 0);
+}
+
+// Global element (row, k-chunk) of piece j, and the LDS chunk it lands in.
+template <class T, bool B_COL>
+struct DmaPiece {
+    int lds_chunk;   // chunk index inside the operand's stage region
+    bool is_a;
+    int row;         // A row / B k-row (row-major) / B column (column-major) inside the tile
+    int kc;          // logical 16-byte k-chunk (A and column-major B), n-chunk for row-major B
+};
+
+template <class T, bool B_COL>
+__device__ __forceinline__ DmaPiece<T, B_COL> dma_piece(int j, int tid)
+{
+    DmaPiece<T, B_COL> d;
+    if (j < T::A_PER_T) {
+        const int c = tid + j * T::THREADS;
+        d.lds_chunk = c;
+        d.is_a = true;
+        d.row = c / T::ACH;
+        d.kc = (c % T::ACH) ^ swz_a<T::ACH>(d.row);
+    } else {
+        const int c = tid + (j - T::A_PER_T) * T::THREADS;
+        d.lds_chunk = c;
+        d.is_a = false;
+        if constexpr (!B_COL) {
+            d.row = c / T::BCH;
+            d.kc = c % T::BCH;
+        } else {
+            d.row = c / T::ACH;
+            d.kc = (c % T::ACH) ^ swz_a<T::ACH>(d.row);
+        }
+    }
+    return d;
+}
+
+template <class T, bool B_COL>
+__device__ __forceinline__ void dma_issue(int j, const GemmArgs &g, __amdgpu_buffer_rsrc_t ra,
+                                          __amdgpu_buffer_rsrc_t rb, int row0, int col0, int kt, int tid,
+                                          int wave, f32x4 *As, f32x4 *Bs)
+{
+    const DmaPiece<T, B_COL> d = dma_piece<T, B_COL>(j, tid);
+    const int k0 = kt * T::BK;
+    const int wave_base = (j < T::A_PER_T ? j : j - T::A_PER_T) * T::THREADS + wave * 64;
+    if (d.is_a) {
+        const int gr = row0 + d.row;
+        dma16(ra, elem_off(gr < g.m, gr, g.lda, k0 + 4 * d.kc), As + wave_base);
+    } else if constexpr (!B_COL) {
+        const int gk = k0 + d.row;
+        dma16(rb, elem_off(gk < g.k, gk, g.ldb, col0 + 4 * d.kc), Bs + wave_base);
+    } else {
+        const int gn = col0 + d.row;
+        dma16(rb, elem_off(gn < g.n, gn, g.ldb, k0 + 4 * d.kc), Bs + wave_base);
+    }
+}
+
+// Zero the elements k >= K of this lane's chunks of the last slab (A and
+// column-major B).  Runs after the lane's copies of that slab have landed.
+template <class T, bool B_COL>
+__device__ __forceinline__ void dma_fix_tail(const GemmArgs &g, int kt, int tid, f32x4 *As, f32x4 *Bs)
+{
+    const int k0 = kt * T::BK;
+#pragma unroll
+    for (int j = 0; j < T::PIECES; ++j) {
+        const DmaPiece<T, B_COL> d = dma_piece<T, B_COL>(j, tid);
+        if (!d.is_a && !B_COL) continue;
+        float *p = reinterpret_cast<float *>((d.is_a ? As : Bs) + d.lds_chunk);
+        const int gk = k0 + 4 * d.kc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (gk + q >= g.k) p[q] = 0.0f;
+    }
+}
+
+// vmcnt wait with every other counter left alone (gfx9 encoding: vmcnt bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Fragments of one wavefront for one slab.  A (and column-major B) come as
+// 16-byte k-chunks, double-buffered per chunk; row-major B as one read per
+// k-step, double-buffered per step.
+template <class T, bool B_COL>
+struct DmaFrags {
+    f32x4 af[2][T::MB];
+    f32x4 bk[2][T::NB];        // column-major B: k-chunk q of block nb in bk[q & 1][nb]
+    BFrag<T::NB> bf[2];        // row-major B: k-step p in bf[p & 1]
+};
+
+template <class T>
+__device__ __forceinline__ void read_bk(const f32x4 *Bs, int wc, int l32, int half, int q, f32x4 (&bk)[T::NB])
+{
+#pragma unroll
+    for (int nb = 0; nb < T::NB; ++nb) {
+        const int n = wc * T::WN + nb * 32 + l32;
+        const int kc = half * T::AQ + q;
+        bk[nb] = Bs[n * T::ACH + (kc ^ swz_a<T::ACH>(n))];
+    }
+}
+
+// Row-major B without a swizzle (the copy lands n-contiguous).
+template <class T>
+__device__ __forceinline__ void read_bn(const f32x4 *Bs, int wc, int l32, int half, int p, BFrag<T::NB> &bf)
+{
+    const int kr = half * T::KH + p;
+    const f32x4 *brow = Bs + kr * T::BCH;
+    if constexpr (T::NB == 4) {
+        const f32x4 t = brow[wc * (T::WN / 4) + l32];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) bf.v[nb] = t[nb];
+    } else if constexpr (T::NB == 2) {
+        const float *cp = reinterpret_cast<const float *>(brow + wc * (T::WN / 4) + (l32 >> 1));
+        const f32x2 t = *reinterpret_cast<const f32x2 *>(cp + 2 * (l32 & 1));
+        bf.v[0] = t[0];
+        bf.v[1] = t[1];
+    } else {
+        const float *cp = reinterpret_cast<const float *>(brow + wc * (T::WN / 4) + (l32 >> 2));
+        bf.v[0] = cp[l32 & 3];
+    }
+}
+
+template <class T, bool B_COL>
+__device__ __forceinline__ void dma_mfma_one(int i, int p, const DmaFrags<T, B_COL> &f, f32x16 (&acc)[T::MB][T::NB])
+{
+    const int mb = i / T::NB, nb = i % T::NB;
+    const float a = f.af[(p >> 2) & 1][mb][p & 3];
+    float b;
+    if constexpr (B_COL) b = f.bk[(p >> 2) & 1][nb][p & 3];
+    else b = f.bf[p & 1].v[nb];
+    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[mb][nb], 0, 0, 0);
+}
+
+// Reads for k-step p+1 issued at the top of k-step p (and the first reads of a
+// slab, p = -1).
+template <class T, bool B_COL>
+__device__ __forceinline__ void dma_prefetch(int p_next, const f32x4 *As, const f32x4 *Bs, int wr, int wc, int l32,
+                                             int half, DmaFrags<T, B_COL> &f)
+{
+    if ((p_next & 3) == 0) {
+        const int q = p_next >> 2;
+        read_a<T>(As, wr, l32, half, q, f.af[q & 1]);
+        if constexpr (B_COL) read_bk<T>(Bs, wc, l32, half, q, f.bk[q & 1]);
+    }
+    if constexpr (!B_COL) read_bn<T>(Bs, wc, l32, half, p_next, f.bf[p_next & 1]);
+}
+
+// One slab kt on stage kt % STAGES.  copy: issue the copies of slab
+// kt + STAGES - 1 (one per two MFMAs from the start of the slab; uniform
+// flag).  WAIT: the vmcnt allowance when waiting for slab kt+1's copies at the
+// end (-1: slab kt is the last one).  fix: zero the k tail of slab kt+1 after
+// it lands (uniform flag).  The barrier precedes the last k-step, whose MFMAs
+// cover the first LDS reads of slab kt+1.
+template <class T, bool B_COL, int WAIT>
+__device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 *lds_b, __amdgpu_buffer_rsrc_t ra,
+                                         __amdgpu_buffer_rsrc_t rb, int row0, int col0, int kt, bool copy, bool fix,
+                                         int tid, int wave, int wr, int wc, int l32, int half,
+                                         DmaFrags<T, B_COL> &f, f32x16 (&acc)[T::MB][T::NB])
+{
+    constexpr int NM = T::MB * T::NB;
+    constexpr int GAP = 2 * T::PIECES <= (T::KH - 1) * NM ? 2 : 1;
+    static_assert(T::PIECES * GAP <= (T::KH - 1) * NM, "copies fit before the barrier");
+    const int cur = kt % T::STAGES;
+    const int nxt = (kt + 1) % T::STAGES;
+    const int cpy = (kt + T::STAGES - 1) % T::STAGES;
+    const f32x4 *As = lds_a + cur * T::A_CHUNKS;
+    const f32x4 *Bs = lds_b + cur * T::B_CHUNKS;
+#pragma unroll
+    for (int p = 0; p < T::KH - 1; ++p) {
+        dma_prefetch<T, B_COL>(p + 1, As, Bs, wr, wc, l32, half, f);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            dma_mfma_one<T, B_COL>(i, p, f, acc);
+            const int t = p * NM + i;
+            if ((t + 1) % GAP == 0 && (t + 1) / GAP - 1 < T::PIECES && copy)
+                dma_issue<T, B_COL>((t + 1) / GAP - 1, g, ra, rb, row0, col0, kt + T::STAGES - 1, tid, wave,
+                                    lds_a + cpy * T::A_CHUNKS, lds_b + cpy * T::B_CHUNKS);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if constexpr (WAIT >= 0) {
+        wait_vmcnt<WAIT>();
+        if (fix) dma_fix_tail<T, B_COL>(g, kt + 1, tid, lds_a + nxt * T::A_CHUNKS, lds_b + nxt * T::B_CHUNKS);
+    }
+    __syncthreads();
+    if constexpr (WAIT >= 0)
+        dma_prefetch<T, B_COL>(0, lds_a + nxt * T::A_CHUNKS, lds_b + nxt * T::B_CHUNKS, wr, wc, l32, half, f);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) dma_mfma_one<T, B_COL>(i, T::KH - 1, f, acc);
+}
+
+template <class T, bool B_COL>
+__global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_kernel(GemmArgs g)
+{
+    __shared__ f32x4 lds[T::STAGES * (T::A_CHUNKS + T::B_CHUNKS)];
+    f32x4 *const lds_a = lds;                                // [STAGES][A_CHUNKS]
+    f32x4 *const lds_b = lds + T::STAGES * T::A_CHUNKS;      // [STAGES][B_CHUNKS]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave % T::WAVES_M, wc = wave / T::WAVES_M;
+    const int l32 = lane & 31, half = lane >> 5;
+
+    int tm, tn;
+    raster_tile(blockIdx.x, g, tm, tn);
+    const int row0 = tm * T::BM, col0 = tn * T::BN;
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, g.b_bytes);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.C, g.c_bytes);
+
+    f32x16 acc[T::MB][T::NB];
+#pragma unroll
+    for (int mb = 0; mb < T::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < T::NB; ++nb) acc[mb][nb] = f32x16{};
+
+    const int KT = g.k_tiles;
+    const bool ktail = g.k % T::BK != 0;
+    DmaFrags<T, B_COL> f;
+
+    // Prologue: copies of slabs 0 .. STAGES-2, wait for slab 0.
+#pragma unroll
+    for (int s = 0; s < T::STAGES - 1; ++s)
+        if (s < KT)
+#pragma unroll
+            for (int j = 0; j < T::PIECES; ++j)
+                dma_issue<T, B_COL>(j, g, ra, rb, row0, col0, s, tid, wave, lds_a + s * T::A_CHUNKS,
+                                    lds_b + s * T::B_CHUNKS);
+    wait_vmcnt<0>();
+    if (KT == 1 && ktail) dma_fix_tail<T, B_COL>(g, 0, tid, lds_a, lds_b);
+    __syncthreads();
+    dma_prefetch<T, B_COL>(0, lds_a, lds_b, wr, wc, l32, half, f);
+
+    // Steady state: slab kt+1 is not the last one and slab kt+STAGES-1
+    // exists, so STAGES-2 slabs' copies may stay in flight while waiting for
+    // slab kt+1.  Then the drain: copies only while slabs remain, every wait
+    // complete, the k tail fixed when slab kt+1 is the last.
+    int kt = 0;
+    for (; kt + T::STAGES - 1 < KT && kt + 2 < KT; ++kt)
+        dma_slab<T, B_COL, (T::STAGES - 2) * T::PIECES>(g, lds_a, lds_b, ra, rb, row0, col0, kt, true, false, tid,
+                                                         wave, wr, wc, l32, half, f, acc);
+    for (; kt + 1 < KT; ++kt)
+        dma_slab<T, B_COL, 0>(g, lds_a, lds_b, ra, rb, row0, col0, kt, kt + T::STAGES - 1 < KT,
+                              ktail && kt + 2 == KT, tid, wave, wr, wc, l32, half, f, acc);
+    dma_slab<T, B_COL, -1>(g, lds_a, lds_b, ra, rb, row0, col0, kt, false, false, tid, wave, wr, wc, l32, half, f,
+                           acc);
+
+    // Epilogue.  Lane (l32, half), element v of block (mb, nb) is C row
+    // mb*32 + 8*(v/4) + 4*half + v%4 of the wavefront tile; its column is
+    // NB*l32 + nb (row-major B) or nb*32 + l32 (column-major B).  A single
+    // path of range-checked element stores: with two copies of the store loop
+    // (checked and unchecked) the register allocator starts moving the 256
+    // accumulators around and spills.  Per instruction, 32 lanes write one row
+    // segment: 128 contiguous bytes (column-major B) or every fourth float of
+    // 512 bytes, completed by the NB stores of the other blocks (row-major B).
+#pragma unroll
+    for (int mb = 0; mb < T::MB; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = row0 + wr * T::WM + mb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+#pragma unroll
+            for (int nb = 0; nb < T::NB; ++nb) {
+                const int c = B_COL ? col0 + wc * T::WN + nb * 32 + l32 : col0 + wc * T::WN + T::NB * l32 + nb;
+                buf_store_x1(acc[mb][nb][v], rc, elem_off(r < g.m && c < g.n, r, g.ldc, c));
+            }
+        }
+}
+
+}  // namespace gemmf32

@@ -15,6 +15,10 @@
 // writes use a row stride of BM + 4 floats, which moves the two k-halves of a
 // wavefront's writes to different banks (padding, 台阶 4).
 //
+// Global loads are 16 bytes when the 4 elements are inside the matrix (4-byte
+// alignment suffices), element by element in the k-tail slab and the tile
+// column at the n edge; out-of-range elements read as zero.
+//
 // The FMAs are plain float multiply-adds (v_fma_f32), one per lane per cycle:
 // the vector-ALU peak this path is measured against is that of unpacked FP32.
 #pragma once
@@ -31,7 +35,7 @@ struct ValuTile {
     static constexpr int LDS_BYTES = 2 * BK * (AS + BS) * 4;
 };
 
-template <bool B_COL, bool VEC>
+template <bool B_COL>
 __global__ __launch_bounds__(ValuTile::THREADS) void gemm_valu_kernel(GemmArgs g)
 {
     using T = ValuTile;
@@ -59,18 +63,20 @@ __global__ __launch_bounds__(ValuTile::THREADS) void gemm_valu_kernel(GemmArgs g
 
     auto load = [&](int kt, f32x4 &va, f32x4 &vb) {
         const int k0 = kt * T::BK;
+        const bool full_k = k0 + T::BK <= g.k;   // uniform: 16-byte loads along k are whole
         const int gr = row0 + a_r, gk = k0 + a_k;
-        if constexpr (VEC) {
-            va = buf_load_x4(ra, elem_off(gr < g.m && gk < g.k, gr, g.lda, gk));
+        if (full_k) {
+            va = buf_load_x4(ra, elem_off(gr < g.m, gr, g.lda, gk));
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 va[q] = buf_load_x1(ra, elem_off(gr < g.m && gk + q < g.k, gr, g.lda, gk + q));
         }
         if constexpr (!B_COL) {
+            const bool full_n = col0 + T::BN <= g.n;
             const int bk = k0 + b_kr, bn = col0 + b_n;
-            if constexpr (VEC) {
-                vb = buf_load_x4(rb, elem_off(bk < g.k && bn < g.n, bk, g.ldb, bn));
+            if (full_n) {
+                vb = buf_load_x4(rb, elem_off(bk < g.k, bk, g.ldb, bn));
             } else {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
@@ -78,8 +84,8 @@ __global__ __launch_bounds__(ValuTile::THREADS) void gemm_valu_kernel(GemmArgs g
             }
         } else {
             const int bn = col0 + bc_n, bk = k0 + bc_k;
-            if constexpr (VEC) {
-                vb = buf_load_x4(rb, elem_off(bn < g.n && bk < g.k, bn, g.ldb, bk));
+            if (full_k) {
+                vb = buf_load_x4(rb, elem_off(bn < g.n, bn, g.ldb, bk));
             } else {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
@@ -140,9 +146,9 @@ __global__ __launch_bounds__(ValuTile::THREADS) void gemm_valu_kernel(GemmArgs g
 #pragma unroll
         for (int hj = 0; hj < 2; ++hj) {
             const int c = col0 + 64 * hj + 4 * tx;
-            if constexpr (VEC) {
+            if (c + 3 < g.n) {
                 const f32x4 out = {acc[i][4 * hj], acc[i][4 * hj + 1], acc[i][4 * hj + 2], acc[i][4 * hj + 3]};
-                buf_store_x4(out, rc, elem_off(r < g.m && c < g.n, r, g.ldc, c));
+                buf_store_x4(out, rc, elem_off(r < g.m, r, g.ldc, c));
             } else {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)

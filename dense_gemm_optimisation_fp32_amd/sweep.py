@@ -1,0 +1,132 @@
+"""Tile-shape / occupancy sweep over the compiled variant table.
+
+For every variant and workload: the compiler's per-kernel resources (VGPRs,
+AGPRs, LDS, scratch, waves per SIMD, from the build's resource report), the
+occupancy the performance model derives from them, and the measured kernel
+time and TFLOPS on the GPU.  This is the reuse-versus-occupancy trade-off of
+"GPU 算子优化中的数据复用" (sections 3-8 and 12): bigger tiles reuse more and
+keep fewer waves resident.
+
+    python -m dense_gemm_optimisation_fp32_amd.sweep --workloads sq4096,ffn --out sweep.jsonl
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+
+from . import perfmodel as pm
+
+RESOURCES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_build", "kernel_resources.txt")
+
+
+def kernel_resources(path: str = RESOURCES):
+    """Parse the compiler's resource remarks: {mangled kernel name: {field: value}}."""
+    out = {}
+    cur = None
+    if not os.path.exists(path):
+        return out
+    for line in open(path):
+        m = re.search(r"remark:\s+([A-Za-z /\[\]]+?):\s+(\S+)", line)
+        if not m:
+            continue
+        key, val = m.group(1).strip(), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key] = val
+    return out
+
+
+def resources_for(info: dict, layout_b: int, res: dict):
+    """Resources of the kernel a variant launches for one B layout."""
+    if info["kind"] == 1:
+        tag = f"gemm_valu_kernelILb{layout_b}E"
+    else:
+        tag = (f"MfmaTileILi{info['bm']}ELi{info['bn']}ELi{info['bk']}ELi{info['waves_m']}"
+               f"ELi{info['waves_n']}EEELb{layout_b}E")
+    for name, r in res.items():
+        if tag in name:
+            vg = int(r.get("VGPRs", 0))
+            ag = int(r.get("AGPRs", 0))
+            lds = int(r.get("LDS Size [bytes/block]", 0))
+            wgs, waves = pm.gfx950_occupancy(vg, ag, lds, info["threads"])
+            return {"vgpr": vg, "agpr": ag, "lds": lds, "scratch": int(r.get("ScratchSize [bytes/lane]", 0)),
+                    "compiler_waves_per_simd": int(r.get("Occupancy [waves/SIMD]", 0)),
+                    "model_wgs_per_cu": wgs, "model_waves_per_simd": waves}
+    return {}
+
+
+def time_variant(g, torch, w, variant, steps, warmup):
+    from workloads import workload_operands
+
+    A, B = workload_operands(w)
+    dev = torch.device("cuda", 0)
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    dC = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
+    ldb = w.n if w.layout_b == 0 else w.k
+    plan = g.Plan(w.m, w.n, w.k, w.layout_b, w.k, ldb, w.n, variant)
+    stream = torch.cuda.current_stream(dev)
+    # Warm up for at least `warmup` launches and 0.25 s of GPU time: the
+    # engine clock ramps for ~0.1 s under sustained matrix-core load.
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    plan.run(dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), stream.cuda_stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    est = max(t0.elapsed_time(t1) / 1e3, 1e-6)
+    for _ in range(max(warmup, int(0.25 / est))):
+        plan.run(dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), stream.cuda_stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for s, e in ev:
+        s.record(stream)
+        plan.run(dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), stream.cuda_stream)
+        e.record(stream)
+    torch.cuda.synchronize()
+    durs = sorted(s.elapsed_time(e) / 1e3 for s, e in ev)
+    med = durs[len(durs) // 2]
+    return plan.info, med, durs[0]
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workloads", default="sq4096,sq4096t,ragged,ffn")
+    ap.add_argument("--variants", default="all")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--out", default="gpurun_out/sweep.jsonl")
+    args = ap.parse_args(argv)
+
+    import torch
+
+    import dense_gemm_optimisation_fp32_amd as g
+    from workloads import WORKLOADS
+
+    res = kernel_resources()
+    nvar = g.gemm_f32_num_variants()
+    variants = range(nvar) if args.variants == "all" else [int(v) for v in args.variants.split(",")]
+    os.makedirs(os.path.dirname(args.out) or ".", exist_ok=True)
+    with open(args.out, "a") as f:
+        for name in args.workloads.split(","):
+            w = WORKLOADS[name]
+            for v in variants:
+                info, med, best = time_variant(g, torch, w, v, args.steps, args.warmup)
+                rec = {"workload": name, "variant": v, "name": info["name"], "kind": info["kind"],
+                       "bm": info["bm"], "bn": info["bn"], "bk": info["bk"],
+                       "waves": info["waves_m"] * info["waves_n"], "wave_tile": [info["wave_m"], info["wave_n"]],
+                       "grid": info["grid"], "t_median_us": round(med * 1e6, 2), "t_min_us": round(best * 1e6, 2),
+                       "tflops": round(pm.tflops(w.m, w.n, w.k, med), 2),
+                       "pct_peak": round(100 * pm.tflops(w.m, w.n, w.k, med) * 1e12 / pm.MI355X_FP32_MATRIX_PEAK, 2)}
+                rec.update(resources_for(info, w.layout_b, res))
+                f.write(json.dumps(rec) + "\n")
+                f.flush()
+                print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

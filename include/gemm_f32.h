@@ -74,7 +74,7 @@ struct gemm_f32_info {
     int lds_bytes;      /* LDS per workgroup (all stages) */
     int stages;         /* LDS buffers along k */
     int split_k;        /* k-splits (1 = none) */
-    int aligned;        /* plan only: 1 if the 16-byte vector-load class was chosen at create */
+    int aligned;        /* plan only: 1 if lda, ldb and ldc are multiples of 4 (informational) */
     int64_t tiles_m, tiles_n, k_tiles, grid; /* plan only: tile counts and workgroups launched */
     int group_m;        /* plan only: tile-rows per rasterisation group */
     char name[64];      /* human-readable variant name */
@@ -112,10 +112,11 @@ int gemm_f32_create_variant(gemm_f32_plan *out, int variant, int64_t m, int64_t 
 
 /*
  * gemm_f32_run: enqueue C = A.B on `stream` (a hipStream_t; NULL = the null
- * stream).  A, B, C: device pointers, 4-byte aligned, non-NULL.  When every
- * pointer is 16-byte aligned and every leading dimension and contiguous extent
- * is a multiple of 4, 16-byte vector loads/stores are used; otherwise a
- * per-element path runs (misalignment is not an error).
+ * stream).  A, B, C: device pointers, 4-byte aligned, non-NULL.  Runs of 4
+ * consecutive elements inside the matrices move with 16-byte accesses at any
+ * 4-byte alignment; the k tail and the edge columns move element by element.
+ * Odd leading dimensions and pointers that are not 16-byte aligned are not
+ * errors.
  * Errors: GEMM_F32_ERR_INVALID_VALUE (NULL plan/pointer, pointer not 4-byte
  *         aligned), GEMM_F32_ERR_HIP (launch failed).  Never synchronises.
  */
