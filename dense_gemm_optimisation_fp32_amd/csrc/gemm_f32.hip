@@ -13,6 +13,7 @@
 #include "gemm_f32.h"
 #include "mfma_dma_gemm.hpp"
 #include "mfma_gemm.hpp"
+#include "skinny_gemm.hpp"
 #include "valu_gemm.hpp"
 
 namespace {
@@ -60,6 +61,15 @@ VariantDesc dma_variant(const char *name)
          reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_kernel<T, true>)}};
 }
 
+template <class T>
+VariantDesc skinny_variant(const char *name)
+{
+    return VariantDesc{
+        name, GEMM_F32_KIND_SKINNY, T::BM, T::BN, T::KQ, 1, T::WAVES, T::THREADS, T::WAVES * T::BM * T::BN * 4, 1,
+        {reinterpret_cast<const void *>(&gemmf32::gemm_skinny_kernel<T, false>),
+         reinterpret_cast<const void *>(&gemmf32::gemm_skinny_kernel<T, true>)}};
+}
+
 VariantDesc valu_variant(const char *name)
 {
     using T = gemmf32::ValuTile;
@@ -83,6 +93,9 @@ enum VariantId {
     V_DMA_128x128x16_S3,
     V_DMA_128x128x32_S3,
     V_DMA_256x128x16_S3,
+    V_SKINNY_W4,
+    V_SKINNY_W8,
+    V_DMA_64x64x16_S3,
     V_COUNT
 };
 
@@ -104,6 +117,9 @@ const VariantDesc &variant(int v)
         dma_variant<DmaTile<128, 128, 16, 2, 2, 3>>("dma_128x128x16_w2x2_s3"),
         dma_variant<DmaTile<128, 128, 32, 2, 2, 3>>("dma_128x128x32_w2x2_s3"),
         dma_variant<DmaTile<256, 128, 16, 2, 2, 3>>("dma_256x128x16_w2x2_s3"),
+        skinny_variant<gemmf32::SkinnyTile<4>>("skinny_16x64_splitk_w4"),
+        skinny_variant<gemmf32::SkinnyTile<8>>("skinny_16x64_splitk_w8"),
+        dma_variant<DmaTile<64, 64, 16, 2, 2, 3>>("dma_64x64x16_w2x2_s3"),
     };
     return table[v];
 }
@@ -188,16 +204,21 @@ struct gemm_f32_plan_impl {
     GemmArgs args;       // pointers filled at run time
     unsigned grid;
     unsigned block;
+    float *workspace;    // split-k partial sums (few-row path), else NULL
+    unsigned reduce_grid;
 };
 
 namespace {
 
-// Shape dispatch: the largest tile that still gives every CU a workgroup.
+// Shape dispatch.  Few rows: the bandwidth-bound split-k path.  Otherwise
+// the direct-to-LDS MFMA kernels, with the largest tile that still gives
+// every CU at least one workgroup (256 x 128 tiles run two per CU).
 int choose_variant(int64_t m, int64_t n, const DeviceFacts &f)
 {
-    const int64_t tiles256 = ceil_div(m, 256) * ceil_div(n, 256);
-    if (tiles256 >= f.cu_count) return V_MFMA_256x256x16;
-    return V_MFMA_128x128x16;
+    if (m <= 32) return V_SKINNY_W8;
+    if (ceil_div(m, 256) * ceil_div(n, 128) >= f.cu_count) return V_DMA_256x128x16_S3;
+    if (ceil_div(m, 128) * ceil_div(n, 128) >= f.cu_count) return V_DMA_128x128x16_S3;
+    return V_DMA_64x64x16_S3;
 }
 
 int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int64_t k, int layout_b,
@@ -250,6 +271,32 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     a.masked_loads = (layout_b == GEMM_F32_ROW_MAJOR && ldb < 4) ? 1 : 0;
     p->grid = (unsigned)((int64_t)a.tiles_m * a.tiles_n);
     p->block = (unsigned)d.threads;
+    p->workspace = nullptr;
+    p->reduce_grid = 0;
+    if (d.kind == GEMM_F32_KIND_SKINNY) {
+        // Split k so that about two workgroups per CU are in flight; each
+        // split is a whole number of 16-k groups.
+        const int64_t per_split = (int64_t)a.tiles_m * a.tiles_n;
+        int64_t split = ceil_div(2 * (int64_t)facts.cu_count, per_split);
+        split = split < 1 ? 1 : split;
+        const int64_t max_split = ceil_div(k, 64);
+        split = split > max_split ? max_split : split;
+        int64_t kps = ceil_div(ceil_div(k, split), 16) * 16;
+        split = ceil_div(k, kps);
+        a.split_k = (int)split;
+        a.k_per_split = (int)kps;
+        p->grid = (unsigned)(per_split * split);
+        if (split > 1) {
+            const size_t bytes = (size_t)split * (size_t)m * (size_t)n * sizeof(float);
+            hipError_t e = hipMalloc(reinterpret_cast<void **>(&p->workspace), bytes);
+            if (e != hipSuccess) {
+                delete p;
+                return hip_fail(e);
+            }
+            a.partial = p->workspace;
+            p->reduce_grid = (unsigned)ceil_div(m * n, 256);
+        }
+    }
 
     if (env_int("GEMM_F32_LOG", 0))
         std::fprintf(stderr, "[gemm_f32] m=%lld n=%lld k=%lld layoutB=%d -> %s grid=%u group_m=%d\n",
@@ -328,16 +375,27 @@ int gemm_f32_run(gemm_f32_plan p, const float *A, const float *B, float *C, void
     const VariantDesc &d = variant(p->variant);
     const void *fn = d.fn[p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0];
     void *kargs[] = {&a};
-    hipError_t e = hipLaunchKernel(fn, dim3(p->grid), dim3(p->block), kargs, 0,
-                                   reinterpret_cast<hipStream_t>(stream));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipLaunchKernel(fn, dim3(p->grid), dim3(p->block), kargs, 0, s);
     if (e != hipSuccess) return hip_fail(e);
+    if (p->reduce_grid) {
+        e = hipLaunchKernel(reinterpret_cast<const void *>(&gemmf32::gemm_skinny_reduce_kernel),
+                            dim3(p->reduce_grid), dim3(256), kargs, 0, s);
+        if (e != hipSuccess) return hip_fail(e);
+    }
     return GEMM_F32_SUCCESS;
 }
 
 int gemm_f32_destroy(gemm_f32_plan p)
 {
+    if (!p) return GEMM_F32_SUCCESS;
+    int st = GEMM_F32_SUCCESS;
+    if (p->workspace) {
+        hipError_t e = hipFree(p->workspace);
+        if (e != hipSuccess) st = hip_fail(e);
+    }
     delete p;
-    return GEMM_F32_SUCCESS;
+    return st;
 }
 
 int gemm_f32_describe(gemm_f32_plan p, gemm_f32_info *info)

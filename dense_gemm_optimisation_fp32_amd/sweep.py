@@ -95,7 +95,7 @@ def time_variant(g, torch, w, variant, steps, warmup):
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("--workloads", default="sq4096,sq4096t,ragged,ffn")
+    ap.add_argument("--workloads", default="sq4096,sq4096t,ragged,ffn,skinny")
     ap.add_argument("--variants", default="all")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
@@ -115,13 +115,17 @@ def main(argv=None):
         for name in args.workloads.split(","):
             w = WORKLOADS[name]
             for v in variants:
+                kind = g.gemm_f32_variant_info(v)["kind"]
+                if (kind == g.GEMM_F32_KIND_SKINNY) != (w.m <= 64):
+                    continue   # the few-row path and the tiled paths serve different shape classes
                 info, med, best = time_variant(g, torch, w, v, args.steps, args.warmup)
                 rec = {"workload": name, "variant": v, "name": info["name"], "kind": info["kind"],
                        "bm": info["bm"], "bn": info["bn"], "bk": info["bk"],
                        "waves": info["waves_m"] * info["waves_n"], "wave_tile": [info["wave_m"], info["wave_n"]],
                        "grid": info["grid"], "t_median_us": round(med * 1e6, 2), "t_min_us": round(best * 1e6, 2),
                        "tflops": round(pm.tflops(w.m, w.n, w.k, med), 2),
-                       "pct_peak": round(100 * pm.tflops(w.m, w.n, w.k, med) * 1e12 / pm.MI355X_FP32_MATRIX_PEAK, 2)}
+                       "pct_peak": round(100 * pm.tflops(w.m, w.n, w.k, med) * 1e12 / pm.MI355X_FP32_MATRIX_PEAK, 2),
+                       "hbm_gbs": round(pm.compulsory_bytes(w.m, w.n, w.k) / med / 1e9, 1)}
                 rec.update(resources_for(info, w.layout_b, res))
                 f.write(json.dumps(rec) + "\n")
                 f.flush()

@@ -25,8 +25,13 @@
  *  - Pointers A, B, C are device pointers (HIP device memory of the current
  *    device), owned by the caller.  C must not overlap A or B.
  *  - Sizes and leading dimensions are in elements (floats).
- *  - Plans hold host state only (no device memory); a plan is immutable after
- *    creation and may be used from several host threads and streams at once.
+ *  - A plan is immutable after creation.  Plans of the tiled kernels hold
+ *    host state only and may be used from several host threads and streams
+ *    at once.  Plans of the few-row path with more than one k-split
+ *    (gemm_f32_info.split_k > 1) own a device workspace for the partial sums
+ *    (split_k * m * n floats, allocated by create, freed by destroy): such a
+ *    plan must not run on two streams at the same time (the runs would share
+ *    the workspace); use one plan per stream.
  *  - Execution is asynchronous on the caller's stream; a device-side fault
  *    is reported by the caller's next synchronisation, not by gemm_f32_run.
  */
@@ -96,7 +101,8 @@ int gemm_f32_validate(int64_t m, int64_t n, int64_t k, int layout_b,
  *   out: receives the plan (set to NULL on failure); must be non-NULL.
  * Errors: GEMM_F32_ERR_INVALID_VALUE (see gemm_f32_validate, or out == NULL),
  *         GEMM_F32_ERR_NO_DEVICE, GEMM_F32_ERR_UNSUPPORTED_DEVICE,
- *         GEMM_F32_ERR_HIP, GEMM_F32_ERR_ALLOC.
+ *         GEMM_F32_ERR_HIP (including a failed workspace allocation),
+ *         GEMM_F32_ERR_ALLOC.
  * The environment variable GEMM_F32_VARIANT=<index> forces a variant.
  */
 int gemm_f32_create(gemm_f32_plan *out, int64_t m, int64_t n, int64_t k, int layout_b,
@@ -122,7 +128,8 @@ int gemm_f32_create_variant(gemm_f32_plan *out, int variant, int64_t m, int64_t 
  */
 int gemm_f32_run(gemm_f32_plan plan, const float *A, const float *B, float *C, void *stream);
 
-/* gemm_f32_destroy: release a plan.  NULL is a no-op returning SUCCESS. */
+/* gemm_f32_destroy: release a plan and its workspace (hipFree, which waits
+ * for the device).  NULL is a no-op returning SUCCESS. */
 int gemm_f32_destroy(gemm_f32_plan plan);
 
 /* gemm_f32_describe: copy the plan's choices into *info (both non-NULL). */
