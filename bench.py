@@ -30,11 +30,39 @@ if ROOT not in sys.path:
 HEADLINE = "sq4096"
 METRIC = "FP32 GEMM TFLOPS (2MNK/t) and % of MI355X FP32 matrix peak at 4096^3"
 
-# FETCH_SIZE / WRITE_SIZE of the GEMM kernel per launch (KiB), read with
-# rocprofv3 --pmc from the current kernels, and the factor that turns the
-# counters into bytes (measured on a plain copy kernel of known size).
-# None until measured for the kernel as it stands.
-TRAFFIC_COUNTERS = None
+# HBM traffic of the GEMM kernel per launch, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch) over
+#   bench.py --workload W --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy 512
+# scaled by what the same counters read for the 512 MiB elementwise copy in
+# that run (FETCH_SIZE 262161 KiB -> x2.000, WRITE_SIZE 524288 KiB -> x1.000).
+# Valid only for the kernel sources they were taken on: the entry carries the
+# SHA-1 of the tiled-kernel sources, and the field is null when they differ.
+TRAFFIC_SOURCES = ("device_common.hpp", "mfma_gemm.hpp", "mfma_dma_gemm.hpp")
+TRAFFIC_COUNTERS = {
+    "sq4096": {"kernel": "dma_256x128x16_w2x2_s3",
+               "sources_sha1": "0d235349fa155f3e4b9650462e4355cb6285dc14",
+               "fetch_kib": 271210.0, "write_kib": 65610.0,
+               "fetch_factor": 2.000, "write_factor": 1.000},
+}
+
+
+def kernel_sources_sha1():
+    import hashlib
+
+    h = hashlib.sha1()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "dense_gemm_optimisation_fp32_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_bytes(workload, kernel):
+    """Counter-derived HBM bytes per launch, or None when not measured for
+    this kernel as it stands."""
+    t = TRAFFIC_COUNTERS.get(workload)
+    if not t or t["kernel"] != kernel or t["sources_sha1"] != kernel_sources_sha1():
+        return None
+    return t["fetch_kib"] * 1024 * t["fetch_factor"] + t["write_kib"] * 1024 * t["write_factor"]
 
 
 def parse():
@@ -49,13 +77,15 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the baseline")
     p.add_argument("--all", action="store_true", help="also time every workload")
     p.add_argument("--all-out", default="gpurun_out/bench_all.jsonl")
+    p.add_argument("--rotate", type=int, default=1,
+                   help="cycle through this many operand sets (defeats the Infinity Cache for small workloads)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="first run one elementwise copy of MIB MiB (reads and writes MIB MiB), "
                         "the reference kernel for scaling the FETCH_SIZE/WRITE_SIZE counters")
     return p.parse_args()
 
 
-def time_workload(name, steps, warmup, variant=None):
+def time_workload(name, steps, warmup, variant=None, rotate=1):
     import numpy as np
     import torch
 
@@ -66,24 +96,29 @@ def time_workload(name, steps, warmup, variant=None):
     w = WORKLOADS[name]
     A, B = workload_operands(w)
     dev = torch.device("cuda", 0)
-    dA = torch.from_numpy(A).to(dev)
-    dB = torch.from_numpy(B).to(dev)
     lda = w.k
     ldb = w.n if w.layout_b == 0 else w.k
-    dC = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
+    # `rotate` distinct operand sets, used in turn, so that a workload smaller
+    # than the 256 MB Infinity Cache is still read from HBM at every step.
+    sets = []
+    for r in range(rotate):
+        dA = torch.from_numpy(A).to(dev)
+        dB = torch.from_numpy(B).to(dev)
+        dC = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
+        sets.append((dA, dB, dC))
+    ptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr()) for a, b, c in sets]
     plan = g.get_plan(w.m, w.n, w.k, w.layout_b, lda, ldb, w.n, variant, 0)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
-    a_ptr, b_ptr, c_ptr = dA.data_ptr(), dB.data_ptr(), dC.data_ptr()
 
-    for _ in range(warmup):
-        plan.run(a_ptr, b_ptr, c_ptr, sh)
+    for i in range(warmup):
+        plan.run(*ptrs[i % rotate], sh)
     torch.cuda.synchronize()
 
     # Timed region: exactly `steps` launches, wall clock bracketed by syncs.
     t0 = time.perf_counter()
-    for _ in range(steps):
-        plan.run(a_ptr, b_ptr, c_ptr, sh)
+    for i in range(steps):
+        plan.run(*ptrs[i % rotate], sh)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -92,11 +127,11 @@ def time_workload(name, steps, warmup, variant=None):
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for i in range(steps):
         starts[i].record(stream)
-        plan.run(a_ptr, b_ptr, c_ptr, sh)
+        plan.run(*ptrs[i % rotate], sh)
         ends[i].record(stream)
     torch.cuda.synchronize()
     durs = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) / 1e3
-    assert torch.isfinite(dC).all().item(), "non-finite output"
+    assert all(torch.isfinite(c).all().item() for _, _, c in sets), "non-finite output"
 
     flops = pm.gemm_flops(w.m, w.n, w.k)
     return {
@@ -159,7 +194,7 @@ def roofline(res):
         achieved = res["bytes"] / res["kernel_avg_s"] / 1e9
         out = {"bound": "hbm", "achieved": round(achieved, 1), "peak": pm.MI355X_HBM_BANDWIDTH / 1e9,
                "unit": "GB/s", "frac": round(achieved / (pm.MI355X_HBM_BANDWIDTH / 1e9), 4)}
-    out["traffic"] = TRAFFIC_COUNTERS.get(w.name) if TRAFFIC_COUNTERS else None
+    out["traffic"] = traffic_bytes(w.name, res["plan"]["name"])
     out["kernel"] = res["plan"]["name"]
     out["kernel_avg_us"] = round(res["kernel_avg_s"] * 1e6, 2)
     return out
@@ -189,7 +224,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    res = time_workload(args.workload, args.steps, args.warmup, args.variant)
+    res = time_workload(args.workload, args.steps, args.warmup, args.variant, args.rotate)
     w = res["workload"]
     line = {
         "metric": METRIC if w.name == HEADLINE else f"FP32 GEMM TFLOPS (2MNK/t), {w.name}",
@@ -206,6 +241,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: C=A.B, M={w.m} N={w.n} K={w.k}, A/C row-major, "
                                f"B {'row' if w.layout_b == 0 else 'column'}-major, {w.dist}, seed {w.seed}",
+                   "operand_sets": args.rotate,
                    "m": w.m, "n": w.n, "k": w.k, "layout_b": "row" if w.layout_b == 0 else "col",
                    "kernel": res["plan"]["name"], "grid": res["plan"]["grid"],
                    "pct_of_fp32_matrix_peak": round(100 * res["tflops"] / (pm.MI355X_FP32_MATRIX_PEAK / 1e12), 2)},
@@ -220,8 +256,10 @@ def main():
         os.makedirs(os.path.dirname(args.all_out) or ".", exist_ok=True)
         with open(args.all_out, "a") as f:
             for name in WORKLOADS:
-                r = time_workload(name, max(5, args.steps // 5), 3, args.variant)
+                r = time_workload(name, max(20, args.steps // 5), max(20, args.warmup // 5), None,
+                                  8 if name == "skinny" else 1)
                 rec = {"workload": name, "kernel": r["plan"]["name"], "grid": r["plan"]["grid"],
+                       "rotate": 8 if name == "skinny" else 1,
                        "tflops": round(r["tflops"], 3), "kernel_avg_us": round(r["kernel_avg_s"] * 1e6, 2),
                        "kernel_min_us": round(r["kernel_min_s"] * 1e6, 2),
                        "roofline": roofline(r)}

@@ -215,7 +215,7 @@ namespace {
 // every CU at least one workgroup (256 x 128 tiles run two per CU).
 int choose_variant(int64_t m, int64_t n, const DeviceFacts &f)
 {
-    if (m <= 32) return V_SKINNY_W8;
+    if (m <= 32) return V_SKINNY_W4;
     if (ceil_div(m, 256) * ceil_div(n, 128) >= f.cu_count) return V_DMA_256x128x16_S3;
     if (ceil_div(m, 128) * ceil_div(n, 128) >= f.cu_count) return V_DMA_128x128x16_S3;
     return V_DMA_64x64x16_S3;
@@ -274,10 +274,11 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     p->workspace = nullptr;
     p->reduce_grid = 0;
     if (d.kind == GEMM_F32_KIND_SKINNY) {
-        // Split k so that about two workgroups per CU are in flight; each
+        // Split k so that about four workgroups per CU are in flight; each
         // split is a whole number of 16-k groups.
         const int64_t per_split = (int64_t)a.tiles_m * a.tiles_n;
-        int64_t split = ceil_div(2 * (int64_t)facts.cu_count, per_split);
+        int64_t split = ceil_div(4 * (int64_t)facts.cu_count, per_split);
+        split = env_int("GEMM_F32_SPLIT_K", (int)split);   // tuning override
         split = split < 1 ? 1 : split;
         const int64_t max_split = ceil_div(k, 64);
         split = split > max_split ? max_split : split;

@@ -125,6 +125,34 @@ def test_run_to_run_bitwise_determinism(variant):
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
+def test_split_k_plan_reused_across_inputs():
+    """A few-row plan with k-splits keeps the previous run's partial sums in
+    its workspace: alternating inputs on one plan must give each input's own
+    result, bit for bit, every time."""
+    import dense_gemm_optimisation_fp32_amd as g
+    m, n, k = 16, 300, 2000
+    plan = g.gemm_f32_create(m, n, k, ROW_MAJOR, k, n, n)
+    try:
+        info = g.gemm_f32_describe(plan)
+        assert info["kind"] == g.GEMM_F32_KIND_SKINNY and info["split_k"] > 1
+        sets = [random_operands(m, n, k, ROW_MAJOR, "normal1", seed=50 + i) for i in range(2)]
+        dev = [(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()) for A, B in sets]
+        refs = [oracle.gemm_f64(A, B, m, n, k, ROW_MAJOR) for A, B in sets]
+        first = [None, None]
+        stream = torch.cuda.current_stream().cuda_stream
+        for it in range(6):
+            i = it % 2
+            C = torch.full((m, n), -1.0, device="cuda")
+            g.gemm_f32_run(plan, dev[i][0].data_ptr(), dev[i][1].data_ptr(), C.data_ptr(), stream)
+            out = C.cpu().numpy()
+            check_close(out, refs[i][0], refs[i][1], f"run {it}")
+            if first[i] is None:
+                first[i] = out
+            assert np.array_equal(out, first[i])
+    finally:
+        g.gemm_f32_destroy(plan)
+
+
 # ---------------------------------------------------------------------------
 # Full workload shapes, in the plan the benchmark times (gemm_f32_create).
 # ---------------------------------------------------------------------------
