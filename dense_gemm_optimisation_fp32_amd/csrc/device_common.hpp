@@ -35,7 +35,9 @@ struct GemmArgs {
     int group_m;           // tile-rows per rasterisation group
     int num_xcd;           // dispatch round-robins workgroups over this many XCDs
     uint32_t a_bytes, b_bytes, c_bytes;
-    float *partial;        // split-k partial sums (skinny path), else unused
+    unsigned long long *partial;  // split-k partial sums, epoch-tagged (skinny path)
+    unsigned *arrivals;           // per-tile arrival counters (skinny path)
+    unsigned epoch;               // tag of this run's partial sums, never 0
     int split_k;           // number of k-splits (skinny path), else 1
     int k_per_split;       // k values per split (multiple of the k tile)
     int masked_loads;      // 1: check every element in every slab (tiny ldb)
@@ -84,14 +86,18 @@ __device__ __forceinline__ uint32_t elem_off(bool valid, uint32_t row, uint32_t 
 // time reuse a few A row-panels and B column-panels instead of one full
 // row of tiles ("GEMM 性能优化", Wave 模型与 L2 命中率: the block order alone
 // changes the L2 hit rate).  Runs once per workgroup.
+__device__ __forceinline__ int xcd_contiguous(int wg, int total, int num_xcd)
+{
+    const int x = wg % num_xcd;
+    const int i = wg / num_xcd;
+    const int per = total / num_xcd;
+    const int rem = total % num_xcd;
+    return x * per + (x < rem ? x : rem) + i;
+}
+
 __device__ __forceinline__ void raster_tile(int wg, const GemmArgs &a, int &tm, int &tn)
 {
-    const int total = a.tiles_m * a.tiles_n;
-    const int x = wg % a.num_xcd;
-    const int i = wg / a.num_xcd;
-    const int per = total / a.num_xcd;
-    const int rem = total % a.num_xcd;
-    const int logical = x * per + (x < rem ? x : rem) + i;
+    const int logical = xcd_contiguous(wg, a.tiles_m * a.tiles_n, a.num_xcd);
 
     const int width = a.group_m * a.tiles_n;
     const int group = logical / width;

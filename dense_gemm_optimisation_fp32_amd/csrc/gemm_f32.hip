@@ -93,9 +93,11 @@ enum VariantId {
     V_DMA_128x128x16_S3,
     V_DMA_128x128x32_S3,
     V_DMA_256x128x16_S3,
-    V_SKINNY_W4,
-    V_SKINNY_W8,
+    V_SKINNY_W4_D4,
+    V_SKINNY_W8_D4,
     V_DMA_64x64x16_S3,
+    V_SKINNY_W16_D4,
+    V_SKINNY16_W16_D4,
     V_COUNT
 };
 
@@ -103,6 +105,7 @@ const VariantDesc &variant(int v)
 {
     using gemmf32::DmaTile;
     using gemmf32::MfmaTile;
+    using gemmf32::SkinnyTile;
     static const VariantDesc table[V_COUNT] = {
         mfma_variant<MfmaTile<256, 256, 16, 2, 2>>("mfma_256x256x16_w2x2_32x32x2"),
         mfma_variant<MfmaTile<128, 128, 16, 2, 2>>("mfma_128x128x16_w2x2_32x32x2"),
@@ -117,9 +120,11 @@ const VariantDesc &variant(int v)
         dma_variant<DmaTile<128, 128, 16, 2, 2, 3>>("dma_128x128x16_w2x2_s3"),
         dma_variant<DmaTile<128, 128, 32, 2, 2, 3>>("dma_128x128x32_w2x2_s3"),
         dma_variant<DmaTile<256, 128, 16, 2, 2, 3>>("dma_256x128x16_w2x2_s3"),
-        skinny_variant<gemmf32::SkinnyTile<4>>("skinny_16x64_splitk_w4"),
-        skinny_variant<gemmf32::SkinnyTile<8>>("skinny_16x64_splitk_w8"),
+        skinny_variant<SkinnyTile<4, 4, 64>>("skinny_16x64_w4_d4"),
+        skinny_variant<SkinnyTile<8, 4, 64>>("skinny_16x64_w8_d4"),
         dma_variant<DmaTile<64, 64, 16, 2, 2, 3>>("dma_64x64x16_w2x2_s3"),
+        skinny_variant<SkinnyTile<16, 4, 64>>("skinny_16x64_w16_d4"),
+        skinny_variant<SkinnyTile<16, 4, 16>>("skinny_16x16_w16_d4"),
     };
     return table[v];
 }
@@ -204,8 +209,8 @@ struct gemm_f32_plan_impl {
     GemmArgs args;       // pointers filled at run time
     unsigned grid;
     unsigned block;
-    float *workspace;    // split-k partial sums (few-row path), else NULL
-    unsigned reduce_grid;
+    void *workspace;     // split-k partial sums and arrival counters (few-row path), else NULL
+    std::atomic<unsigned> runs{0};   // epochs handed out so far
 };
 
 namespace {
@@ -215,7 +220,7 @@ namespace {
 // every CU at least one workgroup (256 x 128 tiles run two per CU).
 int choose_variant(int64_t m, int64_t n, const DeviceFacts &f)
 {
-    if (m <= 32) return V_SKINNY_W4;
+    if (m <= 32) return V_SKINNY_W16_D4;
     if (ceil_div(m, 256) * ceil_div(n, 128) >= f.cu_count) return V_DMA_256x128x16_S3;
     if (ceil_div(m, 128) * ceil_div(n, 128) >= f.cu_count) return V_DMA_128x128x16_S3;
     return V_DMA_64x64x16_S3;
@@ -272,12 +277,11 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     p->grid = (unsigned)((int64_t)a.tiles_m * a.tiles_n);
     p->block = (unsigned)d.threads;
     p->workspace = nullptr;
-    p->reduce_grid = 0;
     if (d.kind == GEMM_F32_KIND_SKINNY) {
-        // Split k so that about four workgroups per CU are in flight; each
-        // split is a whole number of 16-k groups.
+        // Split k across workgroups until about 16 wavefronts per CU are in
+        // flight; each split is a whole number of 16-k groups.
         const int64_t per_split = (int64_t)a.tiles_m * a.tiles_n;
-        int64_t split = ceil_div(4 * (int64_t)facts.cu_count, per_split);
+        int64_t split = ceil_div(16 * (int64_t)facts.cu_count, per_split * (d.threads / 64));
         split = env_int("GEMM_F32_SPLIT_K", (int)split);   // tuning override
         split = split < 1 ? 1 : split;
         const int64_t max_split = ceil_div(k, 64);
@@ -288,14 +292,20 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
         a.k_per_split = (int)kps;
         p->grid = (unsigned)(per_split * split);
         if (split > 1) {
-            const size_t bytes = (size_t)split * (size_t)m * (size_t)n * sizeof(float);
-            hipError_t e = hipMalloc(reinterpret_cast<void **>(&p->workspace), bytes);
+            // split * m * n tagged words, then one arrival counter per tile;
+            // all zero, so no stale word carries a valid (non-zero) epoch.
+            const size_t words = (size_t)split * (size_t)m * (size_t)n * sizeof(unsigned long long);
+            const size_t bytes = words + (size_t)per_split * sizeof(unsigned);
+            hipError_t e = hipMalloc(&p->workspace, bytes);
+            if (e == hipSuccess) e = hipMemsetAsync(p->workspace, 0, bytes, nullptr);
+            if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
             if (e != hipSuccess) {
+                if (p->workspace) (void)hipFree(p->workspace);
                 delete p;
                 return hip_fail(e);
             }
-            a.partial = p->workspace;
-            p->reduce_grid = (unsigned)ceil_div(m * n, 256);
+            a.partial = static_cast<unsigned long long *>(p->workspace);
+            a.arrivals = reinterpret_cast<unsigned *>(static_cast<char *>(p->workspace) + words);
         }
     }
 
@@ -377,13 +387,14 @@ int gemm_f32_run(gemm_f32_plan p, const float *A, const float *B, float *C, void
     const void *fn = d.fn[p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0];
     void *kargs[] = {&a};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (p->workspace) {
+        // A fresh, non-zero tag for this run's split-k partial sums.
+        unsigned ep = ++p->runs;
+        if (ep == 0) ep = ++p->runs;
+        a.epoch = ep;
+    }
     hipError_t e = hipLaunchKernel(fn, dim3(p->grid), dim3(p->block), kargs, 0, s);
     if (e != hipSuccess) return hip_fail(e);
-    if (p->reduce_grid) {
-        e = hipLaunchKernel(reinterpret_cast<const void *>(&gemmf32::gemm_skinny_reduce_kernel),
-                            dim3(p->reduce_grid), dim3(256), kargs, 0, s);
-        if (e != hipSuccess) return hip_fail(e);
-    }
     return GEMM_F32_SUCCESS;
 }
 

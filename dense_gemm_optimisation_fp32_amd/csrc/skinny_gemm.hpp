@@ -5,114 +5,143 @@
 // the kernel is bandwidth-limited), so the goal is to stream B from HBM once
 // at full bandwidth.  Every element of B is used by all M rows in a single
 // v_mfma_f32_16x16x4_f32 and never again, so B goes straight from HBM into
-// MFMA operand registers (no LDS), and the work is split along k so that
-// enough wavefronts keep enough loads in flight ("GPU 算子优化中的数据复用",
+// MFMA operand registers (no LDS), and enough wavefronts with enough loads
+// each stay in flight to cover the memory latency ("GPU 算子优化中的数据复用",
 // 11.1: memory-bound kernels need parallelism to hide latency; "PMPP Chapter
 // 06", section 2: many concurrent requests).
 //
 // MFMA 16x16x4 (f32): lane l supplies A[i = l%16][kk = l/16] and
 // B[kk = l/16][j = l%16]; the 16x16 result sits as 4 values per lane at row
 // 4*(l/16) + v, column l%16.  Lane group h = l/16 walks the k-run
-// kq + 4h + t (t = 0..3) of each 16-k block, so one 16-byte load of A gives a
-// lane its A values for 4 k-steps.  A wavefront covers 64 columns as 4 MFMA
-// blocks with interleaved columns (lane column j stands for column 4*j + nb
-// in block nb), so one 16-byte load of row-major B feeds all 4 blocks of a
-// k-step; column-major B is loaded as 16 bytes along k of one column (4
-// k-steps of one block).
+// kq + 4h + t (t = 0..3) of each 16-k group, so one 16-byte load of A gives a
+// lane its A values for 4 k-steps.
 //
-// Split-k: a workgroup of WAVES wavefronts owns 16 rows x 64 columns x one
-// k-split; each wavefront takes a contiguous share of the split, the shares
-// are added in LDS in wavefront order, and the split's partial sums go to the
-// plan's workspace (or straight to C when there is one split).  A second
-// kernel adds the splits in split order.  Both orders are fixed, so results
-// are reproducible run to run.  (Splitting k over workgroups is the
-// partial-result-then-merge pattern the checklist of "PMPP Chapter 06",
-// section 4, calls privatization.)
+// Tile widths.  BN = 64: four MFMA blocks with interleaved columns (lane
+// column j stands for column 4*j + nb of block nb), so one 16-byte load of
+// row-major B feeds all 4 blocks of a k-step; column-major B is loaded as 16
+// bytes along k of one column.  BN = 16: one block; row-major B is loaded one
+// element per k-step (16 lanes still read 64 contiguous bytes of a row),
+// column-major B as 16 bytes along k.  The narrow tile gives N/16 workgroups,
+// enough to cover the CUs without splitting k across workgroups.
+//
+// Within a workgroup the WAVES wavefronts take contiguous shares of the
+// workgroup's k-range, and the shares are added in LDS in wavefront order.
+// When k is also split across workgroups, each split's partial sums go to
+// the plan's workspace and the last workgroup of a tile to finish adds the
+// splits in split order.  Both orders are fixed, so results are
+// reproducible run to run.  (Splitting
+// k is the partial-result-then-merge pattern the checklist of "PMPP Chapter
+// 06", section 4, calls privatization.)
 #pragma once
 
 #include "device_common.hpp"
 
 namespace gemmf32 {
 
-template <int WAVES_>
+template <int WAVES_, int DEPTH_, int BN_>
 struct SkinnyTile {
+    static_assert(BN_ == 16 || BN_ == 64, "one MFMA block or four interleaved ones");
     static constexpr int WAVES = WAVES_;
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int BM = 16, BN = 64, KQ = 16;   // rows, columns, k per load group
-    static constexpr int UNROLL = 4;                  // k groups in flight per wavefront
+    static constexpr int BM = 16, BN = BN_, KQ = 16;  // rows, columns, k per load group
+    static constexpr int NB = BN / 16;                // MFMA blocks per tile
+    static constexpr int DEPTH = DEPTH_;              // k groups in flight per wavefront
 };
 
 // Loads of one 16-k group for lane (j, h): A[row][kq+4h .. +3] and the B
-// values of the 4 k-steps x 4 blocks.  Element checks only when the group is
-// not whole (tail of a split, or k past K).
-template <bool B_COL>
+// values of the 4 k-steps.  NB = 4: b[t][nb] (row-major B) or b[nb][t]
+// (column-major B) is column 4j + nb; NB = 1: b[0][t] is column j.  Element
+// checks only when the group is not whole (tail of a range, or k past K).
+// Columns at or past N may read other elements of B: they only feed columns
+// of C that are never stored.
+template <class T, bool B_COL>
 __device__ __forceinline__ void skinny_load(const GemmArgs &g, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                             int row, int col0, int j, int h, int kq, int kend, bool whole,
-                                            f32x4 &a, f32x4 (&b)[4])
+                                            bool live, f32x4 &a, f32x4 (&b)[T::NB])
 {
     const int ka = kq + 4 * h;
     if (whole) {
-        a = buf_load_x4(ra, elem_off(row < g.m, row, g.lda, ka));
-        if constexpr (!B_COL) {
+        // A group that is not live reads zeros (out-of-range offsets).
+        a = buf_load_x4(ra, elem_off(live && row < g.m, row, g.lda, ka));
+        if constexpr (T::NB == 4 && !B_COL) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                b[t] = buf_load_x4(rb, (uint32_t)((ka + t) * g.ldb + col0 + 4 * j) * 4u);
-        } else {
+            for (int t = 0; t < 4; ++t) b[t] = buf_load_x4(rb, elem_off(live, ka + t, g.ldb, col0 + 4 * j));
+        } else if constexpr (T::NB == 4) {
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
                 const int col = col0 + 4 * j + nb;
-                b[nb] = buf_load_x4(rb, elem_off(col < g.n, col, g.ldb, ka));
+                b[nb] = buf_load_x4(rb, elem_off(live && col < g.n, col, g.ldb, ka));
             }
+        } else if constexpr (!B_COL) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) b[0][t] = buf_load_x1(rb, elem_off(live, ka + t, g.ldb, col0 + j));
+        } else {
+            b[0] = buf_load_x4(rb, elem_off(live && col0 + j < g.n, col0 + j, g.ldb, ka));
         }
     } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) a[q] = buf_load_x1(ra, elem_off(row < g.m && ka + q < kend, row, g.lda, ka + q));
-        if constexpr (!B_COL) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+        for (int x = 0; x < T::NB; ++x)
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    const int col = col0 + 4 * j + nb;
-                    b[t][nb] = buf_load_x1(rb, elem_off(ka + t < kend && col < g.n, ka + t, g.ldb, col));
-                }
-        } else {
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int col = col0 + 4 * j + nb;
-                    b[nb][q] = buf_load_x1(rb, elem_off(col < g.n && ka + q < kend, col, g.ldb, ka + q));
-                }
-        }
+            for (int q = 0; q < 4; ++q) {
+                // (x, q) = (block, k-step) for column-major B and NB = 1;
+                // (k-step, block) for row-major B with NB = 4.
+                const int kk = (T::NB == 4 && !B_COL) ? x : q;
+                const int nb = (T::NB == 4 && !B_COL) ? q : x;
+                const int col = col0 + T::NB * j + nb;
+                const bool ok = ka + kk < kend && col < g.n;
+                b[x][q] = buf_load_x1(rb, B_COL ? elem_off(ok, col, g.ldb, ka + kk) : elem_off(ok, ka + kk, g.ldb, col));
+            }
     }
 }
 
-template <bool B_COL>
-__device__ __forceinline__ void skinny_mfma(const f32x4 &a, const f32x4 (&b)[4], f32x4 (&acc)[4])
+template <class T, bool B_COL>
+__device__ __forceinline__ void skinny_mfma(const f32x4 &a, const f32x4 (&b)[T::NB], f32x4 (&acc)[T::NB])
 {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const float bv = B_COL ? b[nb][t] : b[t][nb];
+        for (int nb = 0; nb < T::NB; ++nb) {
+            const float bv = (T::NB == 4 && !B_COL) ? b[t][nb] : b[nb][t];
             acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], bv, acc[nb], 0, 0, 0);
         }
 }
 
-// Grid: tiles_m * tiles_n * split_k workgroups.  Writes the split's partial
-// sums to g.partial[split][m][n] (row stride n), or C when split_k == 1.
+// Value of a split's 64-bit partial-sum word once it carries this run's
+// epoch.  The writer has already issued the word when the reader gets here,
+// so the wait ends; the bound only keeps a lost word from hanging the
+// kernel, and then the element reads as NaN.
+__device__ __forceinline__ float skinny_wait_word(const unsigned long long *p, unsigned long long w, unsigned epoch)
+{
+    constexpr int kSpinLimit = 1 << 20;
+    for (int i = 0; (unsigned)(w >> 32) != epoch; ++i) {
+        if (i == kSpinLimit) return __builtin_nanf("");
+        __builtin_amdgcn_s_sleep(1);
+        w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return __uint_as_float((unsigned)w);
+}
+
+// Grid: tiles_m * tiles_n * split_k workgroups.  With one split the
+// workgroup writes its tile of C; otherwise the splits meet through
+// g.partial[split][m][n] (epoch-tagged words) and g.arrivals[tile].
 template <class T, bool B_COL>
 __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
 {
     __shared__ float red[T::WAVES][T::BM * T::BN];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, h = lane >> 4;
 
+    // Workgroups on one XCD take neighbouring tiles of one split, so they
+    // share that XCD's L2 for A and for the cache lines of B that straddle
+    // two tiles.
     const int per_split = g.tiles_m * g.tiles_n;
-    const int split = blockIdx.x / per_split;
-    const int rest = blockIdx.x - split * per_split;
+    const int wg = xcd_contiguous(blockIdx.x, per_split * g.split_k, g.num_xcd);
+    const int split = wg / per_split;
+    const int rest = wg - split * per_split;
     const int tm = rest / g.tiles_n, tn = rest - (rest / g.tiles_n) * g.tiles_n;
     const int row0 = tm * T::BM, col0 = tn * T::BN;
 
@@ -129,69 +158,132 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, g.b_bytes);
 
     const int row = row0 + j;    // A row this lane supplies
-    f32x4 acc[4];
+    f32x4 acc[T::NB];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < T::NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    int kq = kw0;
-    // Whole groups, UNROLL at a time so that UNROLL * 5 loads are in flight.
-    for (; kq + T::UNROLL * T::KQ <= kw1; kq += T::UNROLL * T::KQ) {
-        f32x4 a[T::UNROLL];
-        f32x4 b[T::UNROLL][4];
+    // Whole 16-k groups stream through a ring of DEPTH register slots: the
+    // loads of group q + DEPTH are issued as soon as group q has been
+    // multiplied, so DEPTH groups (5 * DEPTH loads) stay in flight.  The ring
+    // runs a whole number of passes; the groups past the range load zeros,
+    // so every load is unconditional and in group order, and the counter
+    // wait before each group's MFMAs lets the DEPTH - 1 later groups fly.
+    constexpr int D = T::DEPTH;
+    const int kspan = max(0, kw1 - kw0);
+    const int G = kspan / T::KQ;
+    const int passes = (G + D - 1) / D;
+    if (passes > 0) {
+        f32x4 a[D], b[D][T::NB];
 #pragma unroll
-        for (int u = 0; u < T::UNROLL; ++u)
-            skinny_load<B_COL>(g, ra, rb, row, col0, j, h, kq + u * T::KQ, kw1, true, a[u], b[u]);
+        for (int u = 0; u < D; ++u) {
+            skinny_load<T, B_COL>(g, ra, rb, row, col0, j, h, kw0 + u * T::KQ, kw1, true, u < G, a[u], b[u]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int p = 1; p < passes; ++p) {
 #pragma unroll
-        for (int u = 0; u < T::UNROLL; ++u) skinny_mfma<B_COL>(a[u], b[u], acc);
+            for (int u = 0; u < D; ++u) {
+                const int q = p * D + u;
+                skinny_mfma<T, B_COL>(a[u], b[u], acc);
+                __builtin_amdgcn_sched_barrier(0);
+                skinny_load<T, B_COL>(g, ra, rb, row, col0, j, h, kw0 + q * T::KQ, kw1, true, q < G, a[u], b[u]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < D; ++u) skinny_mfma<T, B_COL>(a[u], b[u], acc);
     }
-    for (; kq < kw1; kq += T::KQ) {
-        f32x4 a, b[4];
-        skinny_load<B_COL>(g, ra, rb, row, col0, j, h, kq, kw1, kq + T::KQ <= kw1, a, b);
-        skinny_mfma<B_COL>(a, b, acc);
+    // The partial group at the end of the range, element by element.
+    if (G * T::KQ < kspan) {
+        f32x4 at, bt[T::NB];
+        skinny_load<T, B_COL>(g, ra, rb, row, col0, j, h, kw0 + G * T::KQ, kw1, false, true, at, bt);
+        skinny_mfma<T, B_COL>(at, bt, acc);
     }
 
     // Add the wavefronts' shares in wavefront order.  Element (r, c) of the
-    // 16 x 64 tile: r = 4*h + v, c = 4*j + nb.
+    // 16 x BN tile: r = 4*h + v, c = NB*j + nb.
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < T::NB; ++nb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[wave][(4 * h + v) * T::BN + 4 * j + nb] = acc[nb][v];
+        for (int v = 0; v < 4; ++v) red[wave][(4 * h + v) * T::BN + T::NB * j + nb] = acc[nb][v];
     __syncthreads();
-    float *out = g.split_k > 1 ? g.partial + (size_t)split * g.m * g.n : g.C;
-    const int ld = g.split_k > 1 ? g.n : g.ldc;
-    for (int e = tid; e < T::BM * T::BN; e += T::THREADS) {
-        float s = red[0][e];
-#pragma unroll
-        for (int w = 1; w < T::WAVES; ++w) s += red[w][e];
-        const int r = row0 + e / T::BN, c = col0 + e % T::BN;
-        if (r < g.m && c < g.n) out[(size_t)r * ld + c] = s;
-    }
-}
 
-// C[i][j] = sum over splits s = 0, 1, ... of partial[s][i][j], in that
-// order.  The loads of up to 8 splits are issued together before they are
-// added, so the kernel pays one memory latency per 8 splits, not per split.
-// (Folding this into the split kernel with a last-arriver counter needs
-// device-scope release/acquire fences, which write back and invalidate an
-// XCD's L2 under all the other workgroups' streaming loads; measured 2-3x
-// slower than this second launch.)
-__global__ __launch_bounds__(256) void gemm_skinny_reduce_kernel(GemmArgs g)
-{
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= g.m * g.n) return;
-    const int r = idx / g.n, c = idx - (idx / g.n) * g.n;
-    const size_t plane = (size_t)g.m * g.n;
-    const float *p = g.partial + idx;
-    float s = p[0];
-    for (int s0 = 1; s0 < g.split_k; s0 += 8) {
-        float v[8];
+    constexpr int ELEMS = T::BM * T::BN;
+    constexpr int EPT = (ELEMS + T::THREADS - 1) / T::THREADS;   // elements per thread
+    float own[EPT];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = s0 + u < g.split_k ? p[(size_t)(s0 + u) * plane] : 0.0f;
+    for (int q = 0; q < EPT; ++q) {
+        const int e = tid + q * T::THREADS;
+        float s = 0.0f;
+        if (e < ELEMS) {
+            s = red[0][e];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (s0 + u < g.split_k) s += v[u];
+            for (int w = 1; w < T::WAVES; ++w) s += red[w][e];
+        }
+        own[q] = s;
     }
-    g.C[(size_t)r * g.ldc + c] = s;
+    if (g.split_k == 1) {
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) {
+            const int e = tid + q * T::THREADS;
+            const int r = row0 + e / T::BN, c = col0 + e % T::BN;
+            if (e < ELEMS && r < g.m && c < g.n) g.C[(size_t)r * g.ldc + c] = own[q];
+        }
+        return;
+    }
+
+    // k is split across workgroups.  Each split publishes its partial sums
+    // as 64-bit words {value, epoch}, written whole, so a reader that sees
+    // this run's epoch in a word also sees the value beside it; no fence
+    // orders these words against the arrival counter.  The last workgroup
+    // of a tile to arrive adds the splits in split order and writes C.
+    const size_t plane = (size_t)g.m * g.n;
+    const unsigned long long tag = (unsigned long long)g.epoch << 32;
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const int e = tid + q * T::THREADS;
+        const int r = row0 + e / T::BN, c = col0 + e % T::BN;
+        if (e < ELEMS && r < g.m && c < g.n)
+            __hip_atomic_store(g.partial + split * plane + (size_t)r * g.n + c, tag | __float_as_uint(own[q]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __shared__ int last;
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned before =
+            __hip_atomic_fetch_add(g.arrivals + rest, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = before == (unsigned)(g.split_k - 1);
+        // Every other split of this tile has counted itself in: reset the
+        // counter for the next run.
+        if (last) __hip_atomic_store(g.arrivals + rest, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last) return;
+
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const int e = tid + q * T::THREADS;
+        const int r = row0 + e / T::BN, c = col0 + e % T::BN;
+        if (!(e < ELEMS && r < g.m && c < g.n)) continue;
+        const unsigned long long *p = g.partial + (size_t)r * g.n + c;
+        float sum = 0.0f;
+        // The words of up to 8 splits are loaded together, then checked.
+        for (int s0 = 0; s0 < g.split_k; s0 += 8) {
+            unsigned long long w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                w[u] = (s0 + u < g.split_k && s0 + u != split)
+                           ? __hip_atomic_load(p + (s0 + u) * plane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : tag;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int sp = s0 + u;
+                if (sp >= g.split_k) break;
+                const float v = sp == split ? own[q] : skinny_wait_word(p + sp * plane, w[u], g.epoch);
+                sum = sp == 0 ? v : sum + v;
+            }
+        }
+        g.C[(size_t)r * g.ldc + c] = sum;
+    }
 }
 
 }  // namespace gemmf32

@@ -124,11 +124,11 @@ def boundary_tiles(extent: int, tile: int):
 # --- gfx950 occupancy ---------------------------------------------------------
 
 def gfx950_waves_per_simd_from_regs(vgprs: int, agprs: int) -> int:
-    """Waves per SIMD allowed by the unified register file: architectural VGPRs
-    are allocated in granules of 8 and the accumulation registers follow them
-    (an allocation of at most 512 per lane)."""
-    arch = int(math.ceil(max(vgprs, 1) / 8) * 8)
-    total = arch + agprs if agprs else arch
+    """Waves per SIMD allowed by the unified register file: the accumulation
+    registers start at the first multiple of 4 after the architectural VGPRs,
+    and the whole allocation comes in granules of 8 (at most 512 per lane)."""
+    arch = max(vgprs, 1)
+    total = int(math.ceil(arch / 4) * 4) + agprs if agprs else arch
     total = int(math.ceil(total / 8) * 8)
     return max(0, min(MI355X_MAX_WAVES_PER_SIMD, MI355X_REGS_PER_SIMD_LANE // total))
 

@@ -17,7 +17,7 @@
  * float32 accumulation; the order of the k-sum is the library's (blocked
  * along k, as the block-matrix identity of "GEMM 性能优化" 台阶 1 allows)
  * and is fixed for a given plan: the same plan on the same inputs gives
- * bitwise identical results run after run (no atomics).
+ * bitwise identical results run after run (no floating-point atomics).
  *
  * Conventions for every entry point:
  *  - Return value: a gemm_f32_status code.  Nothing here throws, prints or
@@ -28,10 +28,13 @@
  *  - A plan is immutable after creation.  Plans of the tiled kernels hold
  *    host state only and may be used from several host threads and streams
  *    at once.  Plans of the few-row path with more than one k-split
- *    (gemm_f32_info.split_k > 1) own a device workspace for the partial sums
- *    (split_k * m * n floats, allocated by create, freed by destroy): such a
- *    plan must not run on two streams at the same time (the runs would share
- *    the workspace); use one plan per stream.
+ *    (gemm_f32_info.split_k > 1) own a device workspace: split_k * m * n
+ *    partial sums as 8-byte words tagged with a per-run epoch, and one
+ *    32-bit arrival counter per output tile (zeroed by create, freed by
+ *    destroy).  Each run takes a new epoch from the plan (an atomic counter,
+ *    so runs may be enqueued from several host threads), but two runs of such
+ *    a plan must not execute at the same time on the device (they would share
+ *    the workspace): use one plan per stream, or order the streams.
  *  - Execution is asynchronous on the caller's stream; a device-side fault
  *    is reported by the caller's next synchronisation, not by gemm_f32_run.
  */

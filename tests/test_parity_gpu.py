@@ -153,6 +153,36 @@ def test_split_k_plan_reused_across_inputs():
         g.gemm_f32_destroy(plan)
 
 
+@pytest.mark.parametrize("split", [2, 3, 7, 16])
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+def test_split_k_counts_forced(split, layout_b, monkeypatch):
+    """Few-row plans with a forced number of k-splits (the splits meet in the
+    last workgroup of each tile): every run matches the oracle and repeats
+    bit for bit, including runs after the arrival counters were reset."""
+    import dense_gemm_optimisation_fp32_amd as g
+    monkeypatch.setenv("GEMM_F32_SPLIT_K", str(split))
+    m, n, k = 20, 130, 999
+    print(f"\n[case] forced split={split} layout_b={layout_b}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=60 + split)
+    ldb = n if layout_b == ROW_MAJOR else k
+    plan = g.gemm_f32_create(m, n, k, layout_b, k, ldb, n)
+    try:
+        info = g.gemm_f32_describe(plan)
+        assert info["kind"] == g.GEMM_F32_KIND_SKINNY and info["split_k"] == split
+        dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+        stream = torch.cuda.current_stream().cuda_stream
+        outs = []
+        for _ in range(5):
+            C = torch.full((m, n), float("nan"), device="cuda")
+            g.gemm_f32_run(plan, dA.data_ptr(), dB.data_ptr(), C.data_ptr(), stream)
+            outs.append(C.cpu().numpy())
+        check_close(outs[0], Cref, S, f"split {split}")
+        assert all(np.array_equal(outs[0], o) for o in outs[1:])
+    finally:
+        g.gemm_f32_destroy(plan)
+
+
 # ---------------------------------------------------------------------------
 # Full workload shapes, in the plan the benchmark times (gemm_f32_create).
 # ---------------------------------------------------------------------------
