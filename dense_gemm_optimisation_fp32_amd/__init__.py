@@ -48,7 +48,8 @@ class gemm_f32_info(ctypes.Structure):
         ("waves_m", ctypes.c_int), ("waves_n", ctypes.c_int),
         ("wave_m", ctypes.c_int), ("wave_n", ctypes.c_int),
         ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int), ("stages", ctypes.c_int),
-        ("split_k", ctypes.c_int), ("aligned", ctypes.c_int),
+        ("split_k", ctypes.c_int), ("stream_k", ctypes.c_int),
+        ("stream_k_tiles", ctypes.c_int), ("aligned", ctypes.c_int),
         ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("k_tiles", ctypes.c_int64),
         ("grid", ctypes.c_int64), ("group_m", ctypes.c_int), ("name", ctypes.c_char * 64),
     ]

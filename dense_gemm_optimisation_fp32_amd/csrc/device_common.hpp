@@ -35,9 +35,11 @@ struct GemmArgs {
     int group_m;           // tile-rows per rasterisation group
     int num_xcd;           // dispatch round-robins workgroups over this many XCDs
     uint32_t a_bytes, b_bytes, c_bytes;
-    unsigned long long *partial;  // split-k partial sums, epoch-tagged (skinny path)
-    unsigned *arrivals;           // per-tile arrival counters (skinny path)
+    unsigned long long *partial;  // partial sums of split tiles, epoch-tagged words
+    unsigned *arrivals;           // per-tile arrival counters for split tiles
     unsigned epoch;               // tag of this run's partial sums, never 0
+    int sk_wgs;            // stream-K: workgroups sharing the first sk_tiles tiles' slabs (0: none)
+    int sk_tiles;          // stream-K: tiles [0, sk_tiles) are shared; the rest get a workgroup each
     int split_k;           // number of k-splits (skinny path), else 1
     int k_per_split;       // k values per split (multiple of the k tile)
     int masked_loads;      // 1: check every element in every slab (tiny ldb)
@@ -95,10 +97,8 @@ __device__ __forceinline__ int xcd_contiguous(int wg, int total, int num_xcd)
     return x * per + (x < rem ? x : rem) + i;
 }
 
-__device__ __forceinline__ void raster_tile(int wg, const GemmArgs &a, int &tm, int &tn)
+__device__ __forceinline__ void grouped_tile(int logical, const GemmArgs &a, int &tm, int &tn)
 {
-    const int logical = xcd_contiguous(wg, a.tiles_m * a.tiles_n, a.num_xcd);
-
     const int width = a.group_m * a.tiles_n;
     const int group = logical / width;
     const int first_m = group * a.group_m;
@@ -107,6 +107,42 @@ __device__ __forceinline__ void raster_tile(int wg, const GemmArgs &a, int &tm, 
     const int r = logical - group * width;
     tm = first_m + r % gsize;
     tn = r / gsize;
+}
+
+__device__ __forceinline__ void raster_tile(int wg, const GemmArgs &a, int &tm, int &tn)
+{
+    grouped_tile(xcd_contiguous(wg, a.tiles_m * a.tiles_n, a.num_xcd), a, tm, tn);
+}
+
+// Value of a 64-bit partial-sum word {float bits, epoch} written by another
+// workgroup, once it carries this run's epoch.  `w` is a first load already
+// in hand.  The writer has issued the word before the reader can get here,
+// so the wait ends; `budget` (polls left for the caller, shared by all its
+// waits) only keeps a lost word from hanging the kernel: once it is spent,
+// missing elements read as NaN at once.
+constexpr int kTaggedWaitBudget = 1 << 16;
+
+__device__ __forceinline__ float wait_tagged_word(const unsigned long long *p, unsigned long long w, unsigned epoch,
+                                                  int &budget)
+{
+    while ((unsigned)(w >> 32) != epoch) {
+        if (budget <= 0) return __builtin_nanf("");
+        --budget;
+        __builtin_amdgcn_s_sleep(1);
+        w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return __uint_as_float((unsigned)w);
+}
+
+__device__ __forceinline__ unsigned long long load_tagged_word(const unsigned long long *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_tagged_word(unsigned long long *p, float v, unsigned epoch)
+{
+    __hip_atomic_store(p, ((unsigned long long)epoch << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace gemmf32

@@ -3,6 +3,7 @@
 // include/gemm_f32.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
@@ -40,7 +41,8 @@ struct VariantDesc {
     int threads;
     int lds_bytes;
     int stages;
-    const void *fn[2];  // [column-major B]
+    const void *fn[2];     // [column-major B]
+    const void *fn_sk[2];  // stream-K kernels (tiles' k-slabs shared across workgroups), or NULL
 };
 
 template <class T>
@@ -58,7 +60,9 @@ VariantDesc dma_variant(const char *name)
     return VariantDesc{
         name, GEMM_F32_KIND_MFMA, T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::THREADS, T::LDS_BYTES, T::STAGES,
         {reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_kernel<T, false>),
-         reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_kernel<T, true>)}};
+         reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_kernel<T, true>)},
+        {reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_sk_kernel<T, false>),
+         reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_sk_kernel<T, true>)}};
 }
 
 template <class T>
@@ -217,12 +221,21 @@ namespace {
 
 // Shape dispatch.  Few rows: the bandwidth-bound split-k path.  Otherwise
 // the direct-to-LDS MFMA kernels, with the largest tile that still gives
-// every CU at least one workgroup (256 x 128 tiles run two per CU).
-int choose_variant(int64_t m, int64_t n, const DeviceFacts &f)
+// every CU at least one workgroup (256 x 128 tiles run two per CU).  When
+// even 64 x 64 tiles leave fewer than two workgroups per CU and k is long,
+// 128 x 128 tiles with stream-K (all workgroups share all tiles' k-slabs)
+// fill the GPU instead: measured 83 against 63 TFLOPS at 1024x1024x8192,
+// while at 512x4096x4096 (512 small tiles) the two are even.
+int choose_variant(int64_t m, int64_t n, int64_t k, const DeviceFacts &f, bool *stream_k)
 {
+    *stream_k = false;
     if (m <= 32) return V_SKINNY_W16_D4;
     if (ceil_div(m, 256) * ceil_div(n, 128) >= f.cu_count) return V_DMA_256x128x16_S3;
     if (ceil_div(m, 128) * ceil_div(n, 128) >= f.cu_count) return V_DMA_128x128x16_S3;
+    if (ceil_div(m, 64) * ceil_div(n, 64) < 2 * (int64_t)f.cu_count && k >= 1024) {
+        *stream_k = true;
+        return V_DMA_128x128x16_S3;
+    }
     return V_DMA_64x64x16_S3;
 }
 
@@ -241,9 +254,10 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     if (st != GEMM_F32_SUCCESS) return st;
 
     int v = forced_variant;
+    bool auto_stream_k = false;
     if (v < 0) {
         v = env_int("GEMM_F32_VARIANT", -1);
-        if (v < 0 || v >= V_COUNT) v = choose_variant(m, n, facts);
+        if (v < 0 || v >= V_COUNT) v = choose_variant(m, n, k, facts, &auto_stream_k);
     }
     const VariantDesc &d = variant(v);
 
@@ -309,9 +323,55 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
         }
     }
 
+    if (d.fn_sk[0]) {
+        // Stream-K: as many workgroups as are resident at once share the
+        // k-slabs of all tiles evenly (chosen by the shape dispatch).
+        // GEMM_F32_SK_WGS forces it with that many workgroups, over the
+        // first GEMM_F32_SK_TILES tiles (default all; the other tiles get a
+        // workgroup each); GEMM_F32_STREAMK=0 disables the automatic choice.
+        // (Splitting only the tiles of a partly filled last wave was
+        // measured no faster: a lone workgroup runs a CU at ~92 % of the
+        // throughput of two, and the partial sums cost the rest.)
+        const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+        int64_t wgs = env_int("GEMM_F32_SK_WGS", 0);
+        int64_t shared = wgs > 0 ? env_int("GEMM_F32_SK_TILES", (int)tiles) : tiles;
+        if (wgs <= 0 && auto_stream_k && env_int("GEMM_F32_STREAMK", 1) != 0) {
+            int per_cu = 0;
+            hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, d.fn_sk[layout_b], d.threads, 0);
+            if (e != hipSuccess) {
+                delete p;
+                return hip_fail(e);
+            }
+            // At least 8 slabs per workgroup, so that a tile is shared by few.
+            wgs = std::min<int64_t>((int64_t)per_cu * facts.cu_count, tiles * a.k_tiles / 8);
+            if (wgs < 2) wgs = 0;
+        }
+        if (shared < 1 || shared > tiles) shared = tiles;
+        const int64_t iters = shared * a.k_tiles;
+        if (wgs > iters) wgs = iters;
+        if (wgs > 0) {
+            a.sk_wgs = (int)wgs;
+            a.sk_tiles = (int)shared;
+            p->grid = (unsigned)(wgs + tiles - shared);
+            const size_t words = (size_t)2 * wgs * d.bm * d.bn * sizeof(unsigned long long);
+            const size_t bytes = words + (size_t)shared * sizeof(unsigned);
+            hipError_t e = hipMalloc(&p->workspace, bytes);
+            if (e == hipSuccess) e = hipMemsetAsync(p->workspace, 0, bytes, nullptr);
+            if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+            if (e != hipSuccess) {
+                if (p->workspace) (void)hipFree(p->workspace);
+                delete p;
+                return hip_fail(e);
+            }
+            a.partial = static_cast<unsigned long long *>(p->workspace);
+            a.arrivals = reinterpret_cast<unsigned *>(static_cast<char *>(p->workspace) + words);
+        }
+    }
+
     if (env_int("GEMM_F32_LOG", 0))
-        std::fprintf(stderr, "[gemm_f32] m=%lld n=%lld k=%lld layoutB=%d -> %s grid=%u group_m=%d\n",
-                     (long long)m, (long long)n, (long long)k, layout_b, d.name, p->grid, a.group_m);
+        std::fprintf(stderr, "[gemm_f32] m=%lld n=%lld k=%lld layoutB=%d -> %s grid=%u group_m=%d split_k=%d stream_k=%d over %d tiles\n",
+                     (long long)m, (long long)n, (long long)k, layout_b, d.name, p->grid, a.group_m, a.split_k,
+                     a.sk_wgs, a.sk_tiles);
     *out = p;
     return GEMM_F32_SUCCESS;
 }
@@ -384,7 +444,8 @@ int gemm_f32_run(gemm_f32_plan p, const float *A, const float *B, float *C, void
     a.B = B;
     a.C = C;
     const VariantDesc &d = variant(p->variant);
-    const void *fn = d.fn[p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0];
+    const int col = p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0;
+    const void *fn = p->args.sk_wgs ? d.fn_sk[col] : d.fn[col];
     void *kargs[] = {&a};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (p->workspace) {
@@ -421,6 +482,8 @@ int gemm_f32_describe(gemm_f32_plan p, gemm_f32_info *info)
     info->grid = p->grid;
     info->group_m = p->args.group_m;
     info->split_k = p->args.split_k;
+    info->stream_k = p->args.sk_wgs;
+    info->stream_k_tiles = p->args.sk_tiles;
     return GEMM_F32_SUCCESS;
 }
 

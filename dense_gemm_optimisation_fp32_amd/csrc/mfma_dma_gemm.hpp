@@ -248,6 +248,162 @@ __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 
     for (int i = 0; i < NM; ++i) dma_mfma_one<T, B_COL>(i, T::KH - 1, f, acc);
 }
 
+// Slabs [kt0, kt1) of one tile, accumulated into acc.  The ring stage of
+// slab kt is kt % STAGES.  Every LDS read of the range happens before its
+// last barrier, so the next range may start copying at once.
+template <class T, bool B_COL>
+__device__ __forceinline__ void dma_range(const GemmArgs &g, f32x4 *lds_a, f32x4 *lds_b, __amdgpu_buffer_rsrc_t ra,
+                                          __amdgpu_buffer_rsrc_t rb, int row0, int col0, int kt0, int kt1, int tid,
+                                          int wave, int wr, int wc, int l32, int half,
+                                          f32x16 (&acc)[T::MB][T::NB])
+{
+    const int KT = g.k_tiles;
+    const bool ktail = g.k % T::BK != 0;
+    DmaFrags<T, B_COL> f;
+
+    // Prologue: copies of slabs kt0 .. kt0+STAGES-2, wait for slab kt0.
+#pragma unroll
+    for (int s = 0; s < T::STAGES - 1; ++s)
+        if (kt0 + s < kt1) {
+            const int st = (kt0 + s) % T::STAGES;
+#pragma unroll
+            for (int j = 0; j < T::PIECES; ++j)
+                dma_issue<T, B_COL>(j, g, ra, rb, row0, col0, kt0 + s, tid, wave, lds_a + st * T::A_CHUNKS,
+                                    lds_b + st * T::B_CHUNKS);
+        }
+    wait_vmcnt<0>();
+    const int st0 = kt0 % T::STAGES;
+    if (kt0 + 1 == kt1 && kt1 == KT && ktail)
+        dma_fix_tail<T, B_COL>(g, kt0, tid, lds_a + st0 * T::A_CHUNKS, lds_b + st0 * T::B_CHUNKS);
+    __syncthreads();
+    dma_prefetch<T, B_COL>(0, lds_a + st0 * T::A_CHUNKS, lds_b + st0 * T::B_CHUNKS, wr, wc, l32, half, f);
+
+    // Steady state: slab kt+1 is not the last one and slab kt+STAGES-1
+    // exists, so STAGES-2 slabs' copies may stay in flight while waiting for
+    // slab kt+1.  Then the drain: copies only while slabs remain, every wait
+    // complete, the k tail fixed when slab kt+1 is the tile's last.
+    int kt = kt0;
+    for (; kt + T::STAGES - 1 < kt1 && kt + 2 < kt1; ++kt)
+        dma_slab<T, B_COL, (T::STAGES - 2) * T::PIECES>(g, lds_a, lds_b, ra, rb, row0, col0, kt, true, false, tid,
+                                                         wave, wr, wc, l32, half, f, acc);
+    for (; kt + 1 < kt1; ++kt)
+        dma_slab<T, B_COL, 0>(g, lds_a, lds_b, ra, rb, row0, col0, kt, kt + T::STAGES - 1 < kt1,
+                              ktail && kt + 2 == KT, tid, wave, wr, wc, l32, half, f, acc);
+    dma_slab<T, B_COL, -1>(g, lds_a, lds_b, ra, rb, row0, col0, kt, false, false, tid, wave, wr, wc, l32, half, f,
+                           acc);
+}
+
+// Accumulators -> C.  Lane (l32, half), element v of block (mb, nb) is C row
+// mb*32 + 8*(v/4) + 4*half + v%4 of the wavefront tile; its column is
+// NB*l32 + nb (row-major B) or nb*32 + l32 (column-major B).  A single path
+// of range-checked element stores: with two copies of the store loop
+// (checked and unchecked) the register allocator starts moving the 256
+// accumulators around and spills.  Per instruction, 32 lanes write one row
+// segment: 128 contiguous bytes (column-major B) or every fourth float of 512
+// bytes, completed by the NB stores of the other blocks (row-major B).
+template <class T, bool B_COL>
+__device__ __forceinline__ void dma_store_c(const GemmArgs &g, __amdgpu_buffer_rsrc_t rc, int row0, int col0, int wr,
+                                            int wc, int l32, int half, const f32x16 (&acc)[T::MB][T::NB])
+{
+#pragma unroll
+    for (int mb = 0; mb < T::MB; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = row0 + wr * T::WM + mb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+#pragma unroll
+            for (int nb = 0; nb < T::NB; ++nb) {
+                const int c = B_COL ? col0 + wc * T::WN + nb * 32 + l32 : col0 + wc * T::WN + T::NB * l32 + nb;
+                buf_store_x1(acc[mb][nb][v], rc, elem_off(r < g.m && c < g.n, r, g.ldc, c));
+            }
+        }
+}
+
+// Stream-K bookkeeping.  The slab iterations of all tiles, I = tiles * KT in
+// tile order, are cut into P = sk_wgs equal ranges; range p is
+// [p*I/P, (p+1)*I/P).
+struct StreamK {
+    long long iters;
+    int wgs;
+    __device__ long long start(int p) const { return (long long)p * iters / wgs; }
+    // The range that holds iteration x.
+    __device__ int owner(long long x) const { return (int)(((x + 1) * wgs - 1) / iters); }
+};
+
+// A tile whose slabs are shared by several ranges ("segments", in k order)
+// is finished by the last segment to arrive.  Every segment publishes its
+// partial sums as epoch-tagged 64-bit words in a slot of its own range (two
+// slots per range: its first and its last tile), then counts itself in; the
+// last one reads all segments back and adds them in k order, so the sum does
+// not depend on who arrives last, and writes the tile to C.  (The last one
+// could keep its own part in its accumulators, but adding vector-ALU
+// results to the accumulators makes the compiler hold all of them in vector
+// registers, which halves the occupancy of the whole kernel.)
+template <class T, bool B_COL>
+__device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsrc_t rc, const StreamK &sk, int t,
+                                          int p, int tid, int row0, int col0, int wr, int wc, int l32, int half,
+                                          int *last_flag, const f32x16 (&acc)[T::MB][T::NB])
+{
+    const long long t0 = (long long)t * g.k_tiles;
+    const int p_lo = sk.owner(t0), p_hi = sk.owner(t0 + g.k_tiles - 1);
+    const int nseg = p_hi - p_lo + 1;
+    constexpr size_t SLOT = (size_t)T::BM * T::BN;
+    // Slot of range q's segment of this tile: 2q for a range that starts in
+    // the tile (the tile is its first), 2q + 1 for one that starts before.
+    auto slot = [&](int q) { return (size_t)(2 * q + (sk.start(q) < t0 ? 1 : 0)) * SLOT; };
+
+    unsigned long long *dst = g.partial + slot(p);
+#pragma unroll
+    for (int mb = 0; mb < T::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < T::NB; ++nb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                store_tagged_word(dst + (size_t)(((mb * T::NB + nb) * 16 + v) * T::THREADS + tid), acc[mb][nb][v],
+                                  g.epoch);
+            // One block at a time: keeps the scheduler from pulling all
+            // accumulators into vector registers at once.
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+    if (tid == 0) {
+        const unsigned before = __hip_atomic_fetch_add(g.arrivals + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = before == (unsigned)(nseg - 1);
+        // Every other segment has counted itself in: reset for the next run.
+        if (last) __hip_atomic_store(g.arrivals + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *last_flag = last;
+    }
+    __syncthreads();
+    if (!*last_flag) return;
+    int budget = kTaggedWaitBudget;
+
+#pragma unroll
+    for (int mb = 0; mb < T::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < T::NB; ++nb) {
+            const size_t off = (size_t)((mb * T::NB + nb) * 16) * T::THREADS + tid;
+            f32x16 sum;
+            for (int jj = 0; jj < nseg; ++jj) {
+                const unsigned long long *src = g.partial + slot(p_lo + jj) + off;
+                unsigned long long w[16];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) w[v] = load_tagged_word(src + (size_t)v * T::THREADS);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float x = wait_tagged_word(src + (size_t)v * T::THREADS, w[v], g.epoch, budget);
+                    sum[v] = jj == 0 ? x : sum[v] + x;
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = row0 + wr * T::WM + mb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+                const int c = B_COL ? col0 + wc * T::WN + nb * 32 + l32 : col0 + wc * T::WN + T::NB * l32 + nb;
+                buf_store_x1(sum[v], rc, elem_off(r < g.m && c < g.n, r, g.ldc, c));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+}
+
+// One whole tile per workgroup.
 template <class T, bool B_COL>
 __global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_kernel(GemmArgs g)
 {
@@ -274,57 +430,88 @@ __global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_kernel(GemmArgs g)
     for (int mb = 0; mb < T::MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < T::NB; ++nb) acc[mb][nb] = f32x16{};
+    dma_range<T, B_COL>(g, lds_a, lds_b, ra, rb, row0, col0, 0, g.k_tiles, tid, wave, wr, wc, l32, half, acc);
+    dma_store_c<T, B_COL>(g, rc, row0, col0, wr, wc, l32, half, acc);
+}
 
+// Stream-K ("GEMM 性能优化", Wave 模型: a last, partly filled wave of tiles
+// idles most of the GPU).  The grid's first sk_wgs workgroups share the slab
+// iterations of tiles [0, sk_tiles) evenly; the workgroups after them take
+// one whole tile each of the rest.  With sk_wgs = S * sk_tiles every shared
+// tile is split into S k-segments run side by side, which keeps workgroups
+// at the same k (and in the same L2 lines) as their neighbours.  The shared
+// tiles come first, so their fix-ups overlap the whole-tile work that
+// follows.  Range p covers the tail of its first tile, whole tiles, and the
+// head of its last tile; the two partial segments run first.
+template <class T, bool B_COL>
+__global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_sk_kernel(GemmArgs g)
+{
+    __shared__ f32x4 lds[T::STAGES * (T::A_CHUNKS + T::B_CHUNKS)];
+    __shared__ int last_flag;
+    f32x4 *const lds_a = lds;                                // [STAGES][A_CHUNKS]
+    f32x4 *const lds_b = lds + T::STAGES * T::A_CHUNKS;      // [STAGES][B_CHUNKS]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave % T::WAVES_M, wc = wave / T::WAVES_M;
+    const int l32 = lane & 31, half = lane >> 5;
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, g.b_bytes);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.C, g.c_bytes);
     const int KT = g.k_tiles;
-    const bool ktail = g.k % T::BK != 0;
-    DmaFrags<T, B_COL> f;
 
-    // Prologue: copies of slabs 0 .. STAGES-2, wait for slab 0.
+    f32x16 acc[T::MB][T::NB];
+    if ((int)blockIdx.x >= g.sk_wgs) {
+        // One whole tile of [sk_tiles, tiles).
+        const int whole = g.tiles_m * g.tiles_n - g.sk_tiles;
+        int tm, tn;
+        grouped_tile(g.sk_tiles + xcd_contiguous(blockIdx.x - g.sk_wgs, whole, g.num_xcd), g, tm, tn);
+        const int row0 = tm * T::BM, col0 = tn * T::BN;
 #pragma unroll
-    for (int s = 0; s < T::STAGES - 1; ++s)
-        if (s < KT)
+        for (int mb = 0; mb < T::MB; ++mb)
 #pragma unroll
-            for (int j = 0; j < T::PIECES; ++j)
-                dma_issue<T, B_COL>(j, g, ra, rb, row0, col0, s, tid, wave, lds_a + s * T::A_CHUNKS,
-                                    lds_b + s * T::B_CHUNKS);
-    wait_vmcnt<0>();
-    if (KT == 1 && ktail) dma_fix_tail<T, B_COL>(g, 0, tid, lds_a, lds_b);
-    __syncthreads();
-    dma_prefetch<T, B_COL>(0, lds_a, lds_b, wr, wc, l32, half, f);
+            for (int nb = 0; nb < T::NB; ++nb) acc[mb][nb] = f32x16{};
+        dma_range<T, B_COL>(g, lds_a, lds_b, ra, rb, row0, col0, 0, KT, tid, wave, wr, wc, l32, half, acc);
+        dma_store_c<T, B_COL>(g, rc, row0, col0, wr, wc, l32, half, acc);
+        return;
+    }
 
-    // Steady state: slab kt+1 is not the last one and slab kt+STAGES-1
-    // exists, so STAGES-2 slabs' copies may stay in flight while waiting for
-    // slab kt+1.  Then the drain: copies only while slabs remain, every wait
-    // complete, the k tail fixed when slab kt+1 is the last.
-    int kt = 0;
-    for (; kt + T::STAGES - 1 < KT && kt + 2 < KT; ++kt)
-        dma_slab<T, B_COL, (T::STAGES - 2) * T::PIECES>(g, lds_a, lds_b, ra, rb, row0, col0, kt, true, false, tid,
-                                                         wave, wr, wc, l32, half, f, acc);
-    for (; kt + 1 < KT; ++kt)
-        dma_slab<T, B_COL, 0>(g, lds_a, lds_b, ra, rb, row0, col0, kt, kt + T::STAGES - 1 < KT,
-                              ktail && kt + 2 == KT, tid, wave, wr, wc, l32, half, f, acc);
-    dma_slab<T, B_COL, -1>(g, lds_a, lds_b, ra, rb, row0, col0, kt, false, false, tid, wave, wr, wc, l32, half, f,
-                           acc);
+    const StreamK sk{(long long)g.sk_tiles * KT, g.sk_wgs};
+    const int p = xcd_contiguous(blockIdx.x, g.sk_wgs, g.num_xcd);
+    const long long i0 = sk.start(p), i1 = sk.start(p + 1);
+    if (i0 >= i1) return;
+    const int t_first = (int)(i0 / KT), t_last = (int)((i1 - 1) / KT);
+    const int head0 = (int)(i0 - (long long)t_first * KT);           // first slab in t_first
+    const int tail1 = (int)(i1 - (long long)t_last * KT);            // end slab in t_last
+    // Work items in order: partial first tile, partial last tile, whole tiles.
+    const bool first_partial = head0 != 0 || (t_first == t_last && tail1 != KT);
+    const bool last_partial = t_last != t_first && tail1 != KT;
+    const int n_part = (first_partial ? 1 : 0) + (last_partial ? 1 : 0);
+    const int full0 = first_partial ? t_first + 1 : t_first;
+    const int n_items = n_part + max(0, (last_partial ? t_last : t_last + 1) - full0);
 
-    // Epilogue.  Lane (l32, half), element v of block (mb, nb) is C row
-    // mb*32 + 8*(v/4) + 4*half + v%4 of the wavefront tile; its column is
-    // NB*l32 + nb (row-major B) or nb*32 + l32 (column-major B).  A single
-    // path of range-checked element stores: with two copies of the store loop
-    // (checked and unchecked) the register allocator starts moving the 256
-    // accumulators around and spills.  Per instruction, 32 lanes write one row
-    // segment: 128 contiguous bytes (column-major B) or every fourth float of
-    // 512 bytes, completed by the NB stores of the other blocks (row-major B).
-#pragma unroll
-    for (int mb = 0; mb < T::MB; ++mb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = row0 + wr * T::WM + mb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-#pragma unroll
-            for (int nb = 0; nb < T::NB; ++nb) {
-                const int c = B_COL ? col0 + wc * T::WN + nb * 32 + l32 : col0 + wc * T::WN + T::NB * l32 + nb;
-                buf_store_x1(acc[mb][nb][v], rc, elem_off(r < g.m && c < g.n, r, g.ldc, c));
-            }
+    for (int it = 0; it < n_items; ++it) {
+        int t = full0 + it - n_part, kt0 = 0, kt1 = KT;
+        if (it == 0 && first_partial) {
+            t = t_first; kt0 = head0; kt1 = t_first == t_last ? tail1 : KT;
+        } else if (it < n_part) {
+            t = t_last; kt1 = tail1;
         }
+        int tm, tn;
+        grouped_tile(t, g, tm, tn);
+        const int row0 = tm * T::BM, col0 = tn * T::BN;
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < T::NB; ++nb) acc[mb][nb] = f32x16{};
+        dma_range<T, B_COL>(g, lds_a, lds_b, ra, rb, row0, col0, kt0, kt1, tid, wave, wr, wc, l32, half, acc);
+        if (kt0 == 0 && kt1 == KT)
+            dma_store_c<T, B_COL>(g, rc, row0, col0, wr, wc, l32, half, acc);
+        else
+            dma_fixup<T, B_COL>(g, rc, sk, t, p, tid, row0, col0, wr, wc, l32, half, &last_flag, acc);
+    }
 }
 
 }  // namespace gemmf32

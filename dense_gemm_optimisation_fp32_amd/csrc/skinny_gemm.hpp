@@ -108,21 +108,6 @@ __device__ __forceinline__ void skinny_mfma(const f32x4 &a, const f32x4 (&b)[T::
         }
 }
 
-// Value of a split's 64-bit partial-sum word once it carries this run's
-// epoch.  The writer has already issued the word when the reader gets here,
-// so the wait ends; the bound only keeps a lost word from hanging the
-// kernel, and then the element reads as NaN.
-__device__ __forceinline__ float skinny_wait_word(const unsigned long long *p, unsigned long long w, unsigned epoch)
-{
-    constexpr int kSpinLimit = 1 << 20;
-    for (int i = 0; (unsigned)(w >> 32) != epoch; ++i) {
-        if (i == kSpinLimit) return __builtin_nanf("");
-        __builtin_amdgcn_s_sleep(1);
-        w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    return __uint_as_float((unsigned)w);
-}
-
 // Grid: tiles_m * tiles_n * split_k workgroups.  With one split the
 // workgroup writes its tile of C; otherwise the splits meet through
 // g.partial[split][m][n] (epoch-tagged words) and g.arrivals[tile].
@@ -242,9 +227,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
     for (int q = 0; q < EPT; ++q) {
         const int e = tid + q * T::THREADS;
         const int r = row0 + e / T::BN, c = col0 + e % T::BN;
-        if (e < ELEMS && r < g.m && c < g.n)
-            __hip_atomic_store(g.partial + split * plane + (size_t)r * g.n + c, tag | __float_as_uint(own[q]),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (e < ELEMS && r < g.m && c < g.n) store_tagged_word(g.partial + split * plane + (size_t)r * g.n + c, own[q], g.epoch);
     }
     __shared__ int last;
     __syncthreads();
@@ -258,6 +241,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
     }
     __syncthreads();
     if (!last) return;
+    int budget = kTaggedWaitBudget;
 
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
@@ -272,13 +256,13 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
 #pragma unroll
             for (int u = 0; u < 8; ++u)
                 w[u] = (s0 + u < g.split_k && s0 + u != split)
-                           ? __hip_atomic_load(p + (s0 + u) * plane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           ? load_tagged_word(p + (s0 + u) * plane)
                            : tag;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int sp = s0 + u;
                 if (sp >= g.split_k) break;
-                const float v = sp == split ? own[q] : skinny_wait_word(p + sp * plane, w[u], g.epoch);
+                const float v = sp == split ? own[q] : wait_tagged_word(p + sp * plane, w[u], g.epoch, budget);
                 sum = sp == 0 ? v : sum + v;
             }
         }

@@ -25,13 +25,14 @@
  *  - Pointers A, B, C are device pointers (HIP device memory of the current
  *    device), owned by the caller.  C must not overlap A or B.
  *  - Sizes and leading dimensions are in elements (floats).
- *  - A plan is immutable after creation.  Plans of the tiled kernels hold
- *    host state only and may be used from several host threads and streams
- *    at once.  Plans of the few-row path with more than one k-split
- *    (gemm_f32_info.split_k > 1) own a device workspace: split_k * m * n
- *    partial sums as 8-byte words tagged with a per-run epoch, and one
- *    32-bit arrival counter per output tile (zeroed by create, freed by
- *    destroy).  Each run takes a new epoch from the plan (an atomic counter,
+ *  - A plan is immutable after creation.  Plans of the tiled kernels with
+ *    one tile per workgroup hold host state only and may be used from
+ *    several host threads and streams at once.  Plans that split tiles
+ *    along k own a device workspace (zeroed by create, freed by destroy):
+ *    few-row plans with gemm_f32_info.split_k > 1 hold split_k * m * n
+ *    partial sums, stream-K plans (gemm_f32_info.stream_k = P > 0) hold
+ *    2 * P partial tiles (bm * bn each), all as 8-byte words tagged with a
+ *    per-run epoch, plus one 32-bit arrival counter per output tile.  Each run takes a new epoch from the plan (an atomic counter,
  *    so runs may be enqueued from several host threads), but two runs of such
  *    a plan must not execute at the same time on the device (they would share
  *    the workspace): use one plan per stream, or order the streams.
@@ -82,6 +83,8 @@ struct gemm_f32_info {
     int lds_bytes;      /* LDS per workgroup (all stages) */
     int stages;         /* LDS buffers along k */
     int split_k;        /* k-splits (1 = none) */
+    int stream_k;       /* plan only: workgroups sharing the k-slabs of stream_k_tiles tiles evenly (stream-K), 0 = none */
+    int stream_k_tiles; /* plan only: tiles whose k-slabs are shared; every other tile gets one workgroup */
     int aligned;        /* plan only: 1 if lda, ldb and ldc are multiples of 4 (informational) */
     int64_t tiles_m, tiles_n, k_tiles, grid; /* plan only: tile counts and workgroups launched */
     int group_m;        /* plan only: tile-rows per rasterisation group */

@@ -183,6 +183,75 @@ def test_split_k_counts_forced(split, layout_b, monkeypatch):
         g.gemm_f32_destroy(plan)
 
 
+def dma_variants():
+    import dense_gemm_optimisation_fp32_amd as g
+    return [v for v in variants() if g.gemm_f32_variant_info(v)["name"].startswith("dma_")]
+
+
+@pytest.mark.parametrize("variant", dma_variants())
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+@pytest.mark.parametrize("wgs", [2, 3, 7, 16, 40])
+def test_stream_k_forced(variant, layout_b, wgs, monkeypatch):
+    """Stream-K plans with a forced number of workgroups: tiles split at
+    arbitrary slabs (including ranges shorter than the LDS ring and tiles
+    shared by many ranges) match the oracle, integer inputs bit for bit, and
+    repeated runs (new epochs, reset counters) repeat bit for bit."""
+    monkeypatch.setenv("GEMM_F32_SK_WGS", str(wgs))
+    for shape in [(513, 257, 1000), (300, 520, 77)]:
+        m, n, k = shape
+        print(f"\n[case] stream-K variant={variant} layout_b={layout_b} wgs={wgs} shape={shape}", flush=True)
+        A, B = random_operands(m, n, k, layout_b, "normal1", seed=70 + wgs)
+        C, info, outs = run_gemm(A, B, m, n, k, layout_b, variant=variant, repeat=3)
+        tiles = info["tiles_m"] * info["tiles_n"]
+        assert info["stream_k"] == min(wgs, tiles * info["k_tiles"]) and info["stream_k_tiles"] == tiles
+        Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+        check_close(C, Cref, S, f"{info['name']} stream-K {wgs} {shape}")
+        assert all(np.array_equal(outs[0], o) for o in outs[1:])
+        A, B = random_operands(m, n, k, layout_b, "int8range", seed=80 + wgs)
+        C, _ = run_gemm(A, B, m, n, k, layout_b, variant=variant)
+        Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
+        assert np.array_equal(C.astype(np.float64), Cref)
+
+
+@pytest.mark.parametrize("variant", dma_variants())
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+@pytest.mark.parametrize("wgs,shared", [(4, 2), (9, 3), (5, 5), (7, 1)])
+def test_stream_k_hybrid_forced(variant, layout_b, wgs, shared, monkeypatch):
+    """Stream-K over the first `shared` tiles, one workgroup per tile for the
+    rest, in one launch: matches the oracle and repeats bit for bit."""
+    monkeypatch.setenv("GEMM_F32_SK_WGS", str(wgs))
+    monkeypatch.setenv("GEMM_F32_SK_TILES", str(shared))
+    m, n, k = 513, 257, 1000
+    print(f"\n[case] hybrid stream-K variant={variant} layout_b={layout_b} wgs={wgs} shared={shared}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=90 + wgs)
+    C, info, outs = run_gemm(A, B, m, n, k, layout_b, variant=variant, repeat=3)
+    tiles = info["tiles_m"] * info["tiles_n"]
+    assert info["stream_k_tiles"] == min(shared, tiles)
+    assert info["grid"] == info["stream_k"] + tiles - info["stream_k_tiles"]
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    check_close(C, Cref, S, f"{info['name']} hybrid stream-K {wgs}/{shared}")
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+def test_stream_k_chosen_for_few_tiles_long_k(layout_b):
+    """Shapes with too few tiles for the GPU and a long k get a stream-K plan
+    by default; it matches the oracle (integer inputs bit for bit)."""
+    for (m, n, k) in [(256, 256, 4096), (1024, 1024, 8192)]:
+        print(f"\n[case] default stream-K layout_b={layout_b} shape={(m, n, k)}", flush=True)
+        A, B = random_operands(m, n, k, layout_b, "normal1", seed=95)
+        C, info, outs = run_gemm(A, B, m, n, k, layout_b, repeat=2)
+        assert info["stream_k"] > 1 and info["stream_k_tiles"] == info["tiles_m"] * info["tiles_n"]
+        assert np.array_equal(outs[0], outs[1])
+        rows, cols = sample_indices(m, n, 2000, seed=96)
+        c, s_ = oracle.gemm_f64_sampled(A, B, m, n, k, layout_b, rows, cols)
+        check_close(C[rows, cols], c, s_, f"{info['name']} default stream-K {(m, n, k)}")
+        A, B = random_operands(m, n, k, layout_b, "int8range", seed=97)
+        C, _ = run_gemm(A, B, m, n, k, layout_b)
+        c, _ = oracle.gemm_f64_sampled(A, B, m, n, k, layout_b, rows, cols)
+        assert np.array_equal(C[rows, cols].astype(np.float64), c)
+
+
 # ---------------------------------------------------------------------------
 # Full workload shapes, in the plan the benchmark times (gemm_f32_create).
 # ---------------------------------------------------------------------------
