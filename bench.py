@@ -186,7 +186,7 @@ def roofline(res):
     ridge = pm.ridge_point(pm.MI355X_FP32_MATRIX_PEAK, pm.MI355X_HBM_BANDWIDTH)
     kind = res["plan"]["kind"]
     if intensity >= ridge:
-        peak = pm.MI355X_FP32_MATRIX_PEAK if kind != 1 else pm.MI355X_FP32_VECTOR_UNPACKED_PEAK
+        peak = pm.MI355X_FP32_MATRIX_PEAK if kind != 1 else pm.MI355X_FP32_VECTOR_PEAK
         achieved = res["flops"] / res["kernel_avg_s"] / 1e12
         out = {"bound": "mfma" if kind != 1 else "alu", "achieved": round(achieved, 3),
                "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved / (peak / 1e12), 4)}

@@ -8,6 +8,9 @@ time and TFLOPS on the GPU.  This is the reuse-versus-occupancy trade-off of
 keep fewer waves resident.
 
     python -m dense_gemm_optimisation_fp32_amd.sweep --workloads sq4096,ffn --out sweep.jsonl
+
+The few-row path is swept with bench.py (--workload skinny --variant V
+--rotate 8), which reads B from HBM at every launch.
 """
 from __future__ import annotations
 
@@ -40,13 +43,24 @@ def kernel_resources(path: str = RESOURCES):
     return out
 
 
+def kernel_tag(info: dict, layout_b: int) -> str:
+    """Substring of the mangled name of the kernel a variant launches (the
+    one-tile-per-workgroup kernel) for one B layout."""
+    b = f"Lb{layout_b}E"
+    if info["kind"] == 1:
+        return f"gemm_valu_kernelI{b}"
+    if info["kind"] == 2:
+        m = re.match(r"skinny_16x(\d+)_w(\d+)_d(\d+)", info["name"])
+        return f"SkinnyTileILi{m.group(2)}ELi{m.group(3)}ELi{m.group(1)}EEE{b}"
+    dims = (f"ILi{info['bm']}ELi{info['bn']}ELi{info['bk']}ELi{info['waves_m']}ELi{info['waves_n']}")
+    if info["name"].startswith("dma_"):
+        return f"gemm_mfma_dma_kernelINS_7DmaTile{dims}ELi{info['stages']}EEE{b}"
+    return f"gemm_mfma_kernelINS_8MfmaTile{dims}EEE{b}"
+
+
 def resources_for(info: dict, layout_b: int, res: dict):
     """Resources of the kernel a variant launches for one B layout."""
-    if info["kind"] == 1:
-        tag = f"gemm_valu_kernelILb{layout_b}E"
-    else:
-        tag = (f"MfmaTileILi{info['bm']}ELi{info['bn']}ELi{info['bk']}ELi{info['waves_m']}"
-               f"ELi{info['waves_n']}EEELb{layout_b}E")
+    tag = kernel_tag(info, layout_b)
     for name, r in res.items():
         if tag in name:
             vg = int(r.get("VGPRs", 0))
@@ -82,20 +96,19 @@ def time_variant(g, torch, w, variant, steps, warmup):
     for _ in range(max(warmup, int(0.25 / est))):
         plan.run(dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), stream.cuda_stream)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for s, e in ev:
-        s.record(stream)
+    # Average launch duration: one event pair around `steps` back-to-back
+    # launches on the launch stream.
+    t0.record(stream)
+    for _ in range(steps):
         plan.run(dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), stream.cuda_stream)
-        e.record(stream)
+    t1.record(stream)
     torch.cuda.synchronize()
-    durs = sorted(s.elapsed_time(e) / 1e3 for s, e in ev)
-    med = durs[len(durs) // 2]
-    return plan.info, med, durs[0]
+    return plan.info, t0.elapsed_time(t1) / 1e3 / steps
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("--workloads", default="sq4096,sq4096t,ragged,ffn,skinny")
+    ap.add_argument("--workloads", default="sq4096,sq4096t,ragged,ffn")
     ap.add_argument("--variants", default="all")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
@@ -118,14 +131,14 @@ def main(argv=None):
                 kind = g.gemm_f32_variant_info(v)["kind"]
                 if (kind == g.GEMM_F32_KIND_SKINNY) != (w.m <= 64):
                     continue   # the few-row path and the tiled paths serve different shape classes
-                info, med, best = time_variant(g, torch, w, v, args.steps, args.warmup)
+                info, avg = time_variant(g, torch, w, v, args.steps, args.warmup)
                 rec = {"workload": name, "variant": v, "name": info["name"], "kind": info["kind"],
                        "bm": info["bm"], "bn": info["bn"], "bk": info["bk"],
                        "waves": info["waves_m"] * info["waves_n"], "wave_tile": [info["wave_m"], info["wave_n"]],
-                       "grid": info["grid"], "t_median_us": round(med * 1e6, 2), "t_min_us": round(best * 1e6, 2),
-                       "tflops": round(pm.tflops(w.m, w.n, w.k, med), 2),
-                       "pct_peak": round(100 * pm.tflops(w.m, w.n, w.k, med) * 1e12 / pm.MI355X_FP32_MATRIX_PEAK, 2),
-                       "hbm_gbs": round(pm.compulsory_bytes(w.m, w.n, w.k) / med / 1e9, 1)}
+                       "grid": info["grid"], "t_avg_us": round(avg * 1e6, 2),
+                       "tflops": round(pm.tflops(w.m, w.n, w.k, avg), 2),
+                       "pct_peak": round(100 * pm.tflops(w.m, w.n, w.k, avg) * 1e12 / pm.MI355X_FP32_MATRIX_PEAK, 2),
+                       "hbm_gbs": round(pm.compulsory_bytes(w.m, w.n, w.k) / avg / 1e9, 1)}
                 rec.update(resources_for(info, w.layout_b, res))
                 f.write(json.dumps(rec) + "\n")
                 f.flush()
