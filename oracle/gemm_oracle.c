@@ -10,9 +10,12 @@
  *   C[i][j] = sum_{k=0}^{K-1} A[i][k] * B(k, j)          for 0 <= i < M, 0 <= j < N
  *   S[i][j] = sum_{k=0}^{K-1} |A[i][k] * B(k, j)|        (error scale for the tolerance)
  * with
- *   A[i][k]  = A[i*lda + k]                    (A row-major)
+ *   A[i][k]  = A[i*lda + k]   if layout_a == 0 (A row-major)
+ *            = A[k*lda + i]   if layout_a == 1 (A column-major: column k contiguous)
  *   B(k, j)  = B[k*ldb + j]   if layout_b == 0 (B row-major)
  *            = B[j*ldb + k]   if layout_b == 1 (B column-major: column j contiguous)
+ * The column-major A index is the pages' column-major convention applied to
+ * the first operand (the reading of the linear-layer layouts: transposed A).
  *
  * Sources (pages: "GEMM 性能优化", "GPU 算子优化中的数据复用",
  * "PMPP Chapter 06: Performance considerations"):
@@ -44,34 +47,41 @@
 #define ORACLE_OK 0
 #define ORACLE_BAD_ARGS 1
 
-static int oracle_args_ok(int64_t m, int64_t n, int64_t k, int layout_b,
+static int oracle_args_ok(int64_t m, int64_t n, int64_t k, int layout_a, int layout_b,
                           int64_t lda, int64_t ldb)
 {
     if (m < 0 || n < 0 || k < 0) return 0;
+    if (layout_a != 0 && layout_a != 1) return 0;
     if (layout_b != 0 && layout_b != 1) return 0;
-    if (lda < k) return 0;
+    if (layout_a == 0 && lda < k) return 0;
+    if (layout_a == 1 && lda < m) return 0;
     if (layout_b == 0 && ldb < n) return 0;
     if (layout_b == 1 && ldb < k) return 0;
     return 1;
 }
 
-/* Full product.  C and S are M x N double arrays with row stride ldr. */
-int oracle_gemm_f64(int64_t m, int64_t n, int64_t k, int layout_b,
-                    const float *A, int64_t lda,
-                    const float *B, int64_t ldb,
-                    double *C, double *S, int64_t ldr)
+/* A[i][kk] for either layout of A. */
+static double a_at(const float *A, int64_t lda, int layout_a, int64_t i, int64_t kk)
 {
-    if (!oracle_args_ok(m, n, k, layout_b, lda, ldb) || ldr < n) return ORACLE_BAD_ARGS;
+    return layout_a == 0 ? (double)A[i * lda + kk] : (double)A[kk * lda + i];
+}
+
+/* Full product.  C and S are M x N double arrays with row stride ldr. */
+int oracle_gemm_f64_ex(int64_t m, int64_t n, int64_t k, int layout_a, int layout_b,
+                       const float *A, int64_t lda,
+                       const float *B, int64_t ldb,
+                       double *C, double *S, int64_t ldr)
+{
+    if (!oracle_args_ok(m, n, k, layout_a, layout_b, lda, ldb) || ldr < n) return ORACLE_BAD_ARGS;
 
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < m; ++i) {
         double *c = C + i * ldr;
         double *s = S + i * ldr;
-        const float *a_row = A + i * lda;
         if (layout_b == 0) {
             for (int64_t j = 0; j < n; ++j) { c[j] = 0.0; s[j] = 0.0; }
             for (int64_t kk = 0; kk < k; ++kk) {
-                const double a = (double)a_row[kk];
+                const double a = a_at(A, lda, layout_a, i, kk);
                 const float *b_row = B + kk * ldb;          /* B(kk, j) = B[kk*ldb + j] */
                 for (int64_t j = 0; j < n; ++j) {
                     const double p = a * (double)b_row[j];
@@ -84,7 +94,7 @@ int oracle_gemm_f64(int64_t m, int64_t n, int64_t k, int layout_b,
                 const float *b_col = B + j * ldb;           /* B(kk, j) = B[j*ldb + kk] */
                 double acc = 0.0, acc_abs = 0.0;
                 for (int64_t kk = 0; kk < k; ++kk) {
-                    const double p = (double)a_row[kk] * (double)b_col[kk];
+                    const double p = a_at(A, lda, layout_a, i, kk) * (double)b_col[kk];
                     acc += p;
                     acc_abs += fabs(p);
                 }
@@ -96,15 +106,24 @@ int oracle_gemm_f64(int64_t m, int64_t n, int64_t k, int layout_b,
     return ORACLE_OK;
 }
 
+/* Row-major A. */
+int oracle_gemm_f64(int64_t m, int64_t n, int64_t k, int layout_b,
+                    const float *A, int64_t lda,
+                    const float *B, int64_t ldb,
+                    double *C, double *S, int64_t ldr)
+{
+    return oracle_gemm_f64_ex(m, n, k, 0, layout_b, A, lda, B, ldb, C, S, ldr);
+}
+
 /* The same sum for a list of individual elements (rows[t], cols[t]); used where
  * a full product would take too long on the host. */
-int oracle_gemm_f64_sampled(int64_t m, int64_t n, int64_t k, int layout_b,
-                            const float *A, int64_t lda,
-                            const float *B, int64_t ldb,
-                            int64_t count, const int64_t *rows, const int64_t *cols,
-                            double *c_out, double *s_out)
+int oracle_gemm_f64_sampled_ex(int64_t m, int64_t n, int64_t k, int layout_a, int layout_b,
+                               const float *A, int64_t lda,
+                               const float *B, int64_t ldb,
+                               int64_t count, const int64_t *rows, const int64_t *cols,
+                               double *c_out, double *s_out)
 {
-    if (!oracle_args_ok(m, n, k, layout_b, lda, ldb) || count < 0) return ORACLE_BAD_ARGS;
+    if (!oracle_args_ok(m, n, k, layout_a, layout_b, lda, ldb) || count < 0) return ORACLE_BAD_ARGS;
     for (int64_t t = 0; t < count; ++t)
         if (rows[t] < 0 || rows[t] >= m || cols[t] < 0 || cols[t] >= n) return ORACLE_BAD_ARGS;
 
@@ -114,7 +133,7 @@ int oracle_gemm_f64_sampled(int64_t m, int64_t n, int64_t k, int layout_b,
         double acc = 0.0, acc_abs = 0.0;
         for (int64_t kk = 0; kk < k; ++kk) {
             const double b = layout_b == 0 ? (double)B[kk * ldb + j] : (double)B[j * ldb + kk];
-            const double p = (double)A[i * lda + kk] * b;
+            const double p = a_at(A, lda, layout_a, i, kk) * b;
             acc += p;
             acc_abs += fabs(p);
         }
@@ -122,6 +141,16 @@ int oracle_gemm_f64_sampled(int64_t m, int64_t n, int64_t k, int layout_b,
         s_out[t] = acc_abs;
     }
     return ORACLE_OK;
+}
+
+/* Row-major A. */
+int oracle_gemm_f64_sampled(int64_t m, int64_t n, int64_t k, int layout_b,
+                            const float *A, int64_t lda,
+                            const float *B, int64_t ldb,
+                            int64_t count, const int64_t *rows, const int64_t *cols,
+                            double *c_out, double *s_out)
+{
+    return oracle_gemm_f64_sampled_ex(m, n, k, 0, layout_b, A, lda, B, ldb, count, rows, cols, c_out, s_out);
 }
 
 /* Number of OpenMP threads a parallel region here uses (for reporting). */

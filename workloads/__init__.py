@@ -83,16 +83,26 @@ def b_storage_shape(k: int, n: int, layout_b: int, ldb: int | None = None):
     return n, (k if ldb is None else ldb)
 
 
-def random_operands(m: int, n: int, k: int, layout_b: int, dist: str, seed: int,
-                    lda: int | None = None, ldb: int | None = None, pad_value: float = np.nan):
-    """Draw A (M x K, row-major) and B (K x N, given layout) as storage arrays.
+def a_storage_shape(m: int, k: int, layout_a: int, lda: int | None = None):
+    """(rows, row stride) of A's storage buffer."""
+    if layout_a == ROW_MAJOR:
+        return m, (k if lda is None else lda)
+    return k, (m if lda is None else lda)
 
-    The logical entries are drawn in storage order with packed strides; when a
-    leading dimension larger than the minimum is asked for, the packed values
-    are placed into a wider buffer whose padding holds ``pad_value`` (NaN by
-    default, so that any use of padding shows up in the result)."""
+
+def random_operands(m: int, n: int, k: int, layout_b: int, dist: str, seed: int,
+                    lda: int | None = None, ldb: int | None = None, pad_value: float = np.nan,
+                    layout_a: int = ROW_MAJOR):
+    """Draw A (M x K) and B (K x N), each in the given layout, as storage arrays.
+
+    The logical entries are drawn in storage order with packed strides (a
+    column-major A as its K x M storage buffer); when a leading dimension
+    larger than the minimum is asked for, the packed values are placed into a
+    wider buffer whose padding holds ``pad_value`` (NaN by default, so that
+    any use of padding shows up in the result)."""
     rng = np.random.default_rng(seed)
-    a = _draw(rng, dist, m * k).reshape(m, k)
+    a_rows, a_cols = a_storage_shape(m, k, layout_a)
+    a = _draw(rng, dist, a_rows * a_cols).reshape(a_rows, a_cols)
     b_rows, b_cols = b_storage_shape(k, n, layout_b)
     b = _draw(rng, dist, b_rows * b_cols).reshape(b_rows, b_cols)
     return _pad(a, lda, pad_value), _pad(b, ldb, pad_value)
@@ -106,6 +116,15 @@ def _pad(x: np.ndarray, ld: int | None, pad_value: float) -> np.ndarray:
     out = np.full((x.shape[0], ld), pad_value, dtype=np.float32)
     out[:, : x.shape[1]] = x
     return out
+
+
+def epilogue_operands(m: int, n: int, seed: int):
+    """C_in (M x N, row-major) and bias (N) for the linear-layer epilogue,
+    normal(0, 1), drawn C_in first then bias."""
+    rng = np.random.default_rng(seed)
+    c_in = _draw(rng, "normal1", m * n).reshape(m, n)
+    bias = _draw(rng, "normal1", n)
+    return np.ascontiguousarray(c_in), bias
 
 
 def workload_operands(w: Workload | str, integer: bool = False):
