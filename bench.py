@@ -14,6 +14,9 @@ synchronisation; rank 0 prints one JSON line:
 
 Other workloads: ``--workload ffn`` etc. (see workloads.WORKLOADS);
 ``--all`` also appends a line per workload to the file given by ``--all-out``.
+``--layout-a col`` stores A column-major; ``--epilogue relu|gelu|bias``
+times the fused linear-layer epilogue act(A.B + bias) (``bias``: no
+activation).
 """
 from __future__ import annotations
 
@@ -79,24 +82,29 @@ def parse():
     p.add_argument("--all-out", default="gpurun_out/bench_all.jsonl")
     p.add_argument("--rotate", type=int, default=1,
                    help="cycle through this many operand sets (defeats the Infinity Cache for small workloads)")
+    p.add_argument("--layout-a", choices=["row", "col"], default="row")
+    p.add_argument("--epilogue", choices=["none", "bias", "relu", "gelu"], default="none")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="first run one elementwise copy of MIB MiB (reads and writes MIB MiB), "
                         "the reference kernel for scaling the FETCH_SIZE/WRITE_SIZE counters")
     return p.parse_args()
 
 
-def time_workload(name, steps, warmup, variant=None, rotate=1):
+def time_workload(name, steps, warmup, variant=None, rotate=1, layout_a=0, epilogue="none"):
     import numpy as np
     import torch
 
     import dense_gemm_optimisation_fp32_amd as g
     from dense_gemm_optimisation_fp32_amd import perfmodel as pm
-    from workloads import WORKLOADS, workload_operands
+    from workloads import WORKLOADS, epilogue_operands, random_operands, workload_operands
 
     w = WORKLOADS[name]
-    A, B = workload_operands(w)
+    if layout_a == 0:
+        A, B = workload_operands(w)
+    else:
+        A, B = random_operands(w.m, w.n, w.k, w.layout_b, w.dist, w.seed, layout_a=layout_a)
     dev = torch.device("cuda", 0)
-    lda = w.k
+    lda = w.k if layout_a == 0 else w.m
     ldb = w.n if w.layout_b == 0 else w.k
     # `rotate` distinct operand sets, used in turn, so that a workload smaller
     # than the 256 MB Infinity Cache is still read from HBM at every step.
@@ -107,18 +115,27 @@ def time_workload(name, steps, warmup, variant=None, rotate=1):
         dC = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
         sets.append((dA, dB, dC))
     ptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr()) for a, b, c in sets]
-    plan = g.get_plan(w.m, w.n, w.k, w.layout_b, lda, ldb, w.n, variant, 0)
+    fused = epilogue != "none"
+    plan = g.get_plan(w.m, w.n, w.k, w.layout_b, lda, ldb, w.n, variant, 0, layout_a, 1 if fused else 0)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
+    if fused:
+        bias = torch.from_numpy(epilogue_operands(1, w.n, seed=w.seed + 2000)[1]).to(dev)
+        act = {"bias": 0, "relu": 1, "gelu": 2}[epilogue]
+
+        def plan_run(a, b, c, st):
+            plan.run_ex(a, b, c, 1.0, 0.0, bias.data_ptr(), act, st)
+    else:
+        plan_run = plan.run
 
     for i in range(warmup):
-        plan.run(*ptrs[i % rotate], sh)
+        plan_run(*ptrs[i % rotate], sh)
     torch.cuda.synchronize()
 
     # Timed region: exactly `steps` launches, wall clock bracketed by syncs.
     t0 = time.perf_counter()
     for i in range(steps):
-        plan.run(*ptrs[i % rotate], sh)
+        plan_run(*ptrs[i % rotate], sh)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -129,7 +146,7 @@ def time_workload(name, steps, warmup, variant=None, rotate=1):
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for i in range(steps):
-        plan.run(*ptrs[i % rotate], sh)
+        plan_run(*ptrs[i % rotate], sh)
     ev1.record(stream)
     torch.cuda.synchronize()
     kernel_avg = ev0.elapsed_time(ev1) / 1e3 / steps
@@ -224,7 +241,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    res = time_workload(args.workload, args.steps, args.warmup, args.variant, args.rotate)
+    res = time_workload(args.workload, args.steps, args.warmup, args.variant, args.rotate,
+                        0 if args.layout_a == "row" else 1, args.epilogue)
     w = res["workload"]
     line = {
         "metric": METRIC if w.name == HEADLINE else f"FP32 GEMM TFLOPS (2MNK/t), {w.name}",
@@ -239,8 +257,11 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: C=A.B, M={w.m} N={w.n} K={w.k}, A/C row-major, "
-                               f"B {'row' if w.layout_b == 0 else 'column'}-major, {w.dist}, seed {w.seed}",
+        "config": {"workload": f"{w.name}: C=A.B, M={w.m} N={w.n} K={w.k}, "
+                               f"A {'row' if args.layout_a == 'row' else 'column'}-major, C row-major, "
+                               f"B {'row' if w.layout_b == 0 else 'column'}-major, {w.dist}, seed {w.seed}"
+                               + ("" if args.epilogue == "none" else f", fused epilogue: {args.epilogue}"
+                                  + ("" if args.epilogue == "bias" else " of A.B + bias")),
                    "operand_sets": args.rotate,
                    "m": w.m, "n": w.n, "k": w.k, "layout_b": "row" if w.layout_b == 0 else "col",
                    "kernel": res["plan"]["name"], "grid": res["plan"]["grid"],

@@ -7,7 +7,8 @@ ABI in include/gemm_f32.h; functions return Python values and raise
 library is not built, loading it raises.
 
     import torch, dense_gemm_optimisation_fp32_amd as g
-    C = g.matmul(A, B)          # A (M,K) row-major; B (K,N) row- or column-major
+    C = g.matmul(A, B)          # A (M,K), B (K,N), each row- or column-major
+    Y = g.linear(X, W, bias, activation="gelu")   # act(X.W + bias), fused
 """
 from __future__ import annotations
 
@@ -30,6 +31,11 @@ GEMM_F32_ERR_UNSUPPORTED_DEVICE = 3
 GEMM_F32_ERR_HIP = 4
 GEMM_F32_ERR_ALLOC = 5
 
+GEMM_F32_ACT_NONE = 0
+GEMM_F32_ACT_RELU = 1
+GEMM_F32_ACT_GELU = 2
+_ACTIVATIONS = {None: 0, "none": 0, "relu": 1, "gelu": 2, 0: 0, 1: 1, 2: 2}
+
 GEMM_F32_KIND_MFMA = 0
 GEMM_F32_KIND_VALU = 1
 GEMM_F32_KIND_SKINNY = 2
@@ -37,7 +43,8 @@ GEMM_F32_KIND_SKINNY = 2
 EXPORTED_FUNCTIONS = (
     "gemm_f32_validate", "gemm_f32_create", "gemm_f32_create_variant", "gemm_f32_run",
     "gemm_f32_destroy", "gemm_f32_describe", "gemm_f32_num_variants", "gemm_f32_variant_info",
-    "gemm_f32_error_string", "gemm_f32_last_hip_error",
+    "gemm_f32_error_string", "gemm_f32_last_hip_error", "gemm_f32_validate_ex", "gemm_f32_create_ex",
+    "gemm_f32_run_ex",
 )
 
 
@@ -49,7 +56,8 @@ class gemm_f32_info(ctypes.Structure):
         ("wave_m", ctypes.c_int), ("wave_n", ctypes.c_int),
         ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int), ("stages", ctypes.c_int),
         ("split_k", ctypes.c_int), ("stream_k", ctypes.c_int),
-        ("stream_k_tiles", ctypes.c_int), ("aligned", ctypes.c_int),
+        ("stream_k_tiles", ctypes.c_int), ("layout_a", ctypes.c_int), ("epilogue", ctypes.c_int),
+        ("aligned", ctypes.c_int),
         ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("k_tiles", ctypes.c_int64),
         ("grid", ctypes.c_int64), ("group_m", ctypes.c_int), ("name", ctypes.c_char * 64),
     ]
@@ -97,6 +105,9 @@ def load_library():
             "gemm_f32_variant_info": ([i32, info_p], i32),
             "gemm_f32_error_string": ([i32], ctypes.c_char_p),
             "gemm_f32_last_hip_error": ([], i32),
+            "gemm_f32_validate_ex": ([i64, i64, i64, i32, i32, i64, i64, i64], i32),
+            "gemm_f32_create_ex": ([plan_p, i64, i64, i64, i32, i32, i64, i64, i64, i32], i32),
+            "gemm_f32_run_ex": ([vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp, i32, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -136,6 +147,25 @@ def gemm_f32_run(plan, A_ptr, B_ptr, C_ptr, stream=None) -> None:
         raise GemmF32Error(st, "gemm_f32_run")
 
 
+def gemm_f32_validate_ex(m, n, k, layout_a, layout_b, lda, ldb, ldc) -> int:
+    return int(load_library().gemm_f32_validate_ex(m, n, k, layout_a, layout_b, lda, ldb, ldc))
+
+
+def gemm_f32_create_ex(m, n, k, layout_a, layout_b, lda, ldb, ldc, epilogue=0) -> int:
+    h = ctypes.c_void_p()
+    st = load_library().gemm_f32_create_ex(ctypes.byref(h), m, n, k, layout_a, layout_b, lda, ldb, ldc, epilogue)
+    if st != GEMM_F32_SUCCESS:
+        raise GemmF32Error(st, "gemm_f32_create_ex")
+    return h.value
+
+
+def gemm_f32_run_ex(plan, A_ptr, B_ptr, C_ptr, alpha=1.0, beta=0.0, bias_ptr=None, activation=0,
+                    stream=None) -> None:
+    st = load_library().gemm_f32_run_ex(plan, A_ptr, B_ptr, C_ptr, alpha, beta, bias_ptr, activation, stream)
+    if st != GEMM_F32_SUCCESS:
+        raise GemmF32Error(st, "gemm_f32_run_ex")
+
+
 def gemm_f32_destroy(plan) -> None:
     load_library().gemm_f32_destroy(plan)
 
@@ -171,11 +201,15 @@ def gemm_f32_last_hip_error() -> int:
 # --- torch-tensor convenience (marshalling only) ------------------------------
 
 class Plan:
-    """Owns a plan handle for one (shape, layout, strides, variant)."""
+    """Owns a plan handle for one (shape, layouts, strides, variant, epilogue)."""
 
-    def __init__(self, m, n, k, layout_b, lda, ldb, ldc, variant=None):
-        self.key = (m, n, k, layout_b, lda, ldb, ldc, variant)
-        if variant is None:
+    def __init__(self, m, n, k, layout_b, lda, ldb, ldc, variant=None, layout_a=0, epilogue=0):
+        self.key = (m, n, k, layout_b, lda, ldb, ldc, variant, layout_a, epilogue)
+        if layout_a != GEMM_F32_ROW_MAJOR or epilogue:
+            if variant is not None:
+                raise ValueError("column-major A and the epilogue use the default variant choice")
+            self.handle = gemm_f32_create_ex(m, n, k, layout_a, layout_b, lda, ldb, ldc, epilogue)
+        elif variant is None:
             self.handle = gemm_f32_create(m, n, k, layout_b, lda, ldb, ldc)
         else:
             self.handle = gemm_f32_create_variant(variant, m, n, k, layout_b, lda, ldb, ldc)
@@ -183,6 +217,9 @@ class Plan:
 
     def run(self, A_ptr, B_ptr, C_ptr, stream=None):
         gemm_f32_run(self.handle, A_ptr, B_ptr, C_ptr, stream)
+
+    def run_ex(self, A_ptr, B_ptr, C_ptr, alpha=1.0, beta=0.0, bias_ptr=None, activation=0, stream=None):
+        gemm_f32_run_ex(self.handle, A_ptr, B_ptr, C_ptr, alpha, beta, bias_ptr, activation, stream)
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -194,34 +231,45 @@ class Plan:
 _plan_cache: dict = {}
 
 
-def get_plan(m, n, k, layout_b, lda, ldb, ldc, variant=None, device=None) -> Plan:
-    key = (device, m, n, k, layout_b, lda, ldb, ldc, variant)
+def get_plan(m, n, k, layout_b, lda, ldb, ldc, variant=None, device=None, layout_a=0, epilogue=0) -> Plan:
+    key = (device, m, n, k, layout_b, lda, ldb, ldc, variant, layout_a, epilogue)
     p = _plan_cache.get(key)
     if p is None:
-        p = Plan(m, n, k, layout_b, lda, ldb, ldc, variant)
+        p = Plan(m, n, k, layout_b, lda, ldb, ldc, variant, layout_a, epilogue)
         _plan_cache[key] = p
     return p
 
 
-def operand_strides(A: torch.Tensor, B: torch.Tensor, layout_b=None):
-    """(m, n, k, layout_b, lda, ldb) from tensor shapes and strides.
+def operand_strides(A: torch.Tensor, B: torch.Tensor, layout_b=None, layout_a=None):
+    """(m, n, k, layout_a, layout_b, lda, ldb) from tensor shapes and strides.
 
-    A is (M, K) with unit stride along K.  B is the logical (K, N) matrix:
-    unit stride along N means row-major, unit stride along K (a transposed
-    view of an (N, K) row-major tensor) means column-major."""
+    A is the logical (M, K) matrix: unit stride along K means row-major, unit
+    stride along M (a transposed view of a (K, M) tensor) column-major.  B is
+    the logical (K, N) matrix: unit stride along N means row-major, unit
+    stride along K column-major."""
     if A.dim() != 2 or B.dim() != 2:
         raise ValueError("A and B must be 2-D")
     m, k = A.shape
     k2, n = B.shape
     if k != k2:
         raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
-    if A.stride(1) != 1 and m > 1 and k > 1:
-        raise ValueError("A must be row-major (unit stride along K)")
-    lda = A.stride(0) if m > 1 else k
+    layouts = {"row": GEMM_F32_ROW_MAJOR, "col": GEMM_F32_COL_MAJOR}
+    if layout_a is None:
+        layout_a = GEMM_F32_ROW_MAJOR if (A.stride(1) == 1 or k == 1) else GEMM_F32_COL_MAJOR
+    if isinstance(layout_a, str):
+        layout_a = layouts[layout_a]
+    if layout_a == GEMM_F32_ROW_MAJOR:
+        if A.stride(1) != 1 and m > 1 and k > 1:
+            raise ValueError("row-major A needs unit stride along K")
+        lda = A.stride(0) if m > 1 else k
+    else:
+        if A.stride(0) != 1 and m > 1:
+            raise ValueError("column-major A needs unit stride along M")
+        lda = A.stride(1) if k > 1 else m
     if layout_b is None:
         layout_b = GEMM_F32_ROW_MAJOR if (B.stride(1) == 1 or n == 1) else GEMM_F32_COL_MAJOR
     if isinstance(layout_b, str):
-        layout_b = {"row": GEMM_F32_ROW_MAJOR, "col": GEMM_F32_COL_MAJOR}[layout_b]
+        layout_b = layouts[layout_b]
     if layout_b == GEMM_F32_ROW_MAJOR:
         if B.stride(1) != 1 and n > 1:
             raise ValueError("row-major B needs unit stride along N")
@@ -230,26 +278,57 @@ def operand_strides(A: torch.Tensor, B: torch.Tensor, layout_b=None):
         if B.stride(0) != 1 and k > 1:
             raise ValueError("column-major B needs unit stride along K")
         ldb = B.stride(1) if n > 1 else k
-    return m, n, k, layout_b, lda, ldb
+    return m, n, k, layout_a, layout_b, lda, ldb
+
+
+def _check_pair(A, B):
+    if A.dtype != torch.float32 or B.dtype != torch.float32:
+        raise TypeError("float32 operands only")
+    if not (A.is_cuda and B.is_cuda) or A.device != B.device:
+        raise ValueError("A and B must be on the same GPU")
+
+
+def _output(out, m, n, device):
+    if out is None:
+        return torch.empty((m, n), dtype=torch.float32, device=device)
+    if out.shape != (m, n) or out.dtype != torch.float32 or out.device != device:
+        raise ValueError("out must be a float32 (M, N) tensor on A's device")
+    if out.stride(1) != 1 and n > 1:
+        raise ValueError("out must be row-major")
+    return out
 
 
 def matmul(A: torch.Tensor, B: torch.Tensor, layout_b=None, out: torch.Tensor | None = None,
            variant: int | None = None) -> torch.Tensor:
     """C = A.B on A's device and the current stream (float32 only)."""
-    if A.dtype != torch.float32 or B.dtype != torch.float32:
-        raise TypeError("float32 operands only")
-    if not (A.is_cuda and B.is_cuda) or A.device != B.device:
-        raise ValueError("A and B must be on the same GPU")
-    m, n, k, layout_b, lda, ldb = operand_strides(A, B, layout_b)
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float32, device=A.device)
-    else:
-        if out.shape != (m, n) or out.dtype != torch.float32 or out.device != A.device:
-            raise ValueError("out must be a float32 (M, N) tensor on A's device")
-        if out.stride(1) != 1 and n > 1:
-            raise ValueError("out must be row-major")
+    _check_pair(A, B)
+    m, n, k, layout_a, layout_b, lda, ldb = operand_strides(A, B, layout_b)
+    out = _output(out, m, n, A.device)
     ldc = out.stride(0) if m > 1 else n
-    plan = get_plan(m, n, k, layout_b, lda, ldb, ldc, variant, A.device.index)
+    plan = get_plan(m, n, k, layout_b, lda, ldb, ldc, variant, A.device.index, layout_a)
     stream = torch.cuda.current_stream(A.device).cuda_stream
     plan.run(A.data_ptr(), B.data_ptr(), out.data_ptr(), stream)
+    return out
+
+
+def linear(A: torch.Tensor, B: torch.Tensor, bias: torch.Tensor | None = None, activation=None,
+           alpha: float = 1.0, beta: float = 0.0, out: torch.Tensor | None = None) -> torch.Tensor:
+    """C = act(alpha * A.B + beta * C + bias) in one kernel (float32 only);
+    ``activation`` is None/"none", "relu" or "gelu"; ``out`` supplies C when
+    beta != 0."""
+    _check_pair(A, B)
+    act = _ACTIVATIONS[activation]
+    m, n, k, layout_a, layout_b, lda, ldb = operand_strides(A, B)
+    if beta != 0.0 and out is None:
+        raise ValueError("beta != 0 reads C: pass it as out")
+    out = _output(out, m, n, A.device)
+    ldc = out.stride(0) if m > 1 else n
+    bias_ptr = None
+    if bias is not None:
+        if bias.dtype != torch.float32 or bias.device != A.device or bias.numel() != n or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous float32 tensor of N values on A's device")
+        bias_ptr = bias.data_ptr()
+    plan = get_plan(m, n, k, layout_b, lda, ldb, ldc, None, A.device.index, layout_a, 1)
+    stream = torch.cuda.current_stream(A.device).cuda_stream
+    plan.run_ex(A.data_ptr(), B.data_ptr(), out.data_ptr(), alpha, beta, bias_ptr, act, stream)
     return out

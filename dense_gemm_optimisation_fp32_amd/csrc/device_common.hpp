@@ -43,6 +43,11 @@ struct GemmArgs {
     int split_k;           // number of k-splits (skinny path), else 1
     int k_per_split;       // k values per split (multiple of the k tile)
     int masked_loads;      // 1: check every element in every slab (tiny ldb)
+    // Linear-layer epilogue (kernels built with it): act(alpha * AB + beta * C + bias[col]).
+    float alpha, beta;
+    const float *bias;     // N values, or NULL
+    int use_beta;          // beta != 0: C is read
+    int act;               // 0 none, 1 ReLU, 2 GELU (x * Phi(x))
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
@@ -132,6 +137,22 @@ __device__ __forceinline__ float wait_tagged_word(const unsigned long long *p, u
         w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return __uint_as_float((unsigned)w);
+}
+
+// GELU(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt(2))).  erf by Abramowitz
+// and Stegun, formula 7.1.26 (|error| <= 1.5e-7 on z >= 0): with
+// t = 1 / (1 + p z) and y = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^(-z^2),
+// erf(z) = 1 - y.  erf is odd, so 1 + erf(z) = 2 - y for z >= 0 and y(|z|)
+// for z < 0: no cancellation on the negative side.  A handful of registers,
+// where the library erff, unrolled over a block of outputs, took a hundred.
+__device__ __forceinline__ float gelu_erf(float x)
+{
+    const float z = fabsf(x) * 0.70710678118654752f;
+    const float t = 1.0f / (1.0f + 0.3275911f * z);
+    const float poly =
+        t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+    const float y = poly * __expf(-z * z);
+    return 0.5f * x * (x >= 0.0f ? 2.0f - y : y);
 }
 
 __device__ __forceinline__ unsigned long long load_tagged_word(const unsigned long long *p)

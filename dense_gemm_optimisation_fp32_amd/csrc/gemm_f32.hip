@@ -43,6 +43,7 @@ struct VariantDesc {
     int stages;
     const void *fn[2];     // [column-major B]
     const void *fn_sk[2];  // stream-K kernels (tiles' k-slabs shared across workgroups), or NULL
+    const void *fn_ex[2][2][2];  // [column-major A][column-major B][epilogue], or NULL
 };
 
 template <class T>
@@ -63,6 +64,24 @@ VariantDesc dma_variant(const char *name)
          reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_kernel<T, true>)},
         {reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_sk_kernel<T, false>),
          reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_sk_kernel<T, true>)}};
+}
+
+// A DMA variant that also serves column-major A and the linear-layer
+// epilogue.
+template <class T>
+VariantDesc dma_ex_variant(const char *name)
+{
+    using namespace gemmf32;
+    VariantDesc d = dma_variant<T>(name);
+    d.fn_ex[0][0][0] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, false, false, false>);
+    d.fn_ex[0][1][0] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, true, false, false>);
+    d.fn_ex[1][0][0] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, false, true, false>);
+    d.fn_ex[1][1][0] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, true, true, false>);
+    d.fn_ex[0][0][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, false, false, true>);
+    d.fn_ex[0][1][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, true, false, true>);
+    d.fn_ex[1][0][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, false, true, true>);
+    d.fn_ex[1][1][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, true, true, true>);
+    return d;
 }
 
 template <class T>
@@ -121,12 +140,12 @@ const VariantDesc &variant(int v)
         dma_variant<DmaTile<256, 256, 16, 2, 2, 3>>("dma_256x256x16_w2x2_s3"),
         dma_variant<DmaTile<256, 256, 16, 2, 2, 4>>("dma_256x256x16_w2x2_s4"),
         dma_variant<DmaTile<256, 256, 32, 2, 2, 2>>("dma_256x256x32_w2x2_s2"),
-        dma_variant<DmaTile<128, 128, 16, 2, 2, 3>>("dma_128x128x16_w2x2_s3"),
+        dma_ex_variant<DmaTile<128, 128, 16, 2, 2, 3>>("dma_128x128x16_w2x2_s3"),
         dma_variant<DmaTile<128, 128, 32, 2, 2, 3>>("dma_128x128x32_w2x2_s3"),
-        dma_variant<DmaTile<256, 128, 16, 2, 2, 3>>("dma_256x128x16_w2x2_s3"),
+        dma_ex_variant<DmaTile<256, 128, 16, 2, 2, 3>>("dma_256x128x16_w2x2_s3"),
         skinny_variant<SkinnyTile<4, 4, 64>>("skinny_16x64_w4_d4"),
         skinny_variant<SkinnyTile<8, 4, 64>>("skinny_16x64_w8_d4"),
-        dma_variant<DmaTile<64, 64, 16, 2, 2, 3>>("dma_64x64x16_w2x2_s3"),
+        dma_ex_variant<DmaTile<64, 64, 16, 2, 2, 3>>("dma_64x64x16_w2x2_s3"),
         skinny_variant<SkinnyTile<16, 4, 64>>("skinny_16x64_w16_d4"),
         skinny_variant<SkinnyTile<16, 4, 16>>("skinny_16x16_w16_d4"),
     };
@@ -207,7 +226,10 @@ int env_int(const char *name, int fallback)
 struct gemm_f32_plan_impl {
     int variant;
     int device;
+    int layout_a;
     int layout_b;
+    int epilogue;        // 1: built with the linear-layer epilogue (gemm_f32_run_ex)
+    const void *fn;      // the kernel run launches
     int64_t m, n, k, lda, ldb, ldc;
     bool strides4;       // every leading dimension is a multiple of 4 (informational)
     GemmArgs args;       // pointers filled at run time
@@ -239,14 +261,17 @@ int choose_variant(int64_t m, int64_t n, int64_t k, const DeviceFacts &f, bool *
     return V_DMA_64x64x16_S3;
 }
 
-int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int64_t k, int layout_b,
-              int64_t lda, int64_t ldb, int64_t ldc)
+int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int64_t k, int layout_a,
+              int layout_b, int64_t lda, int64_t ldb, int64_t ldc, int epilogue)
 {
     if (!out) return GEMM_F32_ERR_INVALID_VALUE;
     *out = nullptr;
-    int st = gemm_f32_validate(m, n, k, layout_b, lda, ldb, ldc);
+    int st = gemm_f32_validate_ex(m, n, k, layout_a, layout_b, lda, ldb, ldc);
     if (st != GEMM_F32_SUCCESS) return st;
-    if (forced_variant >= V_COUNT) return GEMM_F32_ERR_INVALID_VALUE;
+    if (forced_variant >= V_COUNT || (epilogue != 0 && epilogue != 1)) return GEMM_F32_ERR_INVALID_VALUE;
+    // Column-major A and the epilogue have kernels in the three default
+    // tiled variants only.
+    const bool ex = layout_a == GEMM_F32_COL_MAJOR || epilogue;
 
     int dev = 0;
     DeviceFacts facts;
@@ -258,14 +283,20 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     if (v < 0) {
         v = env_int("GEMM_F32_VARIANT", -1);
         if (v < 0 || v >= V_COUNT) v = choose_variant(m, n, k, facts, &auto_stream_k);
+        if (ex && !variant(v).fn_ex[0][0][0]) v = V_DMA_64x64x16_S3;
     }
     const VariantDesc &d = variant(v);
+    if (ex && !d.fn_ex[0][0][0]) return GEMM_F32_ERR_INVALID_VALUE;
+    if (ex) auto_stream_k = false;
 
     gemm_f32_plan p = new (std::nothrow) gemm_f32_plan_impl();
     if (!p) return GEMM_F32_ERR_ALLOC;
     p->variant = v;
     p->device = dev;
+    p->layout_a = layout_a;
     p->layout_b = layout_b;
+    p->epilogue = epilogue;
+    p->fn = ex ? d.fn_ex[layout_a][layout_b][epilogue] : d.fn[layout_b];
     p->m = m; p->n = n; p->k = k;
     p->lda = lda; p->ldb = ldb; p->ldc = ldc;
     p->strides4 = lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0;
@@ -280,7 +311,9 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     a.group_m = env_int("GEMM_F32_GROUP_M", 8);
     if (a.group_m < 1) a.group_m = 1;
     a.num_xcd = facts.num_xcd;
-    a.a_bytes = (uint32_t)(((m - 1) * lda + k) * 4);
+    a.a_bytes = (uint32_t)((layout_a == GEMM_F32_ROW_MAJOR ? (m - 1) * lda + k : (k - 1) * lda + m) * 4);
+    a.alpha = 1.0f;
+    a.beta = 0.0f;
     a.b_bytes = (uint32_t)((layout_b == GEMM_F32_ROW_MAJOR ? (k - 1) * ldb + n : (n - 1) * ldb + k) * 4);
     a.c_bytes = (uint32_t)(((m - 1) * ldc + n) * 4);
     a.split_k = 1;
@@ -333,7 +366,7 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
         // measured no faster: a lone workgroup runs a CU at ~92 % of the
         // throughput of two, and the partial sums cost the rest.)
         const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
-        int64_t wgs = env_int("GEMM_F32_SK_WGS", 0);
+        int64_t wgs = ex ? 0 : env_int("GEMM_F32_SK_WGS", 0);
         int64_t shared = wgs > 0 ? env_int("GEMM_F32_SK_TILES", (int)tiles) : tiles;
         if (wgs <= 0 && auto_stream_k && env_int("GEMM_F32_STREAMK", 1) != 0) {
             int per_cu = 0;
@@ -397,11 +430,14 @@ void fill_static_info(int v, gemm_f32_info *info)
 
 extern "C" {
 
-int gemm_f32_validate(int64_t m, int64_t n, int64_t k, int layout_b, int64_t lda, int64_t ldb, int64_t ldc)
+int gemm_f32_validate_ex(int64_t m, int64_t n, int64_t k, int layout_a, int layout_b, int64_t lda, int64_t ldb,
+                         int64_t ldc)
 {
     if (m < 1 || n < 1 || k < 1) return GEMM_F32_ERR_INVALID_VALUE;
+    if (layout_a != GEMM_F32_ROW_MAJOR && layout_a != GEMM_F32_COL_MAJOR) return GEMM_F32_ERR_INVALID_VALUE;
     if (layout_b != GEMM_F32_ROW_MAJOR && layout_b != GEMM_F32_COL_MAJOR) return GEMM_F32_ERR_INVALID_VALUE;
-    if (lda < k || ldc < n) return GEMM_F32_ERR_INVALID_VALUE;
+    if (ldc < n) return GEMM_F32_ERR_INVALID_VALUE;
+    if (layout_a == GEMM_F32_ROW_MAJOR ? lda < k : lda < m) return GEMM_F32_ERR_INVALID_VALUE;
     if (layout_b == GEMM_F32_ROW_MAJOR ? ldb < n : ldb < k) return GEMM_F32_ERR_INVALID_VALUE;
     // Byte extents below 2^31: 32-bit buffer offsets address every element
     // and the out-of-range offset 2^31 is never a valid element.
@@ -409,17 +445,28 @@ int gemm_f32_validate(int64_t m, int64_t n, int64_t k, int layout_b, int64_t lda
     const int64_t cap = limit / 4;  // elements; also bounds each factor against overflow
     if (m >= cap || n >= cap || k >= cap || lda >= cap || ldb >= cap || ldc >= cap)
         return GEMM_F32_ERR_INVALID_VALUE;
-    const int64_t a_ext = (m - 1) * lda + k;
+    const int64_t a_ext = layout_a == GEMM_F32_ROW_MAJOR ? (m - 1) * lda + k : (k - 1) * lda + m;
     const int64_t b_ext = layout_b == GEMM_F32_ROW_MAJOR ? (k - 1) * ldb + n : (n - 1) * ldb + k;
     const int64_t c_ext = (m - 1) * ldc + n;
     if (a_ext >= cap || b_ext >= cap || c_ext >= cap) return GEMM_F32_ERR_INVALID_VALUE;
     return GEMM_F32_SUCCESS;
 }
 
+int gemm_f32_validate(int64_t m, int64_t n, int64_t k, int layout_b, int64_t lda, int64_t ldb, int64_t ldc)
+{
+    return gemm_f32_validate_ex(m, n, k, GEMM_F32_ROW_MAJOR, layout_b, lda, ldb, ldc);
+}
+
 int gemm_f32_create(gemm_f32_plan *out, int64_t m, int64_t n, int64_t k, int layout_b, int64_t lda,
                     int64_t ldb, int64_t ldc)
 {
-    return make_plan(out, -1, m, n, k, layout_b, lda, ldb, ldc);
+    return make_plan(out, -1, m, n, k, GEMM_F32_ROW_MAJOR, layout_b, lda, ldb, ldc, 0);
+}
+
+int gemm_f32_create_ex(gemm_f32_plan *out, int64_t m, int64_t n, int64_t k, int layout_a, int layout_b,
+                       int64_t lda, int64_t ldb, int64_t ldc, int epilogue)
+{
+    return make_plan(out, -1, m, n, k, layout_a, layout_b, lda, ldb, ldc, epilogue);
 }
 
 int gemm_f32_create_variant(gemm_f32_plan *out, int v, int64_t m, int64_t n, int64_t k, int layout_b,
@@ -429,23 +476,13 @@ int gemm_f32_create_variant(gemm_f32_plan *out, int v, int64_t m, int64_t n, int
         if (out) *out = nullptr;
         return GEMM_F32_ERR_INVALID_VALUE;
     }
-    return make_plan(out, v, m, n, k, layout_b, lda, ldb, ldc);
+    return make_plan(out, v, m, n, k, GEMM_F32_ROW_MAJOR, layout_b, lda, ldb, ldc, 0);
 }
 
-int gemm_f32_run(gemm_f32_plan p, const float *A, const float *B, float *C, void *stream)
-{
-    if (!p || !A || !B || !C) return GEMM_F32_ERR_INVALID_VALUE;
-    const uintptr_t ua = reinterpret_cast<uintptr_t>(A), ub = reinterpret_cast<uintptr_t>(B),
-                    uc = reinterpret_cast<uintptr_t>(C);
-    if ((ua | ub | uc) & 3u) return GEMM_F32_ERR_INVALID_VALUE;
+namespace {
 
-    GemmArgs a = p->args;
-    a.A = A;
-    a.B = B;
-    a.C = C;
-    const VariantDesc &d = variant(p->variant);
-    const int col = p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0;
-    const void *fn = p->args.sk_wgs ? d.fn_sk[col] : d.fn[col];
+int launch(gemm_f32_plan p, GemmArgs &a, void *stream)
+{
     void *kargs[] = {&a};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (p->workspace) {
@@ -454,9 +491,51 @@ int gemm_f32_run(gemm_f32_plan p, const float *A, const float *B, float *C, void
         if (ep == 0) ep = ++p->runs;
         a.epoch = ep;
     }
+    const int col = p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0;
+    const void *fn = p->args.sk_wgs ? variant(p->variant).fn_sk[col] : p->fn;
     hipError_t e = hipLaunchKernel(fn, dim3(p->grid), dim3(p->block), kargs, 0, s);
     if (e != hipSuccess) return hip_fail(e);
     return GEMM_F32_SUCCESS;
+}
+
+bool pointers_ok(const float *A, const float *B, const float *C)
+{
+    if (!A || !B || !C) return false;
+    const uintptr_t ua = reinterpret_cast<uintptr_t>(A), ub = reinterpret_cast<uintptr_t>(B),
+                    uc = reinterpret_cast<uintptr_t>(C);
+    return ((ua | ub | uc) & 3u) == 0;
+}
+
+}  // namespace
+
+int gemm_f32_run(gemm_f32_plan p, const float *A, const float *B, float *C, void *stream)
+{
+    if (!p || !pointers_ok(A, B, C)) return GEMM_F32_ERR_INVALID_VALUE;
+    GemmArgs a = p->args;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    return launch(p, a, stream);
+}
+
+int gemm_f32_run_ex(gemm_f32_plan p, const float *A, const float *B, float *C, float alpha, float beta,
+                    const float *bias, int activation, void *stream)
+{
+    if (!p || !pointers_ok(A, B, C)) return GEMM_F32_ERR_INVALID_VALUE;
+    if (activation < GEMM_F32_ACT_NONE || activation > GEMM_F32_ACT_GELU) return GEMM_F32_ERR_INVALID_VALUE;
+    if (bias && (reinterpret_cast<uintptr_t>(bias) & 3u)) return GEMM_F32_ERR_INVALID_VALUE;
+    const bool plain = alpha == 1.0f && beta == 0.0f && !bias && activation == GEMM_F32_ACT_NONE;
+    if (!plain && !p->epilogue) return GEMM_F32_ERR_INVALID_VALUE;
+    GemmArgs a = p->args;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.use_beta = beta != 0.0f ? 1 : 0;
+    a.bias = bias;
+    a.act = activation;
+    return launch(p, a, stream);
 }
 
 int gemm_f32_destroy(gemm_f32_plan p)
@@ -484,6 +563,8 @@ int gemm_f32_describe(gemm_f32_plan p, gemm_f32_info *info)
     info->split_k = p->args.split_k;
     info->stream_k = p->args.sk_wgs;
     info->stream_k_tiles = p->args.sk_tiles;
+    info->layout_a = p->layout_a;
+    info->epilogue = p->epilogue;
     return GEMM_F32_SUCCESS;
 }
 

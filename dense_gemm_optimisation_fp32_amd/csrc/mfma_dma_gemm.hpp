@@ -20,6 +20,11 @@
 //     ("PMPP Chapter 06", section 1: the unfavourable access pattern moves to
 //     on-chip memory).  Columns are block-major here (C column nb*32 + j).
 //
+// Column-major A (A[i][k] at A[k*lda + i]) is the mirror image of row-major
+// B: the tile lands m-contiguous, As_t[kr][mc], and one 16-byte read of a
+// k-row gives the A values of one k-step for the MB interleaved blocks (tile
+// row MB*l32 + mb of the wavefront tile for lane row l32 of block mb).
+//
 // Range checking is per 4-byte element: a chunk that straddles an operand's
 // byte extent keeps its in-range elements and reads zeros past the end, rows
 // of A (columns of column-major B) past m (n) get the out-of-range offset and
@@ -64,7 +69,7 @@ struct DmaPiece {
     int kc;          // logical 16-byte k-chunk (A and column-major B), n-chunk for row-major B
 };
 
-template <class T, bool B_COL>
+template <class T, bool B_COL, bool A_COL = false>
 __device__ __forceinline__ DmaPiece<T, B_COL> dma_piece(int j, int tid)
 {
     DmaPiece<T, B_COL> d;
@@ -72,8 +77,13 @@ __device__ __forceinline__ DmaPiece<T, B_COL> dma_piece(int j, int tid)
         const int c = tid + j * T::THREADS;
         d.lds_chunk = c;
         d.is_a = true;
-        d.row = c / T::ACH;
-        d.kc = (c % T::ACH) ^ swz_a<T::ACH>(d.row);
+        if constexpr (A_COL) {
+            d.row = c / (T::BM / 4);     // k-row
+            d.kc = c % (T::BM / 4);      // m-chunk
+        } else {
+            d.row = c / T::ACH;
+            d.kc = (c % T::ACH) ^ swz_a<T::ACH>(d.row);
+        }
     } else {
         const int c = tid + (j - T::A_PER_T) * T::THREADS;
         d.lds_chunk = c;
@@ -89,15 +99,18 @@ __device__ __forceinline__ DmaPiece<T, B_COL> dma_piece(int j, int tid)
     return d;
 }
 
-template <class T, bool B_COL>
+template <class T, bool B_COL, bool A_COL = false>
 __device__ __forceinline__ void dma_issue(int j, const GemmArgs &g, __amdgpu_buffer_rsrc_t ra,
                                           __amdgpu_buffer_rsrc_t rb, int row0, int col0, int kt, int tid,
                                           int wave, f32x4 *As, f32x4 *Bs)
 {
-    const DmaPiece<T, B_COL> d = dma_piece<T, B_COL>(j, tid);
+    const DmaPiece<T, B_COL> d = dma_piece<T, B_COL, A_COL>(j, tid);
     const int k0 = kt * T::BK;
     const int wave_base = (j < T::A_PER_T ? j : j - T::A_PER_T) * T::THREADS + wave * 64;
-    if (d.is_a) {
+    if (A_COL && d.is_a) {
+        const int gk = k0 + d.row;
+        dma16(ra, elem_off(gk < g.k, gk, g.lda, row0 + 4 * d.kc), As + wave_base);
+    } else if (d.is_a) {
         const int gr = row0 + d.row;
         dma16(ra, elem_off(gr < g.m, gr, g.lda, k0 + 4 * d.kc), As + wave_base);
     } else if constexpr (!B_COL) {
@@ -111,14 +124,14 @@ __device__ __forceinline__ void dma_issue(int j, const GemmArgs &g, __amdgpu_buf
 
 // Zero the elements k >= K of this lane's chunks of the last slab (A and
 // column-major B).  Runs after the lane's copies of that slab have landed.
-template <class T, bool B_COL>
+template <class T, bool B_COL, bool A_COL = false>
 __device__ __forceinline__ void dma_fix_tail(const GemmArgs &g, int kt, int tid, f32x4 *As, f32x4 *Bs)
 {
     const int k0 = kt * T::BK;
 #pragma unroll
     for (int j = 0; j < T::PIECES; ++j) {
-        const DmaPiece<T, B_COL> d = dma_piece<T, B_COL>(j, tid);
-        if (!d.is_a && !B_COL) continue;
+        const DmaPiece<T, B_COL> d = dma_piece<T, B_COL, A_COL>(j, tid);
+        if (d.is_a ? A_COL : !B_COL) continue;   // k-rows past K already read as zero
         float *p = reinterpret_cast<float *>((d.is_a ? As : Bs) + d.lds_chunk);
         const int gk = k0 + 4 * d.kc;
 #pragma unroll
@@ -139,11 +152,12 @@ __device__ __forceinline__ void wait_vmcnt()
 // Fragments of one wavefront for one slab.  A (and column-major B) come as
 // 16-byte k-chunks, double-buffered per chunk; row-major B as one read per
 // k-step, double-buffered per step.
-template <class T, bool B_COL>
+template <class T, bool B_COL, bool A_COL = false>
 struct DmaFrags {
     f32x4 af[2][T::MB];
     f32x4 bk[2][T::NB];        // column-major B: k-chunk q of block nb in bk[q & 1][nb]
     BFrag<T::NB> bf[2];        // row-major B: k-step p in bf[p & 1]
+    BFrag<T::MB> am[2];        // column-major A: k-step p in am[p & 1]
 };
 
 template <class T>
@@ -178,11 +192,33 @@ __device__ __forceinline__ void read_bn(const f32x4 *Bs, int wc, int l32, int ha
     }
 }
 
-template <class T, bool B_COL>
-__device__ __forceinline__ void dma_mfma_one(int i, int p, const DmaFrags<T, B_COL> &f, f32x16 (&acc)[T::MB][T::NB])
+// Column-major A without a swizzle (the copy lands m-contiguous).
+template <class T>
+__device__ __forceinline__ void read_am(const f32x4 *As, int wr, int l32, int half, int p, BFrag<T::MB> &af)
+{
+    const int kr = half * T::KH + p;
+    const f32x4 *arow = As + kr * (T::BM / 4);
+    if constexpr (T::MB == 4) {
+        const f32x4 t = arow[wr * (T::WM / 4) + l32];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) af.v[mb] = t[mb];
+    } else if constexpr (T::MB == 2) {
+        const float *cp = reinterpret_cast<const float *>(arow + wr * (T::WM / 4) + (l32 >> 1));
+        const f32x2 t = *reinterpret_cast<const f32x2 *>(cp + 2 * (l32 & 1));
+        af.v[0] = t[0];
+        af.v[1] = t[1];
+    } else {
+        const float *cp = reinterpret_cast<const float *>(arow + wr * (T::WM / 4) + (l32 >> 2));
+        af.v[0] = cp[l32 & 3];
+    }
+}
+
+template <class T, bool B_COL, bool A_COL = false>
+__device__ __forceinline__ void dma_mfma_one(int i, int p, const DmaFrags<T, B_COL, A_COL> &f,
+                                             f32x16 (&acc)[T::MB][T::NB])
 {
     const int mb = i / T::NB, nb = i % T::NB;
-    const float a = f.af[(p >> 2) & 1][mb][p & 3];
+    const float a = A_COL ? f.am[p & 1].v[mb] : f.af[(p >> 2) & 1][mb][p & 3];
     float b;
     if constexpr (B_COL) b = f.bk[(p >> 2) & 1][nb][p & 3];
     else b = f.bf[p & 1].v[nb];
@@ -191,15 +227,16 @@ __device__ __forceinline__ void dma_mfma_one(int i, int p, const DmaFrags<T, B_C
 
 // Reads for k-step p+1 issued at the top of k-step p (and the first reads of a
 // slab, p = -1).
-template <class T, bool B_COL>
+template <class T, bool B_COL, bool A_COL = false>
 __device__ __forceinline__ void dma_prefetch(int p_next, const f32x4 *As, const f32x4 *Bs, int wr, int wc, int l32,
-                                             int half, DmaFrags<T, B_COL> &f)
+                                             int half, DmaFrags<T, B_COL, A_COL> &f)
 {
     if ((p_next & 3) == 0) {
         const int q = p_next >> 2;
-        read_a<T>(As, wr, l32, half, q, f.af[q & 1]);
+        if constexpr (!A_COL) read_a<T>(As, wr, l32, half, q, f.af[q & 1]);
         if constexpr (B_COL) read_bk<T>(Bs, wc, l32, half, q, f.bk[q & 1]);
     }
+    if constexpr (A_COL) read_am<T>(As, wr, l32, half, p_next, f.am[p_next & 1]);
     if constexpr (!B_COL) read_bn<T>(Bs, wc, l32, half, p_next, f.bf[p_next & 1]);
 }
 
@@ -209,11 +246,11 @@ __device__ __forceinline__ void dma_prefetch(int p_next, const f32x4 *As, const 
 // end (-1: slab kt is the last one).  fix: zero the k tail of slab kt+1 after
 // it lands (uniform flag).  The barrier precedes the last k-step, whose MFMAs
 // cover the first LDS reads of slab kt+1.
-template <class T, bool B_COL, int WAIT>
+template <class T, bool B_COL, int WAIT, bool A_COL = false>
 __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 *lds_b, __amdgpu_buffer_rsrc_t ra,
                                          __amdgpu_buffer_rsrc_t rb, int row0, int col0, int kt, bool copy, bool fix,
                                          int tid, int wave, int wr, int wc, int l32, int half,
-                                         DmaFrags<T, B_COL> &f, f32x16 (&acc)[T::MB][T::NB])
+                                         DmaFrags<T, B_COL, A_COL> &f, f32x16 (&acc)[T::MB][T::NB])
 {
     constexpr int NM = T::MB * T::NB;
     constexpr int GAP = 2 * T::PIECES <= (T::KH - 1) * NM ? 2 : 1;
@@ -225,33 +262,33 @@ __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 
     const f32x4 *Bs = lds_b + cur * T::B_CHUNKS;
 #pragma unroll
     for (int p = 0; p < T::KH - 1; ++p) {
-        dma_prefetch<T, B_COL>(p + 1, As, Bs, wr, wc, l32, half, f);
+        dma_prefetch<T, B_COL, A_COL>(p + 1, As, Bs, wr, wc, l32, half, f);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
-            dma_mfma_one<T, B_COL>(i, p, f, acc);
+            dma_mfma_one<T, B_COL, A_COL>(i, p, f, acc);
             const int t = p * NM + i;
             if ((t + 1) % GAP == 0 && (t + 1) / GAP - 1 < T::PIECES && copy)
-                dma_issue<T, B_COL>((t + 1) / GAP - 1, g, ra, rb, row0, col0, kt + T::STAGES - 1, tid, wave,
+                dma_issue<T, B_COL, A_COL>((t + 1) / GAP - 1, g, ra, rb, row0, col0, kt + T::STAGES - 1, tid, wave,
                                     lds_a + cpy * T::A_CHUNKS, lds_b + cpy * T::B_CHUNKS);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
     if constexpr (WAIT >= 0) {
         wait_vmcnt<WAIT>();
-        if (fix) dma_fix_tail<T, B_COL>(g, kt + 1, tid, lds_a + nxt * T::A_CHUNKS, lds_b + nxt * T::B_CHUNKS);
+        if (fix) dma_fix_tail<T, B_COL, A_COL>(g, kt + 1, tid, lds_a + nxt * T::A_CHUNKS, lds_b + nxt * T::B_CHUNKS);
     }
     __syncthreads();
     if constexpr (WAIT >= 0)
-        dma_prefetch<T, B_COL>(0, lds_a + nxt * T::A_CHUNKS, lds_b + nxt * T::B_CHUNKS, wr, wc, l32, half, f);
+        dma_prefetch<T, B_COL, A_COL>(0, lds_a + nxt * T::A_CHUNKS, lds_b + nxt * T::B_CHUNKS, wr, wc, l32, half, f);
 #pragma unroll
-    for (int i = 0; i < NM; ++i) dma_mfma_one<T, B_COL>(i, T::KH - 1, f, acc);
+    for (int i = 0; i < NM; ++i) dma_mfma_one<T, B_COL, A_COL>(i, T::KH - 1, f, acc);
 }
 
 // Slabs [kt0, kt1) of one tile, accumulated into acc.  The ring stage of
 // slab kt is kt % STAGES.  Every LDS read of the range happens before its
 // last barrier, so the next range may start copying at once.
-template <class T, bool B_COL>
+template <class T, bool B_COL, bool A_COL = false>
 __device__ __forceinline__ void dma_range(const GemmArgs &g, f32x4 *lds_a, f32x4 *lds_b, __amdgpu_buffer_rsrc_t ra,
                                           __amdgpu_buffer_rsrc_t rb, int row0, int col0, int kt0, int kt1, int tid,
                                           int wave, int wr, int wc, int l32, int half,
@@ -259,7 +296,7 @@ __device__ __forceinline__ void dma_range(const GemmArgs &g, f32x4 *lds_a, f32x4
 {
     const int KT = g.k_tiles;
     const bool ktail = g.k % T::BK != 0;
-    DmaFrags<T, B_COL> f;
+    DmaFrags<T, B_COL, A_COL> f;
 
     // Prologue: copies of slabs kt0 .. kt0+STAGES-2, wait for slab kt0.
 #pragma unroll
@@ -268,15 +305,15 @@ __device__ __forceinline__ void dma_range(const GemmArgs &g, f32x4 *lds_a, f32x4
             const int st = (kt0 + s) % T::STAGES;
 #pragma unroll
             for (int j = 0; j < T::PIECES; ++j)
-                dma_issue<T, B_COL>(j, g, ra, rb, row0, col0, kt0 + s, tid, wave, lds_a + st * T::A_CHUNKS,
+                dma_issue<T, B_COL, A_COL>(j, g, ra, rb, row0, col0, kt0 + s, tid, wave, lds_a + st * T::A_CHUNKS,
                                     lds_b + st * T::B_CHUNKS);
         }
     wait_vmcnt<0>();
     const int st0 = kt0 % T::STAGES;
     if (kt0 + 1 == kt1 && kt1 == KT && ktail)
-        dma_fix_tail<T, B_COL>(g, kt0, tid, lds_a + st0 * T::A_CHUNKS, lds_b + st0 * T::B_CHUNKS);
+        dma_fix_tail<T, B_COL, A_COL>(g, kt0, tid, lds_a + st0 * T::A_CHUNKS, lds_b + st0 * T::B_CHUNKS);
     __syncthreads();
-    dma_prefetch<T, B_COL>(0, lds_a + st0 * T::A_CHUNKS, lds_b + st0 * T::B_CHUNKS, wr, wc, l32, half, f);
+    dma_prefetch<T, B_COL, A_COL>(0, lds_a + st0 * T::A_CHUNKS, lds_b + st0 * T::B_CHUNKS, wr, wc, l32, half, f);
 
     // Steady state: slab kt+1 is not the last one and slab kt+STAGES-1
     // exists, so STAGES-2 slabs' copies may stay in flight while waiting for
@@ -284,38 +321,85 @@ __device__ __forceinline__ void dma_range(const GemmArgs &g, f32x4 *lds_a, f32x4
     // complete, the k tail fixed when slab kt+1 is the tile's last.
     int kt = kt0;
     for (; kt + T::STAGES - 1 < kt1 && kt + 2 < kt1; ++kt)
-        dma_slab<T, B_COL, (T::STAGES - 2) * T::PIECES>(g, lds_a, lds_b, ra, rb, row0, col0, kt, true, false, tid,
+        dma_slab<T, B_COL, (T::STAGES - 2) * T::PIECES, A_COL>(g, lds_a, lds_b, ra, rb, row0, col0, kt, true, false, tid,
                                                          wave, wr, wc, l32, half, f, acc);
     for (; kt + 1 < kt1; ++kt)
-        dma_slab<T, B_COL, 0>(g, lds_a, lds_b, ra, rb, row0, col0, kt, kt + T::STAGES - 1 < kt1,
+        dma_slab<T, B_COL, 0, A_COL>(g, lds_a, lds_b, ra, rb, row0, col0, kt, kt + T::STAGES - 1 < kt1,
                               ktail && kt + 2 == KT, tid, wave, wr, wc, l32, half, f, acc);
-    dma_slab<T, B_COL, -1>(g, lds_a, lds_b, ra, rb, row0, col0, kt, false, false, tid, wave, wr, wc, l32, half, f,
+    dma_slab<T, B_COL, -1, A_COL>(g, lds_a, lds_b, ra, rb, row0, col0, kt, false, false, tid, wave, wr, wc, l32, half, f,
                            acc);
 }
 
-// Accumulators -> C.  Lane (l32, half), element v of block (mb, nb) is C row
-// mb*32 + 8*(v/4) + 4*half + v%4 of the wavefront tile; its column is
-// NB*l32 + nb (row-major B) or nb*32 + l32 (column-major B).  A single path
-// of range-checked element stores: with two copies of the store loop
-// (checked and unchecked) the register allocator starts moving the 256
-// accumulators around and spills.  Per instruction, 32 lanes write one row
-// segment: 128 contiguous bytes (column-major B) or every fourth float of 512
-// bytes, completed by the NB stores of the other blocks (row-major B).
-template <class T, bool B_COL>
+// Accumulators -> C.  Lane (l32, half), element v of block (mb, nb) is row
+// i = 8*(v/4) + 4*half + v%4 of the block: tile row mb*32 + i of the
+// wavefront tile (row-major A) or MB*i + mb (column-major A, interleaved
+// rows); its column is NB*l32 + nb (row-major B) or nb*32 + l32
+// (column-major B).  A single path of range-checked element stores: with
+// two copies of the store loop (checked and unchecked) the register
+// allocator starts moving the 256 accumulators around and spills.  Per
+// instruction, 32 lanes write one row segment: 128 contiguous bytes
+// (column-major B) or every fourth float of 512 bytes, completed by the NB
+// stores of the other blocks (row-major B).
+//
+// EPI: the linear-layer epilogue act(alpha * acc + beta * C + bias[col]),
+// with C read only when beta != 0.  The C values of one block are loaded
+// together before any is used, so the epilogue pays one memory latency per
+// block.
+template <class T, bool B_COL, bool A_COL = false, bool EPI = false>
 __device__ __forceinline__ void dma_store_c(const GemmArgs &g, __amdgpu_buffer_rsrc_t rc, int row0, int col0, int wr,
                                             int wc, int l32, int half, const f32x16 (&acc)[T::MB][T::NB])
 {
+    auto row_of = [&](int mb, int v) {
+        const int i = 8 * (v >> 2) + 4 * half + (v & 3);
+        return row0 + wr * T::WM + (A_COL ? T::MB * i + mb : mb * 32 + i);
+    };
+    auto col_of = [&](int nb) {
+        return B_COL ? col0 + wc * T::WN + nb * 32 + l32 : col0 + wc * T::WN + T::NB * l32 + nb;
+    };
+    if constexpr (!EPI) {
 #pragma unroll
-    for (int mb = 0; mb < T::MB; ++mb)
+        for (int mb = 0; mb < T::MB; ++mb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = row0 + wr * T::WM + mb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+            for (int v = 0; v < 16; ++v) {
+                const int r = row_of(mb, v);
+#pragma unroll
+                for (int nb = 0; nb < T::NB; ++nb) {
+                    const int c = col_of(nb);
+                    buf_store_x1(acc[mb][nb][v], rc, elem_off(r < g.m && c < g.n, r, g.ldc, c));
+                }
+            }
+    } else {
+        // Branch-free over the elements: C reads as zero when beta == 0 (an
+        // out-of-range offset), ReLU is max(x, lo) with lo = -inf when off,
+        // GELU is selected.  A branch per element splits the block into
+        // pieces the scheduler cannot see across.
+        const __amdgpu_buffer_rsrc_t rbias = make_rsrc(g.bias, g.bias ? (uint32_t)g.n * 4u : 0u);
+        const float lo = g.act == 1 ? 0.0f : -__builtin_inff();
+        const bool gelu = g.act == 2;
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb)
 #pragma unroll
             for (int nb = 0; nb < T::NB; ++nb) {
-                const int c = B_COL ? col0 + wc * T::WN + nb * 32 + l32 : col0 + wc * T::WN + T::NB * l32 + nb;
-                buf_store_x1(acc[mb][nb][v], rc, elem_off(r < g.m && c < g.n, r, g.ldc, c));
+                const int c = col_of(nb);
+                const float bias = buf_load_x1(rbias, elem_off(c < g.n, 0, 0, c));
+                float cold[16];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = row_of(mb, v);
+                    cold[v] = buf_load_x1(rc, elem_off(g.use_beta && r < g.m && c < g.n, r, g.ldc, c));
+                }
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = row_of(mb, v);
+                    float x = g.alpha * acc[mb][nb][v] + g.beta * cold[v] + bias;
+                    x = fmaxf(x, lo);
+                    x = gelu ? gelu_erf(x) : x;
+                    buf_store_x1(x, rc, elem_off(r < g.m && c < g.n, r, g.ldc, c));
+                }
+                // One block at a time, so its loads are the only ones in flight.
+                __builtin_amdgcn_sched_barrier(0);
             }
-        }
+    }
 }
 
 // Stream-K bookkeeping.  The slab iterations of all tiles, I = tiles * KT in
@@ -403,8 +487,9 @@ __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsr
         }
 }
 
-// One whole tile per workgroup.
-template <class T, bool B_COL>
+// One whole tile per workgroup.  A_COL: column-major A; EPI: the
+// linear-layer epilogue.
+template <class T, bool B_COL, bool A_COL = false, bool EPI = false>
 __global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_kernel(GemmArgs g)
 {
     __shared__ f32x4 lds[T::STAGES * (T::A_CHUNKS + T::B_CHUNKS)];
@@ -430,8 +515,8 @@ __global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_kernel(GemmArgs g)
     for (int mb = 0; mb < T::MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < T::NB; ++nb) acc[mb][nb] = f32x16{};
-    dma_range<T, B_COL>(g, lds_a, lds_b, ra, rb, row0, col0, 0, g.k_tiles, tid, wave, wr, wc, l32, half, acc);
-    dma_store_c<T, B_COL>(g, rc, row0, col0, wr, wc, l32, half, acc);
+    dma_range<T, B_COL, A_COL>(g, lds_a, lds_b, ra, rb, row0, col0, 0, g.k_tiles, tid, wave, wr, wc, l32, half, acc);
+    dma_store_c<T, B_COL, A_COL, EPI>(g, rc, row0, col0, wr, wc, l32, half, acc);
 }
 
 // Stream-K ("GEMM 性能优化", Wave 模型: a last, partly filled wave of tiles

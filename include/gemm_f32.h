@@ -50,10 +50,10 @@ extern "C" {
 
 typedef struct gemm_f32_plan_impl *gemm_f32_plan; /* opaque, library-owned */
 
-/* Storage order of B (A and C are row-major). */
+/* Storage order of B (and, for the *_ex calls, of A; C is always row-major). */
 enum gemm_f32_layout {
-    GEMM_F32_ROW_MAJOR = 0, /* B(kk, j) = B[kk*ldb + j]; needs ldb >= n */
-    GEMM_F32_COL_MAJOR = 1  /* B(kk, j) = B[j*ldb + kk]; needs ldb >= k */
+    GEMM_F32_ROW_MAJOR = 0, /* B(kk, j) = B[kk*ldb + j], needs ldb >= n; A(i, kk) = A[i*lda + kk], lda >= k */
+    GEMM_F32_COL_MAJOR = 1  /* B(kk, j) = B[j*ldb + kk], needs ldb >= k; A(i, kk) = A[kk*lda + i], lda >= m */
 };
 
 enum gemm_f32_status {
@@ -63,6 +63,13 @@ enum gemm_f32_status {
     GEMM_F32_ERR_UNSUPPORTED_DEVICE = 3,  /* current device is not gfx950 */
     GEMM_F32_ERR_HIP = 4,                 /* a HIP runtime call failed; see gemm_f32_last_hip_error */
     GEMM_F32_ERR_ALLOC = 5                /* host allocation failed */
+};
+
+/* Activation of the linear-layer epilogue (gemm_f32_run_ex). */
+enum gemm_f32_activation {
+    GEMM_F32_ACT_NONE = 0,  /* identity */
+    GEMM_F32_ACT_RELU = 1,  /* max(x, 0) */
+    GEMM_F32_ACT_GELU = 2   /* x * Phi(x) = x/2 * (1 + erf(x / sqrt(2))), Phi the normal distribution function */
 };
 
 /* Kernel families (gemm_f32_info.kind). */
@@ -85,6 +92,8 @@ struct gemm_f32_info {
     int split_k;        /* k-splits (1 = none) */
     int stream_k;       /* plan only: workgroups sharing the k-slabs of stream_k_tiles tiles evenly (stream-K), 0 = none */
     int stream_k_tiles; /* plan only: tiles whose k-slabs are shared; every other tile gets one workgroup */
+    int layout_a;       /* plan only: storage order of A (enum gemm_f32_layout) */
+    int epilogue;       /* plan only: 1 if built with the linear-layer epilogue */
     int aligned;        /* plan only: 1 if lda, ldb and ldc are multiples of 4 (informational) */
     int64_t tiles_m, tiles_n, k_tiles, grid; /* plan only: tile counts and workgroups launched */
     int group_m;        /* plan only: tile-rows per rasterisation group */
@@ -133,6 +142,50 @@ int gemm_f32_create_variant(gemm_f32_plan *out, int variant, int64_t m, int64_t 
  *         aligned), GEMM_F32_ERR_HIP (launch failed).  Never synchronises.
  */
 int gemm_f32_run(gemm_f32_plan plan, const float *A, const float *B, float *C, void *stream);
+
+/*
+ * Linear-layer layouts and epilogue.  A linear layer (the FFN and QKV
+ * projections that "GEMM 性能优化" names as GEMMs in its opening) computes
+ *
+ *     C[i][j] = act(alpha * sum_k A(i, k) * B(k, j) + beta * C[i][j] + bias[j])
+ *
+ * with A(i, k) = A[i*lda + k] (layout_a == GEMM_F32_ROW_MAJOR) or
+ * A[k*lda + i] (layout_a == GEMM_F32_COL_MAJOR: column k contiguous, the
+ * column-major convention of "PMPP Chapter 06", section 1, applied to A),
+ * B(k, j) as for gemm_f32_create.  C is read only when beta != 0 (then it
+ * must hold finite values); bias holds n floats (device memory, 4-byte
+ * aligned) or is NULL.  The product is summed as by gemm_f32_run; the
+ * epilogue is evaluated in float32 (alpha*acc + beta*C + bias, multiply-adds
+ * may be fused), then act; GELU's erf is the Abramowitz-Stegun 7.1.26
+ * approximation (|error| <= 1.5e-7).  These plans run on the 256x128, 128x128 and 64x64 direct-to-LDS
+ * kernels (the few-row path and stream-K are not used).
+ */
+
+/* gemm_f32_validate_ex: gemm_f32_validate with A's layout: lda >= k (row-major
+ * A) or lda >= m (column-major A); layout_a in {0, 1}. */
+int gemm_f32_validate_ex(int64_t m, int64_t n, int64_t k, int layout_a, int layout_b,
+                         int64_t lda, int64_t ldb, int64_t ldc);
+
+/*
+ * gemm_f32_create_ex: a plan with A's layout and, with epilogue = 1, the
+ * linear-layer epilogue (then run it with gemm_f32_run_ex).  epilogue = 0
+ * gives plain C = A.B.  Errors: as gemm_f32_create (INVALID_VALUE also for
+ * epilogue not in {0, 1}).
+ */
+int gemm_f32_create_ex(gemm_f32_plan *out, int64_t m, int64_t n, int64_t k, int layout_a, int layout_b,
+                       int64_t lda, int64_t ldb, int64_t ldc, int epilogue);
+
+/*
+ * gemm_f32_run_ex: enqueue C = act(alpha * A.B + beta * C + bias) on
+ * `stream`.  activation: enum gemm_f32_activation.  A plan created without
+ * the epilogue accepts only alpha = 1, beta = 0, bias = NULL, activation =
+ * GEMM_F32_ACT_NONE (plain C = A.B); gemm_f32_run on an epilogue plan is the
+ * same as those values.  Errors: as gemm_f32_run, plus INVALID_VALUE for an
+ * unknown activation, a misaligned bias, or epilogue values on a plan
+ * without it.  Never synchronises.
+ */
+int gemm_f32_run_ex(gemm_f32_plan plan, const float *A, const float *B, float *C, float alpha, float beta,
+                    const float *bias, int activation, void *stream);
 
 /* gemm_f32_destroy: release a plan and its workspace (hipFree, which waits
  * for the device).  NULL is a no-op returning SUCCESS. */

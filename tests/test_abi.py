@@ -91,6 +91,35 @@ def test_validate(lib, args, ok):
     assert st == (g.GEMM_F32_SUCCESS if ok else g.GEMM_F32_ERR_INVALID_VALUE)
 
 
+@pytest.mark.parametrize("args,ok", [
+    ((4, 6, 5, 0, 0, 5, 6, 6), True),
+    ((4, 6, 5, 1, 0, 4, 6, 6), True),        # column-major A needs lda >= m
+    ((4, 6, 5, 1, 0, 3, 6, 6), False),
+    ((4, 6, 5, 1, 1, 7, 5, 6), True),
+    ((4, 6, 5, 0, 0, 4, 6, 6), False),       # row-major A needs lda >= k
+    ((4, 6, 5, 2, 0, 5, 6, 6), False),       # bad layout_a
+    ((1 << 15, 4, 1 << 15, 1, 0, 1 << 15, 4, 4), False),  # column-major A extent >= 2^31 bytes
+])
+def test_validate_ex(lib, args, ok):
+    st = g.gemm_f32_validate_ex(*args)
+    assert st == (g.GEMM_F32_SUCCESS if ok else g.GEMM_F32_ERR_INVALID_VALUE)
+
+
+def test_validate_is_validate_ex_with_row_major_a(lib):
+    for args in [(4, 4, 4, 0, 4, 4, 4), (4, 6, 5, 1, 5, 4, 6), (4, 4, 4, 0, 3, 4, 4)]:
+        m, n, k, lb, lda, ldb, ldc = args
+        assert g.gemm_f32_validate(*args) == g.gemm_f32_validate_ex(m, n, k, 0, lb, lda, ldb, ldc)
+
+
+def test_create_ex_rejects_invalid_before_device(lib):
+    h = ctypes.c_void_p(1234)
+    st = lib.gemm_f32_create_ex(ctypes.byref(h), 4, 4, 4, 1, 0, 3, 4, 4, 0)     # lda < m
+    assert st == g.GEMM_F32_ERR_INVALID_VALUE and h.value is None
+    st = lib.gemm_f32_create_ex(ctypes.byref(h), 4, 4, 4, 0, 0, 4, 4, 4, 2)     # bad epilogue flag
+    assert st == g.GEMM_F32_ERR_INVALID_VALUE and h.value is None
+    assert lib.gemm_f32_run_ex(None, 16, 16, 16, 1.0, 0.0, None, 0, None) == g.GEMM_F32_ERR_INVALID_VALUE
+
+
 def test_create_rejects_invalid_before_device(lib):
     h = ctypes.c_void_p(1234)
     st = lib.gemm_f32_create(ctypes.byref(h), 0, 4, 4, 0, 4, 4, 4)
@@ -143,12 +172,16 @@ def test_variant_table(lib):
 def test_binding_strides_from_tensors():
     A = torch.empty(8, 12)
     B = torch.empty(12, 20)
-    assert g.operand_strides(A, B) == (8, 20, 12, 0, 12, 20)
+    assert g.operand_strides(A, B) == (8, 20, 12, 0, 0, 12, 20)
     Bt = torch.empty(20, 12).t()                      # column-major (12 x 20)
-    assert g.operand_strides(A, Bt) == (8, 20, 12, 1, 12, 12)
+    assert g.operand_strides(A, Bt) == (8, 20, 12, 0, 1, 12, 12)
     Awide = torch.empty(8, 16)[:, :12]
-    assert g.operand_strides(Awide, B) == (8, 20, 12, 0, 16, 20)
+    assert g.operand_strides(Awide, B) == (8, 20, 12, 0, 0, 16, 20)
+    At = torch.empty(12, 8).t()                       # column-major A (8 x 12), lda = 8
+    assert g.operand_strides(At, B) == (8, 20, 12, 1, 0, 8, 20)
+    At_wide = torch.empty(12, 10)[:, :8].t()          # column-major A with lda = 10
+    assert g.operand_strides(At_wide, Bt) == (8, 20, 12, 1, 1, 10, 12)
     with pytest.raises(ValueError):
         g.operand_strides(A, torch.empty(11, 20))
     with pytest.raises(ValueError):
-        g.operand_strides(torch.empty(12, 8).t(), B)   # A not row-major
+        g.operand_strides(torch.empty(8, 24)[:, ::2], B)   # A with no unit stride

@@ -1,0 +1,193 @@
+"""Linear-layer layouts and epilogue on the GPU, through the C ABI.
+
+C = act(alpha * A.B + beta * C_in + bias[j]) with A row- or column-major,
+against the oracle's product and epilogue (float64).  Tolerance: the
+product's |err| <= 1e-5 * S + 1e-6 carries through alpha; the float32
+epilogue adds a few roundings of |alpha|*S + |beta*C_in| + |bias| (the scale
+S' the oracle returns), ReLU is 1-Lipschitz, GELU at most 1.13-Lipschitz with
+an erf approximation error below 1e-7 * |x| <= 1e-7 * S'; so
+|err| <= 1.2e-5 * S' + 1.2e-6.  Integer-valued operands, C_in and bias with
+alpha = beta = 1 and no GELU are exact in float32 and must match bitwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_optimisation_fp32_amd as g
+import oracle
+from tests.gpu_helpers import device, to_dev
+from workloads import (COL_MAJOR, ROW_MAJOR, WORKLOADS, epilogue_operands, random_operands,
+                       sample_indices)
+
+pytestmark = pytest.mark.gpu
+
+REL, ABS = 1.2e-5, 1.2e-6
+EX_VARIANTS = ["dma_256x128x16_w2x2_s3", "dma_128x128x16_w2x2_s3", "dma_64x64x16_w2x2_s3"]
+ACTS = [g.GEMM_F32_ACT_NONE, g.GEMM_F32_ACT_RELU, g.GEMM_F32_ACT_GELU]
+
+
+def variant_index(name):
+    for v in range(g.gemm_f32_num_variants()):
+        if g.gemm_f32_variant_info(v)["name"] == name:
+            return v
+    raise KeyError(name)
+
+
+def run_ex(A, B, m, n, k, layout_a, layout_b, lda=None, ldb=None, ldc=None, epilogue=0, alpha=1.0, beta=0.0,
+           c_in=None, bias=None, act=0, c_fill=0.0, repeat=1):
+    lda = (k if layout_a == ROW_MAJOR else m) if lda is None else lda
+    ldb = (n if layout_b == ROW_MAJOR else k) if ldb is None else ldb
+    ldc = n if ldc is None else ldc
+    dA, dB = to_dev(A), to_dev(B)
+    C0 = np.full((m, ldc), np.float32(c_fill), dtype=np.float32)
+    if c_in is not None:
+        C0[:, :n] = c_in
+    dbias = to_dev(bias) if bias is not None else None
+    plan = g.gemm_f32_create_ex(m, n, k, layout_a, layout_b, lda, ldb, ldc, epilogue)
+    outs = []
+    try:
+        info = g.gemm_f32_describe(plan)
+        stream = torch.cuda.current_stream().cuda_stream
+        for _ in range(repeat):
+            dC = to_dev(C0.reshape(-1)[: (m - 1) * ldc + n])
+            g.gemm_f32_run_ex(plan, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), alpha, beta,
+                              dbias.data_ptr() if dbias is not None else None, act, stream)
+            torch.cuda.synchronize()
+            full = C0.copy().reshape(-1)
+            full[: (m - 1) * ldc + n] = dC.cpu().numpy()
+            outs.append(full.reshape(m, ldc))
+    finally:
+        g.gemm_f32_destroy(plan)
+    return outs[-1], info, outs
+
+
+def check(C, ref, scale, what):
+    ok, ratio = oracle.within_tolerance(C, ref, scale, REL, ABS)
+    assert ok, f"{what}: max error ratio {ratio:.3g}"
+
+
+SHAPES = [(300, 520, 77), (513, 257, 1000), (129, 131, 33), (1, 300, 17), (37, 1, 5), (64, 64, 4096)]
+
+
+@pytest.mark.parametrize("vname", EX_VARIANTS)
+@pytest.mark.parametrize("layout_a", [ROW_MAJOR, COL_MAJOR])
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+def test_layouts_plain_product(vname, layout_a, layout_b, monkeypatch):
+    monkeypatch.setenv("GEMM_F32_VARIANT", str(variant_index(vname)))
+    for (m, n, k) in SHAPES:
+        print(f"\n[case] {vname} layout_a={layout_a} layout_b={layout_b} shape={(m, n, k)}", flush=True)
+        A, B = random_operands(m, n, k, layout_b, "normal1", seed=100 + m + k, layout_a=layout_a)
+        C, info, _ = run_ex(A, B, m, n, k, layout_a, layout_b)
+        assert info["name"] == vname and info["layout_a"] == layout_a
+        Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b, layout_a=layout_a)
+        ok, ratio = oracle.within_tolerance(C, Cref, S)
+        assert ok, f"{vname} {(m, n, k)}: ratio {ratio:.3g}"
+
+
+@pytest.mark.parametrize("vname", EX_VARIANTS)
+@pytest.mark.parametrize("layout_a", [ROW_MAJOR, COL_MAJOR])
+@pytest.mark.parametrize("act", ACTS)
+def test_epilogue_vs_oracle(vname, layout_a, act, monkeypatch):
+    monkeypatch.setenv("GEMM_F32_VARIANT", str(variant_index(vname)))
+    for (m, n, k), layout_b in [((300, 520, 77), ROW_MAJOR), ((513, 257, 1000), COL_MAJOR),
+                                ((129, 131, 33), ROW_MAJOR)]:
+        print(f"\n[case] epilogue {vname} layout_a={layout_a} act={act} shape={(m, n, k)}", flush=True)
+        A, B = random_operands(m, n, k, layout_b, "normal1", seed=200 + m, layout_a=layout_a)
+        c_in, bias = epilogue_operands(m, n, seed=300 + m)
+        AB, S = oracle.gemm_f64(A, B, m, n, k, layout_b, layout_a=layout_a)
+        for alpha, beta, with_bias in [(0.5, -1.5, True), (1.0, 0.0, True), (2.0, 0.25, False)]:
+            C, info, outs = run_ex(A, B, m, n, k, layout_a, layout_b, epilogue=1, alpha=alpha, beta=beta,
+                                   c_in=c_in, bias=bias if with_bias else None, act=act, repeat=2)
+            assert info["epilogue"] == 1
+            ref, scale = oracle.epilogue_f64(AB, S, c_in, alpha, beta, bias if with_bias else None, act)
+            check(C[:, :n], ref, scale, f"{vname} alpha={alpha} beta={beta} bias={with_bias} act={act}")
+            assert np.array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("vname", EX_VARIANTS)
+def test_epilogue_integer_bitexact_and_c_untouched(vname, monkeypatch):
+    """Integer operands, C_in and bias, alpha = beta = 1: exact.  beta = 0
+    leaves C unread (NaN there does not leak), and C's row padding is never
+    written."""
+    monkeypatch.setenv("GEMM_F32_VARIANT", str(variant_index(vname)))
+    m, n, k = 300, 520, 77
+    ldc = n + 5
+    for layout_a in (ROW_MAJOR, COL_MAJOR):
+        A, B = random_operands(m, n, k, ROW_MAJOR, "int8range", seed=400, layout_a=layout_a)
+        rng = np.random.default_rng(401)
+        c_in = rng.integers(-50, 51, (m, n)).astype(np.float32)
+        bias = rng.integers(-9, 10, n).astype(np.float32)
+        AB, S = oracle.gemm_f64(A, B, m, n, k, ROW_MAJOR, layout_a=layout_a)
+        for act in (g.GEMM_F32_ACT_NONE, g.GEMM_F32_ACT_RELU):
+            C, _, _ = run_ex(A, B, m, n, k, layout_a, ROW_MAJOR, ldc=ldc, epilogue=1, alpha=1.0, beta=1.0,
+                             c_in=c_in, bias=bias, act=act, c_fill=-3.5)
+            ref, _ = oracle.epilogue_f64(AB, S, c_in, 1.0, 1.0, bias, act)
+            assert np.array_equal(C[:, :n].astype(np.float64), ref)
+            assert np.all(C[:-1, n:] == np.float32(-3.5))
+        C, _, _ = run_ex(A, B, m, n, k, layout_a, ROW_MAJOR, ldc=ldc, epilogue=1, alpha=1.0, beta=0.0,
+                         c_in=np.full((m, n), np.nan, dtype=np.float32), bias=bias, act=g.GEMM_F32_ACT_NONE)
+        ref, _ = oracle.epilogue_f64(AB, S, None, 1.0, 0.0, bias, g.GEMM_F32_ACT_NONE)
+        assert np.array_equal(C[:, :n].astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("layout_a", [ROW_MAJOR, COL_MAJOR])
+def test_padded_column_major_a(layout_a):
+    """lda above its minimum with NaN in A's padding: the padding never reaches C."""
+    m, n, k = 200, 190, 70
+    lda = (k if layout_a == ROW_MAJOR else m) + 7
+    A, B = random_operands(m, n, k, ROW_MAJOR, "uniform", seed=500, lda=lda, layout_a=layout_a)
+    C, _, _ = run_ex(A, B, m, n, k, layout_a, ROW_MAJOR, lda=lda)
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, ROW_MAJOR, lda=lda, layout_a=layout_a)
+    ok, ratio = oracle.within_tolerance(C, Cref, S)
+    assert ok, ratio
+
+
+def test_run_ex_rejects_epilogue_on_plain_plan():
+    m, n, k = 64, 64, 64
+    plan = g.gemm_f32_create_ex(m, n, k, COL_MAJOR, ROW_MAJOR, m, n, n, 0)
+    try:
+        dA = torch.zeros(m * k, device=device())
+        with pytest.raises(g.GemmF32Error):
+            g.gemm_f32_run_ex(plan, dA.data_ptr(), dA.data_ptr(), dA.data_ptr(), 2.0, 0.0, None, 0,
+                              torch.cuda.current_stream().cuda_stream)
+        with pytest.raises(g.GemmF32Error):
+            g.gemm_f32_run_ex(plan, dA.data_ptr(), dA.data_ptr(), dA.data_ptr(), 1.0, 0.0, None, 7,
+                              torch.cuda.current_stream().cuda_stream)
+    finally:
+        g.gemm_f32_destroy(plan)
+
+
+@pytest.mark.parametrize("act", ["relu", "gelu"])
+def test_ffn_linear_full_size_sampled(act):
+    """The FFN shape as a linear layer: act(X.W + bias), X 8192 x 4096,
+    W 4096 x 14336 stored as the usual (14336, 4096) weight (column-major B)."""
+    w = WORKLOADS["ffn"]
+    m, n, k = w.m, w.n, w.k
+    print(f"\n[case] ffn linear act={act}", flush=True)
+    A, B = random_operands(m, n, k, COL_MAJOR, w.dist, w.seed)
+    _, bias = epilogue_operands(1, n, seed=600)
+    X = torch.from_numpy(A).to(device())
+    W = torch.from_numpy(B).to(device())               # (n, k) row-major = column-major B
+    b = torch.from_numpy(bias).to(device())
+    Y = g.linear(X, W.t(), b, activation=act)
+    torch.cuda.synchronize()
+    rows, cols = sample_indices(m, n, 3000, seed=601)
+    ab, s = oracle.gemm_f64_sampled(A, B, m, n, k, COL_MAJOR, rows, cols)
+    ref, scale = oracle.epilogue_f64(ab, s, None, 1.0, 0.0, bias[cols], oracle.ACT_RELU if act == "relu" else oracle.ACT_GELU)
+    check(Y.cpu().numpy()[rows, cols], ref, scale, f"ffn {act}")
+
+
+def test_binding_linear_column_major_a_and_beta():
+    m, n, k = 250, 270, 190
+    A, B = random_operands(m, n, k, ROW_MAJOR, "normal1", seed=700, layout_a=COL_MAJOR)
+    c_in, bias = epilogue_operands(m, n, seed=701)
+    At = torch.from_numpy(A).to(device()).t()           # logical (m, k), column-major
+    Bt = torch.from_numpy(B).to(device())
+    out = torch.from_numpy(c_in).to(device()).clone()
+    Y = g.linear(At, Bt, torch.from_numpy(bias).to(device()), activation="gelu", alpha=0.75, beta=0.5, out=out)
+    AB, S = oracle.gemm_f64(A, B, m, n, k, ROW_MAJOR, layout_a=COL_MAJOR)
+    ref, scale = oracle.epilogue_f64(AB, S, c_in, 0.75, 0.5, bias, oracle.ACT_GELU)
+    check(Y.cpu().numpy(), ref, scale, "linear")
+    M = g.matmul(At, Bt)
+    ok, ratio = oracle.within_tolerance(M.cpu().numpy(), AB, S)
+    assert ok, ratio
