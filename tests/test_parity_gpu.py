@@ -256,7 +256,7 @@ def test_stream_k_chosen_for_few_tiles_long_k(layout_b):
 # Full workload shapes, in the plan the benchmark times (gemm_f32_create).
 # ---------------------------------------------------------------------------
 
-FULL = ["sq256", "sq4096", "sq4096t", "ragged", "ffn", "skinny"]
+FULL = ["sq256", "sq4096", "sq4096t", "ragged", "ffn", "skinny", "longk"]
 
 
 @pytest.mark.parametrize("name", FULL)

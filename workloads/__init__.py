@@ -18,6 +18,7 @@ sq4096t   4096 x 4096 x 4096     col     normal(0, 1)             2
 ragged    5003 x 4097 x 2049     row     uniform[-1, 1]           3
 ffn       8192 x 14336 x 4096    row     normal(0, 0.02)          4
 skinny    16 x 4096 x 4096       row     normal(0, 0.02)          4
+longk     1024 x 1024 x 8192     row     uniform[-1, 1]           5
 ========  =====================  ======  =======================  ====
 
 Recipe: ``numpy.random.default_rng(seed)`` (PCG64); A is drawn first, then B,
@@ -58,6 +59,7 @@ WORKLOADS = {
         Workload("ragged", 5003, 4097, 2049, ROW_MAJOR, "uniform", 3, "boundary tiles, odd strides"),
         Workload("ffn", 8192, 14336, 4096, ROW_MAJOR, "normal002", 4, "FFN linear layer"),
         Workload("skinny", 16, 4096, 4096, ROW_MAJOR, "normal002", 4, "memory-bound, few rows"),
+        Workload("longk", 1024, 1024, 8192, ROW_MAJOR, "uniform", 5, "few tiles, long k (stream-K)"),
     )
 }
 
