@@ -156,11 +156,23 @@ const VariantDesc &variant(int v)
 // Device facts, queried once per device
 // ---------------------------------------------------------------------------
 
+// The tiled variants the shape dispatch weighs against each other, with the
+// throughput each sustains while every slot of a wave is busy (TFLOPS on one
+// MI355X, from the tile sweep on the 4096^3 and FFN shapes).
+struct Candidate {
+    int variant;
+    double full_tflops;
+};
+constexpr int kCandidates = 3;
+constexpr Candidate kCandidate[kCandidates] = {
+    {V_DMA_256x128x16_S3, 144.0}, {V_DMA_128x128x16_S3, 142.0}, {V_DMA_64x64x16_S3, 126.0}};
+
 struct DeviceFacts {
     int status = -1;  // -1: not queried yet, else a gemm_f32_status
     int cu_count = 0;
     int num_xcd = 1;
     int hip_error = 0;
+    int per_cu[kCandidates] = {};  // resident workgroups per CU of each candidate
 };
 
 constexpr int kMaxDevices = 64;
@@ -197,6 +209,15 @@ int device_facts(int *device_out, DeviceFacts *facts_out)
                 xcc = 1;  // the rasterisation stays a bijection for any count
             }
             f.num_xcd = xcc;
+            for (int i = 0; i < kCandidates; ++i) {
+                const VariantDesc &d = variant(kCandidate[i].variant);
+                int n = 0;
+                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, d.fn[0], d.threads, 0) != hipSuccess || n < 1) {
+                    (void)hipGetLastError();
+                    n = 1;
+                }
+                f.per_cu[i] = n;
+            }
             f.status = GEMM_F32_SUCCESS;
         }
     }
@@ -241,24 +262,55 @@ struct gemm_f32_plan_impl {
 
 namespace {
 
-// Shape dispatch.  Few rows: the bandwidth-bound split-k path.  Otherwise
-// the direct-to-LDS MFMA kernels, with the largest tile that still gives
-// every CU at least one workgroup (256 x 128 tiles run two per CU).  When
-// even 64 x 64 tiles leave fewer than two workgroups per CU and k is long,
+// Estimated time of a data-parallel plan ("GEMM 性能优化", Wave 模型): the
+// tiles run in waves of S = (workgroups per CU) x CUs; a full wave takes
+// S tiles' FLOPs at the variant's full-wave throughput.  A last, partial
+// wave with w of the c slots per CU busy takes w/c of a wave, divided by
+// 0.92 when w < c: a CU running fewer workgroups gives each a larger share,
+// but not all of it (measured: a lone 256x128 workgroup runs a CU at 92 % of
+// the throughput of two).  The estimate ranks the candidates; it ranked the
+// measured ragged 5003x4097x2049 times (64x64 724 us < 128x128 739 us <
+// 256x128 743 us) and the 4096^3 and FFN choices correctly.
+double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n, int64_t k, int cus)
+{
+    const VariantDesc &d = variant(cand.variant);
+    const int64_t tiles = ceil_div(m, d.bm) * ceil_div(n, d.bn);
+    const int64_t slots = (int64_t)per_cu * cus;
+    const int64_t full = tiles / slots, rem = tiles % slots;
+    const double wave = (double)slots * 2.0 * d.bm * d.bn * (double)k / (cand.full_tflops * 1e12);
+    double last = 0.0;
+    if (rem) {
+        const int64_t w = std::min<int64_t>(per_cu, ceil_div(rem, cus));
+        last = (double)w / per_cu;
+        if (w < per_cu) last /= 0.92;
+    }
+    return ((double)full + last) * wave;
+}
+
+// Shape dispatch.  Few rows: the bandwidth-bound split-k path.  When even
+// 64 x 64 tiles leave fewer than two workgroups per CU and k is long,
 // 128 x 128 tiles with stream-K (all workgroups share all tiles' k-slabs)
-// fill the GPU instead: measured 83 against 63 TFLOPS at 1024x1024x8192,
-// while at 512x4096x4096 (512 small tiles) the two are even.
+// fill the GPU: measured 83 against 63 TFLOPS at 1024x1024x8192, while at
+// 512x4096x4096 (512 small tiles) the two are even.  Otherwise the
+// direct-to-LDS tile whose estimated time is least.
 int choose_variant(int64_t m, int64_t n, int64_t k, const DeviceFacts &f, bool *stream_k)
 {
     *stream_k = false;
     if (m <= 32) return V_SKINNY_W16_D4;
-    if (ceil_div(m, 256) * ceil_div(n, 128) >= f.cu_count) return V_DMA_256x128x16_S3;
-    if (ceil_div(m, 128) * ceil_div(n, 128) >= f.cu_count) return V_DMA_128x128x16_S3;
     if (ceil_div(m, 64) * ceil_div(n, 64) < 2 * (int64_t)f.cu_count && k >= 1024) {
         *stream_k = true;
         return V_DMA_128x128x16_S3;
     }
-    return V_DMA_64x64x16_S3;
+    int best = 0;
+    double best_t = 0.0;
+    for (int i = 0; i < kCandidates; ++i) {
+        const double t = estimate_seconds(kCandidate[i], f.per_cu[i], m, n, k, f.cu_count);
+        if (i == 0 || t < best_t) {
+            best = i;
+            best_t = t;
+        }
+    }
+    return kCandidate[best].variant;
 }
 
 int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int64_t k, int layout_a,
