@@ -289,15 +289,17 @@ double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n,
 
 // Shape dispatch.  Few rows: the bandwidth-bound split-k path.  When even
 // 64 x 64 tiles leave fewer than two workgroups per CU and k is long,
-// 128 x 128 tiles with stream-K (all workgroups share all tiles' k-slabs)
-// fill the GPU: measured 83 against 63 TFLOPS at 1024x1024x8192, while at
-// 512x4096x4096 (512 small tiles) the two are even.  Otherwise the
+// 128 x 128 tiles with stream-K (workgroups share the tiles' k-slabs) fill
+// the GPU: measured 83 against 63 TFLOPS at 1024x1024x8192 and 65 against
+// ~62 at 1024x1024x4096, but 47 against 60 at 1024x1024x2048, where the
+// partial tiles cost more than the idle CUs; at 512x4096x4096 (512 small
+// tiles) data-parallel 64 x 64 is as fast.  Otherwise the
 // direct-to-LDS tile whose estimated time is least.
 int choose_variant(int64_t m, int64_t n, int64_t k, const DeviceFacts &f, bool *stream_k)
 {
     *stream_k = false;
     if (m <= 32) return V_SKINNY_W16_D4;
-    if (ceil_div(m, 64) * ceil_div(n, 64) < 2 * (int64_t)f.cu_count && k >= 1024) {
+    if (ceil_div(m, 64) * ceil_div(n, 64) < 2 * (int64_t)f.cu_count && k >= 4096) {
         *stream_k = true;
         return V_DMA_128x128x16_S3;
     }
@@ -427,8 +429,11 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
                 delete p;
                 return hip_fail(e);
             }
-            // At least 8 slabs per workgroup, so that a tile is shared by few.
-            wgs = std::min<int64_t>((int64_t)per_cu * facts.cu_count, tiles * a.k_tiles / 8);
+            // At most 8 segments per tile (the last one to arrive reads all
+            // the others: 32 segments per tile measured 6x slower than 8)
+            // and at least 8 slabs per workgroup.
+            wgs = std::min<int64_t>(std::min<int64_t>((int64_t)per_cu * facts.cu_count, 8 * tiles),
+                                    tiles * a.k_tiles / 8);
             if (wgs < 2) wgs = 0;
         }
         if (shared < 1 || shared > tiles) shared = tiles;
