@@ -99,27 +99,58 @@ __device__ __forceinline__ DmaPiece<T, B_COL> dma_piece(int j, int tid)
     return d;
 }
 
+// Per-lane global offsets of a tile's copies at slab 0, computed once per
+// tile; a slab adds a uniform k term (no per-copy multiply).  Pieces whose
+// rows run along k (column-major A, row-major B) add k0 * ld and drop rows
+// at or past K (only the tail slab has any; their offsets could also wrap);
+// pieces whose 16-byte chunks run along k (row-major A, column-major B) add
+// k0 and carry the out-of-range offset for rows past M (columns past N),
+// which stays out of range after the add.
 template <class T, bool B_COL, bool A_COL = false>
-__device__ __forceinline__ void dma_issue(int j, const GemmArgs &g, __amdgpu_buffer_rsrc_t ra,
-                                          __amdgpu_buffer_rsrc_t rb, int row0, int col0, int kt, int tid,
+struct DmaBases {
+    uint32_t off[T::PIECES];
+};
+
+template <class T, bool B_COL, bool A_COL = false>
+__device__ __forceinline__ DmaBases<T, B_COL, A_COL> dma_bases(const GemmArgs &g, int row0, int col0, int tid)
+{
+    DmaBases<T, B_COL, A_COL> b;
+#pragma unroll
+    for (int j = 0; j < T::PIECES; ++j) {
+        const DmaPiece<T, B_COL> d = dma_piece<T, B_COL, A_COL>(j, tid);
+        if (A_COL && d.is_a) {
+            // (wraps harmlessly for rows at or past K, which are dropped)
+            b.off[j] = ((uint32_t)d.row * (uint32_t)g.lda + (uint32_t)(row0 + 4 * d.kc)) * 4u;
+        } else if (d.is_a) {
+            const int gr = row0 + d.row;
+            b.off[j] = elem_off(gr < g.m, gr, g.lda, 4 * d.kc);
+        } else if (!B_COL) {
+            b.off[j] = ((uint32_t)d.row * (uint32_t)g.ldb + (uint32_t)(col0 + 4 * d.kc)) * 4u;
+        } else {
+            const int gn = col0 + d.row;
+            b.off[j] = elem_off(gn < g.n, gn, g.ldb, 4 * d.kc);
+        }
+    }
+    return b;
+}
+
+template <class T, bool B_COL, bool A_COL = false>
+__device__ __forceinline__ void dma_issue(int j, const GemmArgs &g, const DmaBases<T, B_COL, A_COL> &bases,
+                                          __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int kt, int tid,
                                           int wave, f32x4 *As, f32x4 *Bs)
 {
     const DmaPiece<T, B_COL> d = dma_piece<T, B_COL, A_COL>(j, tid);
     const int k0 = kt * T::BK;
     const int wave_base = (j < T::A_PER_T ? j : j - T::A_PER_T) * T::THREADS + wave * 64;
-    if (A_COL && d.is_a) {
-        const int gk = k0 + d.row;
-        dma16(ra, elem_off(gk < g.k, gk, g.lda, row0 + 4 * d.kc), As + wave_base);
-    } else if (d.is_a) {
-        const int gr = row0 + d.row;
-        dma16(ra, elem_off(gr < g.m, gr, g.lda, k0 + 4 * d.kc), As + wave_base);
-    } else if constexpr (!B_COL) {
-        const int gk = k0 + d.row;
-        dma16(rb, elem_off(gk < g.k, gk, g.ldb, col0 + 4 * d.kc), Bs + wave_base);
+    const bool krows = d.is_a ? A_COL : !B_COL;      // rows of the piece run along k
+    uint32_t off;
+    if (krows) {
+        const int ld = d.is_a ? g.lda : g.ldb;
+        off = d.row < g.k - k0 ? bases.off[j] + (uint32_t)(k0 * ld) * 4u : kOobOffset;
     } else {
-        const int gn = col0 + d.row;
-        dma16(rb, elem_off(gn < g.n, gn, g.ldb, k0 + 4 * d.kc), Bs + wave_base);
+        off = bases.off[j] + (uint32_t)k0 * 4u;
     }
+    dma16(d.is_a ? ra : rb, off, d.is_a ? As + wave_base : Bs + wave_base);
 }
 
 // Zero the elements k >= K of this lane's chunks of the last slab (A and
@@ -248,7 +279,8 @@ __device__ __forceinline__ void dma_prefetch(int p_next, const f32x4 *As, const 
 // cover the first LDS reads of slab kt+1.
 template <class T, bool B_COL, int WAIT, bool A_COL = false>
 __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 *lds_b, __amdgpu_buffer_rsrc_t ra,
-                                         __amdgpu_buffer_rsrc_t rb, int row0, int col0, int kt, bool copy, bool fix,
+                                         __amdgpu_buffer_rsrc_t rb, const DmaBases<T, B_COL, A_COL> &bases,
+                                         int kt, bool copy, bool fix,
                                          int tid, int wave, int wr, int wc, int l32, int half,
                                          DmaFrags<T, B_COL, A_COL> &f, f32x16 (&acc)[T::MB][T::NB])
 {
@@ -269,7 +301,7 @@ __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 
             dma_mfma_one<T, B_COL, A_COL>(i, p, f, acc);
             const int t = p * NM + i;
             if ((t + 1) % GAP == 0 && (t + 1) / GAP - 1 < T::PIECES && copy)
-                dma_issue<T, B_COL, A_COL>((t + 1) / GAP - 1, g, ra, rb, row0, col0, kt + T::STAGES - 1, tid, wave,
+                dma_issue<T, B_COL, A_COL>((t + 1) / GAP - 1, g, bases, ra, rb, kt + T::STAGES - 1, tid, wave,
                                     lds_a + cpy * T::A_CHUNKS, lds_b + cpy * T::B_CHUNKS);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -297,6 +329,7 @@ __device__ __forceinline__ void dma_range(const GemmArgs &g, f32x4 *lds_a, f32x4
     const int KT = g.k_tiles;
     const bool ktail = g.k % T::BK != 0;
     DmaFrags<T, B_COL, A_COL> f;
+    const DmaBases<T, B_COL, A_COL> bases = dma_bases<T, B_COL, A_COL>(g, row0, col0, tid);
 
     // Prologue: copies of slabs kt0 .. kt0+STAGES-2, wait for slab kt0.
 #pragma unroll
@@ -305,7 +338,7 @@ __device__ __forceinline__ void dma_range(const GemmArgs &g, f32x4 *lds_a, f32x4
             const int st = (kt0 + s) % T::STAGES;
 #pragma unroll
             for (int j = 0; j < T::PIECES; ++j)
-                dma_issue<T, B_COL, A_COL>(j, g, ra, rb, row0, col0, kt0 + s, tid, wave, lds_a + st * T::A_CHUNKS,
+                dma_issue<T, B_COL, A_COL>(j, g, bases, ra, rb, kt0 + s, tid, wave, lds_a + st * T::A_CHUNKS,
                                     lds_b + st * T::B_CHUNKS);
         }
     wait_vmcnt<0>();
@@ -321,12 +354,12 @@ __device__ __forceinline__ void dma_range(const GemmArgs &g, f32x4 *lds_a, f32x4
     // complete, the k tail fixed when slab kt+1 is the tile's last.
     int kt = kt0;
     for (; kt + T::STAGES - 1 < kt1 && kt + 2 < kt1; ++kt)
-        dma_slab<T, B_COL, (T::STAGES - 2) * T::PIECES, A_COL>(g, lds_a, lds_b, ra, rb, row0, col0, kt, true, false, tid,
+        dma_slab<T, B_COL, (T::STAGES - 2) * T::PIECES, A_COL>(g, lds_a, lds_b, ra, rb, bases, kt, true, false, tid,
                                                          wave, wr, wc, l32, half, f, acc);
     for (; kt + 1 < kt1; ++kt)
-        dma_slab<T, B_COL, 0, A_COL>(g, lds_a, lds_b, ra, rb, row0, col0, kt, kt + T::STAGES - 1 < kt1,
+        dma_slab<T, B_COL, 0, A_COL>(g, lds_a, lds_b, ra, rb, bases, kt, kt + T::STAGES - 1 < kt1,
                               ktail && kt + 2 == KT, tid, wave, wr, wc, l32, half, f, acc);
-    dma_slab<T, B_COL, -1, A_COL>(g, lds_a, lds_b, ra, rb, row0, col0, kt, false, false, tid, wave, wr, wc, l32, half, f,
+    dma_slab<T, B_COL, -1, A_COL>(g, lds_a, lds_b, ra, rb, bases, kt, false, false, tid, wave, wr, wc, l32, half, f,
                            acc);
 }
 
