@@ -25,6 +25,10 @@
 // k-row gives the A values of one k-step for the MB interleaved blocks (tile
 // row MB*l32 + mb of the wavefront tile for lane row l32 of block mb).
 //
+// The slab body is an explicit schedule: straight-line code fenced with
+// sched_barrier, one copy after every two MFMAs, and the MFMA section at a
+// raised wavefront priority (s_setprio) ahead of the wait and the barrier.
+//
 // Range checking is per 4-byte element: a chunk that straddles an operand's
 // byte extent keeps its in-range elements and reads zeros past the end, rows
 // of A (columns of column-major B) past m (n) get the out-of-range offset and
@@ -292,6 +296,11 @@ __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 
     const int cpy = (kt + T::STAGES - 1) % T::STAGES;
     const f32x4 *As = lds_a + cur * T::A_CHUNKS;
     const f32x4 *Bs = lds_b + cur * T::B_CHUNKS;
+    // The matrix-core part of the slab issues at a raised priority; the wait
+    // for the next slab and the barrier at the normal one, so a wavefront
+    // that is ready to multiply goes ahead of one that is about to wait
+    // (measured +0.6 % at 4096^3).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int p = 0; p < T::KH - 1; ++p) {
         dma_prefetch<T, B_COL, A_COL>(p + 1, As, Bs, wr, wc, l32, half, f);
@@ -306,6 +315,7 @@ __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     if constexpr (WAIT >= 0) {
         wait_vmcnt<WAIT>();
         if (fix) dma_fix_tail<T, B_COL, A_COL>(g, kt + 1, tid, lds_a + nxt * T::A_CHUNKS, lds_b + nxt * T::B_CHUNKS);
