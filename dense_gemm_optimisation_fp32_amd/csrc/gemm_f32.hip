@@ -140,8 +140,8 @@ const VariantDesc &variant(int v)
         dma_variant<DmaTile<256, 256, 16, 2, 2, 3>>("dma_256x256x16_w2x2_s3"),
         dma_variant<DmaTile<256, 256, 16, 2, 2, 4>>("dma_256x256x16_w2x2_s4"),
         dma_variant<DmaTile<256, 256, 32, 2, 2, 2>>("dma_256x256x32_w2x2_s2"),
-        dma_ex_variant<DmaTile<128, 128, 16, 2, 2, 3>>("dma_128x128x16_w2x2_s3"),
-        dma_variant<DmaTile<128, 128, 32, 2, 2, 3>>("dma_128x128x32_w2x2_s3"),
+        dma_ex_variant<DmaTile<128, 128, 16, 2, 2, 3, false>>("dma_128x128x16_w2x2_s3"),
+        dma_variant<DmaTile<128, 128, 32, 2, 2, 3, false>>("dma_128x128x32_w2x2_s3"),
         dma_ex_variant<DmaTile<256, 128, 16, 2, 2, 3>>("dma_256x128x16_w2x2_s3"),
         skinny_variant<SkinnyTile<4, 4, 64>>("skinny_16x64_w4_d4"),
         skinny_variant<SkinnyTile<8, 4, 64>>("skinny_16x64_w8_d4"),
@@ -158,14 +158,19 @@ const VariantDesc &variant(int v)
 
 // The tiled variants the shape dispatch weighs against each other, with the
 // throughput each sustains while every slot of a wave is busy (TFLOPS on one
-// MI355X, from the tile sweep on the 4096^3 and FFN shapes).
+// MI355X: 256x128 on 4096^3 and the FFN shape, 128x128 on 6144^3 (three
+// whole waves), 64x64 on 6144^3 (six)), and the share of a CU's throughput
+// that a lone workgroup gets (one wavefront per SIMD: 256x128 from
+// 2048^3, 128 tiles; 128x128 from 2048^3, 256 tiles; 64x64 not measured,
+// taken as 256x128's).
 struct Candidate {
     int variant;
     double full_tflops;
+    double lone_share;
 };
 constexpr int kCandidates = 3;
 constexpr Candidate kCandidate[kCandidates] = {
-    {V_DMA_256x128x16_S3, 144.0}, {V_DMA_128x128x16_S3, 142.0}, {V_DMA_64x64x16_S3, 126.0}};
+    {V_DMA_256x128x16_S3, 145.0, 0.92}, {V_DMA_128x128x16_S3, 144.0, 0.86}, {V_DMA_64x64x16_S3, 131.0, 0.92}};
 
 struct DeviceFacts {
     int status = -1;  // -1: not queried yet, else a gemm_f32_status
@@ -265,12 +270,14 @@ namespace {
 // Estimated time of a data-parallel plan ("GEMM 性能优化", Wave 模型): the
 // tiles run in waves of S = (workgroups per CU) x CUs; a full wave takes
 // S tiles' FLOPs at the variant's full-wave throughput.  A last, partial
-// wave with w of the c slots per CU busy takes w/c of a wave, divided by
-// 0.92 when w < c: a CU running fewer workgroups gives each a larger share,
-// but not all of it (measured: a lone 256x128 workgroup runs a CU at 92 % of
-// the throughput of two).  The estimate ranks the candidates; it ranked the
-// measured ragged 5003x4097x2049 times (64x64 724 us < 128x128 739 us <
-// 256x128 743 us) and the 4096^3 and FFN choices correctly.
+// wave with w of the c slots per CU busy takes w/c of a wave; with w = 1 the
+// lone workgroup's four wavefronts have a SIMD each and nothing covers their
+// waits, so it gets only lone_share of the CU (two or more workgroups
+// interleave: 64x64 tiles at w = 4 of 6 measured w/c exactly).  Against the
+// measured times (one MI355X) the estimate ranks the three candidates right
+// on 2048^3, 3000^3, 4096^3, 6144^3, 1536x4096x4096, 5003x4097x2049 and
+// 8192x14336x4096; most estimates are within 3 %, the worst (256x128 at
+// 6144^3, where the 128 tiles of the last wave land two to a CU) 13 % low.
 double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n, int64_t k, int cus)
 {
     const VariantDesc &d = variant(cand.variant);
@@ -282,7 +289,7 @@ double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n,
     if (rem) {
         const int64_t w = std::min<int64_t>(per_cu, ceil_div(rem, cus));
         last = (double)w / per_cu;
-        if (w < per_cu) last /= 0.92;
+        if (w == 1 && per_cu > 1) last /= cand.lone_share;
     }
     return ((double)full + last) * wave;
 }

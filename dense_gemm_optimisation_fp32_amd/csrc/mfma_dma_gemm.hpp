@@ -26,8 +26,9 @@
 // row MB*l32 + mb of the wavefront tile for lane row l32 of block mb).
 //
 // The slab body is an explicit schedule: straight-line code fenced with
-// sched_barrier, one copy after every two MFMAs, and the MFMA section at a
-// raised wavefront priority (s_setprio) ahead of the wait and the barrier.
+// sched_barrier, one copy after every two MFMAs, the MFMA section optionally
+// at a raised wavefront priority (s_setprio), then a wait that leaves the
+// copies of the later slabs in flight and a bare s_barrier (ring_barrier).
 //
 // Range checking is per 4-byte element: a chunk that straddles an operand's
 // byte extent keeps its in-range elements and reads zeros past the end, rows
@@ -44,10 +45,15 @@
 
 namespace gemmf32 {
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_>
+// PRIO: raise the wavefront priority for the matrix-core part of each slab.
+// Measured at 4096^3: +0.4-0.8 % with 256x128 tiles (two workgroups per CU)
+// and 64x64 tiles, but 128x128 tiles with three workgroups per CU lose 18 %
+// with it (115.8 against 142.0 TFLOPS), so those variants leave it off.
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, bool PRIO_ = true>
 struct DmaTile : MfmaTile<BM_, BN_, BK_, WAVES_M_, WAVES_N_> {
     using Base = MfmaTile<BM_, BN_, BK_, WAVES_M_, WAVES_N_>;
     static constexpr int STAGES = STAGES_;
+    static constexpr bool PRIO = PRIO_;
     static constexpr int PIECES = Base::A_PER_T + Base::B_PER_T;   // 16-byte copies per lane per slab
     static constexpr int LDS_BYTES = STAGES * (Base::A_CHUNKS + Base::B_CHUNKS) * 16;
     static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
@@ -184,6 +190,23 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// The slab ring's workgroup barrier: this wavefront's LDS reads and writes
+// complete and at most N of its copies still in flight, then s_barrier.
+// __syncthreads() would add a workgroup-scope release fence, and since the
+// copies write LDS through the vector memory counter the fence waits for all
+// of them (vmcnt(0)), copies of the slab after next included: the ring then
+// drains every slab.  The "memory" clobber keeps the compiler from moving LDS
+// accesses across the barrier; the explicit counts give the ordering the
+// fence would: the next slab's copies have landed (vmcnt), and no LDS read of
+// the stage about to be refilled is still pending (lgkmcnt(0)).
+template <int N>
+__device__ __forceinline__ void ring_barrier()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+    asm volatile("s_barrier" ::: "memory");
+}
+
 // Fragments of one wavefront for one slab.  A (and column-major B) come as
 // 16-byte k-chunks, double-buffered per chunk; row-major B as one read per
 // k-step, double-buffered per step.
@@ -296,11 +319,10 @@ __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 
     const int cpy = (kt + T::STAGES - 1) % T::STAGES;
     const f32x4 *As = lds_a + cur * T::A_CHUNKS;
     const f32x4 *Bs = lds_b + cur * T::B_CHUNKS;
-    // The matrix-core part of the slab issues at a raised priority; the wait
-    // for the next slab and the barrier at the normal one, so a wavefront
-    // that is ready to multiply goes ahead of one that is about to wait
-    // (measured +0.6 % at 4096^3).
-    __builtin_amdgcn_s_setprio(1);
+    // With PRIO the matrix-core part of the slab issues at a raised priority
+    // and the wait for the next slab and the barrier at the normal one, so a
+    // wavefront that is ready to multiply goes ahead of one about to wait.
+    if constexpr (T::PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int p = 0; p < T::KH - 1; ++p) {
         dma_prefetch<T, B_COL, A_COL>(p + 1, As, Bs, wr, wc, l32, half, f);
@@ -315,12 +337,14 @@ __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (T::PRIO) __builtin_amdgcn_s_setprio(0);
     if constexpr (WAIT >= 0) {
         wait_vmcnt<WAIT>();
         if (fix) dma_fix_tail<T, B_COL, A_COL>(g, kt + 1, tid, lds_a + nxt * T::A_CHUNKS, lds_b + nxt * T::B_CHUNKS);
     }
-    __syncthreads();
+    // (WAIT < 0: no copies of this range remain; the barrier only orders the
+    // LDS reads before the next range's copies.)
+    ring_barrier<(WAIT < 0 ? 63 : WAIT)>();
     if constexpr (WAIT >= 0)
         dma_prefetch<T, B_COL, A_COL>(0, lds_a + nxt * T::A_CHUNKS, lds_b + nxt * T::B_CHUNKS, wr, wc, l32, half, f);
 #pragma unroll

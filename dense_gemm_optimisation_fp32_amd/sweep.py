@@ -44,8 +44,9 @@ def kernel_resources(path: str = RESOURCES):
 
 
 def kernel_tag(info: dict, layout_b: int) -> str:
-    """Substring of the mangled name of the kernel a variant launches (the
-    one-tile-per-workgroup kernel) for one B layout."""
+    """Regular expression for the mangled name of the kernel a variant
+    launches (the one-tile-per-workgroup kernel, row-major A, no epilogue) for
+    one B layout."""
     b = f"Lb{layout_b}E"
     if info["kind"] == 1:
         return f"gemm_valu_kernelI{b}"
@@ -54,15 +55,16 @@ def kernel_tag(info: dict, layout_b: int) -> str:
         return f"SkinnyTileILi{m.group(2)}ELi{m.group(3)}ELi{m.group(1)}EEE{b}"
     dims = (f"ILi{info['bm']}ELi{info['bn']}ELi{info['bk']}ELi{info['waves_m']}ELi{info['waves_n']}")
     if info["name"].startswith("dma_"):
-        return f"gemm_mfma_dma_kernelINS_7DmaTile{dims}ELi{info['stages']}EEE{b}"
+        # DmaTile<..., STAGES, PRIO>, then B_COL, A_COL = false, EPI = false
+        return f"gemm_mfma_dma_kernelINS_7DmaTile{dims}ELi{info['stages']}ELb[01]EEE{b}Lb0ELb0EEEv"
     return f"gemm_mfma_kernelINS_8MfmaTile{dims}EEE{b}"
 
 
 def resources_for(info: dict, layout_b: int, res: dict):
     """Resources of the kernel a variant launches for one B layout."""
-    tag = kernel_tag(info, layout_b)
+    tag = re.compile(kernel_tag(info, layout_b))
     for name, r in res.items():
-        if tag in name:
+        if tag.search(name):
             vg = int(r.get("VGPRs", 0))
             ag = int(r.get("AGPRs", 0))
             lds = int(r.get("LDS Size [bytes/block]", 0))

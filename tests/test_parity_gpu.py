@@ -252,6 +252,31 @@ def test_stream_k_chosen_for_few_tiles_long_k(layout_b):
         assert np.array_equal(C[rows, cols].astype(np.float64), c)
 
 
+# The shape dispatch's choice on the shapes it was measured on (one MI355X,
+# 256 CUs): the fastest of the three candidate tiles on each.  Plans only,
+# nothing is launched.
+DISPATCH_CASES = [
+    ((4096, 4096, 4096), "dma_256x128x16_w2x2_s3"),
+    ((8192, 14336, 4096), "dma_256x128x16_w2x2_s3"),
+    ((6144, 6144, 6144), "dma_128x128x16_w2x2_s3"),
+    ((3000, 3000, 3000), "dma_64x64x16_w2x2_s3"),
+    ((2048, 2048, 2048), "dma_64x64x16_w2x2_s3"),
+    ((1536, 4096, 4096), "dma_64x64x16_w2x2_s3"),
+    ((5003, 4097, 2049), "dma_64x64x16_w2x2_s3"),
+]
+
+
+@pytest.mark.parametrize("shape,name", DISPATCH_CASES)
+def test_dispatch_choice(shape, name):
+    import dense_gemm_optimisation_fp32_amd as g
+
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the choices were measured on a 256-CU MI355X")
+    m, n, k = shape
+    plan = g.Plan(m, n, k, ROW_MAJOR, k, n, n)
+    assert plan.info["name"] == name and plan.info["stream_k"] == 0
+
+
 # ---------------------------------------------------------------------------
 # Full workload shapes, in the plan the benchmark times (gemm_f32_create).
 # ---------------------------------------------------------------------------
