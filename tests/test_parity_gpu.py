@@ -277,6 +277,54 @@ def test_dispatch_choice(shape, name):
     assert plan.info["name"] == name and plan.info["stream_k"] == 0
 
 
+# Operands whose byte extent is just under the 2^31 limit the plan accepts:
+# the 32-bit buffer offsets of the last rows/columns are near 2^31 and must
+# still address the right elements.  Integer inputs, so every sampled element
+# is exact; the oracle sees only the sampled rows of A and columns of B (the
+# sum of each element is the same sum over its row and column).
+NEAR_LIMIT = {
+    # name: (m, n, k, layout_a, layout_b), the operand near the limit
+    "A": (32768, 64, 16383, ROW_MAJOR, ROW_MAJOR),
+    "A_stream_k": (8192, 64, 65535, ROW_MAJOR, ROW_MAJOR),
+    "A_col": (16383, 64, 32768, COL_MAJOR, ROW_MAJOR),
+    "B_col": (64, 32768, 16383, ROW_MAJOR, COL_MAJOR),
+    "B_few_rows": (16, 32768, 16383, ROW_MAJOR, ROW_MAJOR),
+    "C": (32768, 16383, 64, ROW_MAJOR, ROW_MAJOR),
+}
+
+
+@pytest.mark.parametrize("name", list(NEAR_LIMIT))
+def test_operand_extent_near_limit(name):
+    import dense_gemm_optimisation_fp32_amd as g
+    from workloads import a_storage_shape, b_storage_shape, int_storage
+
+    m, n, k, la, lb = NEAR_LIMIT[name]
+    print(f"\n[case] near-limit extent {name} shape={(m, n, k)} layout_a={la} layout_b={lb}", flush=True)
+    A = int_storage(*a_storage_shape(m, k, la), seed=300)
+    B = int_storage(*b_storage_shape(k, n, lb), seed=301)
+    assert max(A.nbytes, B.nbytes, 4 * m * n) > (1 << 31) - (1 << 20)
+    dev = torch.device("cuda", 0)
+    dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    dC = torch.full((m, n), float("nan"), dtype=torch.float32, device=dev)
+    lda = k if la == ROW_MAJOR else m
+    ldb = n if lb == ROW_MAJOR else k
+    plan = g.Plan(m, n, k, lb, lda, ldb, n, layout_a=la)
+    assert (plan.info["stream_k"] > 0) == (name == "A_stream_k")
+    if la == ROW_MAJOR:
+        plan.run(dA.data_ptr(), dB.data_ptr(), dC.data_ptr())
+    else:
+        plan.run_ex(dA.data_ptr(), dB.data_ptr(), dC.data_ptr())
+    torch.cuda.synchronize()
+    rows, cols = sample_indices(m, n, 64, seed=302)
+    rows, cols = np.unique(rows), np.unique(cols)
+    got = dC[torch.from_numpy(rows).to(dev)][:, torch.from_numpy(cols).to(dev)].cpu().numpy()
+    # the sampled rows of A and columns of B as a small row-major problem
+    a_sub = np.ascontiguousarray(A[rows, :] if la == ROW_MAJOR else A[:, rows].T)
+    b_sub = np.ascontiguousarray(B[:, cols] if lb == ROW_MAJOR else B[cols, :].T)
+    ref, _ = oracle.gemm_f64(a_sub, b_sub, rows.size, cols.size, k, ROW_MAJOR)
+    assert np.array_equal(got.astype(np.float64), ref), f"{plan.info['name']} {name}"
+
+
 # ---------------------------------------------------------------------------
 # Full workload shapes, in the plan the benchmark times (gemm_f32_create).
 # ---------------------------------------------------------------------------

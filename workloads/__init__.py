@@ -156,6 +156,13 @@ def mod_pattern_operands(m: int, n: int, k: int, layout_b: int):
     return np.ascontiguousarray(a), np.ascontiguousarray(b)
 
 
+def int_storage(rows: int, cols: int, seed: int) -> np.ndarray:
+    """A (rows x cols) float32 storage buffer of integers uniform in [-8, 8],
+    drawn as int8 so that operands of a few GiB stay cheap to make."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(-8, 9, (rows, cols), dtype=np.int8).astype(np.float32)
+
+
 def permutation(n: int, seed: int) -> np.ndarray:
     """A seeded permutation of range(n)."""
     return np.random.default_rng(seed).permutation(n)
