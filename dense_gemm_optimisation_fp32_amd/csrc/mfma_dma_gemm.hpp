@@ -207,15 +207,35 @@ __device__ __forceinline__ void ring_barrier()
     asm volatile("s_barrier" ::: "memory");
 }
 
+// How many k-steps ahead of its first use a fragment is read from LDS.  One
+// step is enough for most tile/layout pairs; two paid where both operands
+// are read one k-step at a time or the CU runs three workgroups (4096^3, one
+// MI355X, distance 1 -> 2: 256x128 with column-major A and row-major B 139.0
+// -> 142.5 TFLOPS, 128x128 row-major 140.7 -> 142.6).  Elsewhere two steps
+// measured the same within 0.5 %, or slower (256x128 row-major 145.7 ->
+// 144.5, 128x128 with column-major B 127 -> 119.5), so they keep one.
+template <class T, bool B_COL, bool A_COL>
+constexpr int prefetch_distance()
+{
+    return ((T::BM == 256 && T::BN == 128 && A_COL && !B_COL) || (T::BM == 128 && T::BN == 128 && !A_COL && !B_COL))
+               ? 2
+               : 1;
+}
+
 // Fragments of one wavefront for one slab.  A (and column-major B) come as
-// 16-byte k-chunks, double-buffered per chunk; row-major B as one read per
-// k-step, double-buffered per step.
+// 16-byte k-chunks, double-buffered per chunk (a chunk covers four k-steps,
+// more than the prefetch distance); row-major B and column-major A as one
+// read per k-step, in a ring of 2 x distance registers sets (so that a slab
+// of KH = 8 k-steps maps each k-step to the same set in every slab).
 template <class T, bool B_COL, bool A_COL = false>
 struct DmaFrags {
+    static constexpr int D = prefetch_distance<T, B_COL, A_COL>();
+    static constexpr int FB = 2 * D;
+    static_assert(T::KH % FB == 0 && D <= 4, "k-step ring and chunk buffers");
     f32x4 af[2][T::MB];
     f32x4 bk[2][T::NB];        // column-major B: k-chunk q of block nb in bk[q & 1][nb]
-    BFrag<T::NB> bf[2];        // row-major B: k-step p in bf[p & 1]
-    BFrag<T::MB> am[2];        // column-major A: k-step p in am[p & 1]
+    BFrag<T::NB> bf[FB];       // row-major B: k-step p in bf[p % FB]
+    BFrag<T::MB> am[FB];       // column-major A: k-step p in am[p % FB]
 };
 
 template <class T>
@@ -276,15 +296,16 @@ __device__ __forceinline__ void dma_mfma_one(int i, int p, const DmaFrags<T, B_C
                                              f32x16 (&acc)[T::MB][T::NB])
 {
     const int mb = i / T::NB, nb = i % T::NB;
-    const float a = A_COL ? f.am[p & 1].v[mb] : f.af[(p >> 2) & 1][mb][p & 3];
+    constexpr int FB = DmaFrags<T, B_COL, A_COL>::FB;
+    const float a = A_COL ? f.am[p % FB].v[mb] : f.af[(p >> 2) & 1][mb][p & 3];
     float b;
     if constexpr (B_COL) b = f.bk[(p >> 2) & 1][nb][p & 3];
-    else b = f.bf[p & 1].v[nb];
+    else b = f.bf[p % FB].v[nb];
     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[mb][nb], 0, 0, 0);
 }
 
-// Reads for k-step p+1 issued at the top of k-step p (and the first reads of a
-// slab, p = -1).
+// Reads for k-step p_next: issued at the top of k-step p_next - D, or after
+// the barrier for the first D k-steps of the next slab.
 template <class T, bool B_COL, bool A_COL = false>
 __device__ __forceinline__ void dma_prefetch(int p_next, const f32x4 *As, const f32x4 *Bs, int wr, int wc, int l32,
                                              int half, DmaFrags<T, B_COL, A_COL> &f)
@@ -294,16 +315,17 @@ __device__ __forceinline__ void dma_prefetch(int p_next, const f32x4 *As, const 
         if constexpr (!A_COL) read_a<T>(As, wr, l32, half, q, f.af[q & 1]);
         if constexpr (B_COL) read_bk<T>(Bs, wc, l32, half, q, f.bk[q & 1]);
     }
-    if constexpr (A_COL) read_am<T>(As, wr, l32, half, p_next, f.am[p_next & 1]);
-    if constexpr (!B_COL) read_bn<T>(Bs, wc, l32, half, p_next, f.bf[p_next & 1]);
+    constexpr int FB = DmaFrags<T, B_COL, A_COL>::FB;
+    if constexpr (A_COL) read_am<T>(As, wr, l32, half, p_next, f.am[p_next % FB]);
+    if constexpr (!B_COL) read_bn<T>(Bs, wc, l32, half, p_next, f.bf[p_next % FB]);
 }
 
 // One slab kt on stage kt % STAGES.  copy: issue the copies of slab
 // kt + STAGES - 1 (one per two MFMAs from the start of the slab; uniform
 // flag).  WAIT: the vmcnt allowance when waiting for slab kt+1's copies at the
 // end (-1: slab kt is the last one).  fix: zero the k tail of slab kt+1 after
-// it lands (uniform flag).  The barrier precedes the last k-step, whose MFMAs
-// cover the first LDS reads of slab kt+1.
+// it lands (uniform flag).  The barrier precedes the last D k-steps (D = the
+// prefetch distance), whose MFMAs cover the first LDS reads of slab kt+1.
 template <class T, bool B_COL, int WAIT, bool A_COL = false>
 __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 *lds_b, __amdgpu_buffer_rsrc_t ra,
                                          __amdgpu_buffer_rsrc_t rb, const DmaBases<T, B_COL, A_COL> &bases,
@@ -312,8 +334,9 @@ __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 
                                          DmaFrags<T, B_COL, A_COL> &f, f32x16 (&acc)[T::MB][T::NB])
 {
     constexpr int NM = T::MB * T::NB;
-    constexpr int GAP = 2 * T::PIECES <= (T::KH - 1) * NM ? 2 : 1;
-    static_assert(T::PIECES * GAP <= (T::KH - 1) * NM, "copies fit before the barrier");
+    constexpr int D = DmaFrags<T, B_COL, A_COL>::D;
+    constexpr int GAP = 2 * T::PIECES <= (T::KH - D) * NM ? 2 : 1;
+    static_assert(T::PIECES * GAP <= (T::KH - D) * NM, "copies fit before the barrier");
     const int cur = kt % T::STAGES;
     const int nxt = (kt + 1) % T::STAGES;
     const int cpy = (kt + T::STAGES - 1) % T::STAGES;
@@ -324,8 +347,8 @@ __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 
     // wavefront that is ready to multiply goes ahead of one about to wait.
     if constexpr (T::PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int p = 0; p < T::KH - 1; ++p) {
-        dma_prefetch<T, B_COL, A_COL>(p + 1, As, Bs, wr, wc, l32, half, f);
+    for (int p = 0; p < T::KH - D; ++p) {
+        dma_prefetch<T, B_COL, A_COL>(p + D, As, Bs, wr, wc, l32, half, f);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
@@ -345,10 +368,14 @@ __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 
     // (WAIT < 0: no copies of this range remain; the barrier only orders the
     // LDS reads before the next range's copies.)
     ring_barrier<(WAIT < 0 ? 63 : WAIT)>();
-    if constexpr (WAIT >= 0)
-        dma_prefetch<T, B_COL, A_COL>(0, lds_a + nxt * T::A_CHUNKS, lds_b + nxt * T::B_CHUNKS, wr, wc, l32, half, f);
 #pragma unroll
-    for (int i = 0; i < NM; ++i) dma_mfma_one<T, B_COL, A_COL>(i, T::KH - 1, f, acc);
+    for (int d = 0; d < D; ++d) {
+        if constexpr (WAIT >= 0)
+            dma_prefetch<T, B_COL, A_COL>(d, lds_a + nxt * T::A_CHUNKS, lds_b + nxt * T::B_CHUNKS, wr, wc, l32, half,
+                                          f);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) dma_mfma_one<T, B_COL, A_COL>(i, T::KH - D + d, f, acc);
+    }
 }
 
 // Slabs [kt0, kt1) of one tile, accumulated into acc.  The ring stage of
@@ -380,7 +407,9 @@ __device__ __forceinline__ void dma_range(const GemmArgs &g, f32x4 *lds_a, f32x4
     if (kt0 + 1 == kt1 && kt1 == KT && ktail)
         dma_fix_tail<T, B_COL, A_COL>(g, kt0, tid, lds_a + st0 * T::A_CHUNKS, lds_b + st0 * T::B_CHUNKS);
     __syncthreads();
-    dma_prefetch<T, B_COL, A_COL>(0, lds_a + st0 * T::A_CHUNKS, lds_b + st0 * T::B_CHUNKS, wr, wc, l32, half, f);
+#pragma unroll
+    for (int d = 0; d < DmaFrags<T, B_COL, A_COL>::D; ++d)
+        dma_prefetch<T, B_COL, A_COL>(d, lds_a + st0 * T::A_CHUNKS, lds_b + st0 * T::B_CHUNKS, wr, wc, l32, half, f);
 
     // Steady state: slab kt+1 is not the last one and slab kt+STAGES-1
     // exists, so STAGES-2 slabs' copies may stay in flight while waiting for
