@@ -59,7 +59,8 @@ class gemm_f32_info(ctypes.Structure):
         ("stream_k_tiles", ctypes.c_int), ("layout_a", ctypes.c_int), ("epilogue", ctypes.c_int),
         ("aligned", ctypes.c_int),
         ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("k_tiles", ctypes.c_int64),
-        ("grid", ctypes.c_int64), ("group_m", ctypes.c_int), ("name", ctypes.c_char * 64),
+        ("grid", ctypes.c_int64), ("group_m", ctypes.c_int), ("c_store_width", ctypes.c_int),
+        ("name", ctypes.c_char * 64),
     ]
 
     def as_dict(self):

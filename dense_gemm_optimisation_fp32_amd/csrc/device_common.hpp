@@ -71,6 +71,12 @@ __device__ __forceinline__ void buf_store_x4(f32x4 v, __amdgpu_buffer_rsrc_t r, 
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)byte_off, 0, 0);
 }
 
+__device__ __forceinline__ void buf_store_x2(float a, float b, __amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(
+        u32x2{__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b)}, r, (int)byte_off, 0, 0);
+}
+
 __device__ __forceinline__ void buf_store_x1(float v, __amdgpu_buffer_rsrc_t r, uint32_t byte_off)
 {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)byte_off, 0, 0);

@@ -44,6 +44,8 @@ struct VariantDesc {
     const void *fn[2];     // [column-major B]
     const void *fn_sk[2];  // stream-K kernels (tiles' k-slabs shared across workgroups), or NULL
     const void *fn_ex[2][2][2];  // [column-major A][column-major B][epilogue], or NULL
+    const void *fn_wide[2];  // [column-major A]: row-major B, no epilogue, C stored NB columns
+                             // at a time (N a multiple of NB), or NULL
 };
 
 template <class T>
@@ -58,12 +60,15 @@ VariantDesc mfma_variant(const char *name)
 template <class T>
 VariantDesc dma_variant(const char *name)
 {
-    return VariantDesc{
+    VariantDesc d{
         name, GEMM_F32_KIND_MFMA, T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::THREADS, T::LDS_BYTES, T::STAGES,
         {reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_kernel<T, false>),
          reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_kernel<T, true>)},
         {reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_sk_kernel<T, false>),
          reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_sk_kernel<T, true>)}};
+    if constexpr (T::NB == 2 || T::NB == 4)
+        d.fn_wide[0] = reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_kernel<T, false, false, false, true>);
+    return d;
 }
 
 // A DMA variant that also serves column-major A and the linear-layer
@@ -81,6 +86,8 @@ VariantDesc dma_ex_variant(const char *name)
     d.fn_ex[0][1][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, true, false, true>);
     d.fn_ex[1][0][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, false, true, true>);
     d.fn_ex[1][1][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, true, true, true>);
+    if constexpr (T::NB == 2 || T::NB == 4)
+        d.fn_wide[1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, false, true, false, true>);
     return d;
 }
 
@@ -263,6 +270,7 @@ struct gemm_f32_plan_impl {
     unsigned block;
     void *workspace;     // split-k partial sums and arrival counters (few-row path), else NULL
     std::atomic<unsigned> runs{0};   // epochs handed out so far
+    int c_store_width = 1;           // C elements per store of the whole-tile kernel
 };
 
 namespace {
@@ -358,6 +366,14 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     p->layout_b = layout_b;
     p->epilogue = epilogue;
     p->fn = ex ? d.fn_ex[layout_a][layout_b][epilogue] : d.fn[layout_b];
+    // Row-major B without the epilogue: 8- or 16-byte C stores when N is a
+    // multiple of the columns a lane holds per row (bn / waves_n / 32).
+    const int lane_cols = d.kind == GEMM_F32_KIND_MFMA ? d.bn / d.waves_n / 32 : 0;
+    p->c_store_width = 1;
+    if (layout_b == GEMM_F32_ROW_MAJOR && !epilogue && d.fn_wide[layout_a] && lane_cols > 0 && n % lane_cols == 0) {
+        p->fn = d.fn_wide[layout_a];
+        p->c_store_width = lane_cols;
+    }
     p->m = m; p->n = n; p->k = k;
     p->lda = lda; p->ldb = ldb; p->ldc = ldc;
     p->strides4 = lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0;
@@ -449,6 +465,7 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
         if (wgs > 0) {
             a.sk_wgs = (int)wgs;
             a.sk_tiles = (int)shared;
+            p->c_store_width = 1;   // the stream-K kernel stores one element at a time
             p->grid = (unsigned)(wgs + tiles - shared);
             const size_t words = (size_t)2 * wgs * d.bm * d.bn * sizeof(unsigned long long);
             const size_t bytes = words + (size_t)shared * sizeof(unsigned);
@@ -624,6 +641,7 @@ int gemm_f32_describe(gemm_f32_plan p, gemm_f32_info *info)
     info->k_tiles = p->args.k_tiles;
     info->grid = p->grid;
     info->group_m = p->args.group_m;
+    info->c_store_width = p->c_store_width;
     info->split_k = p->args.split_k;
     info->stream_k = p->args.sk_wgs;
     info->stream_k_tiles = p->args.sk_tiles;

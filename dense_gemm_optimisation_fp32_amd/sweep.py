@@ -55,8 +55,13 @@ def kernel_tag(info: dict, layout_b: int) -> str:
         return f"SkinnyTileILi{m.group(2)}ELi{m.group(3)}ELi{m.group(1)}EEE{b}"
     dims = (f"ILi{info['bm']}ELi{info['bn']}ELi{info['bk']}ELi{info['waves_m']}ELi{info['waves_n']}")
     if info["name"].startswith("dma_"):
-        # DmaTile<..., STAGES, PRIO>, then B_COL, A_COL = false, EPI = false
-        return f"gemm_mfma_dma_kernelINS_7DmaTile{dims}ELi{info['stages']}ELb[01]EEE{b}Lb0ELb0EEEv"
+        # DmaTile<..., STAGES, PRIO>, then B_COL, A_COL = false, EPI = false,
+        # WIDE_C (the 8/16-byte C stores a row-major-B plan takes when N is a
+        # multiple of the wavefront tile's 32-column blocks, as in every
+        # sweep workload)
+        wide = int(layout_b == 0 and info["wave_n"] // 32 in (2, 4))
+        return (f"gemm_mfma_dma_kernelINS_7DmaTile{dims}ELi{info['stages']}ELb[01]EEE{b}"
+                f"Lb0ELb0ELb{wide}EEEv")
     return f"gemm_mfma_kernelINS_8MfmaTile{dims}EEE{b}"
 
 

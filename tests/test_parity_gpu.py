@@ -31,6 +31,7 @@ SMALL_SHAPES = [
     (1, 300, 17),
     (37, 1, 5),
     (129, 131, 33),
+    (70, 130, 40),       # N even but not a multiple of 4
     (64, 64, 4096),      # long k
 ]
 
@@ -275,6 +276,31 @@ def test_dispatch_choice(shape, name):
     m, n, k = shape
     plan = g.Plan(m, n, k, ROW_MAJOR, k, n, n)
     assert plan.info["name"] == name and plan.info["stream_k"] == 0
+
+
+# The whole-tile kernel stores NB adjacent C columns per instruction when B is
+# row-major, there is no epilogue and N is a multiple of NB (the columns a lane
+# holds per row: 2 for 64-column wavefront tiles, 4 for 128-column ones).
+@pytest.mark.parametrize("variant_name,n,layout_b,width", [
+    ("dma_256x128x16_w2x2_s3", 520, ROW_MAJOR, 2),
+    ("dma_256x128x16_w2x2_s3", 130, ROW_MAJOR, 2),
+    ("dma_256x128x16_w2x2_s3", 257, ROW_MAJOR, 1),
+    ("dma_256x128x16_w2x2_s3", 520, COL_MAJOR, 1),
+    ("dma_256x256x16_w2x2_s3", 520, ROW_MAJOR, 4),
+    ("dma_256x256x16_w2x2_s3", 130, ROW_MAJOR, 1),
+    ("dma_64x64x16_w2x2_s3", 520, ROW_MAJOR, 1),
+    ("mfma_256x128x16_w2x2_32x32x2", 520, ROW_MAJOR, 1),
+])
+def test_c_store_width(variant_name, n, layout_b, width):
+    import dense_gemm_optimisation_fp32_amd as g
+
+    v = next(i for i in variants() if g.gemm_f32_variant_info(i)["name"] == variant_name)
+    m, k = 300, 77
+    ldb = n if layout_b == ROW_MAJOR else k
+    assert g.Plan(m, n, k, layout_b, k, ldb, n, v).info["c_store_width"] == width
+    if layout_b == ROW_MAJOR and variant_name.startswith("dma_256x128"):
+        # the epilogue kernels store one element at a time
+        assert g.Plan(m, n, k, layout_b, k, ldb, n, epilogue=1).info["c_store_width"] == 1
 
 
 # Operands whose byte extent is just under the 2^31 limit the plan accepts:
