@@ -174,10 +174,12 @@ struct Candidate {
     int variant;
     double full_tflops;
     double lone_share;
+    bool tail_sk;   // a packed last wave may go to stream-K (measured for these tiles)
 };
 constexpr int kCandidates = 3;
-constexpr Candidate kCandidate[kCandidates] = {
-    {V_DMA_256x128x16_S3, 145.0, 0.92}, {V_DMA_128x128x16_S3, 144.0, 0.86}, {V_DMA_64x64x16_S3, 131.0, 0.92}};
+constexpr Candidate kCandidate[kCandidates] = {{V_DMA_256x128x16_S3, 145.0, 0.92, true},
+                                               {V_DMA_128x128x16_S3, 144.0, 0.86, false},
+                                               {V_DMA_64x64x16_S3, 131.0, 0.92, false}};
 
 struct DeviceFacts {
     int status = -1;  // -1: not queried yet, else a gemm_f32_status
@@ -275,44 +277,73 @@ struct gemm_f32_plan_impl {
 
 namespace {
 
-// Estimated time of a data-parallel plan ("GEMM 性能优化", Wave 模型): the
-// tiles run in waves of S = (workgroups per CU) x CUs; a full wave takes
-// S tiles' FLOPs at the variant's full-wave throughput.  A last, partial
-// wave with w of the c slots per CU busy takes w/c of a wave; with w = 1 the
-// lone workgroup's four wavefronts have a SIMD each and nothing covers their
-// waits, so it gets only lone_share of the CU (two or more workgroups
-// interleave: 64x64 tiles at w = 4 of 6 measured w/c exactly).  Against the
-// measured times (one MI355X) the estimate ranks the three candidates right
-// on 2048^3, 3000^3, 4096^3, 6144^3, 1536x4096x4096, 5003x4097x2049 and
-// 8192x14336x4096; most estimates are within 3 %, the worst (256x128 at
-// 6144^3, where the 128 tiles of the last wave land two to a CU) 13 % low.
-double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n, int64_t k, int cus)
+// Estimated time of a plan ("GEMM 性能优化", Wave 模型): the tiles run in
+// waves of S = (workgroups per CU) x CUs = c x CUs; a full wave takes S
+// tiles' FLOPs at the variant's full-wave throughput.  The last, partial
+// wave of r tiles depends on when it starts.  As the whole grid (no full
+// wave before it) the dispatcher spreads it: w = ceil(r / CUs) workgroups
+// per CU take w/c of a wave, and a lone workgroup (w = 1) gets only
+// lone_share of its CU, its four wavefronts having nothing to cover their
+// waits.  After full waves, tiles with c <= 3 come back packed: the
+// workgroups of a CU finish together, and the CUs that free up first take
+// two each, so the tail runs at least two per CU (measured at k = 4096:
+// 64 to 256 tail tiles of 256x128 took 0.5 to 1.0 of a wave, mostly the
+// whole; 64 and 256 of 128x128 two thirds); with c = 6 (64x64) the
+// workgroups finish staggered and a tail of up to 256 tiles ran spread.
+// When the packed tail of a 256x128 plan has at most one tile per CU and
+// k >= 4096, its tiles' k-slabs may instead be split evenly over one
+// workgroup per CU with stream-K (the full waves unchanged), estimated at
+// the whole plan's FLOPs at the full-wave rate plus 0.18 of a wave for the
+// partial sums and the imbalance (measured 0.12 to 0.18): 4096x5120x4096
+// 103.5 -> 132.3 TFLOPS, 4096x6144x4096 110.2 -> 132.6, 2304x9216x4096
+// 101.9 -> 128.6.  (128x128 tiles gained too, but their stream-K kernel
+// fits two workgroups per CU against three, and with one tile per split it
+// lost: 2048x14336x4096 126.1 -> 116.8.)  The estimates came within 4 % of
+// 28 measured plans (one MI355X, 2048^3 to 8192x14336x4096, the three
+// tiles each) except 256x128 at 6144^3, where the packed tail ran 13 %
+// over, and rank the candidates right on all of those shapes.
+double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n, int64_t k, int cus, bool tail_ok,
+                        int64_t *tail_tiles)
 {
     const VariantDesc &d = variant(cand.variant);
     const int64_t tiles = ceil_div(m, d.bm) * ceil_div(n, d.bn);
     const int64_t slots = (int64_t)per_cu * cus;
     const int64_t full = tiles / slots, rem = tiles % slots;
     const double wave = (double)slots * 2.0 * d.bm * d.bn * (double)k / (cand.full_tflops * 1e12);
+    *tail_tiles = 0;
     double last = 0.0;
     if (rem) {
-        const int64_t w = std::min<int64_t>(per_cu, ceil_div(rem, cus));
+        int64_t w = std::min<int64_t>(per_cu, ceil_div(rem, cus));
+        if (full >= 1 && per_cu <= 3) w = std::min<int64_t>(per_cu, std::max<int64_t>(w, 2));
         last = (double)w / per_cu;
         if (w == 1 && per_cu > 1) last /= cand.lone_share;
     }
-    return ((double)full + last) * wave;
+    const double dp = ((double)full + last) * wave;
+    if (tail_ok && cand.tail_sk && full >= 1 && rem > 0 && rem <= cus && k >= 4096) {
+        const double hybrid = ((double)tiles / slots + 0.18) * wave;
+        if (hybrid < dp) {
+            *tail_tiles = rem;
+            return hybrid;
+        }
+    }
+    return dp;
 }
 
 // Shape dispatch.  Few rows: the bandwidth-bound split-k path.  When even
 // 64 x 64 tiles leave fewer than two workgroups per CU and k is long,
-// 128 x 128 tiles with stream-K (workgroups share the tiles' k-slabs) fill
-// the GPU: measured 83 against 63 TFLOPS at 1024x1024x8192 and 65 against
-// ~62 at 1024x1024x4096, but 47 against 60 at 1024x1024x2048, where the
-// partial tiles cost more than the idle CUs; at 512x4096x4096 (512 small
-// tiles) data-parallel 64 x 64 is as fast.  Otherwise the
-// direct-to-LDS tile whose estimated time is least.
-int choose_variant(int64_t m, int64_t n, int64_t k, const DeviceFacts &f, bool *stream_k)
+// 128 x 128 tiles with stream-K over all tiles (workgroups share the tiles'
+// k-slabs) fill the GPU: measured 83 against 63 TFLOPS at 1024x1024x8192
+// and 65 against ~62 at 1024x1024x4096, but 47 against 60 at
+// 1024x1024x2048, where the partial tiles cost more than the idle CUs; at
+// 512x4096x4096 (512 small tiles) data-parallel 64 x 64 is as fast.
+// Otherwise the direct-to-LDS tile whose estimated time is least, and with
+// it *tail_tiles > 0 when its partial last wave goes to stream-K.  tail_ok:
+// the plan can run the stream-K kernel (row-major A, no epilogue).
+int choose_variant(int64_t m, int64_t n, int64_t k, const DeviceFacts &f, bool tail_ok, bool *stream_k,
+                   int64_t *tail_tiles)
 {
     *stream_k = false;
+    *tail_tiles = 0;
     if (m <= 32) return V_SKINNY_W16_D4;
     if (ceil_div(m, 64) * ceil_div(n, 64) < 2 * (int64_t)f.cu_count && k >= 4096) {
         *stream_k = true;
@@ -321,10 +352,12 @@ int choose_variant(int64_t m, int64_t n, int64_t k, const DeviceFacts &f, bool *
     int best = 0;
     double best_t = 0.0;
     for (int i = 0; i < kCandidates; ++i) {
-        const double t = estimate_seconds(kCandidate[i], f.per_cu[i], m, n, k, f.cu_count);
+        int64_t tail = 0;
+        const double t = estimate_seconds(kCandidate[i], f.per_cu[i], m, n, k, f.cu_count, tail_ok, &tail);
         if (i == 0 || t < best_t) {
             best = i;
             best_t = t;
+            *tail_tiles = tail;
         }
     }
     return kCandidate[best].variant;
@@ -349,14 +382,18 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
 
     int v = forced_variant;
     bool auto_stream_k = false;
+    int64_t auto_tail = 0;
     if (v < 0) {
         v = env_int("GEMM_F32_VARIANT", -1);
-        if (v < 0 || v >= V_COUNT) v = choose_variant(m, n, k, facts, &auto_stream_k);
+        if (v < 0 || v >= V_COUNT) v = choose_variant(m, n, k, facts, !ex, &auto_stream_k, &auto_tail);
         if (ex && !variant(v).fn_ex[0][0][0]) v = V_DMA_64x64x16_S3;
     }
     const VariantDesc &d = variant(v);
     if (ex && !d.fn_ex[0][0][0]) return GEMM_F32_ERR_INVALID_VALUE;
-    if (ex) auto_stream_k = false;
+    if (ex) {
+        auto_stream_k = false;
+        auto_tail = 0;
+    }
 
     gemm_f32_plan p = new (std::nothrow) gemm_f32_plan_impl();
     if (!p) return GEMM_F32_ERR_ALLOC;
@@ -434,18 +471,22 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     }
 
     if (d.fn_sk[0]) {
-        // Stream-K: as many workgroups as are resident at once share the
-        // k-slabs of all tiles evenly (chosen by the shape dispatch).
-        // GEMM_F32_SK_WGS forces it with that many workgroups, over the
-        // first GEMM_F32_SK_TILES tiles (default all; the other tiles get a
-        // workgroup each); GEMM_F32_STREAMK=0 disables the automatic choice.
-        // (Splitting only the tiles of a partly filled last wave was
-        // measured no faster: a lone workgroup runs a CU at ~92 % of the
-        // throughput of two, and the partial sums cost the rest.)
+        // Stream-K, chosen by the shape dispatch: either as many workgroups
+        // as are resident at once share the k-slabs of all tiles evenly, or
+        // one workgroup per CU shares those of the partial last wave's tiles
+        // (the rest run whole).  GEMM_F32_SK_WGS forces it with that many
+        // workgroups, over the first GEMM_F32_SK_TILES tiles (default all;
+        // the other tiles get a workgroup each); GEMM_F32_STREAMK=0 disables
+        // the automatic choice.
         const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
         int64_t wgs = ex ? 0 : env_int("GEMM_F32_SK_WGS", 0);
         int64_t shared = wgs > 0 ? env_int("GEMM_F32_SK_TILES", (int)tiles) : tiles;
-        if (wgs <= 0 && auto_stream_k && env_int("GEMM_F32_STREAMK", 1) != 0) {
+        if (wgs <= 0 && auto_tail > 0 && env_int("GEMM_F32_STREAMK", 1) != 0) {
+            // The partial last wave's tiles (the first ones in raster order)
+            // split over one workgroup per CU; the other tiles whole.
+            wgs = facts.cu_count;
+            shared = auto_tail;
+        } else if (wgs <= 0 && auto_stream_k && env_int("GEMM_F32_STREAMK", 1) != 0) {
             int per_cu = 0;
             hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, d.fn_sk[layout_b], d.threads, 0);
             if (e != hipSuccess) {

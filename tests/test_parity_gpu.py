@@ -256,26 +256,64 @@ def test_stream_k_chosen_for_few_tiles_long_k(layout_b):
 # The shape dispatch's choice on the shapes it was measured on (one MI355X,
 # 256 CUs): the fastest of the three candidate tiles on each.  Plans only,
 # nothing is launched.
+# (shape, tile, tiles of the partial last wave split by stream-K over one
+# workgroup per CU, or 0 for a data-parallel plan)
 DISPATCH_CASES = [
-    ((4096, 4096, 4096), "dma_256x128x16_w2x2_s3"),
-    ((8192, 14336, 4096), "dma_256x128x16_w2x2_s3"),
-    ((6144, 6144, 6144), "dma_128x128x16_w2x2_s3"),
-    ((3000, 3000, 3000), "dma_64x64x16_w2x2_s3"),
-    ((2048, 2048, 2048), "dma_64x64x16_w2x2_s3"),
-    ((1536, 4096, 4096), "dma_64x64x16_w2x2_s3"),
-    ((5003, 4097, 2049), "dma_64x64x16_w2x2_s3"),
+    ((4096, 4096, 4096), "dma_256x128x16_w2x2_s3", 0),
+    ((8192, 14336, 4096), "dma_256x128x16_w2x2_s3", 0),
+    ((6144, 6144, 6144), "dma_128x128x16_w2x2_s3", 0),
+    ((3000, 3000, 3000), "dma_64x64x16_w2x2_s3", 0),
+    ((2048, 2048, 2048), "dma_64x64x16_w2x2_s3", 0),
+    ((1536, 4096, 4096), "dma_64x64x16_w2x2_s3", 0),
+    ((5003, 4097, 2049), "dma_64x64x16_w2x2_s3", 0),
+    ((4096, 4608, 4096), "dma_64x64x16_w2x2_s3", 0),
+    ((4096, 6144, 4096), "dma_128x128x16_w2x2_s3", 0),
+    ((2048, 14336, 4096), "dma_64x64x16_w2x2_s3", 0),
+    ((2304, 9216, 4096), "dma_256x128x16_w2x2_s3", 136),
+    ((1536, 13824, 4096), "dma_256x128x16_w2x2_s3", 136),
 ]
 
 
-@pytest.mark.parametrize("shape,name", DISPATCH_CASES)
-def test_dispatch_choice(shape, name):
+@pytest.mark.parametrize("shape,name,tail", DISPATCH_CASES)
+def test_dispatch_choice(shape, name, tail):
     import dense_gemm_optimisation_fp32_amd as g
 
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the choices were measured on a 256-CU MI355X")
     m, n, k = shape
-    plan = g.Plan(m, n, k, ROW_MAJOR, k, n, n)
-    assert plan.info["name"] == name and plan.info["stream_k"] == 0
+    info = g.Plan(m, n, k, ROW_MAJOR, k, n, n).info
+    assert info["name"] == name
+    if tail:
+        assert info["stream_k"] == 256 and info["stream_k_tiles"] == tail
+    else:
+        assert info["stream_k"] == 0
+    # the linear-layer plans never use stream-K
+    assert g.Plan(m, n, k, ROW_MAJOR, k, n, n, epilogue=1).info["stream_k"] == 0
+
+
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+def test_stream_k_tail_chosen(layout_b):
+    """A plan with one full wave of 256x128 tiles and a short last wave splits
+    the last wave's tiles over one workgroup per CU; it matches the oracle
+    (integer inputs bit for bit) and repeats bit for bit."""
+    import dense_gemm_optimisation_fp32_amd as g
+
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the choice was measured on a 256-CU MI355X")
+    m, n, k = 4352, 4864, 4096     # 17 x 38 = 646 tiles: 512 + 134
+    print(f"\n[case] stream-K tail layout_b={layout_b} shape={(m, n, k)}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=98)
+    C, info, outs = run_gemm(A, B, m, n, k, layout_b, repeat=2)
+    assert info["name"] == "dma_256x128x16_w2x2_s3"
+    assert info["stream_k"] == 256 and info["stream_k_tiles"] == 134
+    assert np.array_equal(outs[0], outs[1])
+    rows, cols = sample_indices(m, n, 2000, seed=99)
+    c, s_ = oracle.gemm_f64_sampled(A, B, m, n, k, layout_b, rows, cols)
+    check_close(C[rows, cols], c, s_, "stream-K tail")
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=100)
+    C, _ = run_gemm(A, B, m, n, k, layout_b)
+    c, _ = oracle.gemm_f64_sampled(A, B, m, n, k, layout_b, rows, cols)
+    assert np.array_equal(C[rows, cols].astype(np.float64), c)
 
 
 # The whole-tile kernel stores NB adjacent C columns per instruction when B is
