@@ -30,12 +30,15 @@
  *    several host threads and streams at once.  Plans that split tiles
  *    along k own a device workspace (zeroed by create, freed by destroy):
  *    few-row plans with gemm_f32_info.split_k > 1 hold split_k * m * n
- *    partial sums, stream-K plans (gemm_f32_info.stream_k = P > 0) hold
- *    2 * P partial tiles (bm * bn each), all as 8-byte words tagged with a
- *    per-run epoch, plus one 32-bit arrival counter per output tile.  Each run takes a new epoch from the plan (an atomic counter,
- *    so runs may be enqueued from several host threads), but two runs of such
- *    a plan must not execute at the same time on the device (they would share
- *    the workspace): use one plan per stream, or order the streams.
+ *    partial sums, stream-K plans (gemm_f32_info.stream_k = P > 0: P
+ *    workgroups share the k-slabs of gemm_f32_info.stream_k_tiles tiles,
+ *    all of them or the partial last wave's) hold 2 * P partial tiles
+ *    (bm * bn each), all as 8-byte words tagged with a per-run epoch, plus
+ *    one 32-bit arrival counter per output tile.  Each run takes a new epoch
+ *    from the plan (an atomic counter, so runs may be enqueued from several
+ *    host threads), but two runs of such a plan must not execute at the same
+ *    time on the device (they would share the workspace): use one plan per
+ *    stream, or order the streams.
  *  - Execution is asynchronous on the caller's stream; a device-side fault
  *    is reported by the caller's next synchronisation, not by gemm_f32_run.
  */
