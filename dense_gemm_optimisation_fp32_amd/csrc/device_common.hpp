@@ -61,6 +61,11 @@ __device__ __forceinline__ f32x4 buf_load_x4(__amdgpu_buffer_rsrc_t r, uint32_t 
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
 
+__device__ __forceinline__ f32x2 buf_load_x2(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 0));
+}
+
 __device__ __forceinline__ float buf_load_x1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0));

@@ -44,8 +44,8 @@ struct VariantDesc {
     const void *fn[2];     // [column-major B]
     const void *fn_sk[2];  // stream-K kernels (tiles' k-slabs shared across workgroups), or NULL
     const void *fn_ex[2][2][2];  // [column-major A][column-major B][epilogue], or NULL
-    const void *fn_wide[2];  // [column-major A]: row-major B, no epilogue, C stored NB columns
-                             // at a time (N a multiple of NB), or NULL
+    const void *fn_wide[2][2];  // [column-major A][epilogue]: row-major B, C stored NB columns
+                                // at a time (N a multiple of NB), or NULL
 };
 
 template <class T>
@@ -67,7 +67,7 @@ VariantDesc dma_variant(const char *name)
         {reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_sk_kernel<T, false>),
          reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_sk_kernel<T, true>)}};
     if constexpr (T::NB == 2 || T::NB == 4)
-        d.fn_wide[0] = reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_kernel<T, false, false, false, true>);
+        d.fn_wide[0][0] = reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_kernel<T, false, false, false, true>);
     return d;
 }
 
@@ -86,8 +86,11 @@ VariantDesc dma_ex_variant(const char *name)
     d.fn_ex[0][1][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, true, false, true>);
     d.fn_ex[1][0][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, false, true, true>);
     d.fn_ex[1][1][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, true, true, true>);
-    if constexpr (T::NB == 2 || T::NB == 4)
-        d.fn_wide[1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, false, true, false, true>);
+    if constexpr (T::NB == 2 || T::NB == 4) {
+        d.fn_wide[1][0] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, false, true, false, true>);
+        d.fn_wide[0][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, false, false, true, true>);
+        d.fn_wide[1][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, false, true, true, true>);
+    }
     return d;
 }
 
@@ -403,12 +406,13 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     p->layout_b = layout_b;
     p->epilogue = epilogue;
     p->fn = ex ? d.fn_ex[layout_a][layout_b][epilogue] : d.fn[layout_b];
-    // Row-major B without the epilogue: 8- or 16-byte C stores when N is a
-    // multiple of the columns a lane holds per row (bn / waves_n / 32).
+    // Row-major B: 8- or 16-byte C stores (and C loads of the epilogue)
+    // when N is a multiple of the columns a lane holds per row
+    // (bn / waves_n / 32).
     const int lane_cols = d.kind == GEMM_F32_KIND_MFMA ? d.bn / d.waves_n / 32 : 0;
     p->c_store_width = 1;
-    if (layout_b == GEMM_F32_ROW_MAJOR && !epilogue && d.fn_wide[layout_a] && lane_cols > 0 && n % lane_cols == 0) {
-        p->fn = d.fn_wide[layout_a];
+    if (layout_b == GEMM_F32_ROW_MAJOR && d.fn_wide[layout_a][epilogue] && lane_cols > 0 && n % lane_cols == 0) {
+        p->fn = d.fn_wide[layout_a][epilogue];
         p->c_store_width = lane_cols;
     }
     p->m = m; p->n = n; p->k = k;

@@ -457,8 +457,8 @@ __device__ __forceinline__ void dma_store_c(const GemmArgs &g, __amdgpu_buffer_r
     auto col_of = [&](int nb) {
         return B_COL ? col0 + wc * T::WN + nb * 32 + l32 : col0 + wc * T::WN + T::NB * l32 + nb;
     };
-    if constexpr (WIDE) {
-        static_assert(!B_COL && !EPI && (T::NB == 2 || T::NB == 4), "wide stores: row-major B, NB of 2 or 4");
+    static_assert(!WIDE || (!B_COL && (T::NB == 2 || T::NB == 4)), "wide stores: row-major B, NB of 2 or 4");
+    if constexpr (WIDE && !EPI) {
 #pragma unroll
         for (int mb = 0; mb < T::MB; ++mb)
 #pragma unroll
@@ -483,6 +483,58 @@ __device__ __forceinline__ void dma_store_c(const GemmArgs &g, __amdgpu_buffer_r
                     buf_store_x1(acc[mb][nb][v], rc, elem_off(r < g.m && c < g.n, r, g.ldc, c));
                 }
             }
+    } else if constexpr (WIDE) {
+        // As below, NB adjacent columns per load and store (N a multiple of
+        // NB, so the group is inside the row when its first column is).
+        const __amdgpu_buffer_rsrc_t rbias = make_rsrc(g.bias, g.bias ? (uint32_t)g.n * 4u : 0u);
+        const float lo = g.act == 1 ? 0.0f : -__builtin_inff();
+        const bool gelu = g.act == 2;
+        const int c = col_of(0);
+        float bias[T::NB];
+        if constexpr (T::NB == 2) {
+            const f32x2 t = buf_load_x2(rbias, elem_off(c < g.n, 0, 0, c));
+            bias[0] = t[0];
+            bias[1] = t[1];
+        } else {
+            const f32x4 t = buf_load_x4(rbias, elem_off(c < g.n, 0, 0, c));
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) bias[nb] = t[nb];
+        }
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+            float cold[16][T::NB];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = row_of(mb, v);
+                const uint32_t off = elem_off(g.use_beta && r < g.m && c < g.n, r, g.ldc, c);
+                if constexpr (T::NB == 2) {
+                    const f32x2 t = buf_load_x2(rc, off);
+                    cold[v][0] = t[0];
+                    cold[v][1] = t[1];
+                } else {
+                    const f32x4 t = buf_load_x4(rc, off);
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb) cold[v][nb] = t[nb];
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = row_of(mb, v);
+                float x[T::NB];
+#pragma unroll
+                for (int nb = 0; nb < T::NB; ++nb) {
+                    x[nb] = g.alpha * acc[mb][nb][v] + g.beta * cold[v][nb] + bias[nb];
+                    x[nb] = fmaxf(x[nb], lo);
+                    x[nb] = gelu ? gelu_erf(x[nb]) : x[nb];
+                }
+                const uint32_t off = elem_off(r < g.m && c < g.n, r, g.ldc, c);
+                if constexpr (T::NB == 2)
+                    buf_store_x2(x[0], x[1], rc, off);
+                else
+                    buf_store_x4(f32x4{x[0], x[1], x[2], x[3]}, rc, off);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     } else {
         // Branch-free over the elements: C reads as zero when beta == 0 (an
         // out-of-range offset), ReLU is max(x, lo) with lo = -inf when off,

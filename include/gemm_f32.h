@@ -101,7 +101,7 @@ struct gemm_f32_info {
     int64_t tiles_m, tiles_n, k_tiles, grid; /* plan only: tile counts and workgroups launched */
     int group_m;        /* plan only: tile-rows per rasterisation group */
     int c_store_width;  /* plan only: C elements per store instruction of the whole-tile kernel
-                           (2 or 4 with row-major B, no epilogue and N a multiple of it; else 1) */
+                           (2 or 4 with row-major B and N a multiple of it; else 1) */
     char name[64];      /* human-readable variant name */
 };
 

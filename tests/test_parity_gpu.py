@@ -329,7 +329,7 @@ def test_stream_k_tail_chosen(layout_b):
     ("dma_64x64x16_w2x2_s3", 520, ROW_MAJOR, 1),
     ("mfma_256x128x16_w2x2_32x32x2", 520, ROW_MAJOR, 1),
 ])
-def test_c_store_width(variant_name, n, layout_b, width):
+def test_c_store_width(variant_name, n, layout_b, width, monkeypatch):
     import dense_gemm_optimisation_fp32_amd as g
 
     v = next(i for i in variants() if g.gemm_f32_variant_info(i)["name"] == variant_name)
@@ -337,8 +337,10 @@ def test_c_store_width(variant_name, n, layout_b, width):
     ldb = n if layout_b == ROW_MAJOR else k
     assert g.Plan(m, n, k, layout_b, k, ldb, n, v).info["c_store_width"] == width
     if layout_b == ROW_MAJOR and variant_name.startswith("dma_256x128"):
-        # the epilogue kernels store one element at a time
-        assert g.Plan(m, n, k, layout_b, k, ldb, n, epilogue=1).info["c_store_width"] == 1
+        # the epilogue kernels take the same width
+        monkeypatch.setenv("GEMM_F32_VARIANT", str(v))
+        info = g.Plan(m, n, k, layout_b, k, ldb, n, epilogue=1).info
+        assert info["name"] == variant_name and info["c_store_width"] == width
 
 
 # Operands whose byte extent is just under the 2^31 limit the plan accepts:
