@@ -402,11 +402,20 @@ __device__ __forceinline__ void dma_range(const GemmArgs &g, f32x4 *lds_a, f32x4
                 dma_issue<T, B_COL, A_COL>(j, g, bases, ra, rb, kt0 + s, tid, wave, lds_a + st * T::A_CHUNKS,
                                     lds_b + st * T::B_CHUNKS);
         }
-    wait_vmcnt<0>();
+    // Wait for slab kt0's copies only: those of the later prologue slabs
+    // were issued after them and may stay in flight.
     const int st0 = kt0 % T::STAGES;
-    if (kt0 + 1 == kt1 && kt1 == KT && ktail)
-        dma_fix_tail<T, B_COL, A_COL>(g, kt0, tid, lds_a + st0 * T::A_CHUNKS, lds_b + st0 * T::B_CHUNKS);
-    __syncthreads();
+    const int n_pro = kt1 - kt0 < T::STAGES - 1 ? kt1 - kt0 : T::STAGES - 1;
+    if (n_pro == 1) {
+        wait_vmcnt<0>();
+        if (kt0 + 1 == kt1 && kt1 == KT && ktail)
+            dma_fix_tail<T, B_COL, A_COL>(g, kt0, tid, lds_a + st0 * T::A_CHUNKS, lds_b + st0 * T::B_CHUNKS);
+        ring_barrier<0>();
+    } else if (T::STAGES >= 4 && n_pro == 3) {
+        ring_barrier<(T::STAGES >= 4 ? 2 : 0) * T::PIECES>();
+    } else {
+        ring_barrier<T::PIECES>();
+    }
 #pragma unroll
     for (int d = 0; d < DmaFrags<T, B_COL, A_COL>::D; ++d)
         dma_prefetch<T, B_COL, A_COL>(d, lds_a + st0 * T::A_CHUNKS, lds_b + st0 * T::B_CHUNKS, wr, wc, l32, half, f);
