@@ -131,6 +131,11 @@ enum VariantId {
     V_DMA_64x64x16_S3,
     V_SKINNY_W16_D4,
     V_SKINNY16_W16_D4,
+    V_DMA_64x64x16_S2,
+    V_DMA_128x64x16_S2,
+    V_DMA_128x64x16_S3,
+    V_DMA_64x128x16_S2,
+    V_DMA_64x128x16_S3,
     V_COUNT
 };
 
@@ -158,6 +163,11 @@ const VariantDesc &variant(int v)
         dma_ex_variant<DmaTile<64, 64, 16, 2, 2, 3>>("dma_64x64x16_w2x2_s3"),
         skinny_variant<SkinnyTile<16, 4, 64>>("skinny_16x64_w16_d4"),
         skinny_variant<SkinnyTile<16, 4, 16>>("skinny_16x16_w16_d4"),
+        dma_ex_variant<DmaTile<64, 64, 16, 2, 2, 2>>("dma_64x64x16_w2x2_s2"),
+        dma_variant<DmaTile<128, 64, 16, 2, 2, 2>>("dma_128x64x16_w2x2_s2"),
+        dma_variant<DmaTile<128, 64, 16, 2, 2, 3>>("dma_128x64x16_w2x2_s3"),
+        dma_ex_variant<DmaTile<64, 128, 16, 2, 2, 2>>("dma_64x128x16_w2x2_s2"),
+        dma_variant<DmaTile<64, 128, 16, 2, 2, 3>>("dma_64x128x16_w2x2_s3"),
     };
     return table[v];
 }
@@ -169,27 +179,29 @@ const VariantDesc &variant(int v)
 // The tiled variants the shape dispatch weighs against each other, with the
 // throughput each sustains while every slot of a wave is busy (TFLOPS on one
 // MI355X: 256x128 on 4096^3 and the FFN shape, 128x128 on 6144^3 (three
-// whole waves), 64x64 on 6144^3 (six)), and the share of a CU's throughput
-// that a lone workgroup gets (one wavefront per SIMD: 256x128 from
-// 2048^3, 128 tiles; 128x128 from 2048^3, 256 tiles; 64x64 not measured,
-// taken as 256x128's).
+// whole waves), 64x128 and 64x64 (two LDS stages, four and eight workgroups
+// per CU) on 4096^3 (two whole waves)), and the share of a CU's throughput
+// that a lone workgroup gets (one wavefront per SIMD: 256x128 from 2048^3,
+// 128 tiles; 128x128 from 2048^3, 256 tiles; the others taken as 256x128's).
 struct Candidate {
     int variant;
     double full_tflops;
     double lone_share;
-    bool tail_sk;   // a packed last wave may go to stream-K (measured for these tiles)
+    bool tail_sk;   // a packed last wave may go to stream-K (measured for this tile)
 };
-constexpr int kCandidates = 3;
+constexpr int kCandidates = 4;
 constexpr Candidate kCandidate[kCandidates] = {{V_DMA_256x128x16_S3, 145.0, 0.92, true},
                                                {V_DMA_128x128x16_S3, 144.0, 0.86, false},
-                                               {V_DMA_64x64x16_S3, 131.0, 0.92, false}};
+                                               {V_DMA_64x128x16_S2, 142.0, 0.92, false},
+                                               {V_DMA_64x64x16_S2, 137.0, 0.92, false}};
 
 struct DeviceFacts {
     int status = -1;  // -1: not queried yet, else a gemm_f32_status
     int cu_count = 0;
     int num_xcd = 1;
     int hip_error = 0;
-    int per_cu[kCandidates] = {};  // resident workgroups per CU of each candidate
+    int per_cu[kCandidates] = {};       // resident workgroups per CU of each candidate's kernel
+    int per_cu_wide[kCandidates] = {};  // the same for its wide-store kernel (0: none)
 };
 
 constexpr int kMaxDevices = 64;
@@ -234,6 +246,16 @@ int device_facts(int *device_out, DeviceFacts *facts_out)
                     n = 1;
                 }
                 f.per_cu[i] = n;
+                // The wide-store kernel may hold a few more registers and
+                // fit fewer workgroups (64x128: four against five).
+                int w = 0;
+                if (d.fn_wide[0][0] &&
+                    (hipOccupancyMaxActiveBlocksPerMultiprocessor(&w, d.fn_wide[0][0], d.threads, 0) != hipSuccess ||
+                     w < 1)) {
+                    (void)hipGetLastError();
+                    w = n;
+                }
+                f.per_cu_wide[i] = w;
             }
             f.status = GEMM_F32_SUCCESS;
         }
@@ -283,28 +305,30 @@ namespace {
 // Estimated time of a plan ("GEMM 性能优化", Wave 模型): the tiles run in
 // waves of S = (workgroups per CU) x CUs = c x CUs; a full wave takes S
 // tiles' FLOPs at the variant's full-wave throughput.  The last, partial
-// wave of r tiles depends on when it starts.  As the whole grid (no full
-// wave before it) the dispatcher spreads it: w = ceil(r / CUs) workgroups
-// per CU take w/c of a wave, and a lone workgroup (w = 1) gets only
-// lone_share of its CU, its four wavefronts having nothing to cover their
-// waits.  After full waves, tiles with c <= 3 come back packed: the
-// workgroups of a CU finish together, and the CUs that free up first take
-// two each, so the tail runs at least two per CU (measured at k = 4096:
-// 64 to 256 tail tiles of 256x128 took 0.5 to 1.0 of a wave, mostly the
-// whole; 64 and 256 of 128x128 two thirds); with c = 6 (64x64) the
-// workgroups finish staggered and a tail of up to 256 tiles ran spread.
+// wave of r tiles: w = ceil(r / CUs) workgroups per CU take w/c of a wave,
+// and a lone workgroup (w = 1) gets only lone_share of its CU, its four
+// wavefronts having nothing to cover their waits.  After full waves, tiles
+// with c <= 4 come back packed: the workgroups of a CU finish together, and
+// the CUs that free up first take two each, so such a tail is charged at
+// least two per CU (measured at k = 4096: 64 to 256 tail tiles of 256x128
+// took 0.5 to 1.0 of a wave, mostly the whole; 64 and 256 of 128x128 two
+// thirds; 104 and 256 of 64x128 (c = 4) half).  With c = 8 (64x64) the
+// workgroups of a CU finish staggered and tails overlap the last full wave
+// (8 tail tiles cost 0.17 of a wave, 161 tiles 0.23).
 // When the packed tail of a 256x128 plan has at most one tile per CU and
 // k >= 4096, its tiles' k-slabs may instead be split evenly over one
-// workgroup per CU with stream-K (the full waves unchanged), estimated at
-// the whole plan's FLOPs at the full-wave rate plus 0.18 of a wave for the
-// partial sums and the imbalance (measured 0.12 to 0.18): 4096x5120x4096
-// 103.5 -> 132.3 TFLOPS, 4096x6144x4096 110.2 -> 132.6, 2304x9216x4096
-// 101.9 -> 128.6.  (128x128 tiles gained too, but their stream-K kernel
-// fits two workgroups per CU against three, and with one tile per split it
-// lost: 2048x14336x4096 126.1 -> 116.8.)  The estimates came within 4 % of
-// 28 measured plans (one MI355X, 2048^3 to 8192x14336x4096, the three
-// tiles each) except 256x128 at 6144^3, where the packed tail ran 13 %
-// over, and rank the candidates right on all of those shapes.
+// workgroup per CU (at most 8 per tile) with stream-K (the full waves
+// unchanged), estimated at the whole plan's FLOPs at the full-wave rate plus
+// 0.25 of a wave for the partial sums and the imbalance (measured 0.12 to
+// 0.24): 4096x5120x4096 103.5 -> 132.3 TFLOPS, 4096x6144x4096 110.2 ->
+// 132.6, 2304x9216x4096 101.9 -> 128.6 against data-parallel 256x128.
+// The smaller tiles usually beat both; the split wins only where a few
+// tail tiles follow many full waves of 256x128.
+// (128x128 tiles gained too, but their stream-K kernel fits two workgroups
+// per CU against three, and with one tile per split it lost:
+// 2048x14336x4096 126.1 -> 116.8.)  On 41 measured shapes (one MI355X, 24
+// of them random in [512, 8192]^2 x {1024, 2048, 3000, 4096}) the choice
+// came within 4.4 % of the fastest candidate, 0.4 % on average.
 double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n, int64_t k, int cus, bool tail_ok,
                         int64_t *tail_tiles)
 {
@@ -317,13 +341,13 @@ double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n,
     double last = 0.0;
     if (rem) {
         int64_t w = std::min<int64_t>(per_cu, ceil_div(rem, cus));
-        if (full >= 1 && per_cu <= 3) w = std::min<int64_t>(per_cu, std::max<int64_t>(w, 2));
+        if (full >= 1 && per_cu <= 4) w = std::min<int64_t>(per_cu, std::max<int64_t>(w, 2));
         last = (double)w / per_cu;
         if (w == 1 && per_cu > 1) last /= cand.lone_share;
     }
     const double dp = ((double)full + last) * wave;
     if (tail_ok && cand.tail_sk && full >= 1 && rem > 0 && rem <= cus && k >= 4096) {
-        const double hybrid = ((double)tiles / slots + 0.18) * wave;
+        const double hybrid = ((double)tiles / slots + 0.25) * wave;
         if (hybrid < dp) {
             *tail_tiles = rem;
             return hybrid;
@@ -342,7 +366,7 @@ double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n,
 // Otherwise the direct-to-LDS tile whose estimated time is least, and with
 // it *tail_tiles > 0 when its partial last wave goes to stream-K.  tail_ok:
 // the plan can run the stream-K kernel (row-major A, no epilogue).
-int choose_variant(int64_t m, int64_t n, int64_t k, const DeviceFacts &f, bool tail_ok, bool *stream_k,
+int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFacts &f, bool tail_ok, bool *stream_k,
                    int64_t *tail_tiles)
 {
     *stream_k = false;
@@ -354,9 +378,19 @@ int choose_variant(int64_t m, int64_t n, int64_t k, const DeviceFacts &f, bool t
     }
     int best = 0;
     double best_t = 0.0;
+    const bool log = env_int("GEMM_F32_LOG", 0) >= 2;
     for (int i = 0; i < kCandidates; ++i) {
         int64_t tail = 0;
-        const double t = estimate_seconds(kCandidate[i], f.per_cu[i], m, n, k, f.cu_count, tail_ok, &tail);
+        // The plan runs the wide-store kernel when B is row-major and N a
+        // multiple of the columns a lane holds; rate it at that occupancy.
+        const VariantDesc &d = variant(kCandidate[i].variant);
+        const int lane_cols = d.bn / d.waves_n / 32;
+        const bool wide = layout_b == GEMM_F32_ROW_MAJOR && f.per_cu_wide[i] > 0 && n % lane_cols == 0;
+        const int per_cu = wide ? f.per_cu_wide[i] : f.per_cu[i];
+        const double t = estimate_seconds(kCandidate[i], per_cu, m, n, k, f.cu_count, tail_ok, &tail);
+        if (log)
+            std::fprintf(stderr, "[gemm_f32] candidate %s: %d per CU, estimate %.1f us%s\n", d.name, per_cu, t * 1e6,
+                         tail ? " (stream-K tail)" : "");
         if (i == 0 || t < best_t) {
             best = i;
             best_t = t;
@@ -388,8 +422,8 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     int64_t auto_tail = 0;
     if (v < 0) {
         v = env_int("GEMM_F32_VARIANT", -1);
-        if (v < 0 || v >= V_COUNT) v = choose_variant(m, n, k, facts, !ex, &auto_stream_k, &auto_tail);
-        if (ex && !variant(v).fn_ex[0][0][0]) v = V_DMA_64x64x16_S3;
+        if (v < 0 || v >= V_COUNT) v = choose_variant(m, n, k, layout_b, facts, !ex, &auto_stream_k, &auto_tail);
+        if (ex && !variant(v).fn_ex[0][0][0]) v = V_DMA_64x64x16_S2;
     }
     const VariantDesc &d = variant(v);
     if (ex && !d.fn_ex[0][0][0]) return GEMM_F32_ERR_INVALID_VALUE;
@@ -487,8 +521,9 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
         int64_t shared = wgs > 0 ? env_int("GEMM_F32_SK_TILES", (int)tiles) : tiles;
         if (wgs <= 0 && auto_tail > 0 && env_int("GEMM_F32_STREAMK", 1) != 0) {
             // The partial last wave's tiles (the first ones in raster order)
-            // split over one workgroup per CU; the other tiles whole.
-            wgs = facts.cu_count;
+            // split over one workgroup per CU, at most 8 per tile (the last
+            // segment reads all the others); the other tiles whole.
+            wgs = std::min<int64_t>(facts.cu_count, 8 * auto_tail);
             shared = auto_tail;
         } else if (wgs <= 0 && auto_stream_k && env_int("GEMM_F32_STREAMK", 1) != 0) {
             int per_cu = 0;

@@ -22,7 +22,8 @@ from workloads import (COL_MAJOR, ROW_MAJOR, WORKLOADS, epilogue_operands, rando
 pytestmark = pytest.mark.gpu
 
 REL, ABS = 1.2e-5, 1.2e-6
-EX_VARIANTS = ["dma_256x128x16_w2x2_s3", "dma_128x128x16_w2x2_s3", "dma_64x64x16_w2x2_s3"]
+EX_VARIANTS = ["dma_256x128x16_w2x2_s3", "dma_128x128x16_w2x2_s3", "dma_64x128x16_w2x2_s2",
+               "dma_64x64x16_w2x2_s2", "dma_64x64x16_w2x2_s3"]
 ACTS = [g.GEMM_F32_ACT_NONE, g.GEMM_F32_ACT_RELU, g.GEMM_F32_ACT_GELU]
 
 

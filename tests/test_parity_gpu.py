@@ -262,15 +262,17 @@ DISPATCH_CASES = [
     ((4096, 4096, 4096), "dma_256x128x16_w2x2_s3", 0),
     ((8192, 14336, 4096), "dma_256x128x16_w2x2_s3", 0),
     ((6144, 6144, 6144), "dma_128x128x16_w2x2_s3", 0),
-    ((3000, 3000, 3000), "dma_64x64x16_w2x2_s3", 0),
-    ((2048, 2048, 2048), "dma_64x64x16_w2x2_s3", 0),
-    ((1536, 4096, 4096), "dma_64x64x16_w2x2_s3", 0),
-    ((5003, 4097, 2049), "dma_64x64x16_w2x2_s3", 0),
-    ((4096, 4608, 4096), "dma_64x64x16_w2x2_s3", 0),
+    ((3000, 3000, 3000), "dma_64x64x16_w2x2_s2", 0),
+    ((2048, 2048, 2048), "dma_64x128x16_w2x2_s2", 0),
+    ((1536, 4096, 4096), "dma_64x128x16_w2x2_s2", 0),
+    ((5003, 4097, 2049), "dma_64x64x16_w2x2_s2", 0),
+    ((4096, 4608, 4096), "dma_64x64x16_w2x2_s2", 0),
     ((4096, 6144, 4096), "dma_128x128x16_w2x2_s3", 0),
-    ((2048, 14336, 4096), "dma_64x64x16_w2x2_s3", 0),
-    ((2304, 9216, 4096), "dma_256x128x16_w2x2_s3", 136),
-    ((1536, 13824, 4096), "dma_256x128x16_w2x2_s3", 136),
+    ((2048, 14336, 4096), "dma_64x128x16_w2x2_s2", 0),
+    ((2304, 9216, 4096), "dma_64x64x16_w2x2_s2", 0),
+    ((1536, 13824, 4096), "dma_64x64x16_w2x2_s2", 0),
+    ((5120, 9856, 4096), "dma_64x64x16_w2x2_s2", 0),
+    ((7424, 13568, 4096), "dma_256x128x16_w2x2_s3", 2),
 ]
 
 
@@ -284,7 +286,8 @@ def test_dispatch_choice(shape, name, tail):
     info = g.Plan(m, n, k, ROW_MAJOR, k, n, n).info
     assert info["name"] == name
     if tail:
-        assert info["stream_k"] == 256 and info["stream_k_tiles"] == tail
+        # one workgroup per CU, at most 8 per split tile
+        assert info["stream_k"] == min(256, 8 * tail) and info["stream_k_tiles"] == tail
     else:
         assert info["stream_k"] == 0
     # the linear-layer plans never use stream-K
@@ -293,19 +296,19 @@ def test_dispatch_choice(shape, name, tail):
 
 @pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
 def test_stream_k_tail_chosen(layout_b):
-    """A plan with one full wave of 256x128 tiles and a short last wave splits
-    the last wave's tiles over one workgroup per CU; it matches the oracle
+    """A plan with full waves of 256x128 tiles and a short last wave splits the
+    last wave's tiles eight ways each; it matches the oracle
     (integer inputs bit for bit) and repeats bit for bit."""
     import dense_gemm_optimisation_fp32_amd as g
 
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the choice was measured on a 256-CU MI355X")
-    m, n, k = 4352, 4864, 4096     # 17 x 38 = 646 tiles: 512 + 134
+    m, n, k = 7424, 13568, 4096    # 29 x 106 = 3074 tiles: 6 x 512 + 2
     print(f"\n[case] stream-K tail layout_b={layout_b} shape={(m, n, k)}", flush=True)
     A, B = random_operands(m, n, k, layout_b, "normal1", seed=98)
     C, info, outs = run_gemm(A, B, m, n, k, layout_b, repeat=2)
     assert info["name"] == "dma_256x128x16_w2x2_s3"
-    assert info["stream_k"] == 256 and info["stream_k_tiles"] == 134
+    assert info["stream_k"] == 16 and info["stream_k_tiles"] == 2
     assert np.array_equal(outs[0], outs[1])
     rows, cols = sample_indices(m, n, 2000, seed=99)
     c, s_ = oracle.gemm_f64_sampled(A, B, m, n, k, layout_b, rows, cols)
