@@ -187,13 +187,17 @@ struct Candidate {
     int variant;
     double full_tflops;
     double lone_share;
-    bool tail_sk;   // a packed last wave may go to stream-K (measured for this tile)
+    double tail_extra;  // waves added to a last wave that follows full waves
+    bool tail_sk;       // a packed last wave may go to stream-K (measured for this tile)
 };
+// tail_extra: 64x64 tails after full waves ran 0.03 to 0.09 of a wave over
+// the count (8 tiles: 0.17 against 0.14, 161: 0.23 against 0.14, 512: 0.32
+// against 0.25).
 constexpr int kCandidates = 4;
-constexpr Candidate kCandidate[kCandidates] = {{V_DMA_256x128x16_S3, 145.0, 0.92, true},
-                                               {V_DMA_128x128x16_S3, 144.0, 0.86, false},
-                                               {V_DMA_64x128x16_S2, 142.0, 0.92, false},
-                                               {V_DMA_64x64x16_S2, 137.0, 0.92, false}};
+constexpr Candidate kCandidate[kCandidates] = {{V_DMA_256x128x16_S3, 145.0, 0.92, 0.0, true},
+                                               {V_DMA_128x128x16_S3, 144.0, 0.86, 0.0, false},
+                                               {V_DMA_64x128x16_S2, 142.0, 0.92, 0.0, false},
+                                               {V_DMA_64x64x16_S2, 137.0, 0.92, 0.05, false}};
 
 struct DeviceFacts {
     int status = -1;  // -1: not queried yet, else a gemm_f32_status
@@ -312,9 +316,11 @@ namespace {
 // the CUs that free up first take two each, so such a tail is charged at
 // least two per CU (measured at k = 4096: 64 to 256 tail tiles of 256x128
 // took 0.5 to 1.0 of a wave, mostly the whole; 64 and 256 of 128x128 two
-// thirds; 104 and 256 of 64x128 (c = 4) half).  With c = 8 (64x64) the
-// workgroups of a CU finish staggered and tails overlap the last full wave
-// (8 tail tiles cost 0.17 of a wave, 161 tiles 0.23).
+// thirds; 104 and 256 of 64x128 (c = 4) half).  A handful of tail tiles
+// (at most one per eight CUs) run alone instead (one 256x128 tile: half a
+// wave; four 64x128 tiles: 0.28 of one).  With c = 8 (64x64) the workgroups
+// of a CU finish staggered and tails overlap the last full wave (8 tail
+// tiles cost 0.17 of a wave, 161 tiles 0.23).
 // When the packed tail of a 256x128 plan has at most one tile per CU and
 // k >= 4096, its tiles' k-slabs may instead be split evenly over one
 // workgroup per CU (at most 8 per tile) with stream-K (the full waves
@@ -326,9 +332,9 @@ namespace {
 // tail tiles follow many full waves of 256x128.
 // (128x128 tiles gained too, but their stream-K kernel fits two workgroups
 // per CU against three, and with one tile per split it lost:
-// 2048x14336x4096 126.1 -> 116.8.)  On 41 measured shapes (one MI355X, 24
+// 2048x14336x4096 126.1 -> 116.8.)  On 39 measured shapes (one MI355X, 24
 // of them random in [512, 8192]^2 x {1024, 2048, 3000, 4096}) the choice
-// came within 4.4 % of the fastest candidate, 0.4 % on average.
+// came within 2 % of the fastest candidate.
 double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n, int64_t k, int cus, bool tail_ok,
                         int64_t *tail_tiles)
 {
@@ -341,9 +347,10 @@ double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n,
     double last = 0.0;
     if (rem) {
         int64_t w = std::min<int64_t>(per_cu, ceil_div(rem, cus));
-        if (full >= 1 && per_cu <= 4) w = std::min<int64_t>(per_cu, std::max<int64_t>(w, 2));
+        if (full >= 1 && per_cu <= 4 && rem > cus / 8) w = std::min<int64_t>(per_cu, std::max<int64_t>(w, 2));
         last = (double)w / per_cu;
         if (w == 1 && per_cu > 1) last /= cand.lone_share;
+        if (full >= 1) last += cand.tail_extra;
     }
     const double dp = ((double)full + last) * wave;
     if (tail_ok && cand.tail_sk && full >= 1 && rem > 0 && rem <= cus && k >= 4096) {

@@ -265,13 +265,13 @@ DISPATCH_CASES = [
     ((3000, 3000, 3000), "dma_64x64x16_w2x2_s2", 0),
     ((2048, 2048, 2048), "dma_64x128x16_w2x2_s2", 0),
     ((1536, 4096, 4096), "dma_64x128x16_w2x2_s2", 0),
-    ((5003, 4097, 2049), "dma_64x64x16_w2x2_s2", 0),
+    ((5003, 4097, 2049), "dma_64x128x16_w2x2_s2", 0),
     ((4096, 4608, 4096), "dma_64x64x16_w2x2_s2", 0),
     ((4096, 6144, 4096), "dma_128x128x16_w2x2_s3", 0),
     ((2048, 14336, 4096), "dma_64x128x16_w2x2_s2", 0),
-    ((2304, 9216, 4096), "dma_64x64x16_w2x2_s2", 0),
-    ((1536, 13824, 4096), "dma_64x64x16_w2x2_s2", 0),
-    ((5120, 9856, 4096), "dma_64x64x16_w2x2_s2", 0),
+    ((2304, 9216, 4096), "dma_64x128x16_w2x2_s2", 0),
+    ((1536, 13824, 4096), "dma_64x128x16_w2x2_s2", 0),
+    ((5120, 9856, 4096), "dma_64x128x16_w2x2_s2", 0),
     ((7424, 13568, 4096), "dma_256x128x16_w2x2_s3", 2),
 ]
 
