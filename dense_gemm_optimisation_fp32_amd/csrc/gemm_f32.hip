@@ -372,14 +372,15 @@ double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n,
 // 512x4096x4096 (512 small tiles) data-parallel 64 x 64 is as fast.
 // Otherwise the direct-to-LDS tile whose estimated time is least, and with
 // it *tail_tiles > 0 when its partial last wave goes to stream-K.  tail_ok:
-// the plan can run the stream-K kernel (row-major A, no epilogue).
+// the plan can run the stream-K kernel (row-major A, no epilogue); when it
+// cannot, few-tile shapes take the best data-parallel tile instead.
 int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFacts &f, bool tail_ok, bool *stream_k,
                    int64_t *tail_tiles)
 {
     *stream_k = false;
     *tail_tiles = 0;
     if (m <= 32) return V_SKINNY_W16_D4;
-    if (ceil_div(m, 64) * ceil_div(n, 64) < 2 * (int64_t)f.cu_count && k >= 4096) {
+    if (tail_ok && ceil_div(m, 64) * ceil_div(n, 64) < 2 * (int64_t)f.cu_count && k >= 4096) {
         *stream_k = true;
         return V_DMA_128x128x16_S3;
     }

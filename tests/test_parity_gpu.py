@@ -294,6 +294,18 @@ def test_dispatch_choice(shape, name, tail):
     assert g.Plan(m, n, k, ROW_MAJOR, k, n, n, epilogue=1).info["stream_k"] == 0
 
 
+def test_linear_plan_for_few_tiles_long_k():
+    """A few-tile long-k shape gets stream-K as a plain product; with the
+    epilogue (no stream-K kernel) it gets the data-parallel tile with the most
+    tiles rather than the stream-K tile run whole."""
+    import dense_gemm_optimisation_fp32_amd as g
+
+    m, n, k = 1024, 1024, 8192
+    assert g.Plan(m, n, k, ROW_MAJOR, k, n, n).info["stream_k"] > 0
+    info = g.Plan(m, n, k, ROW_MAJOR, k, n, n, epilogue=1).info
+    assert info["stream_k"] == 0 and info["name"] == "dma_64x64x16_w2x2_s2"
+
+
 @pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
 def test_stream_k_tail_chosen(layout_b):
     """A plan with full waves of 256x128 tiles and a short last wave splits the
