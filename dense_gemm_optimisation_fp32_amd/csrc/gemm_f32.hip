@@ -364,12 +364,14 @@ double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n,
 }
 
 // Shape dispatch.  Few rows: the bandwidth-bound split-k path.  When even
-// 64 x 64 tiles leave fewer than two workgroups per CU and k is long,
-// 128 x 128 tiles with stream-K over all tiles (workgroups share the tiles'
-// k-slabs) fill the GPU: measured 83 against 63 TFLOPS at 1024x1024x8192
-// and 65 against ~62 at 1024x1024x4096, but 47 against 60 at
-// 1024x1024x2048, where the partial tiles cost more than the idle CUs; at
-// 512x4096x4096 (512 small tiles) data-parallel 64 x 64 is as fast.
+// 64 x 64 tiles leave fewer than two workgroups per CU and k >= 2048,
+// 64 x 64 tiles with stream-K over all tiles (workgroups share the tiles'
+// k-slabs) fill the GPU.  Measured (TFLOPS; data-parallel 64x64 / stream-K
+// over 128x128 tiles / stream-K over 64x64 tiles): 1024x1024x8192 ~64 /
+// 94.4 / 105.1; 1024x1024x4096 ~63 / 74.8 / 95.6; 1024x1024x2048 62.5 / 47 /
+// 81.1; 512x512x8192 16.3 / 32.8 / 60.9; 768x768x8192 - / 53.5 / 83.4;
+// 256x256x4096 6.0 / 7.0 / 17.1.  At 2048x1024x4096 (512 tiles, two per CU)
+// stream-K measured 108.0 against 105.5, inside the noise of the choice.
 // Otherwise the direct-to-LDS tile whose estimated time is least, and with
 // it *tail_tiles > 0 when its partial last wave goes to stream-K.  tail_ok:
 // the plan can run the stream-K kernel (row-major A, no epilogue); when it
@@ -380,9 +382,9 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
     *stream_k = false;
     *tail_tiles = 0;
     if (m <= 32) return V_SKINNY_W16_D4;
-    if (tail_ok && ceil_div(m, 64) * ceil_div(n, 64) < 2 * (int64_t)f.cu_count && k >= 4096) {
+    if (tail_ok && ceil_div(m, 64) * ceil_div(n, 64) < 2 * (int64_t)f.cu_count && k >= 2048) {
         *stream_k = true;
-        return V_DMA_128x128x16_S3;
+        return V_DMA_64x64x16_S2;
     }
     int best = 0;
     double best_t = 0.0;
@@ -540,10 +542,13 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
                 delete p;
                 return hip_fail(e);
             }
-            // At most 8 segments per tile (the last one to arrive reads all
-            // the others: 32 segments per tile measured 6x slower than 8)
-            // and at least 8 slabs per workgroup.
-            wgs = std::min<int64_t>(std::min<int64_t>((int64_t)per_cu * facts.cu_count, 8 * tiles),
+            // As many workgroups as fit at once, but at most 8 segments per
+            // tile (the last one to arrive reads all the others: with 64x64
+            // tiles at 512x512x8192, 8 per tile ran 60.9 TFLOPS, 16 55.4,
+            // 32 40.7) unless that leaves CUs idle (256x256x4096: 16 per
+            // tile 17.1, 32 10.3), and at least 8 slabs per workgroup.
+            const int64_t segs = std::max<int64_t>(8, ceil_div(facts.cu_count, tiles));
+            wgs = std::min<int64_t>(std::min<int64_t>((int64_t)per_cu * facts.cu_count, segs * tiles),
                                     tiles * a.k_tiles / 8);
             if (wgs < 2) wgs = 0;
         }

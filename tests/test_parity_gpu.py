@@ -238,7 +238,8 @@ def test_stream_k_hybrid_forced(variant, layout_b, wgs, shared, monkeypatch):
 def test_stream_k_chosen_for_few_tiles_long_k(layout_b):
     """Shapes with too few tiles for the GPU and a long k get a stream-K plan
     by default; it matches the oracle (integer inputs bit for bit)."""
-    for (m, n, k) in [(256, 256, 4096), (1024, 1024, 8192), (512, 512, 8192)]:
+    for (m, n, k) in [(256, 256, 4096), (1024, 1024, 8192), (512, 512, 8192), (1024, 1024, 2048),
+                      (768, 700, 8192)]:
         print(f"\n[case] default stream-K layout_b={layout_b} shape={(m, n, k)}", flush=True)
         A, B = random_operands(m, n, k, layout_b, "normal1", seed=95)
         C, info, outs = run_gemm(A, B, m, n, k, layout_b, repeat=2)
