@@ -36,6 +36,7 @@ struct GemmArgs {
     int num_xcd;           // dispatch round-robins workgroups over this many XCDs
     uint32_t a_bytes, b_bytes, c_bytes;
     unsigned long long *partial;  // partial sums of split tiles, epoch-tagged words
+    uint32_t partial_bytes;       // byte extent of the stream-K partial-sum words (< 2^31)
     unsigned *arrivals;           // per-tile arrival counters for split tiles
     unsigned epoch;               // tag of this run's partial sums, never 0
     int sk_wgs;            // stream-K: workgroups sharing the first sk_tiles tiles' slabs (0: none)
@@ -175,6 +176,29 @@ __device__ __forceinline__ void store_tagged_word(unsigned long long *p, float v
 {
     __hip_atomic_store(p, ((unsigned long long)epoch << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The same device-scope accesses through a buffer descriptor.  A relaxed
+// agent-scope 64-bit atomic load or store is an ordinary 64-bit access with
+// the sc1 cache policy on gfx950; issued as a buffer access it takes a
+// per-lane offset plus a wavefront-uniform scalar offset, so a lane's words
+// spread over a tile need one address register in all instead of a 64-bit
+// address each.
+constexpr int kAgentScopePolicy = 16;  // sc1
+
+__device__ __forceinline__ unsigned long long buf_load_tagged(__amdgpu_buffer_rsrc_t r, uint32_t lane_off,
+                                                              uint32_t uniform_off)
+{
+    const u32x2 w = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)lane_off, (int)uniform_off, kAgentScopePolicy));
+    return ((unsigned long long)w.y << 32) | w.x;
+}
+
+__device__ __forceinline__ void buf_store_tagged(float v, unsigned epoch, __amdgpu_buffer_rsrc_t r, uint32_t lane_off,
+                                                 uint32_t uniform_off)
+{
+    const u32x2 w = {__float_as_uint(v), epoch};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)lane_off, (int)uniform_off, kAgentScopePolicy);
 }
 
 }  // namespace gemmf32

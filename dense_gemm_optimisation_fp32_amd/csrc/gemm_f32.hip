@@ -562,6 +562,13 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
             p->grid = (unsigned)(wgs + tiles - shared);
             const size_t words = (size_t)2 * wgs * d.bm * d.bn * sizeof(unsigned long long);
             const size_t bytes = words + (size_t)shared * sizeof(unsigned);
+            // The words are addressed through a buffer descriptor (32-bit
+            // extent); the automatic plans stay far below this.
+            if (words >= ((size_t)1 << 31)) {
+                delete p;
+                return GEMM_F32_ERR_INVALID_VALUE;
+            }
+            a.partial_bytes = (uint32_t)words;
             hipError_t e = hipMalloc(&p->workspace, bytes);
             if (e == hipSuccess) e = hipMemsetAsync(p->workspace, 0, bytes, nullptr);
             if (e == hipSuccess) e = hipStreamSynchronize(nullptr);

@@ -597,7 +597,13 @@ struct StreamK {
 // not depend on who arrives last, and writes the tile to C.  (The last one
 // could keep its own part in its accumulators, but adding vector-ALU
 // results to the accumulators makes the compiler hold all of them in vector
-// registers, which halves the occupancy of the whole kernel.)
+// registers, which halves the occupancy of the whole kernel.)  Word w of a
+// slot belongs to lane w % THREADS, so each access instruction covers
+// consecutive words; the words go through a buffer descriptor with the
+// device-scope cache policy, with the lane's offset in one register and the
+// slot and block in the scalar offset, and are read back eight per lane at
+// a time: the fix-up then needs no more registers than the main loop, and
+// the kernel keeps the occupancy of the whole-tile kernel.
 template <class T, bool B_COL>
 __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsrc_t rc, const StreamK &sk, int t,
                                           int p, int tid, int row0, int col0, int wr, int wc, int l32, int half,
@@ -606,20 +612,23 @@ __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsr
     const long long t0 = (long long)t * g.k_tiles;
     const int p_lo = sk.owner(t0), p_hi = sk.owner(t0 + g.k_tiles - 1);
     const int nseg = p_hi - p_lo + 1;
-    constexpr size_t SLOT = (size_t)T::BM * T::BN;
+    constexpr uint32_t SLOT = (uint32_t)T::BM * T::BN;   // words
     // Slot of range q's segment of this tile: 2q for a range that starts in
     // the tile (the tile is its first), 2q + 1 for one that starts before.
-    auto slot = [&](int q) { return (size_t)(2 * q + (sk.start(q) < t0 ? 1 : 0)) * SLOT; };
+    auto slot = [&](int q) { return (uint32_t)(2 * q + (sk.start(q) < t0 ? 1 : 0)) * SLOT; };
+    // Word of (block, element v) relative to the lane's first word.
+    auto word = [](int mb, int nb, int v) { return (uint32_t)(((mb * T::NB + nb) * 16 + v) * T::THREADS); };
 
-    unsigned long long *dst = g.partial + slot(p);
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(g.partial, g.partial_bytes);
+    const uint32_t lane_off = (uint32_t)tid * 8u;
+    const uint32_t mine = slot(p);
 #pragma unroll
     for (int mb = 0; mb < T::MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < T::NB; ++nb) {
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-                store_tagged_word(dst + (size_t)(((mb * T::NB + nb) * 16 + v) * T::THREADS + tid), acc[mb][nb][v],
-                                  g.epoch);
+                buf_store_tagged(acc[mb][nb][v], g.epoch, rp, lane_off, (mine + word(mb, nb, v)) * 8u);
             // One block at a time: keeps the scheduler from pulling all
             // accumulators into vector registers at once.
             __builtin_amdgcn_sched_barrier(0);
@@ -636,31 +645,38 @@ __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsr
     if (!*last_flag) return;
     int budget = kTaggedWaitBudget;
 
+    constexpr int H = 8;   // words per lane in flight
 #pragma unroll
     for (int mb = 0; mb < T::MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < T::NB; ++nb) {
-            const size_t off = (size_t)((mb * T::NB + nb) * 16) * T::THREADS + tid;
-            f32x16 sum;
-            for (int jj = 0; jj < nseg; ++jj) {
-                const unsigned long long *src = g.partial + slot(p_lo + jj) + off;
-                unsigned long long w[16];
+        for (int nb = 0; nb < T::NB; ++nb)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) w[v] = load_tagged_word(src + (size_t)v * T::THREADS);
+            for (int v0 = 0; v0 < 16; v0 += H) {
+                float sum[H];
+                for (int jj = 0; jj < nseg; ++jj) {
+                    const uint32_t base = slot(p_lo + jj);
+                    unsigned long long w[H];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const float x = wait_tagged_word(src + (size_t)v * T::THREADS, w[v], g.epoch, budget);
-                    sum[v] = jj == 0 ? x : sum[v] + x;
+                    for (int v = 0; v < H; ++v) w[v] = buf_load_tagged(rp, lane_off, (base + word(mb, nb, v0 + v)) * 8u);
+#pragma unroll
+                    for (int v = 0; v < H; ++v) {
+                        // The word's address is formed only if it has not arrived yet.
+                        const float x = (unsigned)(w[v] >> 32) == g.epoch
+                                            ? __uint_as_float((unsigned)w[v])
+                                            : wait_tagged_word(g.partial + base + word(mb, nb, v0 + v) + tid, w[v],
+                                                               g.epoch, budget);
+                        sum[v] = jj == 0 ? x : sum[v] + x;
+                    }
                 }
-            }
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = row0 + wr * T::WM + mb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-                const int c = B_COL ? col0 + wc * T::WN + nb * 32 + l32 : col0 + wc * T::WN + T::NB * l32 + nb;
-                buf_store_x1(sum[v], rc, elem_off(r < g.m && c < g.n, r, g.ldc, c));
+                for (int v = 0; v < H; ++v) {
+                    const int e = v0 + v;
+                    const int r = row0 + wr * T::WM + mb * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+                    const int c = B_COL ? col0 + wc * T::WN + nb * 32 + l32 : col0 + wc * T::WN + T::NB * l32 + nb;
+                    buf_store_x1(sum[v], rc, elem_off(r < g.m && c < g.n, r, g.ldc, c));
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
 }
 
 // One whole tile per workgroup.  A_COL: column-major A; EPI: the
@@ -708,8 +724,11 @@ __global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_kernel(GemmArgs g)
 template <class T, bool B_COL>
 __global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_sk_kernel(GemmArgs g)
 {
-    __shared__ f32x4 lds[T::STAGES * (T::A_CHUNKS + T::B_CHUNKS)];
-    __shared__ int last_flag;
+    // The fix-up's flag lives in one extra chunk of the ring's array: with a
+    // second LDS variable the compiler can no longer tell the ring's copies
+    // from the fragment reads, and waits for every copy before each read.
+    __shared__ f32x4 lds[T::STAGES * (T::A_CHUNKS + T::B_CHUNKS) + 1];
+    int *const last_flag = reinterpret_cast<int *>(lds + T::STAGES * (T::A_CHUNKS + T::B_CHUNKS));
     f32x4 *const lds_a = lds;                                // [STAGES][A_CHUNKS]
     f32x4 *const lds_b = lds + T::STAGES * T::A_CHUNKS;      // [STAGES][B_CHUNKS]
 
@@ -772,7 +791,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_sk_kernel(GemmArgs g
         if (kt0 == 0 && kt1 == KT)
             dma_store_c<T, B_COL>(g, rc, row0, col0, wr, wc, l32, half, acc);
         else
-            dma_fixup<T, B_COL>(g, rc, sk, t, p, tid, row0, col0, wr, wc, l32, half, &last_flag, acc);
+            dma_fixup<T, B_COL>(g, rc, sk, t, p, tid, row0, col0, wr, wc, l32, half, last_flag, acc);
     }
 }
 
