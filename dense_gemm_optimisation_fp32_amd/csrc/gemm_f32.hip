@@ -188,16 +188,17 @@ struct Candidate {
     double full_tflops;
     double lone_share;
     double tail_extra;  // waves added to a last wave that follows full waves
-    bool tail_sk;       // a packed last wave may go to stream-K (measured for this tile)
+    double tail_sk;     // waves a stream-K last wave costs beyond its FLOPs (0: not used for this tile)
+    int tail_sk_min_k;  // ... from this k on
 };
 // tail_extra: 64x64 tails after full waves ran 0.03 to 0.09 of a wave over
 // the count (8 tiles: 0.17 against 0.14, 161: 0.23 against 0.14, 512: 0.32
 // against 0.25).
 constexpr int kCandidates = 4;
-constexpr Candidate kCandidate[kCandidates] = {{V_DMA_256x128x16_S3, 145.0, 0.92, 0.0, true},
-                                               {V_DMA_128x128x16_S3, 144.0, 0.86, 0.0, false},
-                                               {V_DMA_64x128x16_S2, 142.0, 0.92, 0.0, false},
-                                               {V_DMA_64x64x16_S2, 137.0, 0.92, 0.05, false}};
+constexpr Candidate kCandidate[kCandidates] = {{V_DMA_256x128x16_S3, 145.0, 0.92, 0.0, 0.25, 4096},
+                                               {V_DMA_128x128x16_S3, 144.0, 0.86, 0.0, 0.0, 0},
+                                               {V_DMA_64x128x16_S2, 142.0, 0.92, 0.0, 0.1, 2048},
+                                               {V_DMA_64x64x16_S2, 136.0, 0.92, 0.05, 0.0, 0}};
 
 struct DeviceFacts {
     int status = -1;  // -1: not queried yet, else a gemm_f32_status
@@ -206,6 +207,7 @@ struct DeviceFacts {
     int hip_error = 0;
     int per_cu[kCandidates] = {};       // resident workgroups per CU of each candidate's kernel
     int per_cu_wide[kCandidates] = {};  // the same for its wide-store kernel (0: none)
+    int per_cu_sk[kCandidates][2] = {}; // the same for its stream-K kernel, by B layout
 };
 
 constexpr int kMaxDevices = 64;
@@ -260,6 +262,16 @@ int device_facts(int *device_out, DeviceFacts *facts_out)
                     w = n;
                 }
                 f.per_cu_wide[i] = w;
+                for (int b = 0; b < 2; ++b) {
+                    int sk = 0;
+                    if (d.fn_sk[b] &&
+                        (hipOccupancyMaxActiveBlocksPerMultiprocessor(&sk, d.fn_sk[b], d.threads, 0) != hipSuccess ||
+                         sk < 1)) {
+                        (void)hipGetLastError();
+                        sk = n;
+                    }
+                    f.per_cu_sk[i][b] = sk;
+                }
             }
             f.status = GEMM_F32_SUCCESS;
         }
@@ -321,22 +333,22 @@ namespace {
 // wave; four 64x128 tiles: 0.28 of one).  With c = 8 (64x64) the workgroups
 // of a CU finish staggered and tails overlap the last full wave (8 tail
 // tiles cost 0.17 of a wave, 161 tiles 0.23).
-// When the packed tail of a 256x128 plan has at most one tile per CU and
-// k >= 4096, its tiles' k-slabs may instead be split evenly over one
-// workgroup per CU (at most 8 per tile) with stream-K (the full waves
-// unchanged), estimated at the whole plan's FLOPs at the full-wave rate plus
-// 0.25 of a wave for the partial sums and the imbalance (measured 0.12 to
-// 0.24): 4096x5120x4096 103.5 -> 132.3 TFLOPS, 4096x6144x4096 110.2 ->
-// 132.6, 2304x9216x4096 101.9 -> 128.6 against data-parallel 256x128.
-// The smaller tiles usually beat both; the split wins only where a few
-// tail tiles follow many full waves of 256x128.
-// (128x128 tiles gained too, but their stream-K kernel fits two workgroups
-// per CU against three, and with one tile per split it lost:
-// 2048x14336x4096 126.1 -> 116.8.)  On 39 measured shapes (one MI355X, 24
-// of them random in [512, 8192]^2 x {1024, 2048, 3000, 4096}) the choice
-// came within 2 % of the fastest candidate.
-double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n, int64_t k, int cus, bool tail_ok,
-                        int64_t *tail_tiles)
+// Stream-K tail: the whole plan runs in the stream-K kernel, whose
+// occupancy c' may differ; when its last wave has at most one tile per CU,
+// those tiles' k-slabs may be split evenly over one workgroup per CU (at
+// most 8 per tile) while the others run whole.  Estimated at the plan's
+// FLOPs at the full-wave rate plus tail_sk of a wave (c' x CUs tiles) for
+// the partial sums and the imbalance.  256x128 from k = 4096 (0.25; measured
+// 0.12 to 0.24): 4096x5120x4096 103.5 -> 132.3 TFLOPS, 4096x6144x4096
+// 110.2 -> 132.6, 2304x9216x4096 101.9 -> 128.6 against data-parallel
+// 256x128.  64x128 from k = 2048 (0.1; measured 0.04 at k = 4096, 0.11 at
+// 2049): 4608x4608x4096 131.3 -> 139.0, 5003x4097x2049 123.6 -> 128.4.
+// (128x128 lost with one tile per split: 2048x14336x4096 126.1 -> 116.8;
+// 64x64 tails, which overlap the last full wave, did not gain.)  On 39
+// measured shapes (one MI355X, 24 of them random in [512, 8192]^2 x {1024,
+// 2048, 3000, 4096}) the choice came within 2 % of the fastest candidate.
+double estimate_seconds(const Candidate &cand, int per_cu, int per_cu_sk, int64_t m, int64_t n, int64_t k, int cus,
+                        bool tail_ok, int64_t *tail_tiles)
 {
     const VariantDesc &d = variant(cand.variant);
     const int64_t tiles = ceil_div(m, d.bm) * ceil_div(n, d.bn);
@@ -353,11 +365,16 @@ double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n,
         if (full >= 1) last += cand.tail_extra;
     }
     const double dp = ((double)full + last) * wave;
-    if (tail_ok && cand.tail_sk && full >= 1 && rem > 0 && rem <= cus && k >= 4096) {
-        const double hybrid = ((double)tiles / slots + 0.25) * wave;
-        if (hybrid < dp) {
-            *tail_tiles = rem;
-            return hybrid;
+    if (tail_ok && cand.tail_sk > 0.0 && k >= cand.tail_sk_min_k && per_cu_sk > 0) {
+        const int64_t s_slots = (int64_t)per_cu_sk * cus;
+        const int64_t s_full = tiles / s_slots, s_rem = tiles % s_slots;
+        if (s_full >= 1 && s_rem > 0 && s_rem <= cus) {
+            const double s_wave = (double)s_slots * 2.0 * d.bm * d.bn * (double)k / (cand.full_tflops * 1e12);
+            const double hybrid = ((double)tiles / s_slots + cand.tail_sk) * s_wave;
+            if (hybrid < dp) {
+                *tail_tiles = s_rem;
+                return hybrid;
+            }
         }
     }
     return dp;
@@ -367,11 +384,10 @@ double estimate_seconds(const Candidate &cand, int per_cu, int64_t m, int64_t n,
 // 64 x 64 tiles leave fewer than two workgroups per CU and k >= 2048,
 // 64 x 64 tiles with stream-K over all tiles (workgroups share the tiles'
 // k-slabs) fill the GPU.  Measured (TFLOPS; data-parallel 64x64 / stream-K
-// over 128x128 tiles / stream-K over 64x64 tiles): 1024x1024x8192 ~64 /
-// 94.4 / 105.1; 1024x1024x4096 ~63 / 74.8 / 95.6; 1024x1024x2048 62.5 / 47 /
-// 81.1; 512x512x8192 16.3 / 32.8 / 60.9; 768x768x8192 - / 53.5 / 83.4;
-// 256x256x4096 6.0 / 7.0 / 17.1.  At 2048x1024x4096 (512 tiles, two per CU)
-// stream-K measured 108.0 against 105.5, inside the noise of the choice.
+// over 64x64 tiles): 1024x1024x8192 ~64 / 118.2; 1024x1024x4096 ~63 /
+// 110.0; 1024x1024x2048 62.5 / 94.2; 512x512x8192 16.3 / 76.3; 256x256x4096
+// 6.0 / 20.2.  At 2048x1024x4096 (512 tiles, two per CU) stream-K measured
+// 108.0 against 105.5, inside the noise of the choice.
 // Otherwise the direct-to-LDS tile whose estimated time is least, and with
 // it *tail_tiles > 0 when its partial last wave goes to stream-K.  tail_ok:
 // the plan can run the stream-K kernel (row-major A, no epilogue); when it
@@ -397,7 +413,8 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
         const int lane_cols = d.bn / d.waves_n / 32;
         const bool wide = layout_b == GEMM_F32_ROW_MAJOR && f.per_cu_wide[i] > 0 && n % lane_cols == 0;
         const int per_cu = wide ? f.per_cu_wide[i] : f.per_cu[i];
-        const double t = estimate_seconds(kCandidate[i], per_cu, m, n, k, f.cu_count, tail_ok, &tail);
+        const double t = estimate_seconds(kCandidate[i], per_cu, f.per_cu_sk[i][layout_b], m, n, k, f.cu_count,
+                                          tail_ok, &tail);
         if (log)
             std::fprintf(stderr, "[gemm_f32] candidate %s: %d per CU, estimate %.1f us%s\n", d.name, per_cu, t * 1e6,
                          tail ? " (stream-K tail)" : "");
@@ -519,9 +536,9 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     }
 
     if (d.fn_sk[0]) {
-        // Stream-K, chosen by the shape dispatch: either as many workgroups
-        // as are resident at once share the k-slabs of all tiles evenly, or
-        // one workgroup per CU shares those of the partial last wave's tiles
+        // Stream-K, chosen by the shape dispatch: either up to three
+        // workgroups per CU share the k-slabs of all tiles evenly, or one
+        // workgroup per CU shares those of the partial last wave's tiles
         // (the rest run whole).  GEMM_F32_SK_WGS forces it with that many
         // workgroups, over the first GEMM_F32_SK_TILES tiles (default all;
         // the other tiles get a workgroup each); GEMM_F32_STREAMK=0 disables
@@ -542,13 +559,16 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
                 delete p;
                 return hip_fail(e);
             }
-            // As many workgroups as fit at once, but at most 8 segments per
-            // tile (the last one to arrive reads all the others: with 64x64
-            // tiles at 512x512x8192, 8 per tile ran 60.9 TFLOPS, 16 55.4,
-            // 32 40.7) unless that leaves CUs idle (256x256x4096: 16 per
-            // tile 17.1, 32 10.3), and at least 8 slabs per workgroup.
-            const int64_t segs = std::max<int64_t>(8, ceil_div(facts.cu_count, tiles));
-            wgs = std::min<int64_t>(std::min<int64_t>((int64_t)per_cu * facts.cu_count, segs * tiles),
+            // Three workgroups per CU (fewer if fewer fit), at most 8
+            // segments per tile (the last one to arrive reads all the
+            // others) and at least 8 slabs per workgroup.  Measured with
+            // 64x64 tiles, TFLOPS at P = 512 / 768 / 1024 / 1280:
+            // 1024x1024x8192 104.1 / 118.2 / 117.1 / 109.6, 1024x1024x2048
+            // 88.8 / 94.2 / 88.6 / 83.1, 768x768x8192 91.5 / 101.5 / 100.5 /
+            // 89.3; 512x512x8192 at P = 256 / 384 / 512 (8 per tile) 52.7 /
+            // 68.3 / 76.3; 256x256x4096 at 64 / 128 (8 per tile) / 256 17.8
+            // / 20.2 / 15.7.
+            wgs = std::min<int64_t>(std::min<int64_t>((int64_t)std::min(3, per_cu) * facts.cu_count, 8 * tiles),
                                     tiles * a.k_tiles / 8);
             if (wgs < 2) wgs = 0;
         }

@@ -602,8 +602,7 @@ struct StreamK {
 // consecutive words; the words go through a buffer descriptor with the
 // device-scope cache policy, with the lane's offset in one register and the
 // slot and block in the scalar offset, and are read back eight per lane at
-// a time: the fix-up then needs no more registers than the main loop, and
-// the kernel keeps the occupancy of the whole-tile kernel.
+// a time, so the fix-up needs few registers beyond the main loop's.
 template <class T, bool B_COL>
 __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsrc_t rc, const StreamK &sk, int t,
                                           int p, int tid, int row0, int col0, int wr, int wc, int l32, int half,
@@ -721,8 +720,21 @@ __global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_kernel(GemmArgs g)
 // tiles come first, so their fix-ups overlap the whole-tile work that
 // follows.  Range p covers the tail of its first tile, whole tiles, and the
 // head of its last tile; the two partial segments run first.
+// Wavefronts per SIMD the stream-K kernel is register-budgeted for: as many
+// workgroups per CU as the whole-tile kernel of the tile holds (its LDS ring
+// and registers allow 8 of 64x64, 5 of 64x128 and 128x64, 3 of 128x128),
+// since a plan that shares only some tiles runs all of them in this kernel.
+// The larger tiles are held to their count by LDS alone.
+template <class T>
+constexpr int sk_waves_per_simd()
+{
+    constexpr int lds_cap = 163840 / (T::LDS_BYTES + 16);
+    constexpr int reg_cap = T::BM * T::BN <= 4096 ? 8 : T::BM * T::BN <= 8192 ? 5 : T::BM * T::BN <= 16384 ? 3 : 1;
+    return lds_cap < reg_cap ? lds_cap : reg_cap;
+}
+
 template <class T, bool B_COL>
-__global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_sk_kernel(GemmArgs g)
+__global__ __launch_bounds__(T::THREADS, sk_waves_per_simd<T>()) void gemm_mfma_dma_sk_kernel(GemmArgs g)
 {
     // The fix-up's flag lives in one extra chunk of the ring's array: with a
     // second LDS variable the compiler can no longer tell the ring's copies
@@ -783,15 +795,22 @@ __global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_sk_kernel(GemmArgs g
         int tm, tn;
         grouped_tile(t, g, tm, tn);
         const int row0 = tm * T::BM, col0 = tn * T::BN;
+        // The lane's position, opaque to the compiler once per work item:
+        // otherwise every per-lane offset of the copies, fragment reads,
+        // stores and fix-up is hoisted out of this loop and held in
+        // registers across all of it.
+        int tid_i = tid;
+        asm volatile("" : "+v"(tid_i));
+        const int l32_i = tid_i & 31, half_i = (tid_i >> 5) & 1;
 #pragma unroll
         for (int mb = 0; mb < T::MB; ++mb)
 #pragma unroll
             for (int nb = 0; nb < T::NB; ++nb) acc[mb][nb] = f32x16{};
-        dma_range<T, B_COL>(g, lds_a, lds_b, ra, rb, row0, col0, kt0, kt1, tid, wave, wr, wc, l32, half, acc);
+        dma_range<T, B_COL>(g, lds_a, lds_b, ra, rb, row0, col0, kt0, kt1, tid_i, wave, wr, wc, l32_i, half_i, acc);
         if (kt0 == 0 && kt1 == KT)
-            dma_store_c<T, B_COL>(g, rc, row0, col0, wr, wc, l32, half, acc);
+            dma_store_c<T, B_COL>(g, rc, row0, col0, wr, wc, l32_i, half_i, acc);
         else
-            dma_fixup<T, B_COL>(g, rc, sk, t, p, tid, row0, col0, wr, wc, l32, half, last_flag, acc);
+            dma_fixup<T, B_COL>(g, rc, sk, t, p, tid_i, row0, col0, wr, wc, l32_i, half_i, last_flag, acc);
     }
 }
 

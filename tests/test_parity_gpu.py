@@ -255,7 +255,7 @@ def test_stream_k_chosen_for_few_tiles_long_k(layout_b):
 
 
 # The shape dispatch's choice on the shapes it was measured on (one MI355X,
-# 256 CUs): the fastest of the three candidate tiles on each.  Plans only,
+# 256 CUs): the fastest of the candidate plans on each.  Plans only,
 # nothing is launched.
 # (shape, tile, tiles of the partial last wave split by stream-K over one
 # workgroup per CU, or 0 for a data-parallel plan)
@@ -266,14 +266,16 @@ DISPATCH_CASES = [
     ((3000, 3000, 3000), "dma_64x64x16_w2x2_s2", 0),
     ((2048, 2048, 2048), "dma_64x128x16_w2x2_s2", 0),
     ((1536, 4096, 4096), "dma_64x128x16_w2x2_s2", 0),
-    ((5003, 4097, 2049), "dma_64x128x16_w2x2_s2", 0),
+    ((5003, 4097, 2049), "dma_64x128x16_w2x2_s2", 47),
     ((4096, 4608, 4096), "dma_64x64x16_w2x2_s2", 0),
     ((4096, 6144, 4096), "dma_128x128x16_w2x2_s3", 0),
     ((2048, 14336, 4096), "dma_64x128x16_w2x2_s2", 0),
-    ((2304, 9216, 4096), "dma_64x128x16_w2x2_s2", 0),
-    ((1536, 13824, 4096), "dma_64x128x16_w2x2_s2", 0),
+    ((2304, 9216, 4096), "dma_64x128x16_w2x2_s2", 32),
+    ((1536, 13824, 4096), "dma_64x128x16_w2x2_s2", 32),
     ((5120, 9856, 4096), "dma_64x128x16_w2x2_s2", 0),
     ((7424, 13568, 4096), "dma_256x128x16_w2x2_s3", 2),
+    ((4608, 4608, 4096), "dma_64x128x16_w2x2_s2", 32),
+    ((7964, 4668, 2048), "dma_64x128x16_w2x2_s2", 0),
 ]
 
 
@@ -327,6 +329,32 @@ def test_stream_k_tail_chosen(layout_b):
     c, s_ = oracle.gemm_f64_sampled(A, B, m, n, k, layout_b, rows, cols)
     check_close(C[rows, cols], c, s_, "stream-K tail")
     A, B = random_operands(m, n, k, layout_b, "int8range", seed=100)
+    C, _ = run_gemm(A, B, m, n, k, layout_b)
+    c, _ = oracle.gemm_f64_sampled(A, B, m, n, k, layout_b, rows, cols)
+    assert np.array_equal(C[rows, cols].astype(np.float64), c)
+
+
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+def test_stream_k_tail_64x128_ragged(layout_b):
+    """The ragged shape (boundary tiles on both edges, k = 16 * 128 + 1) runs
+    64x128 tiles with its last wave's 47 tiles split over one workgroup per
+    CU; it matches the oracle (integer inputs bit for bit) and repeats bit
+    for bit."""
+    import dense_gemm_optimisation_fp32_amd as g
+
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the choice was measured on a 256-CU MI355X")
+    m, n, k = 5003, 4097, 2049    # 79 x 33 = 2607 tiles: 2 x 1280 + 47
+    print(f"\n[case] 64x128 stream-K tail layout_b={layout_b} shape={(m, n, k)}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "uniform", seed=101)
+    C, info, outs = run_gemm(A, B, m, n, k, layout_b, repeat=2)
+    assert info["name"] == "dma_64x128x16_w2x2_s2"
+    assert info["stream_k"] == 256 and info["stream_k_tiles"] == 47
+    assert np.array_equal(outs[0], outs[1])
+    rows, cols = sample_indices(m, n, 2000, seed=102)
+    c, s_ = oracle.gemm_f64_sampled(A, B, m, n, k, layout_b, rows, cols)
+    check_close(C[rows, cols], c, s_, "64x128 stream-K tail")
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=103)
     C, _ = run_gemm(A, B, m, n, k, layout_b)
     c, _ = oracle.gemm_f64_sampled(A, B, m, n, k, layout_b, rows, cols)
     assert np.array_equal(C[rows, cols].astype(np.float64), c)
