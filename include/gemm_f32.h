@@ -20,8 +20,8 @@
  * bitwise identical results run after run (no floating-point atomics).
  *
  * Conventions for every entry point:
- *  - Return value: a gemm_f32_status code.  Nothing here throws, prints or
- *    aborts.
+ *  - Return value: a gemm_f32_status code.  Nothing here throws, prints
+ *    (unless GEMM_F32_LOG is set, see gemm_f32_create) or aborts.
  *  - Pointers A, B, C are device pointers (HIP device memory of the current
  *    device), owned by the caller.  C must not overlap A or B.
  *  - Sizes and leading dimensions are in elements (floats).
@@ -123,7 +123,19 @@ int gemm_f32_validate(int64_t m, int64_t n, int64_t k, int layout_b,
  *         GEMM_F32_ERR_NO_DEVICE, GEMM_F32_ERR_UNSUPPORTED_DEVICE,
  *         GEMM_F32_ERR_HIP (including a failed workspace allocation),
  *         GEMM_F32_ERR_ALLOC.
- * The environment variable GEMM_F32_VARIANT=<index> forces a variant.
+ * Environment overrides, read when a plan is created (for measurement and
+ * tuning; unset means the shape dispatch decides):
+ *   GEMM_F32_VARIANT=<index>  force a kernel variant;
+ *   GEMM_F32_GROUP_M=<rows>   tile-rows per rasterisation group (default 8);
+ *   GEMM_F32_SPLIT_K=<count>  k splits of a few-row plan;
+ *   GEMM_F32_SK_WGS=<P>       stream-K with P workgroups over the first
+ *                             GEMM_F32_SK_TILES=<R> tiles (default all);
+ *                             a partial-sum area of 2^31 bytes or more is
+ *                             rejected with GEMM_F32_ERR_INVALID_VALUE;
+ *   GEMM_F32_STREAMK=0        never choose stream-K automatically;
+ *   GEMM_F32_LOG=1 (or 2)     print the plan (and the dispatch's estimates)
+ *                             to stderr, the one exception to "nothing
+ *                             prints".
  */
 int gemm_f32_create(gemm_f32_plan *out, int64_t m, int64_t n, int64_t k, int layout_b,
                     int64_t lda, int64_t ldb, int64_t ldc);
