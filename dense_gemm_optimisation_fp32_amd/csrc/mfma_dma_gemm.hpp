@@ -144,7 +144,9 @@ __device__ __forceinline__ DmaBases<T, B_COL, A_COL> dma_bases(const GemmArgs &g
     return b;
 }
 
-template <class T, bool B_COL, bool A_COL = false>
+// KCHECK: drop the k-rows at or past K (needed only for the last slab when
+// K is not a multiple of BK; every other slab's k-rows are all below K).
+template <class T, bool B_COL, bool A_COL = false, bool KCHECK = true>
 __device__ __forceinline__ void dma_issue(int j, const GemmArgs &g, const DmaBases<T, B_COL, A_COL> &bases,
                                           __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int kt, int tid,
                                           int wave, f32x4 *As, f32x4 *Bs)
@@ -156,7 +158,7 @@ __device__ __forceinline__ void dma_issue(int j, const GemmArgs &g, const DmaBas
     uint32_t off;
     if (krows) {
         const int ld = d.is_a ? g.lda : g.ldb;
-        off = d.row < g.k - k0 ? bases.off[j] + (uint32_t)(k0 * ld) * 4u : kOobOffset;
+        off = (!KCHECK || d.row < g.k - k0) ? bases.off[j] + (uint32_t)(k0 * ld) * 4u : kOobOffset;
     } else {
         off = bases.off[j] + (uint32_t)k0 * 4u;
     }
@@ -326,7 +328,7 @@ __device__ __forceinline__ void dma_prefetch(int p_next, const f32x4 *As, const 
 // end (-1: slab kt is the last one).  fix: zero the k tail of slab kt+1 after
 // it lands (uniform flag).  The barrier precedes the last D k-steps (D = the
 // prefetch distance), whose MFMAs cover the first LDS reads of slab kt+1.
-template <class T, bool B_COL, int WAIT, bool A_COL = false>
+template <class T, bool B_COL, int WAIT, bool A_COL = false, bool KCHECK = true>
 __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 *lds_b, __amdgpu_buffer_rsrc_t ra,
                                          __amdgpu_buffer_rsrc_t rb, const DmaBases<T, B_COL, A_COL> &bases,
                                          int kt, bool copy, bool fix,
@@ -355,8 +357,8 @@ __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 
             dma_mfma_one<T, B_COL, A_COL>(i, p, f, acc);
             const int t = p * NM + i;
             if ((t + 1) % GAP == 0 && (t + 1) / GAP - 1 < T::PIECES && copy)
-                dma_issue<T, B_COL, A_COL>((t + 1) / GAP - 1, g, bases, ra, rb, kt + T::STAGES - 1, tid, wave,
-                                    lds_a + cpy * T::A_CHUNKS, lds_b + cpy * T::B_CHUNKS);
+                dma_issue<T, B_COL, A_COL, KCHECK>((t + 1) / GAP - 1, g, bases, ra, rb, kt + T::STAGES - 1, tid,
+                                                   wave, lds_a + cpy * T::A_CHUNKS, lds_b + cpy * T::B_CHUNKS);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -422,9 +424,15 @@ __device__ __forceinline__ void dma_range(const GemmArgs &g, f32x4 *lds_a, f32x4
 
     // Steady state: slab kt+1 is not the last one and slab kt+STAGES-1
     // exists, so STAGES-2 slabs' copies may stay in flight while waiting for
-    // slab kt+1.  Then the drain: copies only while slabs remain, every wait
-    // complete, the k tail fixed when slab kt+1 is the tile's last.
+    // slab kt+1; first while the slab being copied lies wholly below K (no
+    // k check on the copies), then for the copy of a partial last slab.
+    // Then the drain: copies only while slabs remain, every wait complete,
+    // the k tail fixed when slab kt+1 is the tile's last.
     int kt = kt0;
+    const int unchecked_end = ktail ? KT - 1 : KT;   // slabs below this copy without a k check
+    for (; kt + T::STAGES - 1 < kt1 && kt + 2 < kt1 && kt + T::STAGES - 1 < unchecked_end; ++kt)
+        dma_slab<T, B_COL, (T::STAGES - 2) * T::PIECES, A_COL, false>(g, lds_a, lds_b, ra, rb, bases, kt, true,
+                                                                      false, tid, wave, wr, wc, l32, half, f, acc);
     for (; kt + T::STAGES - 1 < kt1 && kt + 2 < kt1; ++kt)
         dma_slab<T, B_COL, (T::STAGES - 2) * T::PIECES, A_COL>(g, lds_a, lds_b, ra, rb, bases, kt, true, false, tid,
                                                          wave, wr, wc, l32, half, f, acc);
