@@ -214,6 +214,27 @@ def test_stream_k_forced(variant, layout_b, wgs, monkeypatch):
         assert np.array_equal(C.astype(np.float64), Cref)
 
 
+def test_stream_k_partial_area_limit(monkeypatch):
+    """A forced stream-K plan whose partial-sum words would reach 2^31 bytes
+    (they are addressed through a 32-bit buffer extent) is rejected at
+    creation, before anything is allocated or launched."""
+    import dense_gemm_optimisation_fp32_amd as g
+
+    v = [x for x in dma_variants() if g.gemm_f32_variant_info(x)["name"] == "dma_256x128x16_w2x2_s3"][0]
+    m = n = k = 4096            # 512 tiles of 256x128, 256 slabs each
+    # 2 * P * 256 * 128 * 8 bytes >= 2^31 once P >= 4096
+    monkeypatch.setenv("GEMM_F32_SK_WGS", "4096")
+    with pytest.raises(g.GemmF32Error) as err:
+        g.gemm_f32_create_variant(v, m, n, k, ROW_MAJOR, k, n, n)
+    assert err.value.status == g.GEMM_F32_ERR_INVALID_VALUE
+    monkeypatch.setenv("GEMM_F32_SK_WGS", "4095")   # just below: a valid plan
+    plan = g.gemm_f32_create_variant(v, m, n, k, ROW_MAJOR, k, n, n)
+    try:
+        assert g.gemm_f32_describe(plan)["stream_k"] == 4095
+    finally:
+        g.gemm_f32_destroy(plan)
+
+
 @pytest.mark.parametrize("variant", dma_variants())
 @pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
 @pytest.mark.parametrize("wgs,shared", [(4, 2), (9, 3), (5, 5), (7, 1)])
