@@ -178,16 +178,22 @@ const VariantDesc &variant(int v)
 
 // The tiled variants the shape dispatch weighs against each other, with the
 // throughput each sustains while every slot of a wave is busy (TFLOPS on one
-// MI355X: 256x128 on 4096^3 and the FFN shape, 128x128 on 6144^3 (three
-// whole waves), 64x128 and 64x64 (two LDS stages, four and eight workgroups
-// per CU) on 4096^3 (two whole waves)), and the share of a CU's throughput
+// MI355X: 256x128 on 4096^3 (147.2-147.9) and the FFN shape (148.8),
+// 128x128 on 6144^3 (three whole waves, 148.0-148.6; FFN 149.1-149.4), 64x128
+// and 64x64 (two LDS stages, four and eight workgroups per CU) on 4096^3
+// (two whole waves: 141.8, 138.1-138.4)), and the share of a CU's throughput
 // that a lone workgroup gets (one wavefront per SIMD: 256x128 from 2048^3,
-// 128 tiles; 128x128 from 2048^3, 256 tiles; the others taken as 256x128's).
+// 128 tiles; 128x128 from 2048^3, 256 tiles; the others taken as 0.92).
+// 128x128 is rated a point below its measurements and 64x64 two points
+// below (on large operands 64x64 ran 120.6-127.3 where 64x128 ran
+// 125.3-132.4: 7592x7093x6144, 6569x5664x6144, 3645x5638x6144), which ranks
+// them right on the validation shapes.
 struct Candidate {
     int variant;
     double full_tflops;
     double lone_share;
     double tail_extra;  // waves added to a last wave that follows full waves
+    bool packed_tail;   // a last wave after full waves comes back two workgroups per CU
     double tail_sk;     // waves a stream-K last wave costs beyond its FLOPs (0: not used for this tile)
     int tail_sk_min_k;  // ... from this k on
 };
@@ -195,10 +201,10 @@ struct Candidate {
 // the count (8 tiles: 0.17 against 0.14, 161: 0.23 against 0.14, 512: 0.32
 // against 0.25).
 constexpr int kCandidates = 4;
-constexpr Candidate kCandidate[kCandidates] = {{V_DMA_256x128x16_S3, 145.0, 0.92, 0.0, 0.25, 4096},
-                                               {V_DMA_128x128x16_S3, 144.0, 0.86, 0.0, 0.0, 0},
-                                               {V_DMA_64x128x16_S2, 142.0, 0.92, 0.0, 0.1, 2048},
-                                               {V_DMA_64x64x16_S2, 136.0, 0.92, 0.05, 0.0, 0}};
+constexpr Candidate kCandidate[kCandidates] = {{V_DMA_256x128x16_S3, 147.5, 0.94, 0.0, true, 0.25, 4096},
+                                               {V_DMA_128x128x16_S3, 147.0, 0.91, 0.0, false, 0.0, 0},
+                                               {V_DMA_64x128x16_S2, 142.0, 0.92, 0.0, true, 0.1, 2048},
+                                               {V_DMA_64x64x16_S2, 136.0, 0.92, 0.05, false, 0.0, 0}};
 
 struct DeviceFacts {
     int status = -1;  // -1: not queried yet, else a gemm_f32_status
@@ -323,12 +329,16 @@ namespace {
 // tiles' FLOPs at the variant's full-wave throughput.  The last, partial
 // wave of r tiles: w = ceil(r / CUs) workgroups per CU take w/c of a wave,
 // and a lone workgroup (w = 1) gets only lone_share of its CU, its four
-// wavefronts having nothing to cover their waits.  After full waves, tiles
-// with c <= 4 come back packed: the workgroups of a CU finish together, and
-// the CUs that free up first take two each, so such a tail is charged at
-// least two per CU (measured at k = 4096: 64 to 256 tail tiles of 256x128
-// took 0.5 to 1.0 of a wave, mostly the whole; 64 and 256 of 128x128 two
-// thirds; 104 and 256 of 64x128 (c = 4) half).  A handful of tail tiles
+// wavefronts having nothing to cover their waits.  After full waves, the
+// tails of 256x128 (c = 2) and 64x128 (c = 4 or 5) come back packed: the
+// workgroups of a CU finish together, and the CUs that free up first take
+// two each, so such a tail is charged at least two per CU (measured at
+// k = 4096: 64 to 256 tail tiles of 256x128 took 0.5 to 1.0 of a wave,
+// mostly the whole; 104 and 256 of 64x128 half).  128x128 (c = 3) tails no
+// longer pack since its copies dropped the k check: 186 and 192 tail tiles
+// after two full waves cost 0.36-0.37 of a wave (5239x5308x4096 and
+// 4578x6085x4096, 140.4 and 140.5 TFLOPS, against two thirds of a wave
+// before, 120.6 and 119.8).  A handful of tail tiles
 // (at most one per eight CUs) run alone instead (one 256x128 tile: half a
 // wave; four 64x128 tiles: 0.28 of one).  With c = 8 (64x64) the workgroups
 // of a CU finish staggered and tails overlap the last full wave (8 tail
@@ -359,7 +369,7 @@ double estimate_seconds(const Candidate &cand, int per_cu, int per_cu_sk, int64_
     double last = 0.0;
     if (rem) {
         int64_t w = std::min<int64_t>(per_cu, ceil_div(rem, cus));
-        if (full >= 1 && per_cu <= 4 && rem > cus / 8) w = std::min<int64_t>(per_cu, std::max<int64_t>(w, 2));
+        if (full >= 1 && cand.packed_tail && rem > cus / 8) w = std::min<int64_t>(per_cu, std::max<int64_t>(w, 2));
         last = (double)w / per_cu;
         if (w == 1 && per_cu > 1) last /= cand.lone_share;
         if (full >= 1) last += cand.tail_extra;

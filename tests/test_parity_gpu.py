@@ -290,13 +290,15 @@ DISPATCH_CASES = [
     ((5003, 4097, 2049), "dma_64x128x16_w2x2_s2", 47),
     ((4096, 4608, 4096), "dma_64x64x16_w2x2_s2", 0),
     ((4096, 6144, 4096), "dma_128x128x16_w2x2_s3", 0),
-    ((2048, 14336, 4096), "dma_64x128x16_w2x2_s2", 0),
+    ((2048, 14336, 4096), "dma_128x128x16_w2x2_s3", 0),
     ((2304, 9216, 4096), "dma_64x128x16_w2x2_s2", 32),
     ((1536, 13824, 4096), "dma_64x128x16_w2x2_s2", 32),
     ((5120, 9856, 4096), "dma_64x128x16_w2x2_s2", 0),
     ((7424, 13568, 4096), "dma_256x128x16_w2x2_s3", 2),
     ((4608, 4608, 4096), "dma_64x128x16_w2x2_s2", 32),
     ((7964, 4668, 2048), "dma_64x128x16_w2x2_s2", 0),
+    ((5239, 5308, 4096), "dma_128x128x16_w2x2_s3", 0),
+    ((7511, 5443, 6144), "dma_128x128x16_w2x2_s3", 0),
 ]
 
 
