@@ -43,8 +43,8 @@ METRIC = "FP32 GEMM TFLOPS (2MNK/t) and % of MI355X FP32 matrix peak at 4096^3"
 TRAFFIC_SOURCES = ("device_common.hpp", "mfma_gemm.hpp", "mfma_dma_gemm.hpp")
 TRAFFIC_COUNTERS = {
     "sq4096": {"kernel": "dma_256x128x16_w2x2_s3",
-               "sources_sha1": "6863a491bc7781efab91af886d9bade4945cf3b1",
-               "fetch_kib": 204331.0, "write_kib": 65536.0,
+               "sources_sha1": "7a175e4f4f8081bdf618bcebfb160372b06d8132",
+               "fetch_kib": 213309.2, "write_kib": 65536.0,
                "fetch_factor": 2.000, "write_factor": 1.000},
 }
 

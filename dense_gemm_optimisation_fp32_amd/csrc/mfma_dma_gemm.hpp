@@ -306,8 +306,9 @@ __device__ __forceinline__ void dma_mfma_one(int i, int p, const DmaFrags<T, B_C
     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[mb][nb], 0, 0, 0);
 }
 
-// Reads for k-step p_next: issued at the top of k-step p_next - D, or after
-// the barrier for the first D k-steps of the next slab.
+// Reads for k-step p_next: issued in k-step p_next - D (at its top, or
+// after its first MFMA), or after the barrier for the first D k-steps of
+// the next slab.
 template <class T, bool B_COL, bool A_COL = false>
 __device__ __forceinline__ void dma_prefetch(int p_next, const f32x4 *As, const f32x4 *Bs, int wr, int wc, int l32,
                                              int half, DmaFrags<T, B_COL, A_COL> &f)
@@ -348,13 +349,26 @@ __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 
     // and the wait for the next slab and the barrier at the normal one, so a
     // wavefront that is ready to multiply goes ahead of one about to wait.
     if constexpr (T::PRIO) __builtin_amdgcn_s_setprio(1);
+    // With four or more MFMAs per k-step the reads for k-step p + D go out
+    // after the step's first MFMA: that MFMA then waits only for reads
+    // issued a whole k-step earlier (issued before it, the read for the
+    // next step is caught by the in-order LDS counter wait as well).  With
+    // one or two MFMAs per step the reads go first, so that both MFMAs
+    // cover them.
+    constexpr bool READ_AFTER_FIRST = NM >= 4;
 #pragma unroll
     for (int p = 0; p < T::KH - D; ++p) {
-        dma_prefetch<T, B_COL, A_COL>(p + D, As, Bs, wr, wc, l32, half, f);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!READ_AFTER_FIRST) {
+            dma_prefetch<T, B_COL, A_COL>(p + D, As, Bs, wr, wc, l32, half, f);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
             dma_mfma_one<T, B_COL, A_COL>(i, p, f, acc);
+            if (READ_AFTER_FIRST && i == 0) {
+                __builtin_amdgcn_sched_barrier(0);
+                dma_prefetch<T, B_COL, A_COL>(p + D, As, Bs, wr, wc, l32, half, f);
+            }
             const int t = p * NM + i;
             if ((t + 1) % GAP == 0 && (t + 1) / GAP - 1 < T::PIECES && copy)
                 dma_issue<T, B_COL, A_COL, KCHECK>((t + 1) / GAP - 1, g, bases, ra, rb, kt + T::STAGES - 1, tid,
@@ -370,11 +384,16 @@ __device__ __forceinline__ void dma_slab(const GemmArgs &g, f32x4 *lds_a, f32x4 
     // (WAIT < 0: no copies of this range remain; the barrier only orders the
     // LDS reads before the next range's copies.)
     ring_barrier<(WAIT < 0 ? 63 : WAIT)>();
+    // Fenced: left alone the scheduler moved most of these MFMAs ahead of
+    // the reads (one even above the barrier), and the next slab's first
+    // MFMA waited for LDS.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int d = 0; d < D; ++d) {
         if constexpr (WAIT >= 0)
             dma_prefetch<T, B_COL, A_COL>(d, lds_a + nxt * T::A_CHUNKS, lds_b + nxt * T::B_CHUNKS, wr, wc, l32, half,
                                           f);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < NM; ++i) dma_mfma_one<T, B_COL, A_COL>(i, T::KH - D + d, f, acc);
     }
