@@ -178,16 +178,17 @@ const VariantDesc &variant(int v)
 
 // The tiled variants the shape dispatch weighs against each other, with the
 // throughput each sustains while every slot of a wave is busy (TFLOPS on one
-// MI355X: 256x128 on 4096^3 (147.2-147.9) and the FFN shape (148.8),
-// 128x128 on 6144^3 (three whole waves, 148.0-148.6; FFN 149.1-149.4), 64x128
+// MI355X: 256x128 on 4096^3 (147.2-148.5) and the FFN shape (148.8-149.2),
+// 128x128 on 6144^3 (three whole waves, 147.8-148.6; FFN 149.1-149.4), 64x128
 // and 64x64 (two LDS stages, four and eight workgroups per CU) on 4096^3
-// (two whole waves: 141.8, 138.1-138.4)), and the share of a CU's throughput
+// (two whole waves: 145.2-145.5, 136.2-138.4)), and the share of a CU's throughput
 // that a lone workgroup gets (one wavefront per SIMD: 256x128 from 2048^3,
 // 128 tiles; 128x128 from 2048^3, 256 tiles; the others taken as 0.92).
-// 128x128 is rated a point below its measurements and 64x64 two points
-// below (on large operands 64x64 ran 120.6-127.3 where 64x128 ran
-// 125.3-132.4: 7592x7093x6144, 6569x5664x6144, 3645x5638x6144), which ranks
-// them right on the validation shapes.
+// 128x128 is rated a point below its measurements, 64x64 one or two below
+// (on large operands 64x64 ran 120.6-127.3 where 64x128 ran 125.3-132.4:
+// 7592x7093x6144, 6569x5664x6144, 3645x5638x6144) and 64x128 three below
+// (rated at 145 it took shapes from 128x128 that 128x128 runs 4 % faster),
+// which ranks them right on the validation shapes.
 struct Candidate {
     int variant;
     double full_tflops;
