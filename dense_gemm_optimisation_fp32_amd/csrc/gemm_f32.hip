@@ -335,11 +335,12 @@ namespace {
 // workgroups of a CU finish together, and the CUs that free up first take
 // two each, so such a tail is charged at least two per CU (measured at
 // k = 4096: 64 to 256 tail tiles of 256x128 took 0.5 to 1.0 of a wave,
-// mostly the whole; 104 and 256 of 64x128 half).  128x128 (c = 3) tails no
-// longer pack since its copies dropped the k check: 186 and 192 tail tiles
-// after two full waves cost 0.36-0.37 of a wave (5239x5308x4096 and
-// 4578x6085x4096, 140.4 and 140.5 TFLOPS, against two thirds of a wave
-// before, 120.6 and 119.8).  A handful of tail tiles
+// mostly the whole; 104 and 256 of 64x128 half).  128x128 (c = 3), whose
+// slabs run at normal wavefront priority, no longer packs since its copies
+// dropped the k check: 186 and 192 tail tiles after two full waves cost
+// 0.36-0.37 of a wave (5239x5308x4096 and 4578x6085x4096, 140.4 and 140.5
+// TFLOPS, against two thirds of a wave before, 120.6 and 119.8); built with
+// the raised priority it packs again (4096^3: 145.0 -> 117.8).  A handful of tail tiles
 // (at most one per eight CUs) run alone instead (one 256x128 tile: half a
 // wave; four 64x128 tiles: 0.28 of one).  With c = 8 (64x64) the workgroups
 // of a CU finish staggered and tails overlap the last full wave (8 tail
@@ -355,9 +356,11 @@ namespace {
 // 256x128.  64x128 from k = 2048 (0.1; measured 0.04 at k = 4096, 0.11 at
 // 2049): 4608x4608x4096 131.3 -> 139.0, 5003x4097x2049 123.6 -> 128.4.
 // (128x128 lost with one tile per split: 2048x14336x4096 126.1 -> 116.8;
-// 64x64 tails, which overlap the last full wave, did not gain.)  On 39
-// measured shapes (one MI355X, 24 of them random in [512, 8192]^2 x {1024,
-// 2048, 3000, 4096}) the choice came within 2 % of the fastest candidate.
+// 64x64 tails, which overlap the last full wave, did not gain.)  On 29
+// validation shapes (one MI355X, 21 of them random in [512, 8192]^2 x {1024,
+// 2048, 3000, 4096}) every data-parallel choice came within 0.8 % of the
+// fastest candidate, and the stream-K tails chosen beat every
+// data-parallel plan by 3-7 %.
 double estimate_seconds(const Candidate &cand, int per_cu, int per_cu_sk, int64_t m, int64_t n, int64_t k, int cus,
                         bool tail_ok, int64_t *tail_tiles)
 {
