@@ -214,6 +214,30 @@ def test_stream_k_forced(variant, layout_b, wgs, monkeypatch):
         assert np.array_equal(C.astype(np.float64), Cref)
 
 
+@pytest.mark.parametrize("wgs", [256, 512])
+def test_stream_k_many_segments_per_tile(wgs, monkeypatch):
+    """16 tiles of 64x64 shared by 256 or 512 workgroups: each tile's k-slabs
+    are cut into 16 or 32 segments, so the last one to arrive adds that many
+    partial tiles (read back eight words per lane at a time).  Matches the
+    oracle, integer inputs bit for bit, and repeats bit for bit."""
+    import dense_gemm_optimisation_fp32_amd as g
+
+    v = [x for x in dma_variants() if g.gemm_f32_variant_info(x)["name"] == "dma_64x64x16_w2x2_s2"][0]
+    monkeypatch.setenv("GEMM_F32_SK_WGS", str(wgs))
+    m, n, k = 256, 256, 4096
+    print(f"\n[case] stream-K {wgs} workgroups over 16 tiles", flush=True)
+    A, B = random_operands(m, n, k, ROW_MAJOR, "normal1", seed=104)
+    C, info, outs = run_gemm(A, B, m, n, k, ROW_MAJOR, variant=v, repeat=3)
+    assert info["stream_k"] == wgs and info["stream_k_tiles"] == 16
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, ROW_MAJOR)
+    check_close(C, Cref, S, f"stream-K {wgs} over 16 tiles")
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+    A, B = random_operands(m, n, k, ROW_MAJOR, "int8range", seed=105)
+    C, _ = run_gemm(A, B, m, n, k, ROW_MAJOR, variant=v)
+    Cref, _ = oracle.gemm_f64(A, B, m, n, k, ROW_MAJOR)
+    assert np.array_equal(C.astype(np.float64), Cref)
+
+
 def test_stream_k_partial_area_limit(monkeypatch):
     """A forced stream-K plan whose partial-sum words would reach 2^31 bytes
     (they are addressed through a 32-bit buffer extent) is rejected at
