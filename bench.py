@@ -90,6 +90,61 @@ def parse():
     return p.parse_args()
 
 
+class ClockSampler:
+    """Samples the engine clock the driver reports (the current level of
+    pp_dpm_sclk in sysfs, in MHz) every few milliseconds from a thread, to
+    turn a fraction of the 2.4 GHz peak into one of the peak at the clock the
+    kernel actually ran at.  Only on a host with one GPU in sysfs, so that
+    the clock is the measured GPU's; otherwise no samples."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+
+        paths = glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")
+        self.path = paths[0] if len(paths) == 1 else None
+        self.period = period_s
+        self.samples = []
+        self._stop = None
+        self._thread = None
+
+    def _read(self):
+        import re
+
+        with open(self.path) as f:
+            for line in f:
+                if "*" in line:
+                    m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                    return int(m.group(1)) if m else None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+            except OSError:
+                return
+            if v:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+
+        if self.path:
+            self._stop = threading.Event()
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread:
+            self._stop.set()
+            self._thread.join()
+
+    def mean_mhz(self):
+        return sum(self.samples) / len(self.samples) if self.samples else None
+
+
 def time_workload(name, steps, warmup, variant=None, rotate=1, layout_a=0, epilogue="none"):
     import numpy as np
     import torch
@@ -144,11 +199,12 @@ def time_workload(name, steps, warmup, variant=None, rotate=1, layout_a=0, epilo
     # add its own overhead to microsecond kernels).
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(steps):
-        plan_run(*ptrs[i % rotate], sh)
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    with ClockSampler() as clock:
+        ev0.record(stream)
+        for i in range(steps):
+            plan_run(*ptrs[i % rotate], sh)
+        ev1.record(stream)
+        torch.cuda.synchronize()
     kernel_avg = ev0.elapsed_time(ev1) / 1e3 / steps
     assert all(torch.isfinite(c).all().item() for _, _, c in sets), "non-finite output"
 
@@ -160,6 +216,7 @@ def time_workload(name, steps, warmup, variant=None, rotate=1, layout_a=0, epilo
         "ms_per_step": wall / steps * 1e3,
         "tflops": flops * steps / wall / 1e12,
         "kernel_avg_s": kernel_avg,
+        "sclk_mhz": clock.mean_mhz(),
         "flops": flops,
         "bytes": pm.compulsory_bytes(w.m, w.n, w.k),
     }
@@ -207,6 +264,11 @@ def roofline(res):
         achieved = res["flops"] / res["kernel_avg_s"] / 1e12
         out = {"bound": "mfma" if kind != 1 else "alu", "achieved": round(achieved, 3),
                "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved / (peak / 1e12), 4)}
+        # The peaks assume the 2.4 GHz peak engine clock; the same fraction
+        # against the peak at the clock measured during the timed launches.
+        sclk = res.get("sclk_mhz")
+        out["sclk_mhz"] = round(sclk, 1) if sclk else None
+        out["frac_at_sclk"] = round(achieved / (peak / 1e12 * sclk * 1e6 / pm.MI355X_PEAK_SCLK_HZ), 4) if sclk else None
     else:
         achieved = res["bytes"] / res["kernel_avg_s"] / 1e9
         out = {"bound": "hbm", "achieved": round(achieved, 1), "peak": pm.MI355X_HBM_BANDWIDTH / 1e9,
