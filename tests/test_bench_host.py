@@ -1,0 +1,73 @@
+"""Host-side logic of bench.py (CPU): the engine-clock sampler, the roofline
+object and the counter-gating of the traffic figure."""
+import os
+import sys
+import time
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from workloads import WORKLOADS  # noqa: E402
+
+
+def test_clock_sampler_reads_the_current_level(tmp_path):
+    p = tmp_path / "pp_dpm_sclk"
+    p.write_text("0: 500Mhz\nS: 2387Mhz *\n1: 2400Mhz\n")
+    c = bench.ClockSampler(period_s=0.001)
+    c.path = str(p)
+    with c:
+        time.sleep(0.03)
+    assert c.samples and set(c.samples) == {2387}
+    assert c.mean_mhz() == 2387
+
+
+def test_clock_sampler_without_a_single_gpu_reports_nothing(monkeypatch):
+    import glob
+
+    monkeypatch.setattr(glob, "glob", lambda pattern: ["/a/pp_dpm_sclk", "/b/pp_dpm_sclk"])
+    c = bench.ClockSampler()
+    assert c.path is None
+    with c:
+        pass
+    assert c.mean_mhz() is None
+
+
+def _res(name, kernel_avg_s, sclk, kind=0, plan_name="dma_256x128x16_w2x2_s3"):
+    from dense_gemm_optimisation_fp32_amd import perfmodel as pm
+
+    w = WORKLOADS[name]
+    return {"workload": w, "plan": {"kind": kind, "name": plan_name}, "kernel_avg_s": kernel_avg_s,
+            "sclk_mhz": sclk, "flops": pm.gemm_flops(w.m, w.n, w.k),
+            "bytes": pm.compulsory_bytes(w.m, w.n, w.k)}
+
+
+def test_roofline_scales_the_peak_to_the_measured_clock():
+    flop = 2 * 4096 ** 3
+    t = flop / 150e12                      # 150 TFLOP/s
+    r = bench.roofline(_res("sq4096", t, 2000.0))
+    assert r["bound"] == "mfma" and r["achieved"] == pytest.approx(150.0, rel=1e-3)
+    assert r["frac"] == pytest.approx(150.0 / 157.3, abs=1e-4)
+    # at 2000 MHz the peak is 157.3 * 2000 / 2400
+    assert r["frac_at_sclk"] == pytest.approx(150.0 / (157.3 * 2000 / 2400), abs=1e-4)
+    r = bench.roofline(_res("sq4096", t, None))
+    assert r["sclk_mhz"] is None and r["frac_at_sclk"] is None
+
+
+def test_roofline_bandwidth_bound_and_traffic_gating():
+    w = WORKLOADS["skinny"]
+    nbytes = 4 * (w.m * w.k + w.k * w.n + w.m * w.n)
+    r = bench.roofline(_res("skinny", nbytes / 4e12, None, kind=2, plan_name="skinny_16x64_w16_d4"))
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert r["achieved"] == pytest.approx(4000.0, rel=1e-3)
+    assert r["traffic"] is None            # no counters taken for this kernel
+    # the headline counters apply only while the kernel sources are unchanged
+    rec = bench.TRAFFIC_COUNTERS["sq4096"]
+    got = bench.traffic_bytes("sq4096", rec["kernel"])
+    if rec["sources_sha1"] == bench.kernel_sources_sha1():
+        assert got and got > 0
+    else:
+        assert got is None
+    assert bench.traffic_bytes("sq4096", "some_other_kernel") is None
