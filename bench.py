@@ -79,7 +79,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the baseline")
     p.add_argument("--all", action="store_true", help="also time every workload")
-    p.add_argument("--all-out", default="gpurun_out/bench_all.jsonl")
+    p.add_argument("--all-out", default="bench_all.jsonl")
     p.add_argument("--rotate", type=int, default=1,
                    help="cycle through this many operand sets (defeats the Infinity Cache for small workloads)")
     p.add_argument("--layout-a", choices=["row", "col"], default="row")

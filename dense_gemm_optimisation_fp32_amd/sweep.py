@@ -119,7 +119,7 @@ def main(argv=None):
     ap.add_argument("--variants", default="all")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--out", default="gpurun_out/sweep.jsonl")
+    ap.add_argument("--out", default="sweep.jsonl")
     args = ap.parse_args(argv)
 
     import torch
