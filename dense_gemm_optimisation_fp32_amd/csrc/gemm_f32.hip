@@ -395,13 +395,20 @@ double estimate_seconds(const Candidate &cand, int per_cu, int per_cu_sk, int64_
 }
 
 // Shape dispatch.  Few rows: the bandwidth-bound split-k path.  When even
-// 64 x 64 tiles leave fewer than two workgroups per CU and k >= 2048,
+// 64 x 64 tiles leave fewer than 2.5 workgroups per CU and k >= 2048,
 // 64 x 64 tiles with stream-K over all tiles (workgroups share the tiles'
-// k-slabs) fill the GPU.  Measured (TFLOPS; data-parallel 64x64 / stream-K
-// over 64x64 tiles): 1024x1024x8192 ~64 / 118.2; 1024x1024x4096 ~63 /
-// 110.0; 1024x1024x2048 62.5 / 94.2; 512x512x8192 16.3 / 76.3; 256x256x4096
-// 6.0 / 20.2.  At 2048x1024x4096 (512 tiles, two per CU) stream-K measured
-// 108.0 against 105.5, inside the noise of the choice.
+// k-slabs) fill the GPU.  Measured (TFLOPS; the best data-parallel plan /
+// stream-K over 64x64 tiles): 1024x1024x8192 ~64 / 118.2; 1024x1024x4096
+// ~63 / 110.0; 1024x1024x2048 62.5 / 94.2; 512x512x8192 16.3 / 76.3;
+// 256x256x4096 6.0 / 20.2; and from two to 2.5 tiles per CU, where a
+// data-parallel plan leaves the CUs unevenly loaded: 2048x1024x4096 (512
+// tiles) 115.2 / 122.1, 1280x1792x4096 (560) 90.6 / 116.0, 1536x1536x4096
+// (576) 99.7 / 120.9, 756x3053x6144 (576) 97.7 / 119.6, 702x3590x4096 (627)
+// 99.4 / 106.8, 1536x1536x2048 97.7 / 109.6, 1536x1536x8192 100.7 / 126.4
+// (918x2413x3000 (570) 88.2 / 86.5 and 1864x1288x6144 (630) 99.6 / 98.4
+// lost 1-2 %).  Closer to three tiles per CU the data-parallel plans load the
+// CUs evenly enough and stream-K lost: 1250x2221x6144 (700) 114.2 / 97.4,
+// 2023x1453x2048 (736) 114.9 / 102.2, 2546x1202x3000 (760) 121.7 / 110.8.
 // Otherwise the direct-to-LDS tile whose estimated time is least, and with
 // it *tail_tiles > 0 when its partial last wave goes to stream-K.  tail_ok:
 // the plan can run the stream-K kernel (row-major A, no epilogue); when it
@@ -412,7 +419,7 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
     *stream_k = false;
     *tail_tiles = 0;
     if (m <= 32) return V_SKINNY_W16_D4;
-    if (tail_ok && ceil_div(m, 64) * ceil_div(n, 64) < 2 * (int64_t)f.cu_count && k >= 2048) {
+    if (tail_ok && 2 * ceil_div(m, 64) * ceil_div(n, 64) < 5 * (int64_t)f.cu_count && k >= 2048) {
         *stream_k = true;
         return V_DMA_64x64x16_S2;
     }

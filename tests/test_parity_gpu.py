@@ -284,7 +284,7 @@ def test_stream_k_chosen_for_few_tiles_long_k(layout_b):
     """Shapes with too few tiles for the GPU and a long k get a stream-K plan
     by default; it matches the oracle (integer inputs bit for bit)."""
     for (m, n, k) in [(256, 256, 4096), (1024, 1024, 8192), (512, 512, 8192), (1024, 1024, 2048),
-                      (768, 700, 8192)]:
+                      (768, 700, 8192), (1536, 1536, 4096)]:
         print(f"\n[case] default stream-K layout_b={layout_b} shape={(m, n, k)}", flush=True)
         A, B = random_operands(m, n, k, layout_b, "normal1", seed=95)
         C, info, outs = run_gemm(A, B, m, n, k, layout_b, repeat=2)
@@ -441,10 +441,11 @@ def test_c_store_width(variant_name, n, layout_b, width, monkeypatch):
 # sum of each element is the same sum over its row and column).
 NEAR_LIMIT = {
     # name: (m, n, k, layout_a, layout_b), the operand near the limit
-    "A": (32768, 64, 16383, ROW_MAJOR, ROW_MAJOR),
+    # (enough 64x64 tiles, three per CU, for a data-parallel plan)
+    "A": (32768, 192, 16383, ROW_MAJOR, ROW_MAJOR),
     "A_stream_k": (8192, 64, 65535, ROW_MAJOR, ROW_MAJOR),
     "A_col": (16383, 64, 32768, COL_MAJOR, ROW_MAJOR),
-    "B_col": (64, 32768, 16383, ROW_MAJOR, COL_MAJOR),
+    "B_col": (192, 32768, 16383, ROW_MAJOR, COL_MAJOR),
     "B_few_rows": (16, 32768, 16383, ROW_MAJOR, ROW_MAJOR),
     "C": (32768, 16383, 64, ROW_MAJOR, ROW_MAJOR),
 }
