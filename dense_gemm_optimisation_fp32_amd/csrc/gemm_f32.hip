@@ -197,15 +197,24 @@ struct Candidate {
     bool packed_tail;   // a last wave after full waves comes back two workgroups per CU
     double tail_sk;     // waves a stream-K last wave costs beyond its FLOPs (0: not used for this tile)
     int tail_sk_min_k;  // ... from this k on
+    bool col_b = true;  // weighed for column-major B too
 };
 // tail_extra: 64x64 tails after full waves ran 0.03 to 0.09 of a wave over
 // the count (8 tiles: 0.17 against 0.14, 161: 0.23 against 0.14, 512: 0.32
 // against 0.25).
-constexpr int kCandidates = 4;
+// 256x256 with four LDS stages holds one workgroup per CU (256 accumulators
+// per lane), so its waves quantise coarsely, but on whole waves it leads:
+// 4096^3 147.9-148.9 TFLOPS against 147.5-147.8 for 256x128, FFN
+// 149.0-149.5 against 147.9-148.3, 8192^3 149.7-150.2 against 147.6-147.9
+// (same box, three repeats).  With column-major B it trails (4096^3: 144.9
+// to 145.0 against 146.5), and it has no linear-layer kernels, so plans
+// with column-major B, the epilogue or column-major A skip it.
+constexpr int kCandidates = 5;
 constexpr Candidate kCandidate[kCandidates] = {{V_DMA_256x128x16_S3, 147.5, 0.94, 0.0, true, 0.25, 4096},
                                                {V_DMA_128x128x16_S3, 147.0, 0.91, 0.0, false, 0.0, 0},
                                                {V_DMA_64x128x16_S2, 142.0, 0.92, 0.0, true, 0.1, 2048},
-                                               {V_DMA_64x64x16_S2, 136.0, 0.92, 0.05, false, 0.0, 0}};
+                                               {V_DMA_64x64x16_S2, 136.0, 0.92, 0.05, false, 0.0, 0},
+                                               {V_DMA_256x256x16_S4, 148.8, 1.0, 0.0, false, 0.0, 0, false}};
 
 struct DeviceFacts {
     int status = -1;  // -1: not queried yet, else a gemm_f32_status
@@ -423,11 +432,14 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
         *stream_k = true;
         return V_DMA_64x64x16_S2;
     }
-    int best = 0;
+    int best = -1;
     double best_t = 0.0;
     const bool log = env_int("GEMM_F32_LOG", 0) >= 2;
     for (int i = 0; i < kCandidates; ++i) {
         int64_t tail = 0;
+        // (tail_ok is false exactly for the plans that need linear-layer kernels)
+        if (!tail_ok && !variant(kCandidate[i].variant).fn_ex[0][0][0]) continue;
+        if (layout_b == GEMM_F32_COL_MAJOR && !kCandidate[i].col_b) continue;
         // The plan runs the wide-store kernel when B is row-major and N a
         // multiple of the columns a lane holds; rate it at that occupancy.
         const VariantDesc &d = variant(kCandidate[i].variant);
@@ -439,13 +451,13 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
         if (log)
             std::fprintf(stderr, "[gemm_f32] candidate %s: %d per CU, estimate %.1f us%s\n", d.name, per_cu, t * 1e6,
                          tail ? " (stream-K tail)" : "");
-        if (i == 0 || t < best_t) {
+        if (best < 0 || t < best_t) {
             best = i;
             best_t = t;
             *tail_tiles = tail;
         }
     }
-    return kCandidate[best].variant;
+    return kCandidate[best].variant;   // 256x128, never skipped, is always weighed
 }
 
 int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int64_t k, int layout_a,
