@@ -153,7 +153,7 @@ const VariantDesc &variant(int v)
         mfma_variant<MfmaTile<128, 128, 32, 2, 2>>("mfma_128x128x32_w2x2_32x32x2"),
         dma_variant<DmaTile<256, 256, 16, 2, 2, 2>>("dma_256x256x16_w2x2_s2"),
         dma_variant<DmaTile<256, 256, 16, 2, 2, 3>>("dma_256x256x16_w2x2_s3"),
-        dma_variant<DmaTile<256, 256, 16, 2, 2, 4>>("dma_256x256x16_w2x2_s4"),
+        dma_ex_variant<DmaTile<256, 256, 16, 2, 2, 4>>("dma_256x256x16_w2x2_s4"),
         dma_variant<DmaTile<256, 256, 32, 2, 2, 2>>("dma_256x256x32_w2x2_s2"),
         dma_ex_variant<DmaTile<128, 128, 16, 2, 2, 3, false>>("dma_128x128x16_w2x2_s3"),
         dma_variant<DmaTile<128, 128, 32, 2, 2, 3, false>>("dma_128x128x32_w2x2_s3"),
@@ -198,6 +198,7 @@ struct Candidate {
     double tail_sk;     // waves a stream-K last wave costs beyond its FLOPs (0: not used for this tile)
     int tail_sk_min_k;  // ... from this k on
     bool col_b = true;  // weighed for column-major B too
+    bool epi = true;    // weighed for the linear-layer epilogue too
 };
 // tail_extra: 64x64 tails after full waves ran 0.03 to 0.09 of a wave over
 // the count (8 tiles: 0.17 against 0.14, 161: 0.23 against 0.14, 512: 0.32
@@ -206,15 +207,17 @@ struct Candidate {
 // per lane), so its waves quantise coarsely, but on whole waves it leads:
 // 4096^3 147.9-148.9 TFLOPS against 147.5-147.8 for 256x128, FFN
 // 149.0-149.5 against 147.9-148.3, 8192^3 149.7-150.2 against 147.6-147.9
-// (same box, three repeats).  With column-major B it trails (4096^3: 144.9
-// to 145.0 against 146.5), and it has no linear-layer kernels, so plans
-// with column-major B, the epilogue or column-major A skip it.
+// (same box, three repeats).  With column-major A it leads too (4096^3
+// 147.6-148.1 against 146.5-147.2, FFN 148.9-149.3 against 147.9-148.2);
+// with column-major B it trails (4096^3: 144.9-145.0 against 146.5), and
+// with the bias + GELU epilogue as well (FFN 146.5-146.7 against
+// 147.3-147.4), so plans with column-major B or the epilogue skip it.
 constexpr int kCandidates = 5;
 constexpr Candidate kCandidate[kCandidates] = {{V_DMA_256x128x16_S3, 147.5, 0.94, 0.0, true, 0.25, 4096},
                                                {V_DMA_128x128x16_S3, 147.0, 0.91, 0.0, false, 0.0, 0},
                                                {V_DMA_64x128x16_S2, 142.0, 0.92, 0.0, true, 0.1, 2048},
                                                {V_DMA_64x64x16_S2, 136.0, 0.92, 0.05, false, 0.0, 0},
-                                               {V_DMA_256x256x16_S4, 148.8, 1.0, 0.0, false, 0.0, 0, false}};
+                                               {V_DMA_256x256x16_S4, 148.8, 1.0, 0.0, false, 0.0, 0, false, false}};
 
 struct DeviceFacts {
     int status = -1;  // -1: not queried yet, else a gemm_f32_status
@@ -422,8 +425,9 @@ double estimate_seconds(const Candidate &cand, int per_cu, int per_cu_sk, int64_
 // it *tail_tiles > 0 when its partial last wave goes to stream-K.  tail_ok:
 // the plan can run the stream-K kernel (row-major A, no epilogue); when it
 // cannot, few-tile shapes take the best data-parallel tile instead.
-int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFacts &f, bool tail_ok, bool *stream_k,
-                   int64_t *tail_tiles)
+// epilogue: the plan fuses the linear-layer epilogue.
+int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFacts &f, bool tail_ok, bool epilogue,
+                   bool *stream_k, int64_t *tail_tiles)
 {
     *stream_k = false;
     *tail_tiles = 0;
@@ -440,6 +444,7 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
         // (tail_ok is false exactly for the plans that need linear-layer kernels)
         if (!tail_ok && !variant(kCandidate[i].variant).fn_ex[0][0][0]) continue;
         if (layout_b == GEMM_F32_COL_MAJOR && !kCandidate[i].col_b) continue;
+        if (epilogue && !kCandidate[i].epi) continue;
         // The plan runs the wide-store kernel when B is row-major and N a
         // multiple of the columns a lane holds; rate it at that occupancy.
         const VariantDesc &d = variant(kCandidate[i].variant);
@@ -468,8 +473,8 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     int st = gemm_f32_validate_ex(m, n, k, layout_a, layout_b, lda, ldb, ldc);
     if (st != GEMM_F32_SUCCESS) return st;
     if (forced_variant >= V_COUNT || (epilogue != 0 && epilogue != 1)) return GEMM_F32_ERR_INVALID_VALUE;
-    // Column-major A and the epilogue have kernels in the three default
-    // tiled variants only.
+    // Column-major A and the epilogue have kernels in the dispatch
+    // candidates (and the three-stage 64x64) only.
     const bool ex = layout_a == GEMM_F32_COL_MAJOR || epilogue;
 
     int dev = 0;
@@ -482,7 +487,7 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     int64_t auto_tail = 0;
     if (v < 0) {
         v = env_int("GEMM_F32_VARIANT", -1);
-        if (v < 0 || v >= V_COUNT) v = choose_variant(m, n, k, layout_b, facts, !ex, &auto_stream_k, &auto_tail);
+        if (v < 0 || v >= V_COUNT) v = choose_variant(m, n, k, layout_b, facts, !ex, epilogue != 0, &auto_stream_k, &auto_tail);
         if (ex && !variant(v).fn_ex[0][0][0]) v = V_DMA_64x64x16_S2;
     }
     const VariantDesc &d = variant(v);

@@ -22,8 +22,8 @@ from workloads import (COL_MAJOR, ROW_MAJOR, WORKLOADS, epilogue_operands, rando
 pytestmark = pytest.mark.gpu
 
 REL, ABS = 1.2e-5, 1.2e-6
-EX_VARIANTS = ["dma_256x128x16_w2x2_s3", "dma_128x128x16_w2x2_s3", "dma_64x128x16_w2x2_s2",
-               "dma_64x64x16_w2x2_s2", "dma_64x64x16_w2x2_s3"]
+EX_VARIANTS = ["dma_256x256x16_w2x2_s4", "dma_256x128x16_w2x2_s3", "dma_128x128x16_w2x2_s3",
+               "dma_64x128x16_w2x2_s2", "dma_64x64x16_w2x2_s2", "dma_64x64x16_w2x2_s3"]
 ACTS = [g.GEMM_F32_ACT_NONE, g.GEMM_F32_ACT_RELU, g.GEMM_F32_ACT_GELU]
 
 
@@ -192,3 +192,22 @@ def test_binding_linear_column_major_a_and_beta():
     M = g.matmul(At, Bt)
     ok, ratio = oracle.within_tolerance(M.cpu().numpy(), AB, S)
     assert ok, ratio
+
+
+def test_linear_dispatch_choice():
+    """Column-major A takes the 256x256 four-stage tile on whole-wave shapes,
+    where it measured fastest; the fused epilogue keeps 256x128, which led
+    there (both measured on a 256-CU MI355X)."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the choice was measured on a 256-CU MI355X")
+    m = n = k = 4096
+    info = g.Plan(m, n, k, ROW_MAJOR, m, n, n, layout_a=COL_MAJOR).info
+    assert info["name"] == "dma_256x256x16_w2x2_s4" and info["stream_k"] == 0
+    m, n, k = 8192, 14336, 4096
+    info = g.Plan(m, n, k, ROW_MAJOR, k, n, n, epilogue=1).info
+    assert info["name"] == "dma_256x128x16_w2x2_s3" and info["stream_k"] == 0
+    info = g.Plan(m, n, k, ROW_MAJOR, m, n, n, layout_a=COL_MAJOR).info
+    assert info["name"] == "dma_256x256x16_w2x2_s4"
+    # column-major B keeps 256x128 even with column-major A
+    info = g.Plan(4096, 4096, 4096, COL_MAJOR, 4096, 4096, 4096, layout_a=COL_MAJOR).info
+    assert info["name"] == "dma_256x128x16_w2x2_s3"
