@@ -174,8 +174,9 @@ int gemm_f32_run(gemm_f32_plan plan, const float *A, const float *B, float *C, v
  * aligned) or is NULL.  The product is summed as by gemm_f32_run; the
  * epilogue is evaluated in float32 (alpha*acc + beta*C + bias, multiply-adds
  * may be fused), then act; GELU's erf is the Abramowitz-Stegun 7.1.26
- * approximation (|error| <= 1.5e-7).  These plans run on the 256x128, 128x128 and 64x64 direct-to-LDS
- * kernels (the few-row path and stream-K are not used).
+ * approximation (|error| <= 1.5e-7).  These plans run on the direct-to-LDS tiled kernels
+ * (256x256 for column-major A without the epilogue, else 256x128, 128x128, 64x128 or 64x64);
+ * the few-row path and stream-K are not used.
  */
 
 /* gemm_f32_validate_ex: gemm_f32_validate with A's layout: lda >= k (row-major
