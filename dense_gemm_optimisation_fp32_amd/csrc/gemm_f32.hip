@@ -525,7 +525,10 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     a.tiles_m = (int)ceil_div(m, d.bm);
     a.tiles_n = (int)ceil_div(n, d.bn);
     a.k_tiles = (int)ceil_div(k, d.bk);
-    a.group_m = env_int("GEMM_F32_GROUP_M", 8);
+    // Tile-rows per rasterisation group.  256x256 (one tile per CU) ran
+    // best with 4: 4096^3 148.7 against 148.0-148.3 with 8, FFN 148.8-148.9
+    // against 148.7-148.8 (same box, two repeats; 1, 2 and 16 no better).
+    a.group_m = env_int("GEMM_F32_GROUP_M", d.bm == 256 && d.bn == 256 ? 4 : 8);
     if (a.group_m < 1) a.group_m = 1;
     a.num_xcd = facts.num_xcd;
     a.a_bytes = (uint32_t)((layout_a == GEMM_F32_ROW_MAJOR ? (m - 1) * lda + k : (k - 1) * lda + m) * 4);

@@ -211,3 +211,11 @@ def test_linear_dispatch_choice():
     # column-major B keeps 256x128 even with column-major A
     info = g.Plan(4096, 4096, 4096, COL_MAJOR, 4096, 4096, 4096, layout_a=COL_MAJOR).info
     assert info["name"] == "dma_256x128x16_w2x2_s3"
+
+
+def test_group_m_default_per_tile():
+    """The 256x256 tile rasterises in groups of 4 tile-rows, the others in 8."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the choice was measured on a 256-CU MI355X")
+    assert g.Plan(4096, 4096, 4096, ROW_MAJOR, 4096, 4096, 4096).info["group_m"] == 4
+    assert g.Plan(4096, 4096, 4096, COL_MAJOR, 4096, 4096, 4096).info["group_m"] == 8
