@@ -12,6 +12,16 @@ synchronisation; rank 0 prints one JSON line:
   cpu_baseline  the CPU oracle timed on a bounded row sample of the same
              workload on this host's cores
 
+Before the W warm-up steps the step runs untimed for ``--settle-s`` seconds
+of GPU time (default 0.25 s): under sustained matrix-core load the engine
+clock ramps for about 0.1 s, and a few warm-up steps of a 1 ms kernel do not
+cover that.  The timed region is still exactly K steps.
+
+``configs`` in the line: the other workloads of the metric (256^3, 4096^3
+with column-major B, the ragged 5003 x 4097 x 2049, the FFN and the skinny
+16 x 4096 x 4096 shapes), each timed in the same run with its own kernel
+average (the skinny one over 8 rotating operand sets, so B comes from HBM).
+
 Other workloads: ``--workload ffn`` etc. (see workloads.WORKLOADS);
 ``--all`` also appends a line per workload to the file given by ``--all-out``.
 ``--layout-a col`` stores A column-major; ``--epilogue relu|gelu|bias``
@@ -84,6 +94,9 @@ def parse():
                    help="cycle through this many operand sets (defeats the Infinity Cache for small workloads)")
     p.add_argument("--layout-a", choices=["row", "col"], default="row")
     p.add_argument("--epilogue", choices=["none", "bias", "relu", "gelu"], default="none")
+    p.add_argument("--settle-s", type=float, default=0.25,
+                   help="untimed GPU time before the warm-up steps, so the engine clock has ramped")
+    p.add_argument("--no-configs", action="store_true", help="skip the other workloads of the metric")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="first run one elementwise copy of MIB MiB (reads and writes MIB MiB), "
                         "the reference kernel for scaling the FETCH_SIZE/WRITE_SIZE counters")
@@ -145,7 +158,7 @@ class ClockSampler:
         return sum(self.samples) / len(self.samples) if self.samples else None
 
 
-def time_workload(name, steps, warmup, variant=None, rotate=1, layout_a=0, epilogue="none"):
+def time_workload(name, steps, warmup, variant=None, rotate=1, layout_a=0, epilogue="none", settle_s=0.0):
     import numpy as np
     import torch
 
@@ -183,6 +196,18 @@ def time_workload(name, steps, warmup, variant=None, rotate=1, layout_a=0, epilo
     else:
         plan_run = plan.run
 
+    # Clock settle: launches until settle_s of GPU time has passed (timed
+    # with one event pair around a first launch), then the warm-up steps.
+    if settle_s > 0:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        plan_run(*ptrs[0], sh)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        one = max(e0.elapsed_time(e1) / 1e3, 1e-6)
+        for i in range(int(settle_s / one)):
+            plan_run(*ptrs[i % rotate], sh)
     for i in range(warmup):
         plan_run(*ptrs[i % rotate], sh)
     torch.cuda.synchronize()
@@ -217,6 +242,7 @@ def time_workload(name, steps, warmup, variant=None, rotate=1, layout_a=0, epilo
         "tflops": flops * steps / wall / 1e12,
         "kernel_avg_s": kernel_avg,
         "sclk_mhz": clock.mean_mhz(),
+        "sclk_samples": len(clock.samples),
         "flops": flops,
         "bytes": pm.compulsory_bytes(w.m, w.n, w.k),
     }
@@ -242,14 +268,71 @@ def cpu_baseline(name, target_s):
         if t >= target_s / 3 or rows >= w.m:
             break
         rows = min(w.m, max(rows * 2, int(rows * target_s / 3 / max(t, 1e-3))))
-    return {
+    out = {
         "value": pm.gemm_flops(rows, w.n, w.k) / t / 1e12,
         "unit": "TFLOPS",
         "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": f"first {rows} of {w.m} rows of C for {w.name} ({w.m}x{w.n}x{w.k}), "
                   f"float64 triple loop, {t:.2f} s",
+        "cpu_model": cpu_model(),
     }
+    # The 256^3 case, whole, on one thread and on all of them.
+    s = WORKLOADS["sq256"]
+    A, B = workload_operands(s)
+    t_all = _time_oracle(oracle, A, B, s)
+    before = oracle.set_num_threads(1)
+    try:
+        t_one = _time_oracle(oracle, A, B, s)
+    finally:
+        oracle.set_num_threads(before)
+    out["sq256_seconds"] = {"threads_1": round(t_one, 5), f"threads_{before}": round(t_all, 5)}
+    return out
+
+
+def _time_oracle(oracle, A, B, w, repeats=3):
+    best = None
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.gemm_f64(A, B, w.m, w.n, w.k, w.layout_b)
+        t = time.perf_counter() - t0
+        best = t if best is None else min(best, t)
+    return best
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+MIN_CLOCK_SAMPLES = 5
+
+
+def clock_adjusted(achieved_tflops, peak_tflops, sclk_mhz, samples):
+    """(clock, fraction of the peak at that clock, note).  The published
+    peaks assume the 2.4 GHz peak engine clock; the driver's reported level
+    (pp_dpm_sclk) is only trusted when enough samples were taken and it
+    implies a fraction of at most 1 (a kernel cannot run above the peak of
+    its clock): otherwise the reading did not track the running clock, and
+    the fraction is null."""
+    from dense_gemm_optimisation_fp32_amd import perfmodel as pm
+
+    if not sclk_mhz:
+        return None, None, "no engine-clock reading on this host"
+    if samples < MIN_CLOCK_SAMPLES:
+        return sclk_mhz, None, f"only {samples} clock samples"
+    frac = achieved_tflops / (peak_tflops * sclk_mhz * 1e6 / pm.MI355X_PEAK_SCLK_HZ)
+    if frac > 1.0:
+        return sclk_mhz, None, (f"the reported clock ({sclk_mhz:.0f} MHz) is below what the measured rate "
+                                f"needs ({achieved_tflops / peak_tflops * pm.MI355X_PEAK_SCLK_HZ / 1e6:.0f} MHz): "
+                                f"it did not track the running clock")
+    return sclk_mhz, round(frac, 4), None
 
 
 def roofline(res):
@@ -266,9 +349,11 @@ def roofline(res):
                "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved / (peak / 1e12), 4)}
         # The peaks assume the 2.4 GHz peak engine clock; the same fraction
         # against the peak at the clock measured during the timed launches.
-        sclk = res.get("sclk_mhz")
+        sclk, frac_clk, note = clock_adjusted(achieved, peak / 1e12, res.get("sclk_mhz"), res.get("sclk_samples", 0))
         out["sclk_mhz"] = round(sclk, 1) if sclk else None
-        out["frac_at_sclk"] = round(achieved / (peak / 1e12 * sclk * 1e6 / pm.MI355X_PEAK_SCLK_HZ), 4) if sclk else None
+        out["frac_at_sclk"] = frac_clk
+        if note:
+            out["sclk_note"] = note
     else:
         achieved = res["bytes"] / res["kernel_avg_s"] / 1e9
         out = {"bound": "hbm", "achieved": round(achieved, 1), "peak": pm.MI355X_HBM_BANDWIDTH / 1e9,
@@ -276,6 +361,28 @@ def roofline(res):
     out["traffic"] = traffic_bytes(w.name, res["plan"]["name"])
     out["kernel"] = res["plan"]["name"]
     out["kernel_avg_us"] = round(res["kernel_avg_s"] * 1e6, 2)
+    return out
+
+
+# The other workloads of the metric, by the labels the metric's configs use.
+CONFIGS = (("C1", "sq256", 1), ("C3", "sq4096t", 1), ("C4", "ragged", 1), ("C5a", "ffn", 1),
+           ("C5b", "skinny", 8))
+
+
+def config_lines(steps, warmup, settle_s):
+    """Each other workload timed in this run: its kernel average (HIP events
+    on the launch stream) and the rate against its roofline."""
+    out = {}
+    for label, name, rotate in CONFIGS:
+        r = time_workload(name, steps, warmup, None, rotate, settle_s=settle_s)
+        rf = roofline(r)
+        out[label] = {"workload": name, "kernel": r["plan"]["name"], "grid": r["plan"]["grid"],
+                      "operand_sets": rotate, "kernel_avg_us": rf["kernel_avg_us"],
+                      "tflops_wall": round(r["tflops"], 3), "bound": rf["bound"],
+                      "achieved": rf["achieved"], "unit": rf["unit"], "frac": rf["frac"],
+                      "stream_k": r["plan"]["stream_k"], "split_k": r["plan"]["split_k"]}
+        if rf["bound"] == "hbm":
+            out[label]["tflops_kernel"] = round(r["flops"] / r["kernel_avg_s"] / 1e12, 3)
     return out
 
 
@@ -304,7 +411,7 @@ def main():
         del src, dst
 
     res = time_workload(args.workload, args.steps, args.warmup, args.variant, args.rotate,
-                        0 if args.layout_a == "row" else 1, args.epilogue)
+                        0 if args.layout_a == "row" else 1, args.epilogue, args.settle_s)
     w = res["workload"]
     line = {
         "metric": METRIC if w.name == HEADLINE else f"FP32 GEMM TFLOPS (2MNK/t), {w.name}",
@@ -327,9 +434,13 @@ def main():
                    "operand_sets": args.rotate,
                    "m": w.m, "n": w.n, "k": w.k, "layout_b": "row" if w.layout_b == 0 else "col",
                    "kernel": res["plan"]["name"], "grid": res["plan"]["grid"],
-                   "pct_of_fp32_matrix_peak": round(100 * res["tflops"] / (pm.MI355X_FP32_MATRIX_PEAK / 1e12), 2)},
+                   "pct_of_fp32_matrix_peak": round(100 * res["tflops"] / (pm.MI355X_FP32_MATRIX_PEAK / 1e12), 2),
+                   "settle_s": args.settle_s},
         "roofline": roofline(res),
     }
+    if not args.no_configs and args.workload == HEADLINE and args.variant is None and args.layout_a == "row" \
+            and args.epilogue == "none":
+        line["configs"] = config_lines(max(20, args.steps), max(5, args.warmup), args.settle_s)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
     print(json.dumps(line), flush=True)

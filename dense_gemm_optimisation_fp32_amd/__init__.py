@@ -44,7 +44,7 @@ EXPORTED_FUNCTIONS = (
     "gemm_f32_validate", "gemm_f32_create", "gemm_f32_create_variant", "gemm_f32_run",
     "gemm_f32_destroy", "gemm_f32_describe", "gemm_f32_num_variants", "gemm_f32_variant_info",
     "gemm_f32_error_string", "gemm_f32_last_hip_error", "gemm_f32_validate_ex", "gemm_f32_create_ex",
-    "gemm_f32_run_ex",
+    "gemm_f32_run_ex", "gemm_f32_plan_check",
 )
 
 
@@ -61,6 +61,9 @@ class gemm_f32_info(ctypes.Structure):
         ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("k_tiles", ctypes.c_int64),
         ("grid", ctypes.c_int64), ("group_m", ctypes.c_int), ("c_store_width", ctypes.c_int),
         ("name", ctypes.c_char * 64),
+        ("vgprs", ctypes.c_int), ("agprs", ctypes.c_int), ("sgprs", ctypes.c_int),
+        ("scratch_bytes", ctypes.c_int), ("compiler_waves_per_simd", ctypes.c_int),
+        ("workgroups_per_cu", ctypes.c_int), ("waves_per_simd", ctypes.c_int),
     ]
 
     def as_dict(self):
@@ -109,6 +112,7 @@ def load_library():
             "gemm_f32_validate_ex": ([i64, i64, i64, i32, i32, i64, i64, i64], i32),
             "gemm_f32_create_ex": ([plan_p, i64, i64, i64, i32, i32, i64, i64, i64, i32], i32),
             "gemm_f32_run_ex": ([vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp, i32, vp], i32),
+            "gemm_f32_plan_check": ([vp, ctypes.POINTER(i32)], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -167,6 +171,17 @@ def gemm_f32_run_ex(plan, A_ptr, B_ptr, C_ptr, alpha=1.0, beta=0.0, bias_ptr=Non
         raise GemmF32Error(st, "gemm_f32_run_ex")
 
 
+def gemm_f32_plan_check(plan) -> bool:
+    """True if a run of the plan since the last check gave up waiting for a
+    partial sum (and wrote NaN for it); clears the record.  Synchronise the
+    plan's streams first."""
+    lost = ctypes.c_int(0)
+    st = load_library().gemm_f32_plan_check(plan, ctypes.byref(lost))
+    if st != GEMM_F32_SUCCESS:
+        raise GemmF32Error(st, "gemm_f32_plan_check")
+    return bool(lost.value)
+
+
 def gemm_f32_destroy(plan) -> None:
     load_library().gemm_f32_destroy(plan)
 
@@ -215,6 +230,10 @@ class Plan:
         else:
             self.handle = gemm_f32_create_variant(variant, m, n, k, layout_b, lda, ldb, ldc)
         self.info = gemm_f32_describe(self.handle)
+        # Plans that split tiles along k own a device workspace that two runs
+        # must not share at the same time: such a plan serves one stream.
+        self.has_workspace = self.info["split_k"] > 1 or self.info["stream_k"] > 0
+        self.stream = None
 
     def run(self, A_ptr, B_ptr, C_ptr, stream=None):
         gemm_f32_run(self.handle, A_ptr, B_ptr, C_ptr, stream)
@@ -230,15 +249,34 @@ class Plan:
 
 
 _plan_cache: dict = {}
+_plan_lock = threading.Lock()
 
 
-def get_plan(m, n, k, layout_b, lda, ldb, ldc, variant=None, device=None, layout_a=0, epilogue=0) -> Plan:
+def get_plan(m, n, k, layout_b, lda, ldb, ldc, variant=None, device=None, layout_a=0, epilogue=0,
+             stream=None) -> Plan:
+    """The cached plan for a shape.  A plan with a workspace (split-k or
+    stream-K) belongs to the first stream that asks for it; another stream
+    gets a plan (and workspace) of its own, so runs on two streams never
+    share partial sums."""
     key = (device, m, n, k, layout_b, lda, ldb, ldc, variant, layout_a, epilogue)
-    p = _plan_cache.get(key)
-    if p is None:
-        p = Plan(m, n, k, layout_b, lda, ldb, ldc, variant, layout_a, epilogue)
-        _plan_cache[key] = p
-    return p
+    with _plan_lock:
+        p = _plan_cache.get(key)
+        if p is None:
+            p = Plan(m, n, k, layout_b, lda, ldb, ldc, variant, layout_a, epilogue)
+            _plan_cache[key] = p
+        if not p.has_workspace:
+            return p
+        if p.stream is None:
+            p.stream = stream
+        if p.stream == stream:
+            return p
+        skey = key + (stream,)
+        q = _plan_cache.get(skey)
+        if q is None:
+            q = Plan(m, n, k, layout_b, lda, ldb, ldc, variant, layout_a, epilogue)
+            q.stream = stream
+            _plan_cache[skey] = q
+        return q
 
 
 def operand_strides(A: torch.Tensor, B: torch.Tensor, layout_b=None, layout_a=None):
@@ -306,8 +344,8 @@ def matmul(A: torch.Tensor, B: torch.Tensor, layout_b=None, out: torch.Tensor | 
     m, n, k, layout_a, layout_b, lda, ldb = operand_strides(A, B, layout_b)
     out = _output(out, m, n, A.device)
     ldc = out.stride(0) if m > 1 else n
-    plan = get_plan(m, n, k, layout_b, lda, ldb, ldc, variant, A.device.index, layout_a)
     stream = torch.cuda.current_stream(A.device).cuda_stream
+    plan = get_plan(m, n, k, layout_b, lda, ldb, ldc, variant, A.device.index, layout_a, stream=stream)
     plan.run(A.data_ptr(), B.data_ptr(), out.data_ptr(), stream)
     return out
 
@@ -329,7 +367,7 @@ def linear(A: torch.Tensor, B: torch.Tensor, bias: torch.Tensor | None = None, a
         if bias.dtype != torch.float32 or bias.device != A.device or bias.numel() != n or not bias.is_contiguous():
             raise ValueError("bias must be a contiguous float32 tensor of N values on A's device")
         bias_ptr = bias.data_ptr()
-    plan = get_plan(m, n, k, layout_b, lda, ldb, ldc, None, A.device.index, layout_a, 1)
     stream = torch.cuda.current_stream(A.device).cuda_stream
+    plan = get_plan(m, n, k, layout_b, lda, ldb, ldc, None, A.device.index, layout_a, 1, stream=stream)
     plan.run_ex(A.data_ptr(), B.data_ptr(), out.data_ptr(), alpha, beta, bias_ptr, act, stream)
     return out

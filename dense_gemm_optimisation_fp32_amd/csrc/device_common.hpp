@@ -49,6 +49,12 @@ struct GemmArgs {
     const float *bias;     // N values, or NULL
     int use_beta;          // beta != 0: C is read
     int act;               // 0 none, 1 ReLU, 2 GELU (x * Phi(x))
+    // Waits for partial sums (split-k and stream-K plans).
+    unsigned *status;      // workspace word set to 1 when a wait gave up (a NaN went to C), or NULL
+    int wait_budget;       // polls one thread may spend waiting for partial sums
+    unsigned epoch_xor;    // readers wait for the tag epoch ^ epoch_xor (0; a test sets it so that
+                           // no word ever matches and every wait gives up)
+    int poison_lds;        // 1: fill LDS with NaN before the first copy (a test of the waits)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
@@ -132,23 +138,45 @@ __device__ __forceinline__ void raster_tile(int wg, const GemmArgs &a, int &tm, 
 }
 
 // Value of a 64-bit partial-sum word {float bits, epoch} written by another
-// workgroup, once it carries this run's epoch.  `w` is a first load already
-// in hand.  The writer has issued the word before the reader can get here,
-// so the wait ends; `budget` (polls left for the caller, shared by all its
-// waits) only keeps a lost word from hanging the kernel: once it is spent,
-// missing elements read as NaN at once.
+// workgroup, once it carries the epoch `want`.  `w` is a first load already
+// in hand.  Every writer has issued its words before it counts itself in,
+// and the reader is the last to count in, so the wait ends; `budget` (polls
+// left for the caller, shared by all its waits) only keeps a lost word from
+// hanging the kernel: once it is spent, missing elements read as NaN at once
+// and the budget is left negative, which the caller records in the plan's
+// status word when it is done (record_give_up; gemm_f32_plan_check reports
+// it).  The status store stays out of the wait so that its address is not
+// held in registers across the reads.
 constexpr int kTaggedWaitBudget = 1 << 16;
 
-__device__ __forceinline__ float wait_tagged_word(const unsigned long long *p, unsigned long long w, unsigned epoch,
+__device__ __forceinline__ float wait_tagged_word(const unsigned long long *p, unsigned long long w, unsigned want,
                                                   int &budget)
 {
-    while ((unsigned)(w >> 32) != epoch) {
-        if (budget <= 0) return __builtin_nanf("");
+    while ((unsigned)(w >> 32) != want) {
+        if (budget <= 0) {
+            budget = -1;
+            return __builtin_nanf("");
+        }
         --budget;
         __builtin_amdgcn_s_sleep(1);
         w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return __uint_as_float((unsigned)w);
+}
+
+__device__ __forceinline__ void record_give_up(int budget, unsigned *status)
+{
+    if (budget < 0 && status) __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Test hook: fill `chunks` 16-byte LDS chunks with NaN before a kernel's
+// first copy, so that a read of LDS that no copy or store has written yet
+// (a missing wait or barrier) puts NaN into C.
+__device__ __forceinline__ void poison_lds(f32x4 *lds, int chunks, int tid, int threads)
+{
+    const float nan = __builtin_nanf("");
+    for (int i = tid; i < chunks; i += threads) lds[i] = f32x4{nan, nan, nan, nan};
+    __syncthreads();
 }
 
 // GELU(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt(2))).  erf by Abramowitz

@@ -11,11 +11,15 @@
 #include <mutex>
 #include <new>
 
+#include <dlfcn.h>
+
 #include "gemm_f32.h"
-#include "mfma_dma_gemm.hpp"
-#include "mfma_gemm.hpp"
-#include "skinny_gemm.hpp"
-#include "valu_gemm.hpp"
+#include "kernel_list.hpp"
+#include "kernel_resources.hpp"
+
+// The kernels are compiled in the k_*.hip units; this unit only takes their
+// handles.
+GEMMF32_ALL_UNITS(GEMMF32_EXTERN5, GEMMF32_EXTERN2, GEMMF32_EXTERN1)
 
 namespace {
 
@@ -530,7 +534,8 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     // against 148.7-148.8 (same box, two repeats; 1, 2 and 16 no better).
     a.group_m = env_int("GEMM_F32_GROUP_M", d.bm == 256 && d.bn == 256 ? 4 : 8);
     if (a.group_m < 1) a.group_m = 1;
-    a.num_xcd = facts.num_xcd;
+    a.num_xcd = env_int("GEMM_F32_NUM_XCD", facts.num_xcd);   // 1: no XCD remap (measurement)
+    if (a.num_xcd < 1) a.num_xcd = 1;
     a.a_bytes = (uint32_t)((layout_a == GEMM_F32_ROW_MAJOR ? (m - 1) * lda + k : (k - 1) * lda + m) * 4);
     a.alpha = 1.0f;
     a.beta = 0.0f;
@@ -541,6 +546,15 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
     // The whole-chunk loads of row-major B may run up to 3 elements past the
     // last valid column of a k-row; that stays inside B when ldb >= 4.
     a.masked_loads = (layout_b == GEMM_F32_ROW_MAJOR && ldb < 4) ? 1 : 0;
+    // Waits for partial sums, and two test hooks (environment, read here):
+    // GEMM_F32_WAIT_BUDGET polls per thread before a wait gives up;
+    // GEMM_F32_TEST_LOST_WORDS=1 makes readers wait for a tag that is never
+    // written (every wait gives up, the status word records it);
+    // GEMM_F32_POISON_LDS=1 fills LDS with NaN before the first copy.
+    a.wait_budget = env_int("GEMM_F32_WAIT_BUDGET", gemmf32::kTaggedWaitBudget);
+    if (a.wait_budget < 0) a.wait_budget = 0;
+    a.epoch_xor = env_int("GEMM_F32_TEST_LOST_WORDS", 0) ? 0x80000000u : 0u;
+    a.poison_lds = env_int("GEMM_F32_POISON_LDS", 0) ? 1 : 0;
     p->grid = (unsigned)((int64_t)a.tiles_m * a.tiles_n);
     p->block = (unsigned)d.threads;
     p->workspace = nullptr;
@@ -559,10 +573,11 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
         a.k_per_split = (int)kps;
         p->grid = (unsigned)(per_split * split);
         if (split > 1) {
-            // split * m * n tagged words, then one arrival counter per tile;
-            // all zero, so no stale word carries a valid (non-zero) epoch.
+            // split * m * n tagged words, then one arrival counter per tile
+            // and the status word; all zero, so no stale word carries a
+            // valid (non-zero) epoch.
             const size_t words = (size_t)split * (size_t)m * (size_t)n * sizeof(unsigned long long);
-            const size_t bytes = words + (size_t)per_split * sizeof(unsigned);
+            const size_t bytes = words + ((size_t)per_split + 1) * sizeof(unsigned);
             hipError_t e = hipMalloc(&p->workspace, bytes);
             if (e == hipSuccess) e = hipMemsetAsync(p->workspace, 0, bytes, nullptr);
             if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
@@ -573,6 +588,7 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
             }
             a.partial = static_cast<unsigned long long *>(p->workspace);
             a.arrivals = reinterpret_cast<unsigned *>(static_cast<char *>(p->workspace) + words);
+            a.status = a.arrivals + per_split;
         }
     }
 
@@ -622,7 +638,7 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
             p->c_store_width = 1;   // the stream-K kernel stores one element at a time
             p->grid = (unsigned)(wgs + tiles - shared);
             const size_t words = (size_t)2 * wgs * d.bm * d.bn * sizeof(unsigned long long);
-            const size_t bytes = words + (size_t)shared * sizeof(unsigned);
+            const size_t bytes = words + ((size_t)shared + 1) * sizeof(unsigned);   // + the status word
             // The words are addressed through a buffer descriptor (32-bit
             // extent); the automatic plans stay far below this.
             if (words >= ((size_t)1 << 31)) {
@@ -640,6 +656,7 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
             }
             a.partial = static_cast<unsigned long long *>(p->workspace);
             a.arrivals = reinterpret_cast<unsigned *>(static_cast<char *>(p->workspace) + words);
+            a.status = a.arrivals + shared;
         }
     }
 
@@ -649,6 +666,41 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
                      a.sk_wgs, a.sk_tiles);
     *out = p;
     return GEMM_F32_SUCCESS;
+}
+
+// The build's resource entry of a kernel, found by the mangled name of its
+// handle (the handles are exported symbols of this library), or NULL.
+const gemmf32::KernelResources *kernel_resources(const void *fn)
+{
+    Dl_info d;
+    if (!fn || !dladdr(fn, &d) || !d.dli_sname) return nullptr;
+    for (int i = 0; i < gemmf32::kKernelResourcesCount; ++i)
+        if (std::strcmp(gemmf32::kKernelResources[i].name, d.dli_sname) == 0) return &gemmf32::kKernelResources[i];
+    return nullptr;
+}
+
+void fill_resources(const void *fn, gemm_f32_info *info)
+{
+    const gemmf32::KernelResources *r = kernel_resources(fn);
+    if (!r) return;
+    info->vgprs = r->vgprs;
+    info->agprs = r->agprs;
+    info->sgprs = r->sgprs;
+    info->scratch_bytes = r->scratch_bytes;
+    info->compiler_waves_per_simd = r->waves_per_simd;
+}
+
+// Every kernel handle of a variant.
+template <class F>
+void for_each_kernel(const VariantDesc &d, F f)
+{
+    for (const void *fn : d.fn) f(fn);
+    for (const void *fn : d.fn_sk) f(fn);
+    for (int a = 0; a < 2; ++a)
+        for (int b = 0; b < 2; ++b)
+            for (int e = 0; e < 2; ++e) f(d.fn_ex[a][b][e]);
+    for (int a = 0; a < 2; ++a)
+        for (int e = 0; e < 2; ++e) f(d.fn_wide[a][e]);
 }
 
 void fill_static_info(int v, gemm_f32_info *info)
@@ -666,6 +718,12 @@ void fill_static_info(int v, gemm_f32_info *info)
     info->stages = d.stages;
     info->split_k = 1;
     std::snprintf(info->name, sizeof(info->name), "%s", d.name);
+    fill_resources(d.fn[0], info);
+    // Spills anywhere in the variant: the largest scratch of its kernels.
+    for_each_kernel(d, [&](const void *fn) {
+        const gemmf32::KernelResources *r = fn ? kernel_resources(fn) : nullptr;
+        if (r && r->scratch_bytes > info->scratch_bytes) info->scratch_bytes = r->scratch_bytes;
+    });
 }
 
 }  // namespace
@@ -808,6 +866,31 @@ int gemm_f32_describe(gemm_f32_plan p, gemm_f32_info *info)
     info->stream_k_tiles = p->args.sk_tiles;
     info->layout_a = p->layout_a;
     info->epilogue = p->epilogue;
+    // The kernel this plan launches, its resources and its occupancy.
+    const int col = p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0;
+    const void *fn = p->args.sk_wgs ? variant(p->variant).fn_sk[col] : p->fn;
+    info->vgprs = info->agprs = info->sgprs = info->scratch_bytes = info->compiler_waves_per_simd = 0;
+    fill_resources(fn, info);
+    int wgs = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs, fn, (int)p->block, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        wgs = 0;
+    }
+    info->workgroups_per_cu = wgs;
+    info->waves_per_simd = wgs * ((int)p->block / 64) / 4;
+    return GEMM_F32_SUCCESS;
+}
+
+int gemm_f32_plan_check(gemm_f32_plan p, int *lost)
+{
+    if (!p || !lost) return GEMM_F32_ERR_INVALID_VALUE;
+    *lost = 0;
+    if (!p->args.status) return GEMM_F32_SUCCESS;
+    unsigned v = 0;
+    hipError_t e = hipMemcpy(&v, p->args.status, sizeof(v), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && v) e = hipMemset(p->args.status, 0, sizeof(v));
+    if (e != hipSuccess) return hip_fail(e);
+    *lost = v ? 1 : 0;
     return GEMM_F32_SUCCESS;
 }
 

@@ -1,0 +1,119 @@
+// Every kernel instantiation of the library, as X-macro lists over named
+// tile types.  The host translation unit (gemm_f32.hip) declares each one
+// `extern template`, and the kernel translation units (k_*.hip) define them
+// by explicit instantiation, so the device code is compiled once, in
+// several units that build in parallel.  A kernel the host unit uses that is
+// missing here would be instantiated implicitly in the host unit; the build
+// rejects that (it checks that the host unit compiles no kernel).
+#pragma once
+
+#include "mfma_dma_gemm.hpp"
+#include "mfma_gemm.hpp"
+#include "skinny_gemm.hpp"
+#include "valu_gemm.hpp"
+
+namespace gemmf32 {
+
+// Register-staged MFMA tiles (BM, BN, BK, wavefront grid).
+using Reg256x256x16 = MfmaTile<256, 256, 16, 2, 2>;
+using Reg128x128x16 = MfmaTile<128, 128, 16, 2, 2>;
+using Reg256x128x16 = MfmaTile<256, 128, 16, 2, 2>;
+using Reg256x128x32 = MfmaTile<256, 128, 32, 2, 2>;
+using Reg128x128x32 = MfmaTile<128, 128, 32, 2, 2>;
+
+// Direct-to-LDS tiles (BM, BN, BK, wavefront grid, LDS stages, priority).
+using Dma256x256x16S2 = DmaTile<256, 256, 16, 2, 2, 2>;
+using Dma256x256x16S3 = DmaTile<256, 256, 16, 2, 2, 3>;
+using Dma256x256x16S4 = DmaTile<256, 256, 16, 2, 2, 4>;
+using Dma256x256x32S2 = DmaTile<256, 256, 32, 2, 2, 2>;
+using Dma128x128x16S3 = DmaTile<128, 128, 16, 2, 2, 3, false>;
+using Dma128x128x32S3 = DmaTile<128, 128, 32, 2, 2, 3, false>;
+using Dma256x128x16S3 = DmaTile<256, 128, 16, 2, 2, 3>;
+using Dma64x64x16S3 = DmaTile<64, 64, 16, 2, 2, 3>;
+using Dma64x64x16S2 = DmaTile<64, 64, 16, 2, 2, 2>;
+using Dma128x64x16S2 = DmaTile<128, 64, 16, 2, 2, 2>;
+using Dma128x64x16S3 = DmaTile<128, 64, 16, 2, 2, 3>;
+using Dma64x128x16S2 = DmaTile<64, 128, 16, 2, 2, 2>;
+using Dma64x128x16S3 = DmaTile<64, 128, 16, 2, 2, 3>;
+
+// Few-row tiles (wavefronts, k groups in flight, columns).
+using SkinnyW4D4 = SkinnyTile<4, 4, 64>;
+using SkinnyW8D4 = SkinnyTile<8, 4, 64>;
+using SkinnyW16D4 = SkinnyTile<16, 4, 64>;
+using Skinny16W16D4 = SkinnyTile<16, 4, 16>;
+
+}  // namespace gemmf32
+
+// X5(kernel, Tile, B_COL, A_COL, EPI, WIDE_C) for gemm_mfma_dma_kernel;
+// X2(kernel, Tile, B_COL) for the two-parameter kernels; X1(kernel, B_COL).
+
+// Whole-tile and stream-K kernels of a direct-to-LDS tile (row-major A, no
+// epilogue, one C element per store).
+#define GEMMF32_DMA_BASE(X5, X2, T)                               \
+    X5(gemm_mfma_dma_kernel, T, false, false, false, false)       \
+    X5(gemm_mfma_dma_kernel, T, true, false, false, false)        \
+    X2(gemm_mfma_dma_sk_kernel, T, false)                         \
+    X2(gemm_mfma_dma_sk_kernel, T, true)
+// Row-major B with NB (2 or 4) adjacent C columns per store.
+#define GEMMF32_DMA_WIDE(X5, T) X5(gemm_mfma_dma_kernel, T, false, false, false, true)
+// Column-major A and the linear-layer epilogue.
+#define GEMMF32_DMA_EX(X5, T)                                     \
+    X5(gemm_mfma_dma_kernel, T, false, true, false, false)        \
+    X5(gemm_mfma_dma_kernel, T, true, true, false, false)         \
+    X5(gemm_mfma_dma_kernel, T, false, false, true, false)        \
+    X5(gemm_mfma_dma_kernel, T, true, false, true, false)         \
+    X5(gemm_mfma_dma_kernel, T, false, true, true, false)         \
+    X5(gemm_mfma_dma_kernel, T, true, true, true, false)
+#define GEMMF32_DMA_EX_WIDE(X5, T)                                \
+    X5(gemm_mfma_dma_kernel, T, false, true, false, true)         \
+    X5(gemm_mfma_dma_kernel, T, false, false, true, true)         \
+    X5(gemm_mfma_dma_kernel, T, false, true, true, true)
+
+// Kernel translation units.
+#define GEMMF32_UNIT_DMA256(X5, X2, X1)                           \
+    GEMMF32_DMA_BASE(X5, X2, Dma256x256x16S2) GEMMF32_DMA_WIDE(X5, Dma256x256x16S2) \
+    GEMMF32_DMA_BASE(X5, X2, Dma256x256x16S3) GEMMF32_DMA_WIDE(X5, Dma256x256x16S3) \
+    GEMMF32_DMA_BASE(X5, X2, Dma256x256x32S2) GEMMF32_DMA_WIDE(X5, Dma256x256x32S2)
+#define GEMMF32_UNIT_DMA256S4(X5, X2, X1)                         \
+    GEMMF32_DMA_BASE(X5, X2, Dma256x256x16S4) GEMMF32_DMA_WIDE(X5, Dma256x256x16S4) \
+    GEMMF32_DMA_EX(X5, Dma256x256x16S4) GEMMF32_DMA_EX_WIDE(X5, Dma256x256x16S4)
+#define GEMMF32_UNIT_DMA256x128(X5, X2, X1)                       \
+    GEMMF32_DMA_BASE(X5, X2, Dma256x128x16S3) GEMMF32_DMA_WIDE(X5, Dma256x128x16S3) \
+    GEMMF32_DMA_EX(X5, Dma256x128x16S3) GEMMF32_DMA_EX_WIDE(X5, Dma256x128x16S3)
+#define GEMMF32_UNIT_DMA128(X5, X2, X1)                           \
+    GEMMF32_DMA_BASE(X5, X2, Dma128x128x16S3) GEMMF32_DMA_WIDE(X5, Dma128x128x16S3) \
+    GEMMF32_DMA_EX(X5, Dma128x128x16S3) GEMMF32_DMA_EX_WIDE(X5, Dma128x128x16S3) \
+    GEMMF32_DMA_BASE(X5, X2, Dma128x128x32S3) GEMMF32_DMA_WIDE(X5, Dma128x128x32S3)
+#define GEMMF32_UNIT_DMA64(X5, X2, X1)                            \
+    GEMMF32_DMA_BASE(X5, X2, Dma64x64x16S3) GEMMF32_DMA_EX(X5, Dma64x64x16S3) \
+    GEMMF32_DMA_BASE(X5, X2, Dma64x64x16S2) GEMMF32_DMA_EX(X5, Dma64x64x16S2) \
+    GEMMF32_DMA_BASE(X5, X2, Dma128x64x16S2) GEMMF32_DMA_BASE(X5, X2, Dma128x64x16S3)
+#define GEMMF32_UNIT_DMA64x128(X5, X2, X1)                        \
+    GEMMF32_DMA_BASE(X5, X2, Dma64x128x16S2) GEMMF32_DMA_WIDE(X5, Dma64x128x16S2) \
+    GEMMF32_DMA_EX(X5, Dma64x128x16S2) GEMMF32_DMA_EX_WIDE(X5, Dma64x128x16S2) \
+    GEMMF32_DMA_BASE(X5, X2, Dma64x128x16S3) GEMMF32_DMA_WIDE(X5, Dma64x128x16S3)
+#define GEMMF32_UNIT_OTHER(X5, X2, X1)                            \
+    X2(gemm_mfma_kernel, Reg256x256x16, false) X2(gemm_mfma_kernel, Reg256x256x16, true) \
+    X2(gemm_mfma_kernel, Reg128x128x16, false) X2(gemm_mfma_kernel, Reg128x128x16, true) \
+    X2(gemm_mfma_kernel, Reg256x128x16, false) X2(gemm_mfma_kernel, Reg256x128x16, true) \
+    X2(gemm_mfma_kernel, Reg256x128x32, false) X2(gemm_mfma_kernel, Reg256x128x32, true) \
+    X2(gemm_mfma_kernel, Reg128x128x32, false) X2(gemm_mfma_kernel, Reg128x128x32, true) \
+    X1(gemm_valu_kernel, false) X1(gemm_valu_kernel, true)                                   \
+    X2(gemm_skinny_kernel, SkinnyW4D4, false) X2(gemm_skinny_kernel, SkinnyW4D4, true)       \
+    X2(gemm_skinny_kernel, SkinnyW8D4, false) X2(gemm_skinny_kernel, SkinnyW8D4, true)       \
+    X2(gemm_skinny_kernel, SkinnyW16D4, false) X2(gemm_skinny_kernel, SkinnyW16D4, true)     \
+    X2(gemm_skinny_kernel, Skinny16W16D4, false) X2(gemm_skinny_kernel, Skinny16W16D4, true)
+
+#define GEMMF32_ALL_UNITS(X5, X2, X1)                                                     \
+    GEMMF32_UNIT_DMA256(X5, X2, X1) GEMMF32_UNIT_DMA256S4(X5, X2, X1)                     \
+    GEMMF32_UNIT_DMA256x128(X5, X2, X1) GEMMF32_UNIT_DMA128(X5, X2, X1)                   \
+    GEMMF32_UNIT_DMA64(X5, X2, X1) GEMMF32_UNIT_DMA64x128(X5, X2, X1)                     \
+    GEMMF32_UNIT_OTHER(X5, X2, X1)
+
+// Explicit instantiation definitions (kernel units) and declarations (host unit).
+#define GEMMF32_DEFINE5(K, T, a, b, c, d) template __global__ void gemmf32::K<gemmf32::T, a, b, c, d>(gemmf32::GemmArgs);
+#define GEMMF32_DEFINE2(K, T, a) template __global__ void gemmf32::K<gemmf32::T, a>(gemmf32::GemmArgs);
+#define GEMMF32_DEFINE1(K, a) template __global__ void gemmf32::K<a>(gemmf32::GemmArgs);
+#define GEMMF32_EXTERN5(K, T, a, b, c, d) extern template __global__ void gemmf32::K<gemmf32::T, a, b, c, d>(gemmf32::GemmArgs);
+#define GEMMF32_EXTERN2(K, T, a) extern template __global__ void gemmf32::K<gemmf32::T, a>(gemmf32::GemmArgs);
+#define GEMMF32_EXTERN1(K, a) extern template __global__ void gemmf32::K<a>(gemmf32::GemmArgs);

@@ -660,6 +660,10 @@ __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsr
             __builtin_amdgcn_sched_barrier(0);
         }
 
+    // Every wavefront has issued its words before the segment counts itself
+    // in, so the last segment to arrive finds every word of the others at
+    // least in flight.
+    __syncthreads();
     if (tid == 0) {
         const unsigned before = __hip_atomic_fetch_add(g.arrivals + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool last = before == (unsigned)(nseg - 1);
@@ -669,7 +673,8 @@ __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsr
     }
     __syncthreads();
     if (!*last_flag) return;
-    int budget = kTaggedWaitBudget;
+    int budget = g.wait_budget;
+    const unsigned want = g.epoch ^ g.epoch_xor;
 
     constexpr int H = 8;   // words per lane in flight
 #pragma unroll
@@ -687,10 +692,10 @@ __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsr
 #pragma unroll
                     for (int v = 0; v < H; ++v) {
                         // The word's address is formed only if it has not arrived yet.
-                        const float x = (unsigned)(w[v] >> 32) == g.epoch
+                        const float x = (unsigned)(w[v] >> 32) == want
                                             ? __uint_as_float((unsigned)w[v])
                                             : wait_tagged_word(g.partial + base + word(mb, nb, v0 + v) + tid, w[v],
-                                                               g.epoch, budget);
+                                                               want, budget);
                         sum[v] = jj == 0 ? x : sum[v] + x;
                     }
                 }
@@ -703,6 +708,7 @@ __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsr
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+    record_give_up(budget, g.status);
 }
 
 // One whole tile per workgroup.  A_COL: column-major A; EPI: the
@@ -720,6 +726,10 @@ __global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_kernel(GemmArgs g)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave % T::WAVES_M, wc = wave / T::WAVES_M;
     const int l32 = lane & 31, half = lane >> 5;
+    // (Not in the epilogue kernels, which share the copy ring with the plain
+    // ones: there the test branch cost one of them occupancy.)
+    if constexpr (!EPI)
+        if (g.poison_lds) poison_lds(lds, T::STAGES * (T::A_CHUNKS + T::B_CHUNKS), tid, T::THREADS);
 
     int tm, tn;
     raster_tile(blockIdx.x, g, tm, tn);
@@ -776,6 +786,7 @@ __global__ __launch_bounds__(T::THREADS, sk_waves_per_simd<T>()) void gemm_mfma_
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave % T::WAVES_M, wc = wave / T::WAVES_M;
     const int l32 = lane & 31, half = lane >> 5;
+    if (g.poison_lds) poison_lds(lds, T::STAGES * (T::A_CHUNKS + T::B_CHUNKS), tid, T::THREADS);
 
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, g.b_bytes);

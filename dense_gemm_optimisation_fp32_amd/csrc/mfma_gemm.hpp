@@ -382,6 +382,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_mfma_kernel(GemmArgs g)
     const int lane = tid & 63, wave = tid >> 6;
     const int wr = wave % T::WAVES_M, wc = wave / T::WAVES_M;
     const int l32 = lane & 31, half = lane >> 5;
+    if (g.poison_lds) poison_lds(lds, 2 * (T::A_CHUNKS + T::B_CHUNKS), tid, T::THREADS);
 
     int tm, tn;
     raster_tile(blockIdx.x, g, tm, tn);

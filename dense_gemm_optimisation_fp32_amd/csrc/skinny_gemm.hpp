@@ -230,6 +230,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
         if (e < ELEMS && r < g.m && c < g.n) store_tagged_word(g.partial + split * plane + (size_t)r * g.n + c, own[q], g.epoch);
     }
     __shared__ int last;
+    // (Every wavefront has issued its words before the workgroup counts itself in.)
     __syncthreads();
     if (tid == 0) {
         const unsigned before =
@@ -241,7 +242,8 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
     }
     __syncthreads();
     if (!last) return;
-    int budget = kTaggedWaitBudget;
+    int budget = g.wait_budget;
+    const unsigned want = g.epoch ^ g.epoch_xor;
 
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
@@ -262,12 +264,13 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
             for (int u = 0; u < 8; ++u) {
                 const int sp = s0 + u;
                 if (sp >= g.split_k) break;
-                const float v = sp == split ? own[q] : wait_tagged_word(p + sp * plane, w[u], g.epoch, budget);
+                const float v = sp == split ? own[q] : wait_tagged_word(p + sp * plane, w[u], want, budget);
                 sum = sp == 0 ? v : sum + v;
             }
         }
         g.C[(size_t)r * g.ldc + c] = sum;
     }
+    record_give_up(budget, g.status);
 }
 
 }  // namespace gemmf32

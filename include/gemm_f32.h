@@ -103,6 +103,20 @@ struct gemm_f32_info {
     int c_store_width;  /* plan only: C elements per store instruction of the whole-tile kernel
                            (2 or 4 with row-major B and N a multiple of it; else 1) */
     char name[64];      /* human-readable variant name */
+    /* Resources of one kernel ("GPU 算子优化中的数据复用", section 9: spills;
+     * section 12: resident workgroups are the minimum over the register, LDS
+     * and wave limits), from the compiler's report of this build.  For a
+     * plan: the kernel the plan launches.  For gemm_f32_variant_info: the
+     * variant's whole-tile kernel for row-major A and B, except that
+     * scratch_bytes is the largest over all of the variant's kernels. */
+    int vgprs;              /* architectural vector registers per lane */
+    int agprs;              /* accumulation vector registers per lane (MFMA accumulators) */
+    int sgprs;              /* scalar registers per wavefront */
+    int scratch_bytes;      /* private memory per lane for register spills (0: none) */
+    int compiler_waves_per_simd; /* occupancy the compiler derives from registers and LDS */
+    int workgroups_per_cu;  /* plan only: resident workgroups per CU (the HIP runtime's
+                               occupancy calculator for the launched kernel) */
+    int waves_per_simd;     /* plan only: workgroups_per_cu * wavefronts per workgroup / 4 */
 };
 
 /*
@@ -133,6 +147,17 @@ int gemm_f32_validate(int64_t m, int64_t n, int64_t k, int layout_b,
  *                             a partial-sum area of 2^31 bytes or more is
  *                             rejected with GEMM_F32_ERR_INVALID_VALUE;
  *   GEMM_F32_STREAMK=0        never choose stream-K automatically;
+ *   GEMM_F32_NUM_XCD=<count>  the XCD count the rasterisation undoes
+ *                             (default: the device's; 1 turns the XCD
+ *                             remap off, for measuring it);
+ *   GEMM_F32_WAIT_BUDGET=<polls>  how long one thread waits for partial
+ *                             sums before it gives up (gemm_f32_plan_check);
+ *   GEMM_F32_TEST_LOST_WORDS=1  test hook: every wait for a partial sum
+ *                             gives up (the split tiles of C become NaN);
+ *   GEMM_F32_POISON_LDS=1     test hook: the tiled kernels fill LDS with NaN
+ *                             before their first copy, so a read of LDS
+ *                             before the copy that fills it lands shows up
+ *                             as NaN in C;
  *   GEMM_F32_LOG=1 (or 2)     print the plan (and the dispatch's estimates)
  *                             to stderr, the one exception to "nothing
  *                             prints".
@@ -211,6 +236,20 @@ int gemm_f32_destroy(gemm_f32_plan plan);
 
 /* gemm_f32_describe: copy the plan's choices into *info (both non-NULL). */
 int gemm_f32_describe(gemm_f32_plan plan, struct gemm_f32_info *info);
+
+/*
+ * gemm_f32_plan_check: whether a run of the plan since the last check gave
+ * up waiting for another workgroup's partial sums.  Plans that split tiles
+ * along k (split_k > 1 or stream_k > 0) add the splits in the last
+ * workgroup of each tile to arrive; its wait for each word is bounded so
+ * that a lost word can never hang the kernel, and when a wait gives up that
+ * element of C is written as NaN and the plan's status word records it.
+ * *lost receives 1 if that happened (and the record is cleared), else 0;
+ * plans without a workspace always report 0.  Call it after synchronising
+ * the streams the plan ran on (it reads device memory with a blocking copy).
+ * Errors: INVALID_VALUE (NULL plan or lost), ERR_HIP.
+ */
+int gemm_f32_plan_check(gemm_f32_plan plan, int *lost);
 
 /* gemm_f32_num_variants: number of entries in the compiled variant table. */
 int gemm_f32_num_variants(void);

@@ -76,6 +76,8 @@ def _load():
     lib.oracle_gemm_f64_sampled_ex.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -185,6 +187,11 @@ def epilogue_f64(ab, s_ab, c_in=None, alpha: float = 1.0, beta: float = 0.0, bia
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(threads: int) -> int:
+    """Thread count of later oracle calls; returns the previous one."""
+    return int(_load().oracle_set_num_threads(threads))
 
 
 def within_tolerance(c_test, c_ref, s_ref, rel: float = 1e-5, abs_: float = 1e-6):

@@ -162,3 +162,17 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Set the OpenMP thread count of later calls (the benchmark times the small
+ * case single-threaded as well); returns the previous count. */
+int oracle_set_num_threads(int threads)
+{
+#ifdef _OPENMP
+    int before = omp_get_max_threads();
+    if (threads > 0) omp_set_num_threads(threads);
+    return before;
+#else
+    (void)threads;
+    return 1;
+#endif
+}

@@ -185,3 +185,30 @@ def test_binding_strides_from_tensors():
         g.operand_strides(A, torch.empty(11, 20))
     with pytest.raises(ValueError):
         g.operand_strides(torch.empty(8, 24)[:, ::2], B)   # A with no unit stride
+
+
+def test_variant_resources_from_the_build(lib):
+    """Every variant reports its kernel's registers from the build's resource
+    table; no kernel of any variant spills to scratch; the direct-to-LDS
+    tiles hold their MFMA accumulators (16 per 32x32 block and lane) in the
+    accumulation registers, and their compiler occupancy agrees with the
+    residency model of the registers and LDS they use."""
+    from dense_gemm_optimisation_fp32_amd import perfmodel as pm
+
+    for v in range(g.gemm_f32_num_variants()):
+        info = g.gemm_f32_variant_info(v)
+        assert info["vgprs"] > 0 and info["sgprs"] > 0, info["name"]
+        assert info["scratch_bytes"] == 0, f"{info['name']} spills"
+        assert 1 <= info["compiler_waves_per_simd"] <= 8
+        assert info["workgroups_per_cu"] == 0 and info["waves_per_simd"] == 0   # plan-only fields
+        if info["name"].startswith("dma_"):
+            blocks = (info["wave_m"] // 32) * (info["wave_n"] // 32)
+            assert info["agprs"] == 16 * blocks, info["name"]
+            wgs, waves = pm.gfx950_occupancy(info["vgprs"], info["agprs"], info["lds_bytes"], info["threads"])
+            # the compiler's estimate per SIMD is at least what whole workgroups give
+            assert info["compiler_waves_per_simd"] >= waves, info["name"]
+
+
+def test_plan_check_null_handling(lib):
+    lost = ctypes.c_int(7)
+    assert lib.gemm_f32_plan_check(None, ctypes.byref(lost)) == g.GEMM_F32_ERR_INVALID_VALUE

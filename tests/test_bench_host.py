@@ -47,11 +47,13 @@ def _res(name, kernel_avg_s, sclk, kind=0, plan_name="dma_256x256x16_w2x2_s4"):
 def test_roofline_scales_the_peak_to_the_measured_clock():
     flop = 2 * 4096 ** 3
     t = flop / 150e12                      # 150 TFLOP/s
-    r = bench.roofline(_res("sq4096", t, 2000.0))
+    res = _res("sq4096", t, 2390.0)
+    res["sclk_samples"] = 10
+    r = bench.roofline(res)
     assert r["bound"] == "mfma" and r["achieved"] == pytest.approx(150.0, rel=1e-3)
     assert r["frac"] == pytest.approx(150.0 / 157.3, abs=1e-4)
-    # at 2000 MHz the peak is 157.3 * 2000 / 2400
-    assert r["frac_at_sclk"] == pytest.approx(150.0 / (157.3 * 2000 / 2400), abs=1e-4)
+    # at 2390 MHz the peak is 157.3 * 2390 / 2400
+    assert r["frac_at_sclk"] == pytest.approx(150.0 / (157.3 * 2390 / 2400), abs=1e-4)
     r = bench.roofline(_res("sq4096", t, None))
     assert r["sclk_mhz"] is None and r["frac_at_sclk"] is None
 
@@ -71,3 +73,32 @@ def test_roofline_bandwidth_bound_and_traffic_gating():
     else:
         assert got is None
     assert bench.traffic_bytes("sq4096", "some_other_kernel") is None
+
+
+def test_clock_reading_below_what_the_rate_needs_is_dropped():
+    """An idle-level reading (as pp_dpm_sclk gave on one box: 880 MHz while
+    the kernel ran at 147 TFLOP/s) implies a fraction above 1: null."""
+    flop = 2 * 4096 ** 3
+    res = _res("sq4096", flop / 147e12, 880.0)
+    res["sclk_samples"] = 10
+    r = bench.roofline(res)
+    assert r["frac_at_sclk"] is None and "did not track" in r["sclk_note"]
+    res = _res("sq4096", flop / 147e12, 2380.0)
+    res["sclk_samples"] = 2                  # too few samples
+    r = bench.roofline(res)
+    assert r["frac_at_sclk"] is None
+    res["sclk_samples"] = 10
+    r = bench.roofline(res)
+    assert r["frac_at_sclk"] == pytest.approx(147.0 / (157.3 * 2380 / 2400), abs=1e-4)
+
+
+def test_clock_sampler_idle_level_file(tmp_path):
+    p = tmp_path / "pp_dpm_sclk"
+    p.write_text("S: 880Mhz *\n0: 500Mhz\n1: 2400Mhz\n")
+    c = bench.ClockSampler(period_s=0.001)
+    c.path = str(p)
+    with c:
+        time.sleep(0.03)
+    res = _res("sq4096", 2 * 4096 ** 3 / 147e12, c.mean_mhz())
+    res["sclk_samples"] = len(c.samples)
+    assert bench.roofline(res)["frac_at_sclk"] is None
