@@ -469,11 +469,16 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
     return kCandidate[best].variant;   // 256x128, never skipped, is always weighed
 }
 
-int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int64_t k, int layout_a,
-              int layout_b, int64_t lda, int64_t ldb, int64_t ldc, int epilogue)
+// Everything a plan needs except its workspace: the kernel, grid and launch
+// arguments, and the workspace it asks for (*ws_words bytes of epoch-tagged
+// partial-sum words and *ws_counters 32-bit arrival counters, plus one status
+// word; zero for plans that split no tile along k).  No allocation.
+int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, int64_t k, int layout_a,
+              int layout_b, int64_t lda, int64_t ldb, int64_t ldc, int epilogue, size_t *ws_words,
+              size_t *ws_counters)
 {
-    if (!out) return GEMM_F32_ERR_INVALID_VALUE;
-    *out = nullptr;
+    *ws_words = 0;
+    *ws_counters = 0;
     int st = gemm_f32_validate_ex(m, n, k, layout_a, layout_b, lda, ldb, ldc);
     if (st != GEMM_F32_SUCCESS) return st;
     if (forced_variant >= V_COUNT || (epilogue != 0 && epilogue != 1)) return GEMM_F32_ERR_INVALID_VALUE;
@@ -501,8 +506,6 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
         auto_tail = 0;
     }
 
-    gemm_f32_plan p = new (std::nothrow) gemm_f32_plan_impl();
-    if (!p) return GEMM_F32_ERR_ALLOC;
     p->variant = v;
     p->device = dev;
     p->layout_a = layout_a;
@@ -573,22 +576,9 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
         a.k_per_split = (int)kps;
         p->grid = (unsigned)(per_split * split);
         if (split > 1) {
-            // split * m * n tagged words, then one arrival counter per tile
-            // and the status word; all zero, so no stale word carries a
-            // valid (non-zero) epoch.
-            const size_t words = (size_t)split * (size_t)m * (size_t)n * sizeof(unsigned long long);
-            const size_t bytes = words + ((size_t)per_split + 1) * sizeof(unsigned);
-            hipError_t e = hipMalloc(&p->workspace, bytes);
-            if (e == hipSuccess) e = hipMemsetAsync(p->workspace, 0, bytes, nullptr);
-            if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
-            if (e != hipSuccess) {
-                if (p->workspace) (void)hipFree(p->workspace);
-                delete p;
-                return hip_fail(e);
-            }
-            a.partial = static_cast<unsigned long long *>(p->workspace);
-            a.arrivals = reinterpret_cast<unsigned *>(static_cast<char *>(p->workspace) + words);
-            a.status = a.arrivals + per_split;
+            // split * m * n tagged words and one arrival counter per tile.
+            *ws_words = (size_t)split * (size_t)m * (size_t)n * sizeof(unsigned long long);
+            *ws_counters = (size_t)per_split;
         }
     }
 
@@ -612,10 +602,7 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
         } else if (wgs <= 0 && auto_stream_k && env_int("GEMM_F32_STREAMK", 1) != 0) {
             int per_cu = 0;
             hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, d.fn_sk[layout_b], d.threads, 0);
-            if (e != hipSuccess) {
-                delete p;
-                return hip_fail(e);
-            }
+            if (e != hipSuccess) return hip_fail(e);
             // Three workgroups per CU (fewer if fewer fit), at most 8
             // segments per tile (the last one to arrive reads all the
             // others) and at least 8 slabs per workgroup.  Measured with
@@ -638,25 +625,12 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
             p->c_store_width = 1;   // the stream-K kernel stores one element at a time
             p->grid = (unsigned)(wgs + tiles - shared);
             const size_t words = (size_t)2 * wgs * d.bm * d.bn * sizeof(unsigned long long);
-            const size_t bytes = words + ((size_t)shared + 1) * sizeof(unsigned);   // + the status word
             // The words are addressed through a buffer descriptor (32-bit
             // extent); the automatic plans stay far below this.
-            if (words >= ((size_t)1 << 31)) {
-                delete p;
-                return GEMM_F32_ERR_INVALID_VALUE;
-            }
+            if (words >= ((size_t)1 << 31)) return GEMM_F32_ERR_INVALID_VALUE;
             a.partial_bytes = (uint32_t)words;
-            hipError_t e = hipMalloc(&p->workspace, bytes);
-            if (e == hipSuccess) e = hipMemsetAsync(p->workspace, 0, bytes, nullptr);
-            if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
-            if (e != hipSuccess) {
-                if (p->workspace) (void)hipFree(p->workspace);
-                delete p;
-                return hip_fail(e);
-            }
-            a.partial = static_cast<unsigned long long *>(p->workspace);
-            a.arrivals = reinterpret_cast<unsigned *>(static_cast<char *>(p->workspace) + words);
-            a.status = a.arrivals + shared;
+            *ws_words = words;
+            *ws_counters = (size_t)shared;
         }
     }
 
@@ -664,6 +638,46 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
         std::fprintf(stderr, "[gemm_f32] m=%lld n=%lld k=%lld layoutB=%d -> %s grid=%u group_m=%d split_k=%d stream_k=%d over %d tiles\n",
                      (long long)m, (long long)n, (long long)k, layout_b, d.name, p->grid, a.group_m, a.split_k,
                      a.sk_wgs, a.sk_tiles);
+    return GEMM_F32_SUCCESS;
+}
+
+// Point a plan's launch arguments at its workspace: the words, then the
+// arrival counters and the status word.
+void plan_attach(gemm_f32_plan_impl *p, void *words, unsigned *counters, size_t n_counters)
+{
+    p->args.partial = static_cast<unsigned long long *>(words);
+    p->args.arrivals = counters;
+    p->args.status = counters + n_counters;
+}
+
+int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int64_t k, int layout_a,
+              int layout_b, int64_t lda, int64_t ldb, int64_t ldc, int epilogue)
+{
+    if (!out) return GEMM_F32_ERR_INVALID_VALUE;
+    *out = nullptr;
+    gemm_f32_plan p = new (std::nothrow) gemm_f32_plan_impl();
+    if (!p) return GEMM_F32_ERR_ALLOC;
+    size_t words = 0, counters = 0;
+    int st = plan_fill(p, forced_variant, m, n, k, layout_a, layout_b, lda, ldb, ldc, epilogue, &words, &counters);
+    if (st != GEMM_F32_SUCCESS) {
+        delete p;
+        return st;
+    }
+    if (words) {
+        // The plan's own workspace, all zero, so no word carries a valid
+        // (non-zero) epoch and every counter starts at zero.
+        const size_t bytes = words + (counters + 1) * sizeof(unsigned);
+        hipError_t e = hipMalloc(&p->workspace, bytes);
+        if (e == hipSuccess) e = hipMemsetAsync(p->workspace, 0, bytes, nullptr);
+        if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+        if (e != hipSuccess) {
+            if (p->workspace) (void)hipFree(p->workspace);
+            delete p;
+            return hip_fail(e);
+        }
+        plan_attach(p, p->workspace, reinterpret_cast<unsigned *>(static_cast<char *>(p->workspace) + words),
+                    counters);
+    }
     *out = p;
     return GEMM_F32_SUCCESS;
 }
@@ -781,21 +795,27 @@ int gemm_f32_create_variant(gemm_f32_plan *out, int v, int64_t m, int64_t n, int
 
 namespace {
 
-int launch(gemm_f32_plan p, GemmArgs &a, void *stream)
+// Launch the plan's kernel with arguments `a` (pointers and epoch filled).
+int launch_kernel(const gemm_f32_plan_impl *p, GemmArgs &a, void *stream)
 {
     void *kargs[] = {&a};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int col = p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0;
+    const void *fn = p->args.sk_wgs ? variant(p->variant).fn_sk[col] : p->fn;
+    hipError_t e = hipLaunchKernel(fn, dim3(p->grid), dim3(p->block), kargs, 0, s);
+    if (e != hipSuccess) return hip_fail(e);
+    return GEMM_F32_SUCCESS;
+}
+
+int launch(gemm_f32_plan p, GemmArgs &a, void *stream)
+{
     if (p->workspace) {
         // A fresh, non-zero tag for this run's split-k partial sums.
         unsigned ep = ++p->runs;
         if (ep == 0) ep = ++p->runs;
         a.epoch = ep;
     }
-    const int col = p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0;
-    const void *fn = p->args.sk_wgs ? variant(p->variant).fn_sk[col] : p->fn;
-    hipError_t e = hipLaunchKernel(fn, dim3(p->grid), dim3(p->block), kargs, 0, s);
-    if (e != hipSuccess) return hip_fail(e);
-    return GEMM_F32_SUCCESS;
+    return launch_kernel(p, a, stream);
 }
 
 bool pointers_ok(const float *A, const float *B, const float *C)
