@@ -30,6 +30,7 @@ GEMM_F32_ERR_NO_DEVICE = 2
 GEMM_F32_ERR_UNSUPPORTED_DEVICE = 3
 GEMM_F32_ERR_HIP = 4
 GEMM_F32_ERR_ALLOC = 5
+GEMM_F32_ERR_SCRATCH_TOO_SMALL = 6
 
 GEMM_F32_ACT_NONE = 0
 GEMM_F32_ACT_RELU = 1
@@ -44,7 +45,7 @@ EXPORTED_FUNCTIONS = (
     "gemm_f32_validate", "gemm_f32_create", "gemm_f32_create_variant", "gemm_f32_run",
     "gemm_f32_destroy", "gemm_f32_describe", "gemm_f32_num_variants", "gemm_f32_variant_info",
     "gemm_f32_error_string", "gemm_f32_last_hip_error", "gemm_f32_validate_ex", "gemm_f32_create_ex",
-    "gemm_f32_run_ex", "gemm_f32_plan_check",
+    "gemm_f32_run_ex", "gemm_f32_plan_check", "gemm_f32_run_noalloc",
 )
 
 
@@ -113,6 +114,7 @@ def load_library():
             "gemm_f32_create_ex": ([plan_p, i64, i64, i64, i32, i32, i64, i64, i64, i32], i32),
             "gemm_f32_run_ex": ([vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp, i32, vp], i32),
             "gemm_f32_plan_check": ([vp, ctypes.POINTER(i32)], i32),
+            "gemm_f32_run_noalloc": ([i64, i64, i64, i32, i64, i64, i64, vp, vp, vp, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -150,6 +152,14 @@ def gemm_f32_run(plan, A_ptr, B_ptr, C_ptr, stream=None) -> None:
     st = load_library().gemm_f32_run(plan, A_ptr, B_ptr, C_ptr, stream)
     if st != GEMM_F32_SUCCESS:
         raise GemmF32Error(st, "gemm_f32_run")
+
+
+def gemm_f32_run_noalloc(m, n, k, layout_b, lda, ldb, ldc, A_ptr, B_ptr, C_ptr, stream=None) -> None:
+    """C = A.B with no allocation (partial sums in the library's per-GPU
+    scratch area); calls on one GPU must not overlap in time."""
+    st = load_library().gemm_f32_run_noalloc(m, n, k, layout_b, lda, ldb, ldc, A_ptr, B_ptr, C_ptr, stream)
+    if st != GEMM_F32_SUCCESS:
+        raise GemmF32Error(st, "gemm_f32_run_noalloc")
 
 
 def gemm_f32_validate_ex(m, n, k, layout_a, layout_b, lda, ldb, ldc) -> int:

@@ -21,6 +21,18 @@
 // handles.
 GEMMF32_ALL_UNITS(GEMMF32_EXTERN5, GEMMF32_EXTERN2, GEMMF32_EXTERN1)
 
+// Scratch of gemm_f32_run_noalloc: the arrival counters (and status word)
+// of the split tiles first, then the epoch-tagged partial-sum words.  One
+// copy per GPU, reserved until the process ends; every call on a GPU shares
+// it.  Host code never uses this name as an address: it takes the device
+// address from hipGetSymbolAddress, once per device (scratch_address).
+namespace {
+constexpr size_t kScratchCounters = 65536;             // 32-bit counters, the last one the status word
+constexpr size_t kScratchWordBytes = (size_t)64 << 20;  // 64 MiB of 8-byte words
+constexpr size_t kScratchBytes = kScratchCounters * 4 + kScratchWordBytes;
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 using gemmf32::GemmArgs;
@@ -793,6 +805,8 @@ int gemm_f32_create_variant(gemm_f32_plan *out, int v, int64_t m, int64_t n, int
     return make_plan(out, v, m, n, k, GEMM_F32_ROW_MAJOR, layout_b, lda, ldb, ldc, 0);
 }
 
+}  // extern "C"
+
 namespace {
 
 // Launch the plan's kernel with arguments `a` (pointers and epoch filled).
@@ -818,6 +832,29 @@ int launch(gemm_f32_plan p, GemmArgs &a, void *stream)
     return launch_kernel(p, a, stream);
 }
 
+// The device address of `scratch` on the current device, found once per
+// device with that device current.
+struct ScratchSlot {
+    void *ptr = nullptr;
+    std::atomic<unsigned> epoch{0};   // tags handed out to calls on this device
+};
+ScratchSlot g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+int scratch_address(int dev, void **out)
+{
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    ScratchSlot &s = g_scratch[dev];
+    if (!s.ptr) {
+        void *ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+        s.ptr = ptr;
+    }
+    *out = s.ptr;
+    return GEMM_F32_SUCCESS;
+}
+
 bool pointers_ok(const float *A, const float *B, const float *C)
 {
     if (!A || !B || !C) return false;
@@ -828,6 +865,8 @@ bool pointers_ok(const float *A, const float *B, const float *C)
 
 }  // namespace
 
+extern "C" {
+
 int gemm_f32_run(gemm_f32_plan p, const float *A, const float *B, float *C, void *stream)
 {
     if (!p || !pointers_ok(A, B, C)) return GEMM_F32_ERR_INVALID_VALUE;
@@ -836,6 +875,47 @@ int gemm_f32_run(gemm_f32_plan p, const float *A, const float *B, float *C, void
     a.B = B;
     a.C = C;
     return launch(p, a, stream);
+}
+
+int gemm_f32_run_noalloc(int64_t m, int64_t n, int64_t k, int layout_b, int64_t lda, int64_t ldb, int64_t ldc,
+                         const float *A, const float *B, float *C, void *stream)
+{
+    if (!pointers_ok(A, B, C)) return GEMM_F32_ERR_INVALID_VALUE;
+    gemm_f32_plan_impl p;   // host state on the stack: nothing is allocated
+    size_t words = 0, counters = 0;
+    int st = plan_fill(&p, -1, m, n, k, GEMM_F32_ROW_MAJOR, layout_b, lda, ldb, ldc, 0, &words, &counters);
+    if (st != GEMM_F32_SUCCESS) return st;
+    GemmArgs a = p.args;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    if (words) {
+        if (words > kScratchWordBytes || counters + 1 > kScratchCounters) return GEMM_F32_ERR_SCRATCH_TOO_SMALL;
+        void *base = nullptr;
+        st = scratch_address(p.device, &base);
+        if (st != GEMM_F32_SUCCESS) return st;
+        unsigned *ctr = static_cast<unsigned *>(base);
+        a.partial = reinterpret_cast<unsigned long long *>(static_cast<char *>(base) + kScratchCounters * 4);
+        a.arrivals = ctr;
+        a.status = ctr + counters;
+        // The counters and the status word start at zero: a fill kernel on
+        // the caller's stream ahead of the product (a kernel, not a memset,
+        // so that the call can be captured in a graph).  The words need no
+        // clearing: each call tags its words with an epoch no earlier call
+        // on this device used.
+        const int n_zero = (int)(counters + 1);
+        unsigned *zp = ctr;
+        int zn = n_zero;
+        void *zargs[] = {&zp, &zn};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&gemmf32::zero_words_kernel),
+                                       dim3((unsigned)((n_zero + 255) / 256)), dim3(256), zargs, 0,
+                                       reinterpret_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail(e);
+        unsigned ep = ++g_scratch[p.device].epoch;
+        if (ep == 0) ep = ++g_scratch[p.device].epoch;
+        a.epoch = ep;
+    }
+    return launch_kernel(&p, a, stream);
 }
 
 int gemm_f32_run_ex(gemm_f32_plan p, const float *A, const float *B, float *C, float alpha, float beta,
@@ -932,6 +1012,9 @@ const char *gemm_f32_error_string(int status)
     case GEMM_F32_ERR_UNSUPPORTED_DEVICE: return "current device is not gfx950";
     case GEMM_F32_ERR_HIP: return "HIP runtime call failed (see gemm_f32_last_hip_error)";
     case GEMM_F32_ERR_ALLOC: return "host allocation failed";
+    case GEMM_F32_ERR_SCRATCH_TOO_SMALL:
+        return "the plan's partial sums exceed the static scratch area of gemm_f32_run_noalloc "
+               "(64 MiB of partial-sum words, 65535 split tiles)";
     default: return "unknown status";
     }
 }

@@ -36,6 +36,10 @@ using Dma128x64x16S3 = DmaTile<128, 64, 16, 2, 2, 3>;
 using Dma64x128x16S2 = DmaTile<64, 128, 16, 2, 2, 2>;
 using Dma64x128x16S3 = DmaTile<64, 128, 16, 2, 2, 3>;
 
+// Zero n 32-bit words (the arrival counters of gemm_f32_run_noalloc's
+// scratch area), with vector stores; defined in k_other.hip.
+__global__ void zero_words_kernel(unsigned *p, int n);
+
 // Few-row tiles (wavefronts, k groups in flight, columns).
 using SkinnyW4D4 = SkinnyTile<4, 4, 64>;
 using SkinnyW8D4 = SkinnyTile<8, 4, 64>;

@@ -65,7 +65,8 @@ enum gemm_f32_status {
     GEMM_F32_ERR_NO_DEVICE = 2,           /* no HIP device visible */
     GEMM_F32_ERR_UNSUPPORTED_DEVICE = 3,  /* current device is not gfx950 */
     GEMM_F32_ERR_HIP = 4,                 /* a HIP runtime call failed; see gemm_f32_last_hip_error */
-    GEMM_F32_ERR_ALLOC = 5                /* host allocation failed */
+    GEMM_F32_ERR_ALLOC = 5,               /* host allocation failed */
+    GEMM_F32_ERR_SCRATCH_TOO_SMALL = 6    /* gemm_f32_run_noalloc: the partial sums exceed its scratch area */
 };
 
 /* Activation of the linear-layer epilogue (gemm_f32_run_ex). */
@@ -184,6 +185,34 @@ int gemm_f32_create_variant(gemm_f32_plan *out, int variant, int64_t m, int64_t 
  *         aligned), GEMM_F32_ERR_HIP (launch failed).  Never synchronises.
  */
 int gemm_f32_run(gemm_f32_plan plan, const float *A, const float *B, float *C, void *stream);
+
+/*
+ * gemm_f32_run_noalloc: C = A.B on `stream`, as gemm_f32_create, gemm_f32_run
+ * and gemm_f32_destroy with the same arguments would compute it (the same
+ * plan and kernels), for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  It calls
+ * no hipMalloc, hipFree or other allocating routine, host or device; the
+ * plan lives on the call's stack.  Plans that split tiles along k (the
+ * few-row path's split-k, stream-K) keep their partial sums in a scratch
+ * area the library reserves once on each GPU it runs on, until the process
+ * ends: 64 MiB of partial-sum words and 65536 32-bit counters.
+ *   Arguments: as gemm_f32_create (sizes, layout_b, leading dimensions) and
+ *   gemm_f32_run (device pointers A, B, C, 4-byte aligned, C not overlapping
+ *   A or B; `stream` a hipStream_t, NULL = the null stream).
+ *   Every call on one GPU shares that GPU's scratch area, which keeps the
+ *   last call's contents (each call clears the counters it uses, with a
+ *   small kernel on `stream` ahead of the product, and tags its words with a
+ *   new epoch): two calls that overlap in time on one GPU (other streams or
+ *   host threads) race and can return wrong results; order them.  The
+ *   first call on each device finds the scratch area's device address; make
+ *   it outside graph capture.  Give-ups of the bounded waits (see
+ *   gemm_f32_plan_check) write NaN to C but are not reported here.
+ * Errors: as gemm_f32_create and gemm_f32_run; GEMM_F32_ERR_SCRATCH_TOO_SMALL
+ *   when the plan needs more than the scratch area holds (more than 64 MiB
+ *   of words or more than 65535 split tiles).  Never synchronises.
+ */
+int gemm_f32_run_noalloc(int64_t m, int64_t n, int64_t k, int layout_b, int64_t lda, int64_t ldb, int64_t ldc,
+                         const float *A, const float *B, float *C, void *stream);
 
 /*
  * Linear-layer layouts and epilogue.  A linear layer (the FFN and QKV

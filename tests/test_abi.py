@@ -147,7 +147,7 @@ def test_null_handling(lib):
 
 
 def test_error_strings(lib):
-    for st in range(6):
+    for st in range(7):
         s = g.gemm_f32_error_string(st)
         assert s and s != "unknown status"
     assert g.gemm_f32_error_string(99) == "unknown status"
