@@ -74,13 +74,14 @@ def resources_for(info: dict, layout_b: int, res: dict):
             ag = int(r.get("AGPRs", 0))
             lds = int(r.get("LDS Size [bytes/block]", 0))
             wgs, waves = pm.gfx950_occupancy(vg, ag, lds, info["threads"])
-            return {"vgpr": vg, "agpr": ag, "lds": lds, "scratch": int(r.get("ScratchSize [bytes/lane]", 0)),
+            return {"vgpr": vg, "agpr": ag, "sgpr": int(r.get("TotalSGPRs", 0)), "lds": lds,
+                    "scratch": int(r.get("ScratchSize [bytes/lane]", 0)),
                     "compiler_waves_per_simd": int(r.get("Occupancy [waves/SIMD]", 0)),
                     "model_wgs_per_cu": wgs, "model_waves_per_simd": waves}
     return {}
 
 
-def time_variant(g, torch, w, variant, steps, warmup):
+def time_variant(g, torch, w, variant, steps, warmup, warmup_s=0.25):
     from workloads import workload_operands
 
     A, B = workload_operands(w)
@@ -100,7 +101,7 @@ def time_variant(g, torch, w, variant, steps, warmup):
     t1.record(stream)
     torch.cuda.synchronize()
     est = max(t0.elapsed_time(t1) / 1e3, 1e-6)
-    for _ in range(max(warmup, int(0.25 / est))):
+    for _ in range(max(warmup, int(warmup_s / est))):
         plan.run(dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), stream.cuda_stream)
     torch.cuda.synchronize()
     # Average launch duration: one event pair around `steps` back-to-back
@@ -113,6 +114,64 @@ def time_variant(g, torch, w, variant, steps, warmup):
     return plan.info, t0.elapsed_time(t1) / 1e3 / steps
 
 
+def kernel_short_name(rec: dict, layout_b: int, n: int) -> str:
+    """rocprof_summary.short_name of the kernel a sweep record ran (N
+    decides whether a row-major-B plan takes the wide-store kernel)."""
+    name = rec["name"]
+    if name.startswith("dma_"):
+        stages = re.search(r"_s(\d+)$", name).group(1)
+        base = f"dma_{rec['bm']}x{rec['bn']}x{rec['bk']}_s{stages}"
+        if layout_b == 1:
+            return base + "_bcol"
+        nb = rec["wave_tile"][1] // 32
+        return base + ("_wide" if nb in (2, 4) and n % nb == 0 else "")
+    if name.startswith("mfma_"):
+        return f"mfma_{rec['bm']}x{rec['bn']}x{rec['bk']}"
+    if name.startswith("valu_"):
+        return "valu_128x128x8"
+    return name
+
+
+def table(jsonl: str, counter_dirs: dict) -> str:
+    """Markdown table of a sweep file: one row per variant, per workload the
+    measured TFLOPS, and for the workloads with a counter run the matrix-core
+    busy fraction, the LDS bank-conflict ratio and the L2 hit rate."""
+    from workloads import WORKLOADS
+
+    from . import rocprof_summary as rs
+
+    recs = [json.loads(line) for line in open(jsonl) if line.strip()]
+    workloads = list(dict.fromkeys(r["workload"] for r in recs))
+    ctr = {w: {rs.short_name(k): v for k, v in rs.counters(d).items()} for w, d in counter_dirs.items()}
+    head = ["variant", "tile", "wave tile", "stages", "VGPR", "AGPR", "SGPR", "LDS KiB", "scratch",
+            "waves/SIMD (compiler / model)"]
+    for w in workloads:
+        head.append(f"{w} TFLOPS")
+        if w in ctr:
+            head += [f"{w} MFMA busy", f"{w} LDS conflicts", f"{w} L2 hit"]
+    out = ["| " + " | ".join(head) + " |", "|" + "---|" * len(head)]
+    by_variant = {}
+    for r in recs:
+        by_variant.setdefault(r["variant"], {})[r["workload"]] = r
+    for v, per in by_variant.items():
+        r0 = next(iter(per.values()))
+        row = [f"`{r0['name']}`", f"{r0['bm']}x{r0['bn']}x{r0['bk']}", f"{r0['wave_tile'][0]}x{r0['wave_tile'][1]}",
+               re.search(r"_s(\d+)$", r0["name"]).group(1) if r0["name"].startswith("dma_") else "2",
+               str(r0.get("vgpr", "")), str(r0.get("agpr", "")), str(r0.get("sgpr", "")),
+               str(r0.get("lds", 0) // 1024), str(r0.get("scratch", "")),
+               f"{r0.get('compiler_waves_per_simd', '')} / {r0.get('model_waves_per_simd', '')}"]
+        for w in workloads:
+            r = per.get(w)
+            row.append(f"{r['tflops']:.1f}" if r else "")
+            if w in ctr:
+                c = ctr[w].get(kernel_short_name(r0, WORKLOADS[w].layout_b, WORKLOADS[w].n), {}) if r else {}
+                row += [f"{c['mfma_busy']:.3f}" if "mfma_busy" in c else "",
+                        f"{c['lds_conflict']:.3f}" if "lds_conflict" in c else "",
+                        f"{c['l2_hit']:.3f}" if "l2_hit" in c else ""]
+        out.append("| " + " | ".join(row) + " |")
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--workloads", default="sq4096,sq4096t,ragged,ffn")
@@ -120,7 +179,15 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--out", default="sweep.jsonl")
+    ap.add_argument("--warmup-s", type=float, default=0.25,
+                    help="GPU time of warm-up launches per variant (the clock ramps for ~0.1 s)")
+    ap.add_argument("--table", metavar="JSONL", help="print the markdown table of a sweep file instead")
+    ap.add_argument("--counters", action="append", default=[], metavar="WORKLOAD=DIR",
+                    help="with --table: rocprofv3 counter output of a sweep run over one workload")
     args = ap.parse_args(argv)
+    if args.table:
+        print(table(args.table, dict(c.split("=", 1) for c in args.counters)))
+        return 0
 
     import torch
 
@@ -138,7 +205,7 @@ def main(argv=None):
                 kind = g.gemm_f32_variant_info(v)["kind"]
                 if (kind == g.GEMM_F32_KIND_SKINNY) != (w.m <= 64):
                     continue   # the few-row path and the tiled paths serve different shape classes
-                info, avg = time_variant(g, torch, w, v, args.steps, args.warmup)
+                info, avg = time_variant(g, torch, w, v, args.steps, args.warmup, args.warmup_s)
                 rec = {"workload": name, "variant": v, "name": info["name"], "kind": info["kind"],
                        "bm": info["bm"], "bn": info["bn"], "bk": info["bk"],
                        "waves": info["waves_m"] * info["waves_n"], "wave_tile": [info["wave_m"], info["wave_n"]],
