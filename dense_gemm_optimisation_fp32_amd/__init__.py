@@ -40,6 +40,7 @@ _ACTIVATIONS = {None: 0, "none": 0, "relu": 1, "gelu": 2, 0: 0, 1: 1, 2: 2}
 GEMM_F32_KIND_MFMA = 0
 GEMM_F32_KIND_VALU = 1
 GEMM_F32_KIND_SKINNY = 2
+GEMM_F32_KIND_FEWCOL = 3
 
 EXPORTED_FUNCTIONS = (
     "gemm_f32_validate", "gemm_f32_create", "gemm_f32_create_variant", "gemm_f32_run",
@@ -65,6 +66,7 @@ class gemm_f32_info(ctypes.Structure):
         ("vgprs", ctypes.c_int), ("agprs", ctypes.c_int), ("sgprs", ctypes.c_int),
         ("scratch_bytes", ctypes.c_int), ("compiler_waves_per_simd", ctypes.c_int),
         ("workgroups_per_cu", ctypes.c_int), ("waves_per_simd", ctypes.c_int),
+        ("sliver_cols", ctypes.c_int64), ("sliver_variant", ctypes.c_int), ("sliver_stream_k", ctypes.c_int),
     ]
 
     def as_dict(self):
@@ -242,7 +244,7 @@ class Plan:
         self.info = gemm_f32_describe(self.handle)
         # Plans that split tiles along k own a device workspace that two runs
         # must not share at the same time: such a plan serves one stream.
-        self.has_workspace = self.info["split_k"] > 1 or self.info["stream_k"] > 0
+        self.has_workspace = self.info["split_k"] > 1 or self.info["stream_k"] > 0 or self.info["sliver_stream_k"] > 0
         self.stream = None
 
     def run(self, A_ptr, B_ptr, C_ptr, stream=None):

@@ -1,0 +1,149 @@
+// Few-column FP32 GEMM (N <= 8): the matrix-vector-like shape.
+//
+// With a handful of columns every element of A is used N times and never
+// again, so the product is bound by reading A once from memory ("GEMM 性能优化",
+// Roofline 与平衡点: an arithmetic intensity of N/2 FLOP per byte is far
+// below the ridge).  A tile of the matrix-core kernels would spend a whole
+// 64- or 128-column k-loop on these few columns; here A streams straight
+// into registers with 16-byte loads along k (64 lanes cover 1 KiB of one
+// row per instruction, "PMPP Chapter 06", section 1: adjacent lanes read
+// adjacent addresses) and meets the few B columns, which every row shares,
+// in LDS.
+//
+// Workgroup: 4 wavefronts, ROWS_PER_WAVE rows each (grid over row blocks and
+// groups of R columns).  k runs in chunks of KC: the workgroup copies the
+// chunk of its R columns of B into LDS (k-contiguous per column, zeros past
+// K and past N), then each wavefront reads its rows' k-chunk, lane l taking
+// k = 4l + 256q + t (t = 0..3), multiplies with one 16-byte LDS read per
+// column and accumulates per lane.  The 64 lanes' partial sums of each
+// output are then added by a butterfly over the wavefront (a fixed order, so
+// results repeat bit for bit), and lane 0 stores them.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace gemmf32 {
+
+template <int R_>
+struct FewColTile {
+    static_assert(R_ == 1 || R_ == 4 || R_ == 8, "columns per workgroup");
+    static constexpr int R = R_;                 // columns of C per workgroup
+    static constexpr int WAVES = 4;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int ROWS_PER_WAVE = 2;
+    static constexpr int ROWS = WAVES * ROWS_PER_WAVE;   // rows of C per workgroup
+    static constexpr int KC = 2048;              // k per LDS chunk
+    static constexpr int GROUPS = KC / 256;      // 16-byte loads per lane per row and chunk
+    static constexpr int LDS_BYTES = R * KC * 4;
+};
+
+// Workgroup barrier that waits for this wavefront's LDS accesses only
+// (lgkmcnt(0); vmcnt, expcnt left at their maxima in the gfx9 encoding), so
+// global loads issued before it stay in flight; the "memory" clobber keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void fewcol_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// Sum over the 64 lanes of a wavefront, butterfly order (every lane ends
+// with the same total).
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Grid: ceil(m / ROWS) row blocks x ceil(n / R) column groups (row block
+// fastest).
+template <class T, bool B_COL>
+__global__ __launch_bounds__(T::THREADS) void gemm_fewcol_kernel(GemmArgs g)
+{
+    __shared__ f32x4 bs[T::R * T::KC / 4];   // [column][k] chunk of B, k-contiguous
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row_blocks = (g.m + T::ROWS - 1) / T::ROWS;
+    const int rb = (int)blockIdx.x % row_blocks;
+    const int j0 = ((int)blockIdx.x / row_blocks) * T::R;
+    const int row0 = rb * T::ROWS + wave * T::ROWS_PER_WAVE;
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
+    const __amdgpu_buffer_rsrc_t rb_ = make_rsrc(g.B, g.b_bytes);
+    float *const bsf = reinterpret_cast<float *>(bs);
+
+    float acc[T::ROWS_PER_WAVE][T::R];
+#pragma unroll
+    for (int t = 0; t < T::ROWS_PER_WAVE; ++t)
+#pragma unroll
+        for (int j = 0; j < T::R; ++j) acc[t][j] = 0.0f;
+
+    for (int kc = 0; kc < g.k; kc += T::KC) {
+        const int klen = min(T::KC, g.k - kc);
+        // This chunk's A loads first (ROWS_PER_WAVE * GROUPS 16-byte loads
+        // per lane), so that they are in flight with the B chunk's.
+        f32x4 a[T::ROWS_PER_WAVE][T::GROUPS];
+        if (klen == T::KC) {
+            // A whole chunk: every group is whole (uniform branch).
+#pragma unroll
+            for (int t = 0; t < T::ROWS_PER_WAVE; ++t)
+#pragma unroll
+                for (int q = 0; q < T::GROUPS; ++q)
+                    a[t][q] = buf_load_x4(ra, elem_off(row0 + t < g.m, row0 + t, g.lda, kc + 4 * lane + 256 * q));
+        } else {
+            // The last chunk: element by element (elements past K may be
+            // the next row's, or padding).
+#pragma unroll
+            for (int t = 0; t < T::ROWS_PER_WAVE; ++t)
+#pragma unroll
+                for (int q = 0; q < T::GROUPS; ++q)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int kk = 4 * lane + 256 * q + u;
+                        a[t][q][u] = buf_load_x1(ra, elem_off(row0 + t < g.m && kk < klen, row0 + t, g.lda, kc + kk));
+                    }
+        }
+        // The B chunk: element (k, column j0 + j) for k < klen and j0 + j < n,
+        // zero elsewhere.  Column-major B is read along k; row-major B along
+        // its few columns.  The barriers wait for LDS only: the A loads stay
+        // in flight (the compiler waits for each load where its value is
+        // used).
+        fewcol_barrier();   // the previous chunk's LDS reads are done
+        for (int e = tid; e < T::R * T::KC; e += T::THREADS) {
+            const int j = B_COL ? e / T::KC : e % T::R;
+            const int kk = B_COL ? e % T::KC : e / T::R;
+            const bool ok = kk < klen && j0 + j < g.n;
+            const uint32_t off = B_COL ? elem_off(ok, j0 + j, g.ldb, kc + kk) : elem_off(ok, kc + kk, g.ldb, j0 + j);
+            bsf[j * T::KC + kk] = buf_load_x1(rb_, off);
+        }
+        fewcol_barrier();
+
+#pragma unroll
+        for (int q = 0; q < T::GROUPS; ++q) {
+            const int kk = 4 * lane + 256 * q;
+#pragma unroll
+            for (int j = 0; j < T::R; ++j) {
+                const f32x4 b = bs[(j * T::KC + kk) / 4];
+#pragma unroll
+                for (int t = 0; t < T::ROWS_PER_WAVE; ++t)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[t][j] += a[t][q][u] * b[u];
+            }
+        }
+    }
+
+#pragma unroll
+    for (int t = 0; t < T::ROWS_PER_WAVE; ++t) {
+        const int row = row0 + t;
+#pragma unroll
+        for (int j = 0; j < T::R; ++j) {
+            const float v = wave_sum(acc[t][j]);
+            if (lane == 0 && row < g.m && j0 + j < g.n) g.C[(size_t)row * g.ldc + j0 + j] = v;
+        }
+    }
+}
+
+}  // namespace gemmf32

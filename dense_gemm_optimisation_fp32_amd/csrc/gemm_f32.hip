@@ -111,6 +111,15 @@ VariantDesc dma_ex_variant(const char *name)
 }
 
 template <class T>
+VariantDesc fewcol_variant(const char *name)
+{
+    return VariantDesc{
+        name, GEMM_F32_KIND_FEWCOL, T::ROWS, T::R, T::KC, T::WAVES, 1, T::THREADS, T::LDS_BYTES, 1,
+        {reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_kernel<T, false>),
+         reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_kernel<T, true>)}};
+}
+
+template <class T>
 VariantDesc skinny_variant(const char *name)
 {
     return VariantDesc{
@@ -152,6 +161,9 @@ enum VariantId {
     V_DMA_128x64x16_S3,
     V_DMA_64x128x16_S2,
     V_DMA_64x128x16_S3,
+    V_FEWCOL_R1,
+    V_FEWCOL_R4,
+    V_FEWCOL_R8,
     V_COUNT
 };
 
@@ -184,6 +196,9 @@ const VariantDesc &variant(int v)
         dma_variant<DmaTile<128, 64, 16, 2, 2, 3>>("dma_128x64x16_w2x2_s3"),
         dma_ex_variant<DmaTile<64, 128, 16, 2, 2, 2>>("dma_64x128x16_w2x2_s2"),
         dma_variant<DmaTile<64, 128, 16, 2, 2, 3>>("dma_64x128x16_w2x2_s3"),
+        fewcol_variant<gemmf32::FewColR1>("fewcol_8x1_k2048"),
+        fewcol_variant<gemmf32::FewColR4>("fewcol_8x4_k2048"),
+        fewcol_variant<gemmf32::FewColR8>("fewcol_8x8_k2048"),
     };
     return table[v];
 }
@@ -349,6 +364,10 @@ struct gemm_f32_plan_impl {
     void *workspace;     // split-k partial sums and arrival counters (few-row path), else NULL
     std::atomic<unsigned> runs{0};   // epochs handed out so far
     int c_store_width = 1;           // C elements per store of the whole-tile kernel
+    // Column sliver: the last sliver_cols columns of C run as a second launch
+    // with a plan of their own (this plan then covers columns [0, n)).
+    gemm_f32_plan_impl *sliver = nullptr;
+    int64_t sliver_col0 = 0;
 };
 
 namespace {
@@ -422,6 +441,12 @@ double estimate_seconds(const Candidate &cand, int per_cu, int per_cu_sk, int64_
     return dp;
 }
 
+// The few-tile, long-k rule of the shape dispatch (below).
+bool few_tile_stream_k(int64_t m, int64_t n, int64_t k, const DeviceFacts &f, bool tail_ok)
+{
+    return tail_ok && 2 * ceil_div(m, 64) * ceil_div(n, 64) < 5 * (int64_t)f.cu_count && k >= 2048;
+}
+
 // Shape dispatch.  Few rows: the bandwidth-bound split-k path.  When even
 // 64 x 64 tiles leave fewer than 2.5 workgroups per CU and k >= 2048,
 // 64 x 64 tiles with stream-K over all tiles (workgroups share the tiles'
@@ -443,12 +468,14 @@ double estimate_seconds(const Candidate &cand, int per_cu, int per_cu_sk, int64_
 // cannot, few-tile shapes take the best data-parallel tile instead.
 // epilogue: the plan fuses the linear-layer epilogue.
 int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFacts &f, bool tail_ok, bool epilogue,
-                   bool *stream_k, int64_t *tail_tiles)
+                   bool *stream_k, int64_t *tail_tiles, double *estimate = nullptr)
 {
     *stream_k = false;
     *tail_tiles = 0;
+    if (estimate) *estimate = 0.0;   // (not estimated for the few-row and few-tile plans)
     if (m <= 32) return V_SKINNY_W16_D4;
-    if (tail_ok && 2 * ceil_div(m, 64) * ceil_div(n, 64) < 5 * (int64_t)f.cu_count && k >= 2048) {
+    if (tail_ok && n <= 8) return n == 1 ? V_FEWCOL_R1 : n <= 4 ? V_FEWCOL_R4 : V_FEWCOL_R8;
+    if (few_tile_stream_k(m, n, k, f, tail_ok)) {
         *stream_k = true;
         return V_DMA_64x64x16_S2;
     }
@@ -478,7 +505,39 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
             *tail_tiles = tail;
         }
     }
+    if (estimate) *estimate = best_t;
     return kCandidate[best].variant;   // 256x128, never skipped, is always weighed
+}
+
+// Column sliver.  When the chosen tile leaves a last tile-column that is at
+// most an eighth full (n mod BN <= BN / 8, and at most 8 columns), every
+// tile of that column runs the whole k-loop for a few columns ("GPU 算子优化中的
+// 数据复用", 10.3: boundary tiles waste work): at 5003 x 4097 x 2049 the
+// 4097th column costs a column of 79 tiles of 64x128, 3 % of them.  The plan
+// can instead cover the first n - r columns (whose tiles may also fill the
+// waves better) and run the last r columns as a second launch on the
+// few-column kernel, which reads A once more: estimated at 4 m k bytes at
+// 5 TB/s plus 3 us of launch.  Returns r, or 0 when one launch is estimated
+// faster.  GEMM_F32_SLIVER=0 turns it off.
+int64_t choose_sliver(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFacts &f)
+{
+    if (env_int("GEMM_F32_SLIVER", 1) == 0 || m <= 32 || n < 512) return 0;
+    bool sk = false;
+    int64_t tail = 0;
+    double t_full = 0.0;
+    const int v = choose_variant(m, n, k, layout_b, f, true, false, &sk, &tail, &t_full);
+    if (sk || t_full <= 0.0) return 0;
+    const int bn = variant(v).bn;
+    const int64_t r = n % bn;
+    if (r == 0 || r * 8 > bn || r > 8) return 0;
+    double t_main = 0.0;
+    choose_variant(m, n - r, k, layout_b, f, true, false, &sk, &tail, &t_main);
+    if (sk || t_main <= 0.0) return 0;
+    const double t_sliver = 4.0 * (double)m * (double)k / 5e12 + 3e-6;
+    if (env_int("GEMM_F32_LOG", 0) >= 2)
+        std::fprintf(stderr, "[gemm_f32] sliver of %lld columns: %.1f + %.1f us against %.1f us in one launch\n",
+                     (long long)r, t_main * 1e6, t_sliver * 1e6, t_full * 1e6);
+    return t_main + t_sliver < t_full ? r : 0;
 }
 
 // Everything a plan needs except its workspace: the kernel, grid and launch
@@ -662,15 +721,41 @@ void plan_attach(gemm_f32_plan_impl *p, void *words, unsigned *counters, size_t 
     p->args.status = counters + n_counters;
 }
 
+// Columns of a column sliver for a plan (0: none): plain products with the
+// shape dispatch's own choices only (no forced variant, stream-K or split).
+int64_t plan_sliver(int forced_variant, int64_t m, int64_t n, int64_t k, int layout_a, int layout_b, int64_t lda,
+                    int64_t ldb, int64_t ldc, int epilogue)
+{
+    if (forced_variant >= 0 || layout_a != GEMM_F32_ROW_MAJOR || epilogue) return 0;
+    if (env_int("GEMM_F32_VARIANT", -1) >= 0 || env_int("GEMM_F32_SK_WGS", 0) > 0 ||
+        env_int("GEMM_F32_SPLIT_K", 0) > 0)
+        return 0;
+    if (gemm_f32_validate_ex(m, n, k, layout_a, layout_b, lda, ldb, ldc) != GEMM_F32_SUCCESS) return 0;
+    int dev = 0;
+    DeviceFacts facts;
+    if (device_facts(&dev, &facts) != GEMM_F32_SUCCESS) return 0;
+    return choose_sliver(m, n, k, layout_b, facts);
+}
+
+// B and C of a plan's sliver: column sliver_col0 of B (row-major: the next
+// element of each k-row; column-major: the next column) and of C.
+const float *sliver_b(const gemm_f32_plan_impl *p, const float *B)
+{
+    return p->layout_b == GEMM_F32_ROW_MAJOR ? B + p->sliver_col0 : B + p->sliver_col0 * p->ldb;
+}
+
 int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int64_t k, int layout_a,
-              int layout_b, int64_t lda, int64_t ldb, int64_t ldc, int epilogue)
+              int layout_b, int64_t lda, int64_t ldb, int64_t ldc, int epilogue, bool allow_sliver = true)
 {
     if (!out) return GEMM_F32_ERR_INVALID_VALUE;
     *out = nullptr;
     gemm_f32_plan p = new (std::nothrow) gemm_f32_plan_impl();
     if (!p) return GEMM_F32_ERR_ALLOC;
+    const int64_t r =
+        allow_sliver ? plan_sliver(forced_variant, m, n, k, layout_a, layout_b, lda, ldb, ldc, epilogue) : 0;
     size_t words = 0, counters = 0;
-    int st = plan_fill(p, forced_variant, m, n, k, layout_a, layout_b, lda, ldb, ldc, epilogue, &words, &counters);
+    int st = plan_fill(p, forced_variant, m, n - r, k, layout_a, layout_b, lda, ldb, ldc, epilogue, &words,
+                       &counters);
     if (st != GEMM_F32_SUCCESS) {
         delete p;
         return st;
@@ -689,6 +774,15 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
         }
         plan_attach(p, p->workspace, reinterpret_cast<unsigned *>(static_cast<char *>(p->workspace) + words),
                     counters);
+    }
+    if (r) {
+        st = make_plan(&p->sliver, -1, m, r, k, layout_a, layout_b, lda, ldb, ldc, epilogue, false);
+        if (st != GEMM_F32_SUCCESS) {
+            if (p->workspace) (void)hipFree(p->workspace);
+            delete p;
+            return st;
+        }
+        p->sliver_col0 = n - r;
     }
     *out = p;
     return GEMM_F32_SUCCESS;
@@ -874,48 +968,66 @@ int gemm_f32_run(gemm_f32_plan p, const float *A, const float *B, float *C, void
     a.A = A;
     a.B = B;
     a.C = C;
-    return launch(p, a, stream);
+    const int st = launch(p, a, stream);
+    if (st != GEMM_F32_SUCCESS || !p->sliver) return st;
+    return gemm_f32_run(p->sliver, A, sliver_b(p, B), C + p->sliver_col0, stream);
 }
 
 int gemm_f32_run_noalloc(int64_t m, int64_t n, int64_t k, int layout_b, int64_t lda, int64_t ldb, int64_t ldc,
                          const float *A, const float *B, float *C, void *stream)
 {
     if (!pointers_ok(A, B, C)) return GEMM_F32_ERR_INVALID_VALUE;
-    gemm_f32_plan_impl p;   // host state on the stack: nothing is allocated
-    size_t words = 0, counters = 0;
-    int st = plan_fill(&p, -1, m, n, k, GEMM_F32_ROW_MAJOR, layout_b, lda, ldb, ldc, 0, &words, &counters);
+    // Host state on the stack, nothing allocated: the plan and, when the
+    // dispatch splits off a column sliver, the sliver's plan.
+    const int64_t r = plan_sliver(-1, m, n, k, GEMM_F32_ROW_MAJOR, layout_b, lda, ldb, ldc, 0);
+    gemm_f32_plan_impl parts[2];
+    size_t words[2] = {0, 0}, counters[2] = {0, 0};
+    int st = plan_fill(&parts[0], -1, m, n - r, k, GEMM_F32_ROW_MAJOR, layout_b, lda, ldb, ldc, 0, &words[0],
+                       &counters[0]);
+    if (st == GEMM_F32_SUCCESS && r)
+        st = plan_fill(&parts[1], -1, m, r, k, GEMM_F32_ROW_MAJOR, layout_b, lda, ldb, ldc, 0, &words[1],
+                       &counters[1]);
     if (st != GEMM_F32_SUCCESS) return st;
-    GemmArgs a = p.args;
-    a.A = A;
-    a.B = B;
-    a.C = C;
-    if (words) {
-        if (words > kScratchWordBytes || counters + 1 > kScratchCounters) return GEMM_F32_ERR_SCRATCH_TOO_SMALL;
-        void *base = nullptr;
-        st = scratch_address(p.device, &base);
+    for (int i = 0; i < (r ? 2 : 1); ++i)
+        if (words[i] > kScratchWordBytes || counters[i] + 1 > kScratchCounters) return GEMM_F32_ERR_SCRATCH_TOO_SMALL;
+    parts[0].sliver_col0 = n - r;
+    for (int i = 0; i < (r ? 2 : 1); ++i) {
+        // The two launches run one after the other on `stream`, so they can
+        // share the scratch area.
+        gemm_f32_plan_impl &p = parts[i];
+        GemmArgs a = p.args;
+        a.A = A;
+        a.B = i ? sliver_b(&parts[0], B) : B;
+        a.C = i ? C + parts[0].sliver_col0 : C;
+        if (words[i]) {
+            void *base = nullptr;
+            st = scratch_address(p.device, &base);
+            if (st != GEMM_F32_SUCCESS) return st;
+            unsigned *ctr = static_cast<unsigned *>(base);
+            a.partial = reinterpret_cast<unsigned long long *>(static_cast<char *>(base) + kScratchCounters * 4);
+            a.arrivals = ctr;
+            a.status = ctr + counters[i];
+            // The counters and the status word start at zero: a fill kernel
+            // on the caller's stream ahead of the product (a kernel, not a
+            // memset, so that the call can be captured in a graph).  The
+            // words need no clearing: each launch tags its words with an
+            // epoch no earlier launch on this device used.
+            const int n_zero = (int)(counters[i] + 1);
+            unsigned *zp = ctr;
+            int zn = n_zero;
+            void *zargs[] = {&zp, &zn};
+            hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&gemmf32::zero_words_kernel),
+                                           dim3((unsigned)((n_zero + 255) / 256)), dim3(256), zargs, 0,
+                                           reinterpret_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return hip_fail(e);
+            unsigned ep = ++g_scratch[p.device].epoch;
+            if (ep == 0) ep = ++g_scratch[p.device].epoch;
+            a.epoch = ep;
+        }
+        st = launch_kernel(&p, a, stream);
         if (st != GEMM_F32_SUCCESS) return st;
-        unsigned *ctr = static_cast<unsigned *>(base);
-        a.partial = reinterpret_cast<unsigned long long *>(static_cast<char *>(base) + kScratchCounters * 4);
-        a.arrivals = ctr;
-        a.status = ctr + counters;
-        // The counters and the status word start at zero: a fill kernel on
-        // the caller's stream ahead of the product (a kernel, not a memset,
-        // so that the call can be captured in a graph).  The words need no
-        // clearing: each call tags its words with an epoch no earlier call
-        // on this device used.
-        const int n_zero = (int)(counters + 1);
-        unsigned *zp = ctr;
-        int zn = n_zero;
-        void *zargs[] = {&zp, &zn};
-        hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&gemmf32::zero_words_kernel),
-                                       dim3((unsigned)((n_zero + 255) / 256)), dim3(256), zargs, 0,
-                                       reinterpret_cast<hipStream_t>(stream));
-        if (e != hipSuccess) return hip_fail(e);
-        unsigned ep = ++g_scratch[p.device].epoch;
-        if (ep == 0) ep = ++g_scratch[p.device].epoch;
-        a.epoch = ep;
     }
-    return launch_kernel(&p, a, stream);
+    return GEMM_F32_SUCCESS;
 }
 
 int gemm_f32_run_ex(gemm_f32_plan p, const float *A, const float *B, float *C, float alpha, float beta,
@@ -935,7 +1047,10 @@ int gemm_f32_run_ex(gemm_f32_plan p, const float *A, const float *B, float *C, f
     a.use_beta = beta != 0.0f ? 1 : 0;
     a.bias = bias;
     a.act = activation;
-    return launch(p, a, stream);
+    const int st = launch(p, a, stream);
+    // (Only plain plans have a sliver, so these are the plain values.)
+    if (st != GEMM_F32_SUCCESS || !p->sliver) return st;
+    return gemm_f32_run(p->sliver, A, sliver_b(p, B), C + p->sliver_col0, stream);
 }
 
 int gemm_f32_destroy(gemm_f32_plan p)
@@ -945,6 +1060,10 @@ int gemm_f32_destroy(gemm_f32_plan p)
     if (p->workspace) {
         hipError_t e = hipFree(p->workspace);
         if (e != hipSuccess) st = hip_fail(e);
+    }
+    if (p->sliver) {
+        const int s2 = gemm_f32_destroy(p->sliver);
+        if (st == GEMM_F32_SUCCESS) st = s2;
     }
     delete p;
     return st;
@@ -978,6 +1097,11 @@ int gemm_f32_describe(gemm_f32_plan p, gemm_f32_info *info)
     }
     info->workgroups_per_cu = wgs;
     info->waves_per_simd = wgs * ((int)p->block / 64) / 4;
+    if (p->sliver) {
+        info->sliver_cols = p->sliver->n;
+        info->sliver_variant = p->sliver->variant;
+        info->sliver_stream_k = p->sliver->args.sk_wgs;
+    }
     return GEMM_F32_SUCCESS;
 }
 
@@ -985,12 +1109,16 @@ int gemm_f32_plan_check(gemm_f32_plan p, int *lost)
 {
     if (!p || !lost) return GEMM_F32_ERR_INVALID_VALUE;
     *lost = 0;
+    if (p->sliver) {
+        const int st = gemm_f32_plan_check(p->sliver, lost);
+        if (st != GEMM_F32_SUCCESS) return st;
+    }
     if (!p->args.status) return GEMM_F32_SUCCESS;
     unsigned v = 0;
     hipError_t e = hipMemcpy(&v, p->args.status, sizeof(v), hipMemcpyDeviceToHost);
     if (e == hipSuccess && v) e = hipMemset(p->args.status, 0, sizeof(v));
     if (e != hipSuccess) return hip_fail(e);
-    *lost = v ? 1 : 0;
+    if (v) *lost = 1;
     return GEMM_F32_SUCCESS;
 }
 

@@ -11,6 +11,7 @@
 #include "mfma_gemm.hpp"
 #include "skinny_gemm.hpp"
 #include "valu_gemm.hpp"
+#include "fewcol_gemm.hpp"
 
 namespace gemmf32 {
 
@@ -39,6 +40,11 @@ using Dma64x128x16S3 = DmaTile<64, 128, 16, 2, 2, 3>;
 // Zero n 32-bit words (the arrival counters of gemm_f32_run_noalloc's
 // scratch area), with vector stores; defined in k_other.hip.
 __global__ void zero_words_kernel(unsigned *p, int n);
+
+// Few-column tiles (columns per workgroup).
+using FewColR1 = FewColTile<1>;
+using FewColR4 = FewColTile<4>;
+using FewColR8 = FewColTile<8>;
 
 // Few-row tiles (wavefronts, k groups in flight, columns).
 using SkinnyW4D4 = SkinnyTile<4, 4, 64>;
@@ -106,7 +112,10 @@ using Skinny16W16D4 = SkinnyTile<16, 4, 16>;
     X2(gemm_skinny_kernel, SkinnyW4D4, false) X2(gemm_skinny_kernel, SkinnyW4D4, true)       \
     X2(gemm_skinny_kernel, SkinnyW8D4, false) X2(gemm_skinny_kernel, SkinnyW8D4, true)       \
     X2(gemm_skinny_kernel, SkinnyW16D4, false) X2(gemm_skinny_kernel, SkinnyW16D4, true)     \
-    X2(gemm_skinny_kernel, Skinny16W16D4, false) X2(gemm_skinny_kernel, Skinny16W16D4, true)
+    X2(gemm_skinny_kernel, Skinny16W16D4, false) X2(gemm_skinny_kernel, Skinny16W16D4, true)     \
+    X2(gemm_fewcol_kernel, FewColR1, false) X2(gemm_fewcol_kernel, FewColR1, true)             \
+    X2(gemm_fewcol_kernel, FewColR4, false) X2(gemm_fewcol_kernel, FewColR4, true)             \
+    X2(gemm_fewcol_kernel, FewColR8, false) X2(gemm_fewcol_kernel, FewColR8, true)
 
 #define GEMMF32_ALL_UNITS(X5, X2, X1)                                                     \
     GEMMF32_UNIT_DMA256(X5, X2, X1) GEMMF32_UNIT_DMA256S4(X5, X2, X1)                     \

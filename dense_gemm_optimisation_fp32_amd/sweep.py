@@ -203,8 +203,8 @@ def main(argv=None):
             w = WORKLOADS[name]
             for v in variants:
                 kind = g.gemm_f32_variant_info(v)["kind"]
-                if (kind == g.GEMM_F32_KIND_SKINNY) != (w.m <= 64):
-                    continue   # the few-row path and the tiled paths serve different shape classes
+                if (kind == g.GEMM_F32_KIND_SKINNY) != (w.m <= 64) or kind == g.GEMM_F32_KIND_FEWCOL:
+                    continue   # the few-row, few-column and tiled paths serve different shape classes
                 info, avg = time_variant(g, torch, w, v, args.steps, args.warmup, args.warmup_s)
                 rec = {"workload": name, "variant": v, "name": info["name"], "kind": info["kind"],
                        "bm": info["bm"], "bn": info["bn"], "bk": info["bk"],

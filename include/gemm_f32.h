@@ -80,7 +80,8 @@ enum gemm_f32_activation {
 enum gemm_f32_kind {
     GEMM_F32_KIND_MFMA = 0,   /* LDS-tiled, wavefront tiles on v_mfma_f32_32x32x2_f32 */
     GEMM_F32_KIND_VALU = 1,   /* LDS-tiled, per-thread register outer product on the vector ALU */
-    GEMM_F32_KIND_SKINNY = 2  /* few-row (memory-bound) path */
+    GEMM_F32_KIND_SKINNY = 2, /* few-row (memory-bound) path */
+    GEMM_F32_KIND_FEWCOL = 3  /* few-column (memory-bound, matrix-vector-like) path */
 };
 
 /* What a plan (or a variant) does; filled by gemm_f32_describe / gemm_f32_variant_info. */
@@ -118,6 +119,15 @@ struct gemm_f32_info {
     int workgroups_per_cu;  /* plan only: resident workgroups per CU (the HIP runtime's
                                occupancy calculator for the launched kernel) */
     int waves_per_simd;     /* plan only: workgroups_per_cu * wavefronts per workgroup / 4 */
+    /* Column sliver (plan only): when the tile the dispatch picks would leave
+     * a last tile-column at most an eighth full, the plan covers the first
+     * n - sliver_cols columns (tiles_n, grid, ... describe that launch) and
+     * runs the last sliver_cols columns as a second launch on the same stream,
+     * with a plan of its own (variant sliver_variant, stream-K over
+     * sliver_stream_k workgroups).  0: one launch. */
+    int64_t sliver_cols;
+    int sliver_variant;
+    int sliver_stream_k;
 };
 
 /*
@@ -148,6 +158,8 @@ int gemm_f32_validate(int64_t m, int64_t n, int64_t k, int layout_b,
  *                             a partial-sum area of 2^31 bytes or more is
  *                             rejected with GEMM_F32_ERR_INVALID_VALUE;
  *   GEMM_F32_STREAMK=0        never choose stream-K automatically;
+ *   GEMM_F32_SLIVER=0         never split off a column sliver (see
+ *                             gemm_f32_info.sliver_cols);
  *   GEMM_F32_NUM_XCD=<count>  the XCD count the rasterisation undoes
  *                             (default: the device's; 1 turns the XCD
  *                             remap off, for measuring it);

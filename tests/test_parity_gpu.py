@@ -311,7 +311,7 @@ DISPATCH_CASES = [
     ((3000, 3000, 3000), "dma_64x64x16_w2x2_s2", 0),
     ((2048, 2048, 2048), "dma_64x128x16_w2x2_s2", 0),
     ((1536, 4096, 4096), "dma_64x128x16_w2x2_s2", 0),
-    ((5003, 4097, 2049), "dma_64x128x16_w2x2_s2", 47),
+    ((5003, 4097, 2049), "dma_128x128x16_w2x2_s3", 0),    # + a one-column sliver (test_column_sliver_plan)
     ((4096, 4608, 4096), "dma_64x64x16_w2x2_s2", 0),
     ((4096, 6144, 4096), "dma_128x128x16_w2x2_s3", 0),
     ((2048, 14336, 4096), "dma_128x128x16_w2x2_s3", 0),
@@ -335,6 +335,7 @@ def test_dispatch_choice(shape, name, tail):
     m, n, k = shape
     info = g.Plan(m, n, k, ROW_MAJOR, k, n, n).info
     assert info["name"] == name
+    assert info["sliver_cols"] == (1 if shape == (5003, 4097, 2049) else 0)
     if tail:
         # one workgroup per CU, at most 8 per split tile
         assert info["stream_k"] == min(256, 8 * tail) and info["stream_k_tiles"] == tail
@@ -382,15 +383,16 @@ def test_stream_k_tail_chosen(layout_b):
 
 
 @pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
-def test_stream_k_tail_64x128_ragged(layout_b):
-    """The ragged shape (boundary tiles on both edges, k = 16 * 128 + 1) runs
-    64x128 tiles with its last wave's 47 tiles split over one workgroup per
-    CU; it matches the oracle (integer inputs bit for bit) and repeats bit
-    for bit."""
+def test_stream_k_tail_64x128_ragged(layout_b, monkeypatch):
+    """Without the column sliver, the ragged shape (boundary tiles on both
+    edges, k = 16 * 128 + 1) runs 64x128 tiles with its last wave's 47 tiles
+    split over one workgroup per CU; it matches the oracle (integer inputs
+    bit for bit) and repeats bit for bit."""
     import dense_gemm_optimisation_fp32_amd as g
 
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the choice was measured on a 256-CU MI355X")
+    monkeypatch.setenv("GEMM_F32_SLIVER", "0")
     m, n, k = 5003, 4097, 2049    # 79 x 33 = 2607 tiles: 2 x 1280 + 47
     print(f"\n[case] 64x128 stream-K tail layout_b={layout_b} shape={(m, n, k)}", flush=True)
     A, B = random_operands(m, n, k, layout_b, "uniform", seed=101)
@@ -551,3 +553,64 @@ def test_binding_matmul_matches_oracle_both_layouts():
     check_close(g.matmul(dA, dB).cpu().numpy(), Cref, S, "matmul row-major B")
     dBt = dB.t().contiguous().t()                      # same values, column-major storage
     check_close(g.matmul(dA, dBt).cpu().numpy(), Cref, S, "matmul column-major B")
+
+
+# Few columns (N <= 8): the matrix-vector-like path, chosen by the shape
+# dispatch; k beyond one LDS chunk (2048) and with a tail, both B layouts.
+FEWCOL_SHAPES = [(5003, 1, 2049), (300, 3, 77), (1000, 4, 4096), (777, 5, 2500), (4096, 8, 4096), (64, 2, 1),
+                 (33, 7, 6000)]
+
+
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+@pytest.mark.parametrize("shape", FEWCOL_SHAPES)
+def test_few_columns_vs_oracle(shape, layout_b):
+    import dense_gemm_optimisation_fp32_amd as g
+
+    m, n, k = shape
+    print(f"\n[case] few columns layout_b={layout_b} shape={shape}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=1700 + k)
+    C, info, outs = run_gemm(A, B, m, n, k, layout_b, repeat=2)
+    assert info["kind"] == g.GEMM_F32_KIND_FEWCOL and info["bn"] >= n
+    assert np.array_equal(outs[0], outs[1])
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    check_close(C, Cref, S, f"few columns {shape}")
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=1800 + k)
+    C, _ = run_gemm(A, B, m, n, k, layout_b)
+    Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    assert np.array_equal(C.astype(np.float64), Cref)
+
+
+def test_few_columns_padded_strides():
+    """NaN padding of A's and B's rows never reaches C; C's padding is kept."""
+    m, n, k = 700, 3, 2100
+    for layout_b in (ROW_MAJOR, COL_MAJOR):
+        lda, ldb, ldc = k + 3, (n if layout_b == ROW_MAJOR else k) + 5, n + 2
+        A, B = random_operands(m, n, k, layout_b, "uniform", seed=1900, lda=lda, ldb=ldb)
+        C, info = run_gemm(A, B, m, n, k, layout_b, lda, ldb, ldc, c_fill=-7.25)
+        Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b, lda, ldb)
+        check_close(C[:, :n], Cref, S, "few columns, padded")
+        assert np.all(C[:-1, n:] == np.float32(-7.25))
+
+
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+def test_column_sliver_plan(layout_b):
+    """A shape whose last tile-column would hold one column runs it as a
+    second launch on the few-column kernel: every element matches the oracle
+    (integer inputs bit for bit) and repeats bit for bit."""
+    import dense_gemm_optimisation_fp32_amd as g
+
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the choice was measured on a 256-CU MI355X")
+    m, n, k = 5003, 4097, 2049
+    print(f"\n[case] column sliver layout_b={layout_b}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "uniform", seed=2000)
+    C, info, outs = run_gemm(A, B, m, n, k, layout_b, repeat=2)
+    assert info["sliver_cols"] == 1 and info["sliver_variant"] == [
+        v for v in range(g.gemm_f32_num_variants()) if g.gemm_f32_variant_info(v)["name"] == "fewcol_8x1_k2048"][0]
+    assert np.array_equal(outs[0], outs[1])
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    check_close(C, Cref, S, "column sliver")
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=2001)
+    C, _ = run_gemm(A, B, m, n, k, layout_b)
+    Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    assert np.array_equal(C.astype(np.float64), Cref)
