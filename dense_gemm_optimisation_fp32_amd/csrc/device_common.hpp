@@ -169,6 +169,16 @@ __device__ __forceinline__ void record_give_up(int budget, unsigned *status)
     if (budget < 0 && status) __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Workgroup barrier without a memory fence: every wavefront has issued all
+// it did before the barrier, and nothing is waited for.  Used before a
+// split tile's arrival count: the partial-sum words need only be issued
+// (their readers wait for each word's tag), so the store round trip a
+// fence would add stays off the critical path.
+__device__ __forceinline__ void issue_barrier()
+{
+    asm volatile("s_barrier" ::: "memory");
+}
+
 // Test hook: fill `chunks` 16-byte LDS chunks with NaN before a kernel's
 // first copy, so that a read of LDS that no copy or store has written yet
 // (a missing wait or barrier) puts NaN into C.

@@ -663,7 +663,7 @@ __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsr
     // Every wavefront has issued its words before the segment counts itself
     // in, so the last segment to arrive finds every word of the others at
     // least in flight.
-    __syncthreads();
+    issue_barrier();
     if (tid == 0) {
         const unsigned before = __hip_atomic_fetch_add(g.arrivals + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool last = before == (unsigned)(nseg - 1);

@@ -230,8 +230,8 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
         if (e < ELEMS && r < g.m && c < g.n) store_tagged_word(g.partial + split * plane + (size_t)r * g.n + c, own[q], g.epoch);
     }
     __shared__ int last;
-    // (Every wavefront has issued its words before the workgroup counts itself in.)
-    __syncthreads();
+    // Every wavefront has issued its words before the workgroup counts itself in.
+    issue_barrier();
     if (tid == 0) {
         const unsigned before =
             __hip_atomic_fetch_add(g.arrivals + rest, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -10,6 +10,8 @@ shapes run in the plan the benchmark times and are compared element by
 element with the full oracle (random and integer-valued inputs), plus a
 closed-form integer product checked on every element.
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -491,12 +493,13 @@ def test_operand_extent_near_limit(name):
 FULL = ["sq256", "sq4096", "sq4096t", "ragged", "ffn", "skinny", "longk"]
 
 
-def record_ratio(what, ratio):
-    """Print a full-size comparison's max error ratio (and append it to the
-    file named by GEMM_F32_PARITY_LOG, when set)."""
+def record_ratio(what, ratio, oracle_s=None):
+    """Print a full-size comparison's max error ratio and the oracle's time
+    (and append them to the file named by GEMM_F32_PARITY_LOG, when set)."""
     import json
     import os
-    line = json.dumps({"case": what, "max_error_ratio": ratio})
+    line = json.dumps({"case": what, "max_error_ratio": ratio, "oracle_s": oracle_s,
+                       "oracle_threads": oracle.num_threads()})
     print(f"\n[parity] {line}", flush=True)
     path = os.environ.get("GEMM_F32_PARITY_LOG")
     if path:
@@ -513,9 +516,11 @@ def test_workload_every_element_vs_oracle(name):
     A, B = workload_operands(w)
     C, info = run_gemm(A, B, w.m, w.n, w.k, w.layout_b)
     assert np.isfinite(C).all()
+    t0 = time.perf_counter()
     Cref, S = oracle.gemm_f64(A, B, w.m, w.n, w.k, w.layout_b)
+    t_oracle = time.perf_counter() - t0
     ratio = check_close(C, Cref, S, f"{name} via {info['name']}")
-    record_ratio(f"{name} {info['name']} random", ratio)
+    record_ratio(f"{name} {info['name']} random", ratio, round(t_oracle, 3))
 
 
 @pytest.mark.parametrize("name", FULL)
