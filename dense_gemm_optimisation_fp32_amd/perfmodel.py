@@ -23,9 +23,14 @@ import math
 
 # MI355X (gfx950) published peaks.
 MI355X_FP32_MATRIX_PEAK = 157.3e12    # FLOP/s, dense FP32 on the matrix cores
-# FLOP/s, published FP32 vector peak.  The vector-ALU kernel here uses only
-# unpacked v_fmac_f32 and was measured at 85 TFLOP/s, above half of this
-# figure, so unpacked FMAs are not limited to half of it on gfx950.
+# FLOP/s, published FP32 vector peak: 256 CUs x 4 SIMDs x 64 lanes x 2 FLOP
+# per 2 cycles x 2.4 GHz.  Unpacked FMAs reach it in their two-operand form:
+# a probe of independent FMA chains (one MI355X, not shipped) issued
+# v_fmac_f32_e32 (VOP2) at 127.6 TFLOP/s with 32 chains per lane (0.81 of
+# this, with the loop's own instructions), i.e. one wavefront instruction
+# every two cycles per SIMD, while the three-operand v_fma_f32 (VOP3) topped
+# out at 75.7 (half the rate).  The vector-ALU kernel here emits only
+# v_fmac_f32_e32 (packed FP32 is disabled in every kernel).
 MI355X_FP32_VECTOR_PEAK = 157.3e12
 MI355X_HBM_BANDWIDTH = 8.0e12         # B/s
 MI355X_CUS = 256
