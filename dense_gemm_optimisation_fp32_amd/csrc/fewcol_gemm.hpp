@@ -32,9 +32,10 @@ struct FewColTile {
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int ROWS_PER_WAVE = 2;
     static constexpr int ROWS = WAVES * ROWS_PER_WAVE;   // rows of C per workgroup
-    static constexpr int KC = 2048;              // k per LDS chunk
+    static constexpr int KC = R_ == 8 ? 1024 : 2048;   // k per LDS chunk (at most 32 KiB of B)
     static constexpr int GROUPS = KC / 256;      // 16-byte loads per lane per row and chunk
-    static constexpr int LDS_BYTES = R * KC * 4;
+    static constexpr int LD = KC + 4;             // LDS floats per column (padded: conflict-free copies)
+    static constexpr int LDS_BYTES = R * LD * 4;
 };
 
 // Workgroup barrier that waits for this wavefront's LDS accesses only
@@ -56,12 +57,59 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// The B chunk into LDS: element (k, column j0 + j) for k < klen and
+// j0 + j < n, zero elsewhere, at bsf[j * LD + k].  Column-major B: 16-byte
+// loads along k of one column, one 16-byte LDS write each.  Row-major B with
+// 4 or 8 columns: 16-byte loads of 4 columns of one k-row, four 4-byte LDS
+// writes (the padded column stride spreads them over the banks).  One
+// column of row-major B: 4-byte loads.  Partial groups (at K, or at N)
+// element by element.
+template <class T, bool B_COL>
+__device__ __forceinline__ void fewcol_copy_b(const GemmArgs &g, __amdgpu_buffer_rsrc_t rb, f32x4 *bs, float *bsf,
+                                              int kc, int klen, int j0, int tid)
+{
+    if constexpr (B_COL) {
+        for (int e = tid; e < T::R * T::KC / 4; e += T::THREADS) {
+            const int j = e / (T::KC / 4), kk = 4 * (e % (T::KC / 4));
+            const bool col_ok = j0 + j < g.n;
+            f32x4 v;
+            if (col_ok && kk + 4 <= klen) {
+                v = buf_load_x4(rb, elem_off(true, j0 + j, g.ldb, kc + kk));
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u] = buf_load_x1(rb, elem_off(col_ok && kk + u < klen, j0 + j, g.ldb, kc + kk + u));
+            }
+            bs[(j * T::LD + kk) / 4] = v;
+        }
+    } else if constexpr (T::R >= 4) {
+        constexpr int Q = T::R / 4;
+        for (int e = tid; e < T::KC * Q; e += T::THREADS) {
+            const int kk = e / Q, c = e % Q;
+            const int col = j0 + 4 * c;
+            f32x4 v;
+            if (kk < klen && col + 4 <= g.n) {
+                v = buf_load_x4(rb, elem_off(true, kc + kk, g.ldb, col));
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u] = buf_load_x1(rb, elem_off(kk < klen && col + u < g.n, kc + kk, g.ldb, col + u));
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) bsf[(4 * c + u) * T::LD + kk] = v[u];
+        }
+    } else {
+        for (int kk = tid; kk < T::KC; kk += T::THREADS)
+            bsf[kk] = buf_load_x1(rb, elem_off(kk < klen && j0 < g.n, kc + kk, g.ldb, j0));
+    }
+}
+
 // Grid: ceil(m / ROWS) row blocks x ceil(n / R) column groups (row block
 // fastest).
+// (Registers are held to four wavefronts per SIMD, 16 per CU, so that enough
+// loads of A are in flight.)
 template <class T, bool B_COL>
-__global__ __launch_bounds__(T::THREADS) void gemm_fewcol_kernel(GemmArgs g)
+__global__ __launch_bounds__(T::THREADS, 4) void gemm_fewcol_kernel(GemmArgs g)
 {
-    __shared__ f32x4 bs[T::R * T::KC / 4];   // [column][k] chunk of B, k-contiguous
+    __shared__ f32x4 bs[T::R * T::LD / 4];   // [column][k] chunk of B, k-contiguous
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -112,13 +160,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_fewcol_kernel(GemmArgs g)
         // in flight (the compiler waits for each load where its value is
         // used).
         fewcol_barrier();   // the previous chunk's LDS reads are done
-        for (int e = tid; e < T::R * T::KC; e += T::THREADS) {
-            const int j = B_COL ? e / T::KC : e % T::R;
-            const int kk = B_COL ? e % T::KC : e / T::R;
-            const bool ok = kk < klen && j0 + j < g.n;
-            const uint32_t off = B_COL ? elem_off(ok, j0 + j, g.ldb, kc + kk) : elem_off(ok, kc + kk, g.ldb, j0 + j);
-            bsf[j * T::KC + kk] = buf_load_x1(rb_, off);
-        }
+        fewcol_copy_b<T, B_COL>(g, rb_, bs, bsf, kc, klen, j0, tid);
         fewcol_barrier();
 
 #pragma unroll
@@ -126,7 +168,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_fewcol_kernel(GemmArgs g)
             const int kk = 4 * lane + 256 * q;
 #pragma unroll
             for (int j = 0; j < T::R; ++j) {
-                const f32x4 b = bs[(j * T::KC + kk) / 4];
+                const f32x4 b = bs[(j * T::LD + kk) / 4];
 #pragma unroll
                 for (int t = 0; t < T::ROWS_PER_WAVE; ++t)
 #pragma unroll

@@ -198,7 +198,7 @@ const VariantDesc &variant(int v)
         dma_variant<DmaTile<64, 128, 16, 2, 2, 3>>("dma_64x128x16_w2x2_s3"),
         fewcol_variant<gemmf32::FewColR1>("fewcol_8x1_k2048"),
         fewcol_variant<gemmf32::FewColR4>("fewcol_8x4_k2048"),
-        fewcol_variant<gemmf32::FewColR8>("fewcol_8x8_k2048"),
+        fewcol_variant<gemmf32::FewColR8>("fewcol_8x8_k1024"),
     };
     return table[v];
 }
