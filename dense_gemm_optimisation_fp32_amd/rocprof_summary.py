@@ -55,6 +55,9 @@ def short_name(kernel: str) -> str:
     m = re.search(r"MfmaTile<(\d+), (\d+), (\d+), \d+, \d+>", k) or re.search(r"MfmaTileILi(\d+)ELi(\d+)ELi(\d+)", k)
     if m and "gemm_mfma_kernel" in k:
         return f"mfma_{m.group(1)}x{m.group(2)}x{m.group(3)}"
+    m = re.search(r"FewColTile<(\d+)>, (true|false)", k) or re.search(r"FewColTileILi(\d+)EEELb([01])", k)
+    if m:
+        return f"fewcol_r{m.group(1)}" + ("_bcol" if m.group(2) in ("true", "1") else "")
     if "gemm_valu_kernel" in k:
         return "valu_128x128x8"
     if "zero_words_kernel" in k:
