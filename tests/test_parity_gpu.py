@@ -619,3 +619,38 @@ def test_column_sliver_plan(layout_b):
     C, _ = run_gemm(A, B, m, n, k, layout_b)
     Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
     assert np.array_equal(C.astype(np.float64), Cref)
+
+
+# Seeded random shapes through the default dispatch (every path the shape
+# classes select: few rows, few columns, few tiles with stream-K, column
+# slivers, the whole-tile candidates), both B layouts, every element.
+def _random_shapes(count, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        kind = rng.integers(0, 4)
+        if kind == 0:      # few rows or few columns
+            m, n = (int(rng.integers(1, 33)), int(rng.integers(1, 2049))) if rng.random() < 0.5 else \
+                   (int(rng.integers(33, 3000)), int(rng.integers(1, 9)))
+        elif kind == 1:    # a few tiles
+            m, n = int(rng.integers(33, 700)), int(rng.integers(9, 700))
+        else:              # many tiles, ragged edges
+            m, n = int(rng.integers(700, 2600)), int(rng.integers(700, 2600))
+        k = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(300, 2200)), int(rng.integers(2048, 4500))]))
+        out.append((m, n, k))
+    return out
+
+
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+@pytest.mark.parametrize("shape", _random_shapes(16, 2024))
+def test_random_shapes_default_plan(shape, layout_b):
+    m, n, k = shape
+    print(f"\n[case] random shape {shape} layout_b={layout_b}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=3000 + m + n + k)
+    C, info = run_gemm(A, B, m, n, k, layout_b)
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    check_close(C, Cref, S, f"random {shape} via {info['name']} (sliver {info['sliver_cols']})")
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=4000 + m + n + k)
+    C, _ = run_gemm(A, B, m, n, k, layout_b)
+    Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    assert np.array_equal(C.astype(np.float64), Cref)
