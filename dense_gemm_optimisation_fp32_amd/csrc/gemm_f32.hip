@@ -441,19 +441,69 @@ double estimate_seconds(const Candidate &cand, int per_cu, int per_cu_sk, int64_
     return dp;
 }
 
+// Few tiles on the few-row kernel.  When the tiled plans leave most CUs
+// idle, 16-row tiles give 4 to 16 times as many workgroups as 64 x 64 tiles,
+// and the k split over a workgroup's wavefronts keeps all four SIMDs of each
+// CU on one tile ("GEMM 性能优化", Wave 模型: a wave that fills the GPU).
+// T16 / T64: the number of 16 x 16 / 16 x 64 tiles.  16 x 16 tiles while
+// T16 <= CUs (k < 2048, or T16 <= CUs / 2 with the k split over up to 8
+// workgroups that bring the grid to one workgroup per CU; at most 3072 k per
+// tile otherwise); then 16 x 64 tiles with 16 wavefronts and the same k
+// split; then 16 x 64 tiles with 8 wavefronts while T64 is within one
+// workgroup per CU, or two for k in [512, 4096], or three for k in [512,
+// 2048] (row-major B; column-major B, whose columns the few-row kernel reads
+// less evenly, up to one, and only to k = 2048 unless T64 <= CUs / 2).  Measured on one MI355X (us, this rule's plan / the tiled
+// or stream-K plan it replaces): 256x256x256 5.5 / 7.6, 128x512x1024 5.6 /
+// 21.2, 64x256x4096 6.8 / 25.4, 128x512x4096 10.2 / 26.6, 256x256x16384
+// 23.9 / 80.7, 300x700x1500 12.0 / 42.3, 640x320x1024 7.7 / 21.3,
+// 512x512x8192 39.9 / 54.0, 800x600x3000 33.8 / 44.7, 768x768x1024 17.7 /
+// 28.3; the tiled plans stay ahead from 1024x1024 (1024 tiles of 16 x 64)
+// and on 768x768x4096 (57.1 / 61.4 on 16 x 64 tiles).  Returns the variant
+// and *split, its k-split count, or -1.
+int few_tile_rows(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFacts &f, int *split)
+{
+    const int64_t cus = f.cu_count;
+    const int64_t t16 = ceil_div(m, 16) * ceil_div(n, 16);
+    const int64_t t64 = ceil_div(m, 16) * ceil_div(n, 64);
+    auto fill = [&](int64_t tiles) { return (int)std::max<int64_t>(1, std::min<int64_t>(8, cus / tiles)); };
+    if (2 * t16 <= cus) {
+        *split = k < 2048 ? 1 : fill(t16);
+        return V_SKINNY16_W16_D4;
+    }
+    if (t16 <= cus && k <= 3072) {
+        *split = 1;
+        return V_SKINNY16_W16_D4;
+    }
+    if (t16 <= cus) {
+        *split = fill(t64);
+        return V_SKINNY_W16_D4;
+    }
+    const bool w8 = layout_b == GEMM_F32_ROW_MAJOR
+                        ? t64 <= cus || (t64 <= 2 * cus && k >= 512 && k <= 4096) ||
+                              (t64 <= 3 * cus && k >= 512 && k <= 2048)
+                        : 2 * t64 <= cus || (t64 <= cus && k <= 2048);
+    if (w8) {
+        *split = k < 2048 ? 1 : fill(t64);
+        return V_SKINNY_W8_D4;
+    }
+    return -1;
+}
+
 // The few-tile, long-k rule of the shape dispatch (below).
 bool few_tile_stream_k(int64_t m, int64_t n, int64_t k, const DeviceFacts &f, bool tail_ok)
 {
     return tail_ok && 2 * ceil_div(m, 64) * ceil_div(n, 64) < 5 * (int64_t)f.cu_count && k >= 2048;
 }
 
-// Shape dispatch.  Few rows: the bandwidth-bound split-k path.  When even
+// Shape dispatch.  Few rows: the bandwidth-bound split-k path.  Few tiles:
+// the few-row kernel on 16-row tiles (few_tile_rows).  When even
 // 64 x 64 tiles leave fewer than 2.5 workgroups per CU and k >= 2048,
 // 64 x 64 tiles with stream-K over all tiles (workgroups share the tiles'
 // k-slabs) fill the GPU.  Measured (TFLOPS; the best data-parallel plan /
 // stream-K over 64x64 tiles): 1024x1024x8192 ~64 / 118.2; 1024x1024x4096
 // ~63 / 110.0; 1024x1024x2048 62.5 / 94.2; 512x512x8192 16.3 / 76.3;
-// 256x256x4096 6.0 / 20.2; and from two to 2.5 tiles per CU, where a
+// 256x256x4096 6.0 / 20.2 (these two now run faster on the few-row kernel,
+// the first with row-major B only); and from two to 2.5 tiles per CU, where a
 // data-parallel plan leaves the CUs unevenly loaded: 2048x1024x4096 (512
 // tiles) 115.2 / 122.1, 1280x1792x4096 (560) 90.6 / 116.0, 1536x1536x4096
 // (576) 99.7 / 120.9, 756x3053x6144 (576) 97.7 / 119.6, 702x3590x4096 (627)
@@ -468,13 +518,22 @@ bool few_tile_stream_k(int64_t m, int64_t n, int64_t k, const DeviceFacts &f, bo
 // cannot, few-tile shapes take the best data-parallel tile instead.
 // epilogue: the plan fuses the linear-layer epilogue.
 int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFacts &f, bool tail_ok, bool epilogue,
-                   bool *stream_k, int64_t *tail_tiles, double *estimate = nullptr)
+                   bool *stream_k, int64_t *tail_tiles, double *estimate = nullptr, int *split = nullptr)
 {
     *stream_k = false;
     *tail_tiles = 0;
     if (estimate) *estimate = 0.0;   // (not estimated for the few-row and few-tile plans)
+    if (split) *split = 0;           // few-row plans: their k-split count (0: the automatic count)
     if (m <= 32) return V_SKINNY_W16_D4;
     if (tail_ok && n <= 8) return n == 1 ? V_FEWCOL_R1 : n <= 4 ? V_FEWCOL_R4 : V_FEWCOL_R8;
+    if (tail_ok) {
+        int s = 0;
+        const int v = few_tile_rows(m, n, k, layout_b, f, &s);
+        if (v >= 0) {
+            if (split) *split = s;
+            return v;
+        }
+    }
     if (few_tile_stream_k(m, n, k, f, tail_ok)) {
         *stream_k = true;
         return V_DMA_64x64x16_S2;
@@ -565,9 +624,12 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
     int v = forced_variant;
     bool auto_stream_k = false;
     int64_t auto_tail = 0;
+    int auto_split = 0;
     if (v < 0) {
         v = env_int("GEMM_F32_VARIANT", -1);
-        if (v < 0 || v >= V_COUNT) v = choose_variant(m, n, k, layout_b, facts, !ex, epilogue != 0, &auto_stream_k, &auto_tail);
+        if (v < 0 || v >= V_COUNT)
+            v = choose_variant(m, n, k, layout_b, facts, !ex, epilogue != 0, &auto_stream_k, &auto_tail, nullptr,
+                               &auto_split);
         if (ex && !variant(v).fn_ex[0][0][0]) v = V_DMA_64x64x16_S2;
     }
     const VariantDesc &d = variant(v);
@@ -633,10 +695,14 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
     p->block = (unsigned)d.threads;
     p->workspace = nullptr;
     if (d.kind == GEMM_F32_KIND_SKINNY) {
-        // Split k across workgroups until about 16 wavefronts per CU are in
-        // flight; each split is a whole number of 16-k groups.
+        // Split k across workgroups up to 16 wavefronts per CU (rounded
+        // down: a few workgroups past one per CU make a second wave, e.g.
+        // 200x200x3000 on 16x64 tiles: 260 workgroups 15.8 us, 208 9.9 us),
+        // or as the few-tile rule chose; each split is a whole number of 16-k
+        // groups.
         const int64_t per_split = (int64_t)a.tiles_m * a.tiles_n;
-        int64_t split = ceil_div(16 * (int64_t)facts.cu_count, per_split * (d.threads / 64));
+        int64_t split = auto_split > 0 ? auto_split
+                                       : std::max<int64_t>(1, 16 * (int64_t)facts.cu_count / (per_split * (d.threads / 64)));
         split = env_int("GEMM_F32_SPLIT_K", (int)split);   // tuning override
         split = split < 1 ? 1 : split;
         const int64_t max_split = ceil_div(k, 64);

@@ -285,7 +285,7 @@ def test_stream_k_hybrid_forced(variant, layout_b, wgs, shared, monkeypatch):
 def test_stream_k_chosen_for_few_tiles_long_k(layout_b):
     """Shapes with too few tiles for the GPU and a long k get a stream-K plan
     by default; it matches the oracle (integer inputs bit for bit)."""
-    for (m, n, k) in [(256, 256, 4096), (1024, 1024, 8192), (512, 512, 8192), (1024, 1024, 2048),
+    for (m, n, k) in [(2048, 512, 4096), (1024, 1024, 8192), (640, 2048, 8192), (1024, 1024, 2048),
                       (768, 700, 8192), (1536, 1536, 4096)]:
         print(f"\n[case] default stream-K layout_b={layout_b} shape={(m, n, k)}", flush=True)
         A, B = random_operands(m, n, k, layout_b, "normal1", seed=95)
@@ -298,6 +298,58 @@ def test_stream_k_chosen_for_few_tiles_long_k(layout_b):
         C, _ = run_gemm(A, B, m, n, k, layout_b)
         Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
         assert np.array_equal(C.astype(np.float64), Cref)
+
+
+# Few tiles on the few-row kernel: (shape, the plan with row-major B, with
+# column-major B), a plan being (variant, k-split count), or None for a tiled
+# plan.  Measured on one MI355X, 256 CUs.
+FEW_TILE_CASES = [
+    ((256, 256, 256), ("skinny_16x16_w16_d4", 1), ("skinny_16x16_w16_d4", 1)),
+    ((64, 256, 4096), ("skinny_16x16_w16_d4", 4), ("skinny_16x16_w16_d4", 4)),
+    ((64, 128, 8192), ("skinny_16x16_w16_d4", 8), ("skinny_16x16_w16_d4", 8)),
+    ((200, 200, 3000), ("skinny_16x16_w16_d4", 1), ("skinny_16x16_w16_d4", 1)),
+    ((128, 512, 4096), ("skinny_16x64_w16_d4", 4), ("skinny_16x64_w16_d4", 4)),
+    ((40, 1000, 5000), ("skinny_16x64_w16_d4", 5), ("skinny_16x64_w16_d4", 5)),
+    ((300, 700, 1500), ("skinny_16x64_w8_d4", 1), ("skinny_16x64_w8_d4", 1)),
+    ((300, 300, 3000), ("skinny_16x64_w8_d4", 2), ("skinny_16x64_w8_d4", 2)),
+    ((800, 600, 3000), ("skinny_16x64_w8_d4", 1), None),
+    ((768, 768, 1024), ("skinny_16x64_w8_d4", 1), None),
+    ((512, 512, 8192), ("skinny_16x64_w8_d4", 1), None),
+    ((1024, 1024, 1024), None, None),
+]
+
+
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+@pytest.mark.parametrize("shape,row_plan,col_plan", FEW_TILE_CASES)
+def test_few_tile_rows_plan(shape, row_plan, col_plan, layout_b):
+    """Shapes with few tiles run the few-row kernel on 16-row tiles with the
+    k-split the shape dispatch chose; every element matches the oracle
+    (integer inputs bit for bit) and runs repeat bit for bit."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the choices were measured on a 256-CU MI355X")
+    m, n, k = shape
+    want = row_plan if layout_b == ROW_MAJOR else col_plan
+    print(f"\n[case] few tiles layout_b={layout_b} shape={shape} plan={want}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=1700 + m + k)
+    C, info, outs = run_gemm(A, B, m, n, k, layout_b, repeat=2)
+    if want is None:
+        assert info["kind"] == 0 and info["name"].startswith("dma_")
+    else:
+        assert (info["name"], info["split_k"]) == want
+        assert info["grid"] == info["tiles_m"] * info["tiles_n"] * want[1]
+        if want[1] > 1:
+            assert info["grid"] <= 256       # the split fills one workgroup per CU at most
+    assert np.array_equal(outs[0], outs[1])
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    check_close(C, Cref, S, f"{info['name']} split {info['split_k']} {shape}")
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=1800 + m + k)
+    C, _ = run_gemm(A, B, m, n, k, layout_b)
+    Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    assert np.array_equal(C.astype(np.float64), Cref)
+    # the linear-layer plans (no few-row kernel for them) stay tiled
+    import dense_gemm_optimisation_fp32_amd as g
+    ldb = n if layout_b == ROW_MAJOR else k
+    assert g.Plan(m, n, k, layout_b, k, ldb, n, epilogue=1).info["name"].startswith("dma_")
 
 
 # The shape dispatch's choice on the shapes it was measured on (one MI355X,
