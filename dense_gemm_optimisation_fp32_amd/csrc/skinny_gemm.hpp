@@ -46,7 +46,15 @@ struct SkinnyTile {
     static constexpr int BM = 16, BN = BN_, KQ = 16;  // rows, columns, k per load group
     static constexpr int NB = BN / 16;                // MFMA blocks per tile
     static constexpr int DEPTH = DEPTH_;              // k groups in flight per wavefront
+    static constexpr int SKEW = NB == 4 ? 1 : 16;     // LDS offset per 4 rows of the reduction
+    static constexpr int RED = BM * BN + 3 * SKEW;    // LDS floats per wavefront in the reduction
 };
+
+template <class T>
+__device__ __forceinline__ int red_index(int r, int c)
+{
+    return r * T::BN + c + (r >> 2) * T::SKEW;
+}
 
 // Loads of one 16-k group for lane (j, h): A[row][kq+4h .. +3] and the B
 // values of the 4 k-steps.  NB = 4: b[t][nb] (row-major B) or b[nb][t]
@@ -114,7 +122,7 @@ __device__ __forceinline__ void skinny_mfma(const f32x4 &a, const f32x4 (&b)[T::
 template <class T, bool B_COL>
 __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
 {
-    __shared__ float red[T::WAVES][T::BM * T::BN];
+    __shared__ float red[T::WAVES][T::RED];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -153,6 +161,9 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
     // runs a whole number of passes; the groups past the range load zeros,
     // so every load is unconditional and in group order, and the counter
     // wait before each group's MFMAs lets the DEPTH - 1 later groups fly.
+    // Only the last pass can hold such groups, and their MFMAs are skipped
+    // (a wavefront-uniform branch): with short k-shares (16 k per wavefront
+    // at 256^3) they would be most of the matrix-core work.
     constexpr int D = T::DEPTH;
     const int kspan = max(0, kw1 - kw0);
     const int G = kspan / T::KQ;
@@ -174,8 +185,15 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        const int last0 = (passes - 1) * D;
+        if (last0 + D <= G) {
 #pragma unroll
-        for (int u = 0; u < D; ++u) skinny_mfma<T, B_COL>(a[u], b[u], acc);
+            for (int u = 0; u < D; ++u) skinny_mfma<T, B_COL>(a[u], b[u], acc);
+        } else {
+#pragma unroll
+            for (int u = 0; u < D; ++u)
+                if (last0 + u < G) skinny_mfma<T, B_COL>(a[u], b[u], acc);
+        }
     }
     // The partial group at the end of the range, element by element.
     if (G * T::KQ < kspan) {
@@ -185,11 +203,14 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
     }
 
     // Add the wavefronts' shares in wavefront order.  Element (r, c) of the
-    // 16 x BN tile: r = 4*h + v, c = NB*j + nb.
+    // 16 x BN tile (r = 4*h + v, c = NB*j + nb) sits at r*BN + c +
+    // (r/4)*SKEW in LDS: the skew puts the 64 lanes of each accumulator
+    // write on distinct banks (pairs on 32 banks), and the reads below,
+    // consecutive c of one row, stay contiguous.
 #pragma unroll
     for (int nb = 0; nb < T::NB; ++nb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[wave][(4 * h + v) * T::BN + T::NB * j + nb] = acc[nb][v];
+        for (int v = 0; v < 4; ++v) red[wave][red_index<T>(4 * h + v, T::NB * j + nb)] = acc[nb][v];
     __syncthreads();
 
     constexpr int ELEMS = T::BM * T::BN;
@@ -200,9 +221,10 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
         const int e = tid + q * T::THREADS;
         float s = 0.0f;
         if (e < ELEMS) {
-            s = red[0][e];
+            const int x = red_index<T>(e / T::BN, e % T::BN);
+            s = red[0][x];
 #pragma unroll
-            for (int w = 1; w < T::WAVES; ++w) s += red[w][e];
+            for (int w = 1; w < T::WAVES; ++w) s += red[w][x];
         }
         own[q] = s;
     }
