@@ -46,14 +46,35 @@ struct SkinnyTile {
     static constexpr int BM = 16, BN = BN_, KQ = 16;  // rows, columns, k per load group
     static constexpr int NB = BN / 16;                // MFMA blocks per tile
     static constexpr int DEPTH = DEPTH_;              // k groups in flight per wavefront
-    static constexpr int SKEW = NB == 4 ? 1 : 16;     // LDS offset per 4 rows of the reduction
-    static constexpr int RED = BM * BN + 3 * SKEW;    // LDS floats per wavefront in the reduction
+    static constexpr int RED = BN == 64 ? 1046 : 304;   // LDS floats per wavefront in the reduction
 };
 
+// LDS position of element (r, c) of a wavefront's 16 x BN share in the
+// reduction.  An accumulator write puts lanes (h, j) = (l / 16, l % 16) at
+// row 4h + v, column NB*j + nb, and LDS serves 32 lanes per cycle from 32
+// banks: for BN = 16 the 16 columns of two row groups land 16 banks apart;
+// for BN = 64 (rows 65 floats apart) the columns 4j (8 banks, twice) are
+// skewed by one bank from column 32 on and the row groups by two more.  The
+// reads, consecutive c of one row, stay on distinct banks.
 template <class T>
-__device__ __forceinline__ int red_index(int r, int c)
+constexpr __host__ __device__ int red_index(int r, int c)
 {
-    return r * T::BN + c + (r >> 2) * T::SKEW;
+    if constexpr (T::BN == 64) return r * 65 + c + (c >> 5) + 2 * (r >> 2);
+    else return r * 16 + c + 16 * (r >> 2);
+}
+
+// Every element of the tile has a position of its own inside RED.
+template <class T>
+constexpr bool red_index_one_to_one()
+{
+    bool used[T::RED] = {};
+    for (int r = 0; r < T::BM; ++r)
+        for (int c = 0; c < T::BN; ++c) {
+            const int x = red_index<T>(r, c);
+            if (x < 0 || x >= T::RED || used[x]) return false;
+            used[x] = true;
+        }
+    return true;
 }
 
 // Loads of one 16-k group for lane (j, h): A[row][kq+4h .. +3] and the B
@@ -122,6 +143,7 @@ __device__ __forceinline__ void skinny_mfma(const f32x4 &a, const f32x4 (&b)[T::
 template <class T, bool B_COL>
 __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
 {
+    static_assert(red_index_one_to_one<T>(), "reduction layout");
     __shared__ float red[T::WAVES][T::RED];
 
     const int tid = threadIdx.x;
@@ -202,11 +224,9 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
         skinny_mfma<T, B_COL>(at, bt, acc);
     }
 
-    // Add the wavefronts' shares in wavefront order.  Element (r, c) of the
-    // 16 x BN tile (r = 4*h + v, c = NB*j + nb) sits at r*BN + c +
-    // (r/4)*SKEW in LDS: the skew puts the 64 lanes of each accumulator
-    // write on distinct banks (pairs on 32 banks), and the reads below,
-    // consecutive c of one row, stay contiguous.
+    // Add the wavefronts' shares in wavefront order (element (r, c) of the
+    // 16 x BN tile: r = 4*h + v, c = NB*j + nb; LDS positions by red_index,
+    // free of bank conflicts).
 #pragma unroll
     for (int nb = 0; nb < T::NB; ++nb)
 #pragma unroll
