@@ -693,6 +693,29 @@ def _random_shapes(count, seed):
     return out
 
 
+def _random_small_shapes(count, seed):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 900)), int(rng.integers(1, 900)), int(rng.integers(1, 5000))) for _ in range(count)]
+
+
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+@pytest.mark.parametrize("shape", _random_small_shapes(40, 7))
+def test_random_small_shapes_default_plan(shape, layout_b):
+    """Small seeded random shapes (ragged in every dimension) through the
+    default dispatch: few-row, few-column, few-tile and tiled plans alike
+    match the oracle on every element, integer inputs bit for bit."""
+    m, n, k = shape
+    print(f"\n[case] random small shape {shape} layout_b={layout_b}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=5000 + m + n + k)
+    C, info = run_gemm(A, B, m, n, k, layout_b)
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    check_close(C, Cref, S, f"random small {shape} via {info['name']} split {info['split_k']}")
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=6000 + m + n + k)
+    C, _ = run_gemm(A, B, m, n, k, layout_b)
+    Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    assert np.array_equal(C.astype(np.float64), Cref)
+
+
 @pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
 @pytest.mark.parametrize("shape", _random_shapes(16, 2024))
 def test_random_shapes_default_plan(shape, layout_b):

@@ -43,6 +43,7 @@ def _both(m, n, k, layout_b, seed):
 @pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
 @pytest.mark.parametrize("first,second,kind", [
     ((16, 4096, 4096), (16, 300, 2000), "split_k"),       # few rows: split-k partial sums
+    ((64, 256, 4096), (64, 200, 3000), "split_k"),        # few tiles on 16x16 tiles, k split 4 ways
     ((1024, 1024, 8192), (1200, 700, 3000), "stream_k"),  # few tiles, long k: stream-K
     ((513, 257, 1000), (300, 520, 77), "tiles"),          # whole tiles, no scratch
 ])
