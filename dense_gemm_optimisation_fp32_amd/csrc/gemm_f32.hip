@@ -164,6 +164,10 @@ enum VariantId {
     V_FEWCOL_R1,
     V_FEWCOL_R4,
     V_FEWCOL_R8,
+    V_DMA_256x256x16_W24_S4,
+    V_DMA_256x256x16_W42_S4,
+    V_DMA_256x256x16_W42_S2,
+    V_DMA_256x256x16_W44_S4,
     V_COUNT
 };
 
@@ -199,6 +203,10 @@ const VariantDesc &variant(int v)
         fewcol_variant<gemmf32::FewColR1>("fewcol_8x1_k2048"),
         fewcol_variant<gemmf32::FewColR4>("fewcol_8x4_k2048"),
         fewcol_variant<gemmf32::FewColR8>("fewcol_8x8_k1024"),
+        dma_variant<DmaTile<256, 256, 16, 2, 4, 4>>("dma_256x256x16_w2x4_s4"),
+        dma_ex_variant<DmaTile<256, 256, 16, 4, 2, 4>>("dma_256x256x16_w4x2_s4"),
+        dma_variant<DmaTile<256, 256, 16, 4, 2, 2>>("dma_256x256x16_w4x2_s2"),
+        dma_variant<DmaTile<256, 256, 16, 4, 4, 4>>("dma_256x256x16_w4x4_s4"),
     };
     return table[v];
 }
@@ -234,21 +242,22 @@ struct Candidate {
 // tail_extra: 64x64 tails after full waves ran 0.03 to 0.09 of a wave over
 // the count (8 tiles: 0.17 against 0.14, 161: 0.23 against 0.14, 512: 0.32
 // against 0.25).
-// 256x256 with four LDS stages holds one workgroup per CU (256 accumulators
-// per lane), so its waves quantise coarsely, but on whole waves it leads:
-// 4096^3 147.9-148.9 TFLOPS against 147.5-147.8 for 256x128, FFN
-// 149.0-149.5 against 147.9-148.3, 8192^3 149.7-150.2 against 147.6-147.9
-// (same box, three repeats).  With column-major A it leads too (4096^3
-// 147.6-148.1 against 146.5-147.2, FFN 148.9-149.3 against 147.9-148.2);
-// with column-major B it trails (4096^3: 144.9-145.0 against 146.5), and
-// with the bias + GELU epilogue as well (FFN 146.5-146.7 against
-// 147.3-147.4), so plans with column-major B or the epilogue skip it.
+// 256x256 holds one workgroup per CU, so its waves quantise coarsely, but on
+// whole waves it leads.  Its eight wavefronts (4 x 2, 64 x 128 each, two per
+// SIMD) run ahead of four (2 x 2, 128 x 128, one per SIMD), whose stalls at
+// the slab barrier and LDS reads nothing covers (one MI355X, TFLOPS, median
+// of three interleaved runs; 8 waves / 4 waves / 256x128): 4096^3 149.3 /
+// 148.6 / 148.1, FFN 150.7 / 149.8 / 149.6, column-major B 149.9 / 145.6 /
+// 147.3; column-major A 4096^3 148.7 / 146.8-147.3 / 145.5-146.1, FFN 149.6
+// / 148.2-148.5 / 147.2-147.4; bias + GELU epilogue, FFN 147.9-148.2 /
+// 145.9-146.1 / 145.7-145.8, column-major B 146.6-146.9 / 141.3 / 144.1-144.3.
+// So it is weighed for every layout and for the epilogue.
 constexpr int kCandidates = 5;
 constexpr Candidate kCandidate[kCandidates] = {{V_DMA_256x128x16_S3, 147.5, 0.94, 0.0, true, 0.25, 4096},
                                                {V_DMA_128x128x16_S3, 147.0, 0.91, 0.0, false, 0.0, 0},
                                                {V_DMA_64x128x16_S2, 142.0, 0.92, 0.0, true, 0.1, 2048},
                                                {V_DMA_64x64x16_S2, 136.0, 0.92, 0.05, false, 0.0, 0},
-                                               {V_DMA_256x256x16_S4, 148.8, 1.0, 0.0, false, 0.0, 0, false, false}};
+                                               {V_DMA_256x256x16_W42_S4, 149.5, 1.0, 0.0, false, 0.0, 0}};
 
 struct DeviceFacts {
     int status = -1;  // -1: not queried yet, else a gemm_f32_status

@@ -36,6 +36,10 @@ using Dma128x64x16S2 = DmaTile<128, 64, 16, 2, 2, 2>;
 using Dma128x64x16S3 = DmaTile<128, 64, 16, 2, 2, 3>;
 using Dma64x128x16S2 = DmaTile<64, 128, 16, 2, 2, 2>;
 using Dma64x128x16S3 = DmaTile<64, 128, 16, 2, 2, 3>;
+using Dma256x256x16W24S4 = DmaTile<256, 256, 16, 2, 4, 4>;
+using Dma256x256x16W42S4 = DmaTile<256, 256, 16, 4, 2, 4>;
+using Dma256x256x16W42S2 = DmaTile<256, 256, 16, 4, 2, 2>;
+using Dma256x256x16W44S4 = DmaTile<256, 256, 16, 4, 4, 4>;
 
 // Zero n 32-bit words (the arrival counters of gemm_f32_run_noalloc's
 // scratch area), with vector stores; defined in k_other.hip.
@@ -102,6 +106,12 @@ using Skinny16W16D4 = SkinnyTile<16, 4, 16>;
     GEMMF32_DMA_BASE(X5, X2, Dma64x128x16S2) GEMMF32_DMA_WIDE(X5, Dma64x128x16S2) \
     GEMMF32_DMA_EX(X5, Dma64x128x16S2) GEMMF32_DMA_EX_WIDE(X5, Dma64x128x16S2) \
     GEMMF32_DMA_BASE(X5, X2, Dma64x128x16S3) GEMMF32_DMA_WIDE(X5, Dma64x128x16S3)
+#define GEMMF32_UNIT_DMA256W8(X5, X2, X1)                         \
+    GEMMF32_DMA_BASE(X5, X2, Dma256x256x16W24S4) GEMMF32_DMA_WIDE(X5, Dma256x256x16W24S4) \
+    GEMMF32_DMA_BASE(X5, X2, Dma256x256x16W42S4) GEMMF32_DMA_WIDE(X5, Dma256x256x16W42S4) \
+    GEMMF32_DMA_EX(X5, Dma256x256x16W42S4) GEMMF32_DMA_EX_WIDE(X5, Dma256x256x16W42S4) \
+    GEMMF32_DMA_BASE(X5, X2, Dma256x256x16W42S2) GEMMF32_DMA_WIDE(X5, Dma256x256x16W42S2) \
+    GEMMF32_DMA_BASE(X5, X2, Dma256x256x16W44S4) GEMMF32_DMA_WIDE(X5, Dma256x256x16W44S4)
 #define GEMMF32_UNIT_OTHER(X5, X2, X1)                            \
     X2(gemm_mfma_kernel, Reg256x256x16, false) X2(gemm_mfma_kernel, Reg256x256x16, true) \
     X2(gemm_mfma_kernel, Reg128x128x16, false) X2(gemm_mfma_kernel, Reg128x128x16, true) \
@@ -121,7 +131,7 @@ using Skinny16W16D4 = SkinnyTile<16, 4, 16>;
     GEMMF32_UNIT_DMA256(X5, X2, X1) GEMMF32_UNIT_DMA256S4(X5, X2, X1)                     \
     GEMMF32_UNIT_DMA256x128(X5, X2, X1) GEMMF32_UNIT_DMA128(X5, X2, X1)                   \
     GEMMF32_UNIT_DMA64(X5, X2, X1) GEMMF32_UNIT_DMA64x128(X5, X2, X1)                     \
-    GEMMF32_UNIT_OTHER(X5, X2, X1)
+    GEMMF32_UNIT_DMA256W8(X5, X2, X1) GEMMF32_UNIT_OTHER(X5, X2, X1)
 
 // Explicit instantiation definitions (kernel units) and declarations (host unit).
 #define GEMMF32_DEFINE5(K, T, a, b, c, d) template __global__ void gemmf32::K<gemmf32::T, a, b, c, d>(gemmf32::GemmArgs);

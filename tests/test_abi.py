@@ -191,7 +191,8 @@ def test_variant_resources_from_the_build(lib):
     """Every variant reports its kernel's registers from the build's resource
     table; no kernel of any variant spills to scratch; the direct-to-LDS
     tiles hold their MFMA accumulators (16 per 32x32 block and lane) in the
-    accumulation registers, and their compiler occupancy agrees with the
+    accumulation registers, or, where two or more wavefronts share a SIMD,
+    among the ordinary ones, and their compiler occupancy agrees with the
     residency model of the registers and LDS they use."""
     from dense_gemm_optimisation_fp32_amd import perfmodel as pm
 
@@ -203,7 +204,10 @@ def test_variant_resources_from_the_build(lib):
         assert info["workgroups_per_cu"] == 0 and info["waves_per_simd"] == 0   # plan-only fields
         if info["name"].startswith("dma_"):
             blocks = (info["wave_m"] // 32) * (info["wave_n"] // 32)
-            assert info["agprs"] == 16 * blocks, info["name"]
+            if info["threads"] <= 256:
+                assert info["agprs"] == 16 * blocks, info["name"]
+            else:
+                assert info["agprs"] in (0, 16 * blocks) and info["vgprs"] + info["agprs"] >= 16 * blocks, info["name"]
             wgs, waves = pm.gfx950_occupancy(info["vgprs"], info["agprs"], info["lds_bytes"], info["threads"])
             # the compiler's estimate per SIMD is at least what whole workgroups give
             assert info["compiler_waves_per_simd"] >= waves, info["name"]

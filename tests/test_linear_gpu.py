@@ -22,8 +22,8 @@ from workloads import (COL_MAJOR, ROW_MAJOR, WORKLOADS, epilogue_operands, rando
 pytestmark = pytest.mark.gpu
 
 REL, ABS = 1.2e-5, 1.2e-6
-EX_VARIANTS = ["dma_256x256x16_w2x2_s4", "dma_256x128x16_w2x2_s3", "dma_128x128x16_w2x2_s3",
-               "dma_64x128x16_w2x2_s2", "dma_64x64x16_w2x2_s2", "dma_64x64x16_w2x2_s3"]
+EX_VARIANTS = ["dma_256x256x16_w4x2_s4", "dma_256x256x16_w2x2_s4", "dma_256x128x16_w2x2_s3",
+               "dma_128x128x16_w2x2_s3", "dma_64x128x16_w2x2_s2", "dma_64x64x16_w2x2_s2", "dma_64x64x16_w2x2_s3"]
 ACTS = [g.GEMM_F32_ACT_NONE, g.GEMM_F32_ACT_RELU, g.GEMM_F32_ACT_GELU]
 
 
@@ -201,22 +201,23 @@ def test_binding_linear_column_major_a_and_beta():
 
 
 def test_linear_dispatch_choice():
-    """Column-major A takes the 256x256 four-stage tile on whole-wave shapes,
-    where it measured fastest; the fused epilogue keeps 256x128, which led
-    there (both measured on a 256-CU MI355X)."""
+    """Column-major A, the fused epilogue and column-major B all take the
+    eight-wavefront 256x256 tile on whole-wave shapes, where it measured
+    fastest (on a 256-CU MI355X); a shape of 2.25 waves of it keeps 128x128."""
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the choice was measured on a 256-CU MI355X")
     m = n = k = 4096
     info = g.Plan(m, n, k, ROW_MAJOR, m, n, n, layout_a=COL_MAJOR).info
-    assert info["name"] == "dma_256x256x16_w2x2_s4" and info["stream_k"] == 0
+    assert info["name"] == "dma_256x256x16_w4x2_s4" and info["stream_k"] == 0
     m, n, k = 8192, 14336, 4096
     info = g.Plan(m, n, k, ROW_MAJOR, k, n, n, epilogue=1).info
-    assert info["name"] == "dma_256x128x16_w2x2_s3" and info["stream_k"] == 0
+    assert info["name"] == "dma_256x256x16_w4x2_s4" and info["stream_k"] == 0
     info = g.Plan(m, n, k, ROW_MAJOR, m, n, n, layout_a=COL_MAJOR).info
-    assert info["name"] == "dma_256x256x16_w2x2_s4"
-    # column-major B keeps 256x128 even with column-major A
+    assert info["name"] == "dma_256x256x16_w4x2_s4"
     info = g.Plan(4096, 4096, 4096, COL_MAJOR, 4096, 4096, 4096, layout_a=COL_MAJOR).info
-    assert info["name"] == "dma_256x128x16_w2x2_s3"
+    assert info["name"] == "dma_256x256x16_w4x2_s4"
+    info = g.Plan(6144, 6144, 6144, COL_MAJOR, 6144, 6144, 6144, epilogue=1).info
+    assert info["name"] == "dma_128x128x16_w2x2_s3"
 
 
 def test_group_m_default_per_tile():
@@ -224,4 +225,5 @@ def test_group_m_default_per_tile():
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the choice was measured on a 256-CU MI355X")
     assert g.Plan(4096, 4096, 4096, ROW_MAJOR, 4096, 4096, 4096).info["group_m"] == 4
-    assert g.Plan(4096, 4096, 4096, COL_MAJOR, 4096, 4096, 4096).info["group_m"] == 8
+    assert g.Plan(4096, 4096, 4096, COL_MAJOR, 4096, 4096, 4096).info["group_m"] == 4
+    assert g.Plan(6144, 6144, 6144, ROW_MAJOR, 6144, 6144, 6144).info["group_m"] == 8

@@ -358,9 +358,9 @@ def test_few_tile_rows_plan(shape, row_plan, col_plan, layout_b):
 # (shape, tile, tiles of the partial last wave split by stream-K over one
 # workgroup per CU, or 0 for a data-parallel plan)
 DISPATCH_CASES = [
-    ((4096, 4096, 4096), "dma_256x256x16_w2x2_s4", 0),
-    ((8192, 14336, 4096), "dma_256x256x16_w2x2_s4", 0),
-    ((8192, 8192, 8192), "dma_256x256x16_w2x2_s4", 0),
+    ((4096, 4096, 4096), "dma_256x256x16_w4x2_s4", 0),
+    ((8192, 14336, 4096), "dma_256x256x16_w4x2_s4", 0),
+    ((8192, 8192, 8192), "dma_256x256x16_w4x2_s4", 0),
     ((6144, 6144, 6144), "dma_128x128x16_w2x2_s3", 0),
     ((3000, 3000, 3000), "dma_64x64x16_w2x2_s2", 0),
     ((2048, 2048, 2048), "dma_64x128x16_w2x2_s2", 0),

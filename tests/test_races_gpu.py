@@ -37,7 +37,8 @@ def by_name():
 # Kernels that share a tile shape, hence the k order of every element.
 FAMILIES = {
     "256x256x16": ["mfma_256x256x16_w2x2_32x32x2", "dma_256x256x16_w2x2_s2", "dma_256x256x16_w2x2_s3",
-                   "dma_256x256x16_w2x2_s4"],
+                   "dma_256x256x16_w2x2_s4", "dma_256x256x16_w2x4_s4", "dma_256x256x16_w4x2_s4",
+                   "dma_256x256x16_w4x2_s2", "dma_256x256x16_w4x4_s4"],
     "256x128x16": ["mfma_256x128x16_w2x2_32x32x2", "dma_256x128x16_w2x2_s3"],
     "128x128x16": ["mfma_128x128x16_w2x2_32x32x2", "dma_128x128x16_w2x2_s3"],
     "128x128x32": ["mfma_128x128x32_w2x2_32x32x2", "dma_128x128x32_w2x2_s3"],
@@ -102,7 +103,7 @@ def test_poisoned_lds_stream_k(layout_b, wgs, monkeypatch):
     names = by_name()
     m, n, k = 300, 520, 1000
     for vname in ["dma_64x64x16_w2x2_s2", "dma_64x128x16_w2x2_s2", "dma_256x128x16_w2x2_s3",
-                  "dma_256x256x16_w2x2_s4"]:
+                  "dma_256x256x16_w2x2_s4", "dma_256x256x16_w4x2_s4"]:
         print(f"\n[case] poisoned LDS stream-K {vname} wgs={wgs} layout_b={layout_b}", flush=True)
         A, B = random_operands(m, n, k, layout_b, "uniform", seed=1300 + wgs)
         C, info = run_gemm(A, B, m, n, k, layout_b, variant=names[vname])
