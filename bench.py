@@ -48,14 +48,14 @@ METRIC = "FP32 GEMM TFLOPS (2MNK/t) and % of MI355X FP32 matrix peak at 4096^3"
 #   bench.py --workload W --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy 512
 # scaled by what the same counters read for the 512 MiB elementwise copy in
 # that run (FETCH_SIZE 262161 KiB -> x2.000, WRITE_SIZE 524288 KiB -> x1.000);
-# the summary is profiles/dma_256x256x16_s4_sq4096_counters.md.
+# the summary is profiles/dma_256x256x16_w4x2_s4_sq4096_counters.md.
 # Valid only for the kernel sources they were taken on: the entry carries the
 # SHA-1 of the tiled-kernel sources, and the field is null when they differ.
 TRAFFIC_SOURCES = ("device_common.hpp", "mfma_gemm.hpp", "mfma_dma_gemm.hpp")
 TRAFFIC_COUNTERS = {
-    "sq4096": {"kernel": "dma_256x256x16_w2x2_s4",
+    "sq4096": {"kernel": "dma_256x256x16_w4x2_s4",
                "sources_sha1": "610c79bb57d6decaab7159f7c10c22a2d907e14b",
-               "fetch_kib": 196738.7, "write_kib": 65536.0,
+               "fetch_kib": 196683.5, "write_kib": 65536.0,
                "fetch_factor": 2.000, "write_factor": 1.000},
 }
 

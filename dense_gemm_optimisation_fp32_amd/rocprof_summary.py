@@ -18,7 +18,8 @@ tooling; nothing here runs on the GPU).
 
 The profiler's kernel names are the demangled template names; ``short_name``
 maps them to the variant-style names the library reports
-(``dma_256x256x16_s4``, ``sk_dma_64x128x16_s2``, ``skinny_16x64_w16_d4`` ...).
+(``dma_256x256x16_s4``, ``dma_256x256x16_w4x2_s4`` (wavefront layouts other than 2 x 2
+named), ``sk_dma_64x128x16_s2``, ``skinny_16x64_w16_d4`` ...).
 """
 from __future__ import annotations
 
@@ -37,11 +38,12 @@ XCDS = 8
 def short_name(kernel: str) -> str:
     """A compact name for a kernel from its (demangled or mangled) name."""
     k = kernel
-    m = re.search(r"DmaTile<(\d+), (\d+), (\d+), \d+, \d+, (\d+)(?:, (?:true|false))?>", k)
+    m = re.search(r"DmaTile<(\d+), (\d+), (\d+), (\d+), (\d+), (\d+)(?:, (?:true|false))?>", k)
     if m is None:
-        m = re.search(r"DmaTileILi(\d+)ELi(\d+)ELi(\d+)ELi\d+ELi\d+ELi(\d+)", k)
+        m = re.search(r"DmaTileILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)", k)
     if m and "gemm_mfma_dma" in k:
-        base = f"dma_{m.group(1)}x{m.group(2)}x{m.group(3)}_s{m.group(4)}"
+        waves = "" if (m.group(4), m.group(5)) == ("2", "2") else f"_w{m.group(4)}x{m.group(5)}"
+        base = f"dma_{m.group(1)}x{m.group(2)}x{m.group(3)}{waves}_s{m.group(6)}"
         if "sk_kernel" in k:
             return "sk_" + base + ("_bcol" if re.search(r"EEELb1EEEv|>, true>", k) else "")
         flags = re.search(r">, (true|false), (true|false), (true|false), (true|false)>", k)

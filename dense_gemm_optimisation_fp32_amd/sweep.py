@@ -120,7 +120,9 @@ def kernel_short_name(rec: dict, layout_b: int, n: int) -> str:
     name = rec["name"]
     if name.startswith("dma_"):
         stages = re.search(r"_s(\d+)$", name).group(1)
-        base = f"dma_{rec['bm']}x{rec['bn']}x{rec['bk']}_s{stages}"
+        w = re.search(r"_w(\d+)x(\d+)_", name)
+        waves = "" if w is None or w.groups() == ("2", "2") else f"_w{w.group(1)}x{w.group(2)}"
+        base = f"dma_{rec['bm']}x{rec['bn']}x{rec['bk']}{waves}_s{stages}"
         if layout_b == 1:
             return base + "_bcol"
         nb = rec["wave_tile"][1] // 32

@@ -35,7 +35,7 @@ def test_clock_sampler_without_a_single_gpu_reports_nothing(monkeypatch):
     assert c.mean_mhz() is None
 
 
-def _res(name, kernel_avg_s, sclk, kind=0, plan_name="dma_256x256x16_w2x2_s4"):
+def _res(name, kernel_avg_s, sclk, kind=0, plan_name="dma_256x256x16_w4x2_s4"):
     from dense_gemm_optimisation_fp32_amd import perfmodel as pm
 
     w = WORKLOADS[name]
