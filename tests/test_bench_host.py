@@ -102,3 +102,19 @@ def test_clock_sampler_idle_level_file(tmp_path):
     res = _res("sq4096", 2 * 4096 ** 3 / 147e12, c.mean_mhz())
     res["sclk_samples"] = len(c.samples)
     assert bench.roofline(res)["frac_at_sclk"] is None
+
+
+def test_profile_kernel_short_names():
+    """The profile summaries name kernels the way the variant table does."""
+    from dense_gemm_optimisation_fp32_amd.rocprof_summary import short_name
+
+    assert short_name("void gemmf32::gemm_mfma_dma_kernel<gemmf32::DmaTile<256, 256, 16, 4, 2, 4, true>, "
+                      "false, false, false, true>(gemmf32::GemmArgs)") == "dma_256x256x16_w4x2_s4_wide"
+    assert short_name("void gemmf32::gemm_mfma_dma_kernel<gemmf32::DmaTile<256, 128, 16, 2, 2, 3, true>, "
+                      "true, false, false, false>(gemmf32::GemmArgs)") == "dma_256x128x16_s3_bcol"
+    assert short_name("void gemmf32::gemm_mfma_dma_sk_kernel<gemmf32::DmaTile<64, 128, 16, 2, 2, 2, true>, "
+                      "false>(gemmf32::GemmArgs)") == "sk_dma_64x128x16_s2"
+    assert short_name("void gemmf32::gemm_skinny_kernel<gemmf32::SkinnyTile<16, 4, 16>, false>"
+                      "(gemmf32::GemmArgs)") == "skinny_16x16_w16_d4"
+    assert short_name("void gemmf32::gemm_fewcol_kernel<gemmf32::FewColTile<1>, true>"
+                      "(gemmf32::GemmArgs)") == "fewcol_r1_bcol"
