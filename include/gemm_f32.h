@@ -80,7 +80,7 @@ enum gemm_f32_activation {
 enum gemm_f32_kind {
     GEMM_F32_KIND_MFMA = 0,   /* LDS-tiled, wavefront tiles on v_mfma_f32_32x32x2_f32 */
     GEMM_F32_KIND_VALU = 1,   /* LDS-tiled, per-thread register outer product on the vector ALU */
-    GEMM_F32_KIND_SKINNY = 2, /* few-row (memory-bound) path */
+    GEMM_F32_KIND_SKINNY = 2, /* few-row path: M <= 32 (memory-bound), and shapes with few tiles */
     GEMM_F32_KIND_FEWCOL = 3  /* few-column (memory-bound, matrix-vector-like) path */
 };
 
