@@ -54,8 +54,8 @@ METRIC = "FP32 GEMM TFLOPS (2MNK/t) and % of MI355X FP32 matrix peak at 4096^3"
 TRAFFIC_SOURCES = ("device_common.hpp", "mfma_gemm.hpp", "mfma_dma_gemm.hpp")
 TRAFFIC_COUNTERS = {
     "sq4096": {"kernel": "dma_256x256x16_w4x2_s4",
-               "sources_sha1": "610c79bb57d6decaab7159f7c10c22a2d907e14b",
-               "fetch_kib": 196683.5, "write_kib": 65536.0,
+               "sources_sha1": "56e5641c34952e8b9814d57e86221e51e20358f6",
+               "fetch_kib": 196677.7, "write_kib": 65536.0,
                "fetch_factor": 2.000, "write_factor": 1.000},
 }
 

@@ -38,7 +38,11 @@ struct GemmArgs {
     unsigned long long *partial;  // partial sums of split tiles, epoch-tagged words
     uint32_t partial_bytes;       // byte extent of the stream-K partial-sum words (< 2^31)
     unsigned *arrivals;           // per-tile arrival counters for split tiles
-    unsigned epoch;               // tag of this run's partial sums, never 0
+    unsigned epoch;               // tag of this run's partial sums (bit 31 clear, never 0), unless:
+    unsigned *epoch_word;         // non-NULL: the run takes its tag from this workspace word
+                                  // (launches captured in a graph; see load_run_epoch)
+    unsigned *done_tiles;         // workspace counter of the run's finished split tiles
+    int split_tiles;              // tiles that workgroups share (finished by a last arriver)
     int sk_wgs;            // stream-K: workgroups sharing the first sk_tiles tiles' slabs (0: none)
     int sk_tiles;          // stream-K: tiles [0, sk_tiles) are shared; the rest get a workgroup each
     int split_k;           // number of k-splits (skinny path), else 1
@@ -52,8 +56,8 @@ struct GemmArgs {
     // Waits for partial sums (split-k and stream-K plans).
     unsigned *status;      // workspace word set to 1 when a wait gave up (a NaN went to C), or NULL
     int wait_budget;       // polls one thread may spend waiting for partial sums
-    unsigned epoch_xor;    // readers wait for the tag epoch ^ epoch_xor (0; a test sets it so that
-                           // no word ever matches and every wait gives up)
+    unsigned epoch_xor;    // readers wait for the tag (this run's epoch) ^ epoch_xor (0; a test sets
+                           // it so that no word ever matches and every wait gives up)
     int poison_lds;        // 1: fill LDS with NaN before the first copy (a test of the waits)
 };
 
@@ -162,6 +166,39 @@ __device__ __forceinline__ float wait_tagged_word(const unsigned long long *p, u
         w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return __uint_as_float((unsigned)w);
+}
+
+// Tags of partial-sum words.  A launch made outside graph capture carries
+// its tag as an argument, a fresh one per run (bit 31 clear).  A launch
+// captured in a graph would replay the argument it was recorded with, so a
+// replay could take the previous replay's words for its own; such launches
+// take the tag from a word of the workspace instead, which the run's last
+// split tile advances: one past the word's count, bit 31 set (so the two
+// kinds never meet, and no tag is 0, the tag of words never written).
+// Every workgroup that shares a tile reads the word before it tags a word.
+__device__ __forceinline__ unsigned load_run_epoch(const GemmArgs &g)
+{
+    return ((__hip_atomic_load(g.epoch_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u) & 0x7fffffffu) |
+           0x80000000u;
+}
+
+// Counts split tiles finished (one thread of their last arriver,
+// word-tagged launches only); returns the count before them.  The run's last split tile
+// then stores the run's count in the epoch word (advance_epoch): by that
+// time every workgroup that tags words has read the old value (it counted
+// itself in on its tile after tagging), and the next run, on the same
+// stream, starts after this one.
+__device__ __forceinline__ unsigned count_split_tiles(const GemmArgs &g, int tiles = 1)
+{
+    return __hip_atomic_fetch_add(g.done_tiles, (unsigned)tiles, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void advance_epoch(const GemmArgs &g, unsigned done_before, unsigned epoch, int tiles = 1)
+{
+    if (done_before + (unsigned)tiles == (unsigned)g.split_tiles) {
+        __hip_atomic_store(g.done_tiles, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(g.epoch_word, epoch & 0x7fffffffu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 __device__ __forceinline__ void record_give_up(int budget, unsigned *status)

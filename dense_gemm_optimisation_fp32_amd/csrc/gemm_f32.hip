@@ -21,13 +21,15 @@
 // handles.
 GEMMF32_ALL_UNITS(GEMMF32_EXTERN5, GEMMF32_EXTERN2, GEMMF32_EXTERN1)
 
-// Scratch of gemm_f32_run_noalloc: the arrival counters (and status word)
-// of the split tiles first, then the epoch-tagged partial-sum words.  One
-// copy per GPU, reserved until the process ends; every call on a GPU shares
-// it.  Host code never uses this name as an address: it takes the device
-// address from hipGetSymbolAddress, once per device (scratch_address).
+// Scratch of gemm_f32_run_noalloc: the arrival counters of the split tiles,
+// the status word and the count of finished split tiles first (the epoch
+// word, shared by every call, is the area's last counter), then the
+// epoch-tagged partial-sum words.  One copy per GPU, reserved until the
+// process ends; every call on a GPU shares it.  Host code never uses this
+// name as an address: it takes the device address from hipGetSymbolAddress,
+// once per device (scratch_address).
 namespace {
-constexpr size_t kScratchCounters = 65536;             // 32-bit counters, the last one the status word
+constexpr size_t kScratchCounters = 65536;             // 32-bit counters (see above)
 constexpr size_t kScratchWordBytes = (size_t)64 << 20;  // 64 MiB of 8-byte words
 constexpr size_t kScratchBytes = kScratchCounters * 4 + kScratchWordBytes;
 }  // namespace
@@ -371,7 +373,7 @@ struct gemm_f32_plan_impl {
     unsigned grid;
     unsigned block;
     void *workspace;     // split-k partial sums and arrival counters (few-row path), else NULL
-    std::atomic<unsigned> runs{0};   // epochs handed out so far
+    std::atomic<unsigned> runs{0};   // argument tags handed out so far
     int c_store_width = 1;           // C elements per store of the whole-tile kernel
     // Column sliver: the last sliver_cols columns of C run as a second launch
     // with a plan of their own (this plan then covers columns [0, n)).
@@ -608,6 +610,20 @@ int64_t choose_sliver(int64_t m, int64_t n, int64_t k, int layout_b, const Devic
     return t_main + t_sliver < t_full ? r : 0;
 }
 
+// Tiles of a stream-K plan that more than one workgroup shares, the ones a
+// last arriver finishes: the kernel cuts the shared tiles' shared * k_tiles
+// slabs into wgs ranges, range q = [q * iters / wgs, (q + 1) * iters / wgs),
+// and a tile is shared when its first and last slabs fall in different ranges.
+int64_t stream_k_split_tiles(int64_t shared, int64_t k_tiles, int64_t wgs)
+{
+    const int64_t iters = shared * k_tiles;
+    auto owner = [&](int64_t x) { return ((x + 1) * wgs - 1) / iters; };
+    int64_t n = 0;
+    for (int64_t t = 0; t < shared; ++t)
+        if (owner(t * k_tiles) != owner(t * k_tiles + k_tiles - 1)) ++n;
+    return n;
+}
+
 // Everything a plan needs except its workspace: the kernel, grid and launch
 // arguments, and the workspace it asks for (*ws_words bytes of epoch-tagged
 // partial-sum words and *ws_counters 32-bit arrival counters, plus one status
@@ -698,7 +714,7 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
     // GEMM_F32_POISON_LDS=1 fills LDS with NaN before the first copy.
     a.wait_budget = env_int("GEMM_F32_WAIT_BUDGET", gemmf32::kTaggedWaitBudget);
     if (a.wait_budget < 0) a.wait_budget = 0;
-    a.epoch_xor = env_int("GEMM_F32_TEST_LOST_WORDS", 0) ? 0x80000000u : 0u;
+    a.epoch_xor = env_int("GEMM_F32_TEST_LOST_WORDS", 0) ? 0xc0000000u : 0u;
     a.poison_lds = env_int("GEMM_F32_POISON_LDS", 0) ? 1 : 0;
     p->grid = (unsigned)((int64_t)a.tiles_m * a.tiles_n);
     p->block = (unsigned)d.threads;
@@ -722,9 +738,11 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
         a.k_per_split = (int)kps;
         p->grid = (unsigned)(per_split * split);
         if (split > 1) {
-            // split * m * n tagged words and one arrival counter per tile.
+            // split * m * n tagged words and one arrival counter per tile;
+            // every tile is shared by its splits.
             *ws_words = (size_t)split * (size_t)m * (size_t)n * sizeof(unsigned long long);
             *ws_counters = (size_t)per_split;
+            a.split_tiles = (int)per_split;
         }
     }
 
@@ -777,6 +795,7 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
             a.partial_bytes = (uint32_t)words;
             *ws_words = words;
             *ws_counters = (size_t)shared;
+            a.split_tiles = (int)stream_k_split_tiles(shared, a.k_tiles, wgs);
         }
     }
 
@@ -787,13 +806,20 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
     return GEMM_F32_SUCCESS;
 }
 
+// Counters of a plan's workspace beyond the per-tile arrival counters: the
+// status word, the count of finished split tiles and the epoch word.
+constexpr size_t kExtraCounters = 3;
+
 // Point a plan's launch arguments at its workspace: the words, then the
-// arrival counters and the status word.
+// arrival counters, the status word, the finished-tile count and the epoch
+// word.
 void plan_attach(gemm_f32_plan_impl *p, void *words, unsigned *counters, size_t n_counters)
 {
     p->args.partial = static_cast<unsigned long long *>(words);
     p->args.arrivals = counters;
     p->args.status = counters + n_counters;
+    p->args.done_tiles = counters + n_counters + 1;
+    p->args.epoch_word = counters + n_counters + 2;
 }
 
 // Columns of a column sliver for a plan (0: none): plain products with the
@@ -836,9 +862,10 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
         return st;
     }
     if (words) {
-        // The plan's own workspace, all zero, so no word carries a valid
-        // (non-zero) epoch and every counter starts at zero.
-        const size_t bytes = words + (counters + 1) * sizeof(unsigned);
+        // The plan's own workspace, all zero: every counter starts at zero,
+        // the epoch word too, so the first run tags its words 1 and no word
+        // carries a valid tag before it is written.
+        const size_t bytes = words + (counters + kExtraCounters) * sizeof(unsigned);
         hipError_t e = hipMalloc(&p->workspace, bytes);
         if (e == hipSuccess) e = hipMemsetAsync(p->workspace, 0, bytes, nullptr);
         if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
@@ -978,7 +1005,7 @@ int gemm_f32_create_variant(gemm_f32_plan *out, int v, int64_t m, int64_t n, int
 
 namespace {
 
-// Launch the plan's kernel with arguments `a` (pointers and epoch filled).
+// Launch the plan's kernel with arguments `a` (pointers filled).
 int launch_kernel(const gemm_f32_plan_impl *p, GemmArgs &a, void *stream)
 {
     void *kargs[] = {&a};
@@ -990,14 +1017,33 @@ int launch_kernel(const gemm_f32_plan_impl *p, GemmArgs &a, void *stream)
     return GEMM_F32_SUCCESS;
 }
 
+// Whether `stream` is capturing into a graph (or the query fails: then the
+// launch takes the tag kind that is right either way).
+bool capturing(void *stream)
+{
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &st) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;
+    }
+    return st != hipStreamCaptureStatusNone;
+}
+
+// The tag of a split plan's run: a fresh argument tag (bit 31 clear, never
+// 0) from `counter`, or, for a launch captured in a graph, the workspace
+// word (a.epoch_word stays set; see load_run_epoch).
+void tag_run(GemmArgs &a, std::atomic<unsigned> &counter, void *stream)
+{
+    if (capturing(stream)) return;
+    a.epoch_word = nullptr;
+    unsigned ep = ++counter & 0x7fffffffu;
+    if (ep == 0) ep = ++counter & 0x7fffffffu;
+    a.epoch = ep;
+}
+
 int launch(gemm_f32_plan p, GemmArgs &a, void *stream)
 {
-    if (p->workspace) {
-        // A fresh, non-zero tag for this run's split-k partial sums.
-        unsigned ep = ++p->runs;
-        if (ep == 0) ep = ++p->runs;
-        a.epoch = ep;
-    }
+    if (p->workspace) tag_run(a, p->runs, stream);
     return launch_kernel(p, a, stream);
 }
 
@@ -1005,7 +1051,7 @@ int launch(gemm_f32_plan p, GemmArgs &a, void *stream)
 // device with that device current.
 struct ScratchSlot {
     void *ptr = nullptr;
-    std::atomic<unsigned> epoch{0};   // tags handed out to calls on this device
+    std::atomic<unsigned> runs{0};   // argument tags handed out to calls on this device
 };
 ScratchSlot g_scratch[kMaxDevices];
 std::mutex g_scratch_mutex;
@@ -1064,7 +1110,8 @@ int gemm_f32_run_noalloc(int64_t m, int64_t n, int64_t k, int layout_b, int64_t 
                        &counters[1]);
     if (st != GEMM_F32_SUCCESS) return st;
     for (int i = 0; i < (r ? 2 : 1); ++i)
-        if (words[i] > kScratchWordBytes || counters[i] + 1 > kScratchCounters) return GEMM_F32_ERR_SCRATCH_TOO_SMALL;
+        if (words[i] > kScratchWordBytes || counters[i] + kExtraCounters > kScratchCounters)
+            return GEMM_F32_ERR_SCRATCH_TOO_SMALL;
     parts[0].sliver_col0 = n - r;
     for (int i = 0; i < (r ? 2 : 1); ++i) {
         // The two launches run one after the other on `stream`, so they can
@@ -1082,12 +1129,16 @@ int gemm_f32_run_noalloc(int64_t m, int64_t n, int64_t k, int layout_b, int64_t 
             a.partial = reinterpret_cast<unsigned long long *>(static_cast<char *>(base) + kScratchCounters * 4);
             a.arrivals = ctr;
             a.status = ctr + counters[i];
-            // The counters and the status word start at zero: a fill kernel
-            // on the caller's stream ahead of the product (a kernel, not a
-            // memset, so that the call can be captured in a graph).  The
-            // words need no clearing: each launch tags its words with an
-            // epoch no earlier launch on this device used.
-            const int n_zero = (int)(counters[i] + 1);
+            a.done_tiles = ctr + counters[i] + 1;
+            a.epoch_word = ctr + (kScratchCounters - 1);
+            // The arrival counters, the status word and the finished-tile
+            // count start at zero: a fill kernel on the caller's stream ahead
+            // of the product (a kernel, not a memset, so that the call can be
+            // captured in a graph).  The words need no clearing: each launch
+            // on this device tags its words afresh, with an argument tag or,
+            // captured in a graph, from the epoch word, which is never
+            // cleared.
+            const int n_zero = (int)(counters[i] + 2);
             unsigned *zp = ctr;
             int zn = n_zero;
             void *zargs[] = {&zp, &zn};
@@ -1095,9 +1146,7 @@ int gemm_f32_run_noalloc(int64_t m, int64_t n, int64_t k, int layout_b, int64_t 
                                            dim3((unsigned)((n_zero + 255) / 256)), dim3(256), zargs, 0,
                                            reinterpret_cast<hipStream_t>(stream));
             if (e != hipSuccess) return hip_fail(e);
-            unsigned ep = ++g_scratch[p.device].epoch;
-            if (ep == 0) ep = ++g_scratch[p.device].epoch;
-            a.epoch = ep;
+            tag_run(a, g_scratch[p.device].runs, stream);
         }
         st = launch_kernel(&p, a, stream);
         if (st != GEMM_F32_SUCCESS) return st;

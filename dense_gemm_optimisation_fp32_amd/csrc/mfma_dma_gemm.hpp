@@ -633,8 +633,9 @@ struct StreamK {
 template <class T, bool B_COL>
 __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsrc_t rc, const StreamK &sk, int t,
                                           int p, int tid, int row0, int col0, int wr, int wc, int l32, int half,
-                                          int *last_flag, const f32x16 (&acc)[T::MB][T::NB])
+                                          int *last_flag, unsigned epoch, const f32x16 (&acc)[T::MB][T::NB])
 {
+
     const long long t0 = (long long)t * g.k_tiles;
     const int p_lo = sk.owner(t0), p_hi = sk.owner(t0 + g.k_tiles - 1);
     const int nseg = p_hi - p_lo + 1;
@@ -654,7 +655,7 @@ __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsr
         for (int nb = 0; nb < T::NB; ++nb) {
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-                buf_store_tagged(acc[mb][nb][v], g.epoch, rp, lane_off, (mine + word(mb, nb, v)) * 8u);
+                buf_store_tagged(acc[mb][nb][v], epoch, rp, lane_off, (mine + word(mb, nb, v)) * 8u);
             // One block at a time: keeps the scheduler from pulling all
             // accumulators into vector registers at once.
             __builtin_amdgcn_sched_barrier(0);
@@ -667,14 +668,19 @@ __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsr
     if (tid == 0) {
         const unsigned before = __hip_atomic_fetch_add(g.arrivals + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool last = before == (unsigned)(nseg - 1);
-        // Every other segment has counted itself in: reset for the next run.
-        if (last) __hip_atomic_store(g.arrivals + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (last) {
+            // Every other segment has counted itself in: reset for the next
+            // run, and count one more tile this workgroup finishes (a
+            // word-tagged launch reports them at the kernel's end).
+            __hip_atomic_store(g.arrivals + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ++last_flag[1];
+        }
         *last_flag = last;
     }
     __syncthreads();
     if (!*last_flag) return;
     int budget = g.wait_budget;
-    const unsigned want = g.epoch ^ g.epoch_xor;
+    const unsigned want = epoch ^ g.epoch_xor;
 
     constexpr int H = 8;   // words per lane in flight
 #pragma unroll
@@ -811,6 +817,11 @@ __global__ __launch_bounds__(T::THREADS, sk_waves_per_simd<T>()) void gemm_mfma_
 
     const StreamK sk{(long long)g.sk_tiles * KT, g.sk_wgs};
     const int p = xcd_contiguous(blockIdx.x, g.sk_wgs, g.num_xcd);
+    // This run's tag, in a scalar register: the argument, or for a
+    // word-tagged launch the epoch word's (read here, before the copies).
+    unsigned epoch = g.epoch;
+    if (g.epoch_word) epoch = __builtin_amdgcn_readfirstlane(load_run_epoch(g));
+    if (tid == 0) last_flag[1] = 0;   // split tiles this workgroup finishes (thread 0's count)
     const long long i0 = sk.start(p), i1 = sk.start(p + 1);
     if (i0 >= i1) return;
     const int t_first = (int)(i0 / KT), t_last = (int)((i1 - 1) / KT);
@@ -848,7 +859,13 @@ __global__ __launch_bounds__(T::THREADS, sk_waves_per_simd<T>()) void gemm_mfma_
         if (kt0 == 0 && kt1 == KT)
             dma_store_c<T, B_COL>(g, rc, row0, col0, wr, wc, l32_i, half_i, acc);
         else
-            dma_fixup<T, B_COL>(g, rc, sk, t, p, tid_i, row0, col0, wr, wc, l32_i, half_i, last_flag, acc);
+            dma_fixup<T, B_COL>(g, rc, sk, t, p, tid_i, row0, col0, wr, wc, l32_i, half_i, last_flag, epoch, acc);
+    }
+    // A word-tagged launch counts the split tiles this workgroup finished
+    // (here, where the registers are free, rather than in the fix-up).
+    if (g.epoch_word && tid == 0 && last_flag[1] > 0) {
+        const int finished = last_flag[1];
+        advance_epoch(g, count_split_tiles(g, finished), epoch, finished);
     }
 }
 

@@ -231,7 +231,14 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
     for (int nb = 0; nb < T::NB; ++nb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[wave][red_index<T>(4 * h + v, T::NB * j + nb)] = acc[nb][v];
+    // Split plans: this run's tag for the partial sums, the argument or, for
+    // a word-tagged launch, the epoch word's, read by one thread here (after
+    // the k-loop, so that it holds no register there) and passed on through
+    // LDS with the wavefronts' sums.
+    __shared__ unsigned run_epoch;
+    if (g.epoch_word && g.split_k > 1 && tid == 0) run_epoch = load_run_epoch(g);
     __syncthreads();
+    const unsigned epoch = g.epoch_word ? __builtin_amdgcn_readfirstlane(run_epoch) : g.epoch;
 
     constexpr int ELEMS = T::BM * T::BN;
     constexpr int EPT = (ELEMS + T::THREADS - 1) / T::THREADS;   // elements per thread
@@ -264,12 +271,12 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
     // orders these words against the arrival counter.  The last workgroup
     // of a tile to arrive adds the splits in split order and writes C.
     const size_t plane = (size_t)g.m * g.n;
-    const unsigned long long tag = (unsigned long long)g.epoch << 32;
+    const unsigned long long tag = (unsigned long long)epoch << 32;
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
         const int e = tid + q * T::THREADS;
         const int r = row0 + e / T::BN, c = col0 + e % T::BN;
-        if (e < ELEMS && r < g.m && c < g.n) store_tagged_word(g.partial + split * plane + (size_t)r * g.n + c, own[q], g.epoch);
+        if (e < ELEMS && r < g.m && c < g.n) store_tagged_word(g.partial + split * plane + (size_t)r * g.n + c, own[q], epoch);
     }
     __shared__ int last;
     // Every wavefront has issued its words before the workgroup counts itself in.
@@ -278,14 +285,18 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
         const unsigned before =
             __hip_atomic_fetch_add(g.arrivals + rest, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last = before == (unsigned)(g.split_k - 1);
-        // Every other split of this tile has counted itself in: reset the
-        // counter for the next run.
-        if (last) __hip_atomic_store(g.arrivals + rest, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (last) {
+            // Every other split of this tile has counted itself in: reset the
+            // counter for the next run; a word-tagged launch counts the tile
+            // finished.
+            __hip_atomic_store(g.arrivals + rest, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (g.epoch_word) advance_epoch(g, count_split_tiles(g), epoch);
+        }
     }
     __syncthreads();
     if (!last) return;
     int budget = g.wait_budget;
-    const unsigned want = g.epoch ^ g.epoch_xor;
+    const unsigned want = epoch ^ g.epoch_xor;
 
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {

@@ -34,11 +34,16 @@
  *    workgroups share the k-slabs of gemm_f32_info.stream_k_tiles tiles,
  *    all of them or the partial last wave's) hold 2 * P partial tiles
  *    (bm * bn each), all as 8-byte words tagged with a per-run epoch, plus
- *    one 32-bit arrival counter per output tile.  Each run takes a new epoch
- *    from the plan (an atomic counter, so runs may be enqueued from several
- *    host threads), but two runs of such a plan must not execute at the same
- *    time on the device (they would share the workspace): use one plan per
- *    stream, or order the streams.
+ *    one 32-bit arrival counter per output tile and three more words (a
+ *    status word, a count of finished split tiles, an epoch word).  A run
+ *    launched outside graph capture takes a fresh tag from the plan (an
+ *    atomic counter, so runs may be enqueued from several host threads); a
+ *    launch captured in a HIP graph, whose arguments every replay repeats,
+ *    takes its tag from the epoch word instead, which each such run advances
+ *    when its last split tile is done, so every replay is tagged afresh.
+ *    Two runs of such a plan must not execute at the same time on the device
+ *    (they would share the workspace): use one plan per stream, or order the
+ *    streams.
  *  - Execution is asynchronous on the caller's stream; a device-side fault
  *    is reported by the caller's next synchronisation, not by gemm_f32_run.
  */
@@ -213,15 +218,17 @@ int gemm_f32_run(gemm_f32_plan plan, const float *A, const float *B, float *C, v
  *   A or B; `stream` a hipStream_t, NULL = the null stream).
  *   Every call on one GPU shares that GPU's scratch area, which keeps the
  *   last call's contents (each call clears the counters it uses, with a
- *   small kernel on `stream` ahead of the product, and tags its words with a
- *   new epoch): two calls that overlap in time on one GPU (other streams or
- *   host threads) race and can return wrong results; order them.  The
- *   first call on each device finds the scratch area's device address; make
- *   it outside graph capture.  Give-ups of the bounded waits (see
+ *   small kernel on `stream` ahead of the product, and tags its words
+ *   afresh: with a new tag per call, or, captured in a graph, from an epoch
+ *   word in the scratch area that each replay advances): two calls that
+ *   overlap in time on one GPU (other streams or host threads) race and can
+ *   return wrong results; order them.
+ *   The first call on each device finds the scratch area's device address;
+ *   make it outside graph capture.  Give-ups of the bounded waits (see
  *   gemm_f32_plan_check) write NaN to C but are not reported here.
  * Errors: as gemm_f32_create and gemm_f32_run; GEMM_F32_ERR_SCRATCH_TOO_SMALL
  *   when the plan needs more than the scratch area holds (more than 64 MiB
- *   of words or more than 65535 split tiles).  Never synchronises.
+ *   of words or more than 65533 split tiles).  Never synchronises.
  */
 int gemm_f32_run_noalloc(int64_t m, int64_t n, int64_t k, int layout_b, int64_t lda, int64_t ldb, int64_t ldc,
                          const float *A, const float *B, float *C, void *stream);
