@@ -143,8 +143,10 @@ __device__ __forceinline__ void raster_tile(int wg, const GemmArgs &a, int &tm, 
 
 // Value of a 64-bit partial-sum word {float bits, epoch} written by another
 // workgroup, once it carries the epoch `want`.  `w` is a first load already
-// in hand.  Every writer has issued its words before it counts itself in,
-// and the reader is the last to count in, so the wait ends; `budget` (polls
+// in hand.  A writer counts itself in on the tile only when all it has
+// left is to finish and issue its words (the stream-K kernel once they are
+// issued, the few-row kernel once its last loads are), and the reader is
+// the last to count in, so the wait ends; `budget` (polls
 // left for the caller, shared by all its waits) only keeps a lost word from
 // hanging the kernel: once it is spent, missing elements read as NaN at once
 // and the budget is left negative, which the caller records in the plan's
@@ -185,8 +187,8 @@ __device__ __forceinline__ unsigned load_run_epoch(const GemmArgs &g)
 // Counts split tiles finished (one thread of their last arriver,
 // word-tagged launches only); returns the count before them.  The run's last split tile
 // then stores the run's count in the epoch word (advance_epoch): by that
-// time every workgroup that tags words has read the old value (it counted
-// itself in on its tile after tagging), and the next run, on the same
+// time every workgroup that tags words has read the old value (it reads it
+// before it counts itself in on its tile), and the next run, on the same
 // stream, starts after this one.
 __device__ __forceinline__ unsigned count_split_tiles(const GemmArgs &g, int tiles = 1)
 {

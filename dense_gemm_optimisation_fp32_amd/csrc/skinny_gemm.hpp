@@ -177,6 +177,26 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
 #pragma unroll
     for (int nb = 0; nb < T::NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Split plans: the workgroups of a tile count themselves in on the
+    // tile's arrival counter as soon as thread 0's wavefront has issued its
+    // last loads, so the count's round trip overlaps the stream; the last to
+    // count in adds the splits.  Every workgroup counted in is resident and
+    // has only its last loads, the sums and its stores left, so the last
+    // one's wait for their words is short (and bounded in any case).  A
+    // word-tagged launch (captured in a graph) reads its tag first, so that
+    // when the run's last split tile advances the epoch word every workgroup
+    // has read it.
+    __shared__ unsigned run_epoch;
+    const bool word_tag = g.epoch_word != nullptr && g.split_k > 1;
+    unsigned tag_read = 0, before = 0;
+    if (word_tag && tid == 0) tag_read = load_run_epoch(g);
+    auto count_in = [&]() {
+        if (g.split_k > 1 && tid == 0) {
+            if (word_tag) run_epoch = tag_read;
+            before = __hip_atomic_fetch_add(g.arrivals + rest, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+
     // Whole 16-k groups stream through a ring of DEPTH register slots: the
     // loads of group q + DEPTH are issued as soon as group q has been
     // multiplied, so DEPTH groups (5 * DEPTH loads) stay in flight.  The ring
@@ -207,6 +227,8 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        count_in();
+        __builtin_amdgcn_sched_barrier(0);
         const int last0 = (passes - 1) * D;
         if (last0 + D <= G) {
 #pragma unroll
@@ -216,6 +238,8 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
             for (int u = 0; u < D; ++u)
                 if (last0 + u < G) skinny_mfma<T, B_COL>(a[u], b[u], acc);
         }
+    } else {
+        count_in();
     }
     // The partial group at the end of the range, element by element.
     if (G * T::KQ < kspan) {
@@ -231,14 +255,20 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
     for (int nb = 0; nb < T::NB; ++nb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[wave][red_index<T>(4 * h + v, T::NB * j + nb)] = acc[nb][v];
-    // Split plans: this run's tag for the partial sums, the argument or, for
-    // a word-tagged launch, the epoch word's, read by one thread here (after
-    // the k-loop, so that it holds no register there) and passed on through
-    // LDS with the wavefronts' sums.
-    __shared__ unsigned run_epoch;
-    if (g.epoch_word && g.split_k > 1 && tid == 0) run_epoch = load_run_epoch(g);
+    __shared__ int last;
+    if (g.split_k > 1 && tid == 0) {
+        last = before == (unsigned)(g.split_k - 1);
+        if (last) {
+            // Every split of this tile has counted itself in: reset the
+            // counter for the next run; a word-tagged launch counts the tile
+            // finished.
+            __hip_atomic_store(g.arrivals + rest, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (word_tag) advance_epoch(g, count_split_tiles(g), tag_read);
+        }
+    }
     __syncthreads();
-    const unsigned epoch = g.epoch_word ? __builtin_amdgcn_readfirstlane(run_epoch) : g.epoch;
+    // This run's tag for the partial sums.
+    const unsigned epoch = word_tag ? __builtin_amdgcn_readfirstlane(run_epoch) : g.epoch;
 
     constexpr int ELEMS = T::BM * T::BN;
     constexpr int EPT = (ELEMS + T::THREADS - 1) / T::THREADS;   // elements per thread
@@ -265,36 +295,23 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
         return;
     }
 
-    // k is split across workgroups.  Each split publishes its partial sums
-    // as 64-bit words {value, epoch}, written whole, so a reader that sees
-    // this run's epoch in a word also sees the value beside it; no fence
-    // orders these words against the arrival counter.  The last workgroup
-    // of a tile to arrive adds the splits in split order and writes C.
+    // k is split across workgroups.  Each split but the last to count in
+    // publishes its partial sums as 64-bit words {value, epoch}, written
+    // whole, so a reader that sees this run's epoch in a word also sees the
+    // value beside it (no fence needed).  The last to count in adds the
+    // splits in split order and writes C.
     const size_t plane = (size_t)g.m * g.n;
     const unsigned long long tag = (unsigned long long)epoch << 32;
+    if (!last) {
 #pragma unroll
-    for (int q = 0; q < EPT; ++q) {
-        const int e = tid + q * T::THREADS;
-        const int r = row0 + e / T::BN, c = col0 + e % T::BN;
-        if (e < ELEMS && r < g.m && c < g.n) store_tagged_word(g.partial + split * plane + (size_t)r * g.n + c, own[q], epoch);
-    }
-    __shared__ int last;
-    // Every wavefront has issued its words before the workgroup counts itself in.
-    issue_barrier();
-    if (tid == 0) {
-        const unsigned before =
-            __hip_atomic_fetch_add(g.arrivals + rest, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = before == (unsigned)(g.split_k - 1);
-        if (last) {
-            // Every other split of this tile has counted itself in: reset the
-            // counter for the next run; a word-tagged launch counts the tile
-            // finished.
-            __hip_atomic_store(g.arrivals + rest, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (g.epoch_word) advance_epoch(g, count_split_tiles(g), epoch);
+        for (int q = 0; q < EPT; ++q) {
+            const int e = tid + q * T::THREADS;
+            const int r = row0 + e / T::BN, c = col0 + e % T::BN;
+            if (e < ELEMS && r < g.m && c < g.n)
+                store_tagged_word(g.partial + split * plane + (size_t)r * g.n + c, own[q], epoch);
         }
+        return;
     }
-    __syncthreads();
-    if (!last) return;
     int budget = g.wait_budget;
     const unsigned want = epoch ^ g.epoch_xor;
 
