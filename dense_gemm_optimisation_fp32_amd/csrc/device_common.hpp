@@ -178,10 +178,19 @@ __device__ __forceinline__ float wait_tagged_word(const unsigned long long *p, u
 // split tile advances: one past the word's count, bit 31 set (so the two
 // kinds never meet, and no tag is 0, the tag of words never written).
 // Every workgroup that shares a tile reads the word before it tags a word.
+__device__ __forceinline__ unsigned load_epoch_word(const GemmArgs &g)
+{
+    return __hip_atomic_load(g.epoch_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned run_epoch_of(unsigned epoch_word)
+{
+    return ((epoch_word + 1u) & 0x7fffffffu) | 0x80000000u;
+}
+
 __device__ __forceinline__ unsigned load_run_epoch(const GemmArgs &g)
 {
-    return ((__hip_atomic_load(g.epoch_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u) & 0x7fffffffu) |
-           0x80000000u;
+    return run_epoch_of(load_epoch_word(g));
 }
 
 // Counts split tiles finished (one thread of their last arriver,

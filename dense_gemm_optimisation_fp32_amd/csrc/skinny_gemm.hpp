@@ -188,12 +188,21 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
     // has read it.
     __shared__ unsigned run_epoch;
     const bool word_tag = g.epoch_word != nullptr && g.split_k > 1;
-    unsigned tag_read = 0, before = 0;
-    if (word_tag && tid == 0) tag_read = load_run_epoch(g);
+    unsigned word_read = 0, tag_read = 0, before = 0;
+    if (word_tag && tid == 0) word_read = load_epoch_word(g);   // waited for at the count
     auto count_in = [&]() {
         if (g.split_k > 1 && tid == 0) {
-            if (word_tag) run_epoch = tag_read;
-            before = __hip_atomic_fetch_add(g.arrivals + rest, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            int slot = rest;
+            if (word_tag) {
+                // The count goes out only once the word has come back: the
+                // empty asm takes the word here (not earlier) and makes the
+                // counter's index depend on it.
+                unsigned w = word_read;
+                asm volatile("" : "+v"(w), "+v"(slot));
+                tag_read = run_epoch_of(w);
+                run_epoch = tag_read;
+            }
+            before = __hip_atomic_fetch_add(g.arrivals + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     };
 
