@@ -59,6 +59,14 @@ struct GemmArgs {
     unsigned epoch_xor;    // readers wait for the tag (this run's epoch) ^ epoch_xor (0; a test sets
                            // it so that no word ever matches and every wait gives up)
     int poison_lds;        // 1: fill LDS with NaN before the first copy (a test of the waits)
+    // Column sliver carried by a whole-tile launch (gemm_mfma_dma_sliver_kernel):
+    // workgroups from sliver_wg0 on compute the sliver_cols columns after
+    // the tiles' n with the few-column method.
+    int sliver_wg0;        // first workgroup of the sliver (the tiles' count)
+    int sliver_cols;
+    const float *sliver_B; // B at the sliver's first column
+    uint32_t sliver_b_bytes;
+    float *sliver_C;       // C at the sliver's first column
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)

@@ -10,8 +10,8 @@
 // adjacent addresses) and meets the few B columns, which every row shares,
 // in LDS.
 //
-// Workgroup: 4 wavefronts, ROWS_PER_WAVE rows each (grid over row blocks and
-// groups of R columns).  k runs in chunks of KC: the workgroup copies the
+// Workgroup: 4 wavefronts (WAVES), ROWS_PER_WAVE rows each (grid over row
+// blocks and groups of R columns).  k runs in chunks of KC: the workgroup copies the
 // chunk of its R columns of B into LDS (k-contiguous per column, zeros past
 // K and past N), then each wavefront reads its rows' k-chunk, lane l taking
 // k = 4l + 256q + t (t = 0..3), multiplies with one 16-byte LDS read per
@@ -24,13 +24,13 @@
 
 namespace gemmf32 {
 
-template <int R_>
+template <int R_, int WAVES_ = 4, int ROWS_PER_WAVE_ = 2>
 struct FewColTile {
     static_assert(R_ == 1 || R_ == 4 || R_ == 8, "columns per workgroup");
     static constexpr int R = R_;                 // columns of C per workgroup
-    static constexpr int WAVES = 4;
+    static constexpr int WAVES = WAVES_;
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int ROWS_PER_WAVE = 2;
+    static constexpr int ROWS_PER_WAVE = ROWS_PER_WAVE_;
     static constexpr int ROWS = WAVES * ROWS_PER_WAVE;   // rows of C per workgroup
     static constexpr int KC = R_ == 8 ? 1024 : 2048;   // k per LDS chunk (at most 32 KiB of B)
     static constexpr int GROUPS = KC / 256;      // 16-byte loads per lane per row and chunk
@@ -102,21 +102,19 @@ __device__ __forceinline__ void fewcol_copy_b(const GemmArgs &g, __amdgpu_buffer
     }
 }
 
-// Grid: ceil(m / ROWS) row blocks x ceil(n / R) column groups (row block
-// fastest).
-// (Registers are held to four wavefronts per SIMD, 16 per CU, so that enough
-// loads of A are in flight.)
+// Workgroup `block` of the grid: ceil(m / ROWS) row blocks x ceil(n / R)
+// column groups (row block fastest).  `bs`: LDS for the B chunk
+// (T::LDS_BYTES).  Every row is computed the same way whatever the number of
+// wavefronts, so a tile with more wavefronts gives bitwise the same C.
 template <class T, bool B_COL>
-__global__ __launch_bounds__(T::THREADS, 4) void gemm_fewcol_kernel(GemmArgs g)
+__device__ __forceinline__ void fewcol_body(const GemmArgs &g, int block, f32x4 *bs)
 {
-    __shared__ f32x4 bs[T::R * T::LD / 4];   // [column][k] chunk of B, k-contiguous
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int row_blocks = (g.m + T::ROWS - 1) / T::ROWS;
-    const int rb = (int)blockIdx.x % row_blocks;
-    const int j0 = ((int)blockIdx.x / row_blocks) * T::R;
+    const int rb = block % row_blocks;
+    const int j0 = (block / row_blocks) * T::R;
     const int row0 = rb * T::ROWS + wave * T::ROWS_PER_WAVE;
 
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
@@ -142,17 +140,22 @@ __global__ __launch_bounds__(T::THREADS, 4) void gemm_fewcol_kernel(GemmArgs g)
                 for (int q = 0; q < T::GROUPS; ++q)
                     a[t][q] = buf_load_x4(ra, elem_off(row0 + t < g.m, row0 + t, g.lda, kc + 4 * lane + 256 * q));
         } else {
-            // The last chunk: element by element (elements past K may be
-            // the next row's, or padding).
+            // The last chunk: the groups below K with one load each, zeros
+            // past it, and the group that K cuts element by element
+            // (elements past K may be the next row's, or padding).
 #pragma unroll
             for (int t = 0; t < T::ROWS_PER_WAVE; ++t)
 #pragma unroll
-                for (int q = 0; q < T::GROUPS; ++q)
+                for (int q = 0; q < T::GROUPS; ++q) {
+                    const int kk = 4 * lane + 256 * q;
+                    const bool row_ok = row0 + t < g.m;
+                    a[t][q] = buf_load_x4(ra, elem_off(row_ok && kk + 4 <= klen, row0 + t, g.lda, kc + kk));
+                    if (kk < klen && kk + 4 > klen) {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int kk = 4 * lane + 256 * q + u;
-                        a[t][q][u] = buf_load_x1(ra, elem_off(row0 + t < g.m && kk < klen, row0 + t, g.lda, kc + kk));
+                        for (int u = 0; u < 4; ++u)
+                            a[t][q][u] = buf_load_x1(ra, elem_off(row_ok && kk + u < klen, row0 + t, g.lda, kc + kk + u));
                     }
+                }
         }
         // The B chunk: element (k, column j0 + j) for k < klen and j0 + j < n,
         // zero elsewhere.  Column-major B is read along k; row-major B along
@@ -186,6 +189,15 @@ __global__ __launch_bounds__(T::THREADS, 4) void gemm_fewcol_kernel(GemmArgs g)
             if (lane == 0 && row < g.m && j0 + j < g.n) g.C[(size_t)row * g.ldc + j0 + j] = v;
         }
     }
+}
+
+// (Registers are held to four wavefronts per SIMD, 16 per CU, so that enough
+// loads of A are in flight.)
+template <class T, bool B_COL>
+__global__ __launch_bounds__(T::THREADS, 4) void gemm_fewcol_kernel(GemmArgs g)
+{
+    __shared__ f32x4 bs[T::R * T::LD / 4];   // [column][k] chunk of B, k-contiguous
+    fewcol_body<T, B_COL>(g, (int)blockIdx.x, bs);
 }
 
 }  // namespace gemmf32

@@ -64,6 +64,8 @@ struct VariantDesc {
     const void *fn_ex[2][2][2];  // [column-major A][column-major B][epilogue], or NULL
     const void *fn_wide[2][2];  // [column-major A][epilogue]: row-major B, C stored NB columns
                                 // at a time (N a multiple of NB), or NULL
+    const void *fn_sliver[2];   // [column-major B]: whole tiles carrying a column sliver, or NULL
+    const void *fn_sliver_wide; // the same with the wide C stores, or NULL
 };
 
 template <class T>
@@ -109,6 +111,19 @@ VariantDesc dma_ex_variant(const char *name)
         d.fn_wide[0][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, false, false, true, true>);
         d.fn_wide[1][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, false, true, true, true>);
     }
+    return d;
+}
+
+// A dispatch candidate's tile of 128 x 128 or more: also the kernels that
+// carry a column sliver.
+template <class T>
+VariantDesc with_sliver(VariantDesc d)
+{
+    using namespace gemmf32;
+    d.fn_sliver[0] = reinterpret_cast<const void *>(&gemm_mfma_dma_sliver_kernel<T, false>);
+    d.fn_sliver[1] = reinterpret_cast<const void *>(&gemm_mfma_dma_sliver_kernel<T, true>);
+    if constexpr (T::NB == 2 || T::NB == 4)
+        d.fn_sliver_wide = reinterpret_cast<const void *>(&gemm_mfma_dma_sliver_kernel<T, false, false, false, true>);
     return d;
 }
 
@@ -189,9 +204,9 @@ const VariantDesc &variant(int v)
         dma_variant<DmaTile<256, 256, 16, 2, 2, 3>>("dma_256x256x16_w2x2_s3"),
         dma_ex_variant<DmaTile<256, 256, 16, 2, 2, 4>>("dma_256x256x16_w2x2_s4"),
         dma_variant<DmaTile<256, 256, 32, 2, 2, 2>>("dma_256x256x32_w2x2_s2"),
-        dma_ex_variant<DmaTile<128, 128, 16, 2, 2, 3, false>>("dma_128x128x16_w2x2_s3"),
+        with_sliver<DmaTile<128, 128, 16, 2, 2, 3, false>>(dma_ex_variant<DmaTile<128, 128, 16, 2, 2, 3, false>>("dma_128x128x16_w2x2_s3")),
         dma_variant<DmaTile<128, 128, 32, 2, 2, 3, false>>("dma_128x128x32_w2x2_s3"),
-        dma_ex_variant<DmaTile<256, 128, 16, 2, 2, 3>>("dma_256x128x16_w2x2_s3"),
+        with_sliver<DmaTile<256, 128, 16, 2, 2, 3>>(dma_ex_variant<DmaTile<256, 128, 16, 2, 2, 3>>("dma_256x128x16_w2x2_s3")),
         skinny_variant<SkinnyTile<4, 4, 64>>("skinny_16x64_w4_d4"),
         skinny_variant<SkinnyTile<8, 4, 64>>("skinny_16x64_w8_d4"),
         dma_ex_variant<DmaTile<64, 64, 16, 2, 2, 3>>("dma_64x64x16_w2x2_s3"),
@@ -206,7 +221,7 @@ const VariantDesc &variant(int v)
         fewcol_variant<gemmf32::FewColR4>("fewcol_8x4_k2048"),
         fewcol_variant<gemmf32::FewColR8>("fewcol_8x8_k1024"),
         dma_variant<DmaTile<256, 256, 16, 2, 4, 4>>("dma_256x256x16_w2x4_s4"),
-        dma_ex_variant<DmaTile<256, 256, 16, 4, 2, 4>>("dma_256x256x16_w4x2_s4"),
+        with_sliver<DmaTile<256, 256, 16, 4, 2, 4>>(dma_ex_variant<DmaTile<256, 256, 16, 4, 2, 4>>("dma_256x256x16_w4x2_s4")),
         dma_variant<DmaTile<256, 256, 16, 4, 2, 2>>("dma_256x256x16_w4x2_s2"),
         dma_variant<DmaTile<256, 256, 16, 4, 4, 4>>("dma_256x256x16_w4x4_s4"),
     };
@@ -376,9 +391,11 @@ struct gemm_f32_plan_impl {
     std::atomic<unsigned> runs{0};   // argument tags handed out so far
     int c_store_width = 1;           // C elements per store of the whole-tile kernel
     // Column sliver: the last sliver_cols columns of C run as a second launch
-    // with a plan of their own (this plan then covers columns [0, n)).
+    // with a plan of their own (this plan then covers columns [0, n)), or,
+    // with sliver_fused, as further workgroups of this plan's launch.
     gemm_f32_plan_impl *sliver = nullptr;
     int64_t sliver_col0 = 0;
+    bool sliver_fused = false;
 };
 
 namespace {
@@ -845,6 +862,54 @@ const float *sliver_b(const gemm_f32_plan_impl *p, const float *B)
     return p->layout_b == GEMM_F32_ROW_MAJOR ? B + p->sliver_col0 : B + p->sliver_col0 * p->ldb;
 }
 
+// Fused column sliver.  A whole-tile plan whose last wave of tiles leaves
+// workgroup slots idle can carry its sliver in the same launch
+// (gemm_mfma_dma_sliver_kernel): the few-column workgroups come after every
+// tile in the grid, so they are dispatched into those idle slots instead of
+// running as a second launch after the last tile.  Taken when the kernel
+// exists for the plan's tile and B layout, holds as many workgroups per CU
+// as the plan's own kernel, and the idle slot time of the last wave (idle
+// slots x one tile's time at that occupancy) is at least twice the sliver's
+// estimated work (per workgroup: 3 us plus its rows of A at 40 GB/s).
+// At 5003 x 4097 x 2049 (1280 tiles of 128 x 128 in 768 slots) the 626
+// few-column workgroups run in the 256 slots the second wave leaves idle.
+// GEMM_F32_SLIVER_FUSE=0 keeps the second launch.
+void fuse_sliver(gemm_f32_plan p, const DeviceFacts &f)
+{
+    if (!p->sliver || p->workspace || p->args.sk_wgs || p->args.split_k != 1 || p->epilogue ||
+        p->layout_a != GEMM_F32_ROW_MAJOR || env_int("GEMM_F32_SLIVER_FUSE", 1) == 0)
+        return;
+    const VariantDesc &d = variant(p->variant);
+    const int col = p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0;
+    const void *fn = p->c_store_width > 1 ? d.fn_sliver_wide : d.fn_sliver[col];
+    if (!fn) return;
+    int plain = 0, fused = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&plain, p->fn, (int)p->block, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&fused, fn, (int)p->block, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return;
+    }
+    if (fused < 1 || fused != plain) return;
+    const int64_t slots = (int64_t)plain * f.cu_count;
+    const int64_t last = (int64_t)p->grid % slots;
+    if (last == 0) return;
+    const int rows = (int)p->block / 64;   // rows per few-column workgroup (one per wavefront)
+    const int64_t wgs = ceil_div(p->m, rows) * p->sliver->n;
+    const double t_tile = 2.0 * d.bm * d.bn * (double)p->k * plain / (157.3e12 / f.cu_count);
+    const double t_wg = 3e-6 + 4.0 * rows * (double)p->k / 40e9;
+    if ((double)(slots - last) * t_tile < 2.0 * (double)wgs * t_wg) return;
+    if ((int64_t)p->grid + wgs > INT32_MAX) return;
+    p->fn = fn;
+    p->args.sliver_wg0 = (int)p->grid;
+    p->args.sliver_cols = (int)p->sliver->n;
+    p->args.sliver_b_bytes = p->sliver->args.b_bytes;
+    p->grid += (unsigned)wgs;
+    p->sliver_fused = true;
+    if (env_int("GEMM_F32_LOG", 0))
+        std::fprintf(stderr, "[gemm_f32] column sliver of %lld columns in the same launch: %lld workgroups after %d tiles\n",
+                     (long long)p->sliver->n, (long long)wgs, p->args.sliver_wg0);
+}
+
 int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int64_t k, int layout_a,
               int layout_b, int64_t lda, int64_t ldb, int64_t ldc, int epilogue, bool allow_sliver = true)
 {
@@ -885,6 +950,9 @@ int make_plan(gemm_f32_plan *out, int forced_variant, int64_t m, int64_t n, int6
             return st;
         }
         p->sliver_col0 = n - r;
+        int dev = 0;
+        DeviceFacts facts;
+        if (device_facts(&dev, &facts) == GEMM_F32_SUCCESS) fuse_sliver(p, facts);
     }
     *out = p;
     return GEMM_F32_SUCCESS;
@@ -1089,8 +1157,12 @@ int gemm_f32_run(gemm_f32_plan p, const float *A, const float *B, float *C, void
     a.A = A;
     a.B = B;
     a.C = C;
+    if (p->sliver_fused) {
+        a.sliver_B = sliver_b(p, B);
+        a.sliver_C = C + p->sliver_col0;
+    }
     const int st = launch(p, a, stream);
-    if (st != GEMM_F32_SUCCESS || !p->sliver) return st;
+    if (st != GEMM_F32_SUCCESS || !p->sliver || p->sliver_fused) return st;
     return gemm_f32_run(p->sliver, A, sliver_b(p, B), C + p->sliver_col0, stream);
 }
 
@@ -1171,9 +1243,13 @@ int gemm_f32_run_ex(gemm_f32_plan p, const float *A, const float *B, float *C, f
     a.use_beta = beta != 0.0f ? 1 : 0;
     a.bias = bias;
     a.act = activation;
+    if (p->sliver_fused) {
+        a.sliver_B = sliver_b(p, B);
+        a.sliver_C = C + p->sliver_col0;
+    }
     const int st = launch(p, a, stream);
     // (Only plain plans have a sliver, so these are the plain values.)
-    if (st != GEMM_F32_SUCCESS || !p->sliver) return st;
+    if (st != GEMM_F32_SUCCESS || !p->sliver || p->sliver_fused) return st;
     return gemm_f32_run(p->sliver, A, sliver_b(p, B), C + p->sliver_col0, stream);
 }
 
@@ -1225,6 +1301,7 @@ int gemm_f32_describe(gemm_f32_plan p, gemm_f32_info *info)
         info->sliver_cols = p->sliver->n;
         info->sliver_variant = p->sliver->variant;
         info->sliver_stream_k = p->sliver->args.sk_wgs;
+        info->sliver_fused = p->sliver_fused ? 1 : 0;
     }
     return GEMM_F32_SUCCESS;
 }

@@ -719,11 +719,11 @@ __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsr
 
 // One whole tile per workgroup.  A_COL: column-major A; EPI: the
 // linear-layer epilogue; WIDE_C: row-major B, N a multiple of T::NB, C
-// stored NB adjacent columns per instruction.
+// stored NB adjacent columns per instruction.  `lds`: the copy ring,
+// T::STAGES * (T::A_CHUNKS + T::B_CHUNKS) chunks.
 template <class T, bool B_COL, bool A_COL = false, bool EPI = false, bool WIDE_C = false>
-__global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_kernel(GemmArgs g)
+__device__ __forceinline__ void dma_whole_tile(const GemmArgs &g, f32x4 *lds)
 {
-    __shared__ f32x4 lds[T::STAGES * (T::A_CHUNKS + T::B_CHUNKS)];
     f32x4 *const lds_a = lds;                                // [STAGES][A_CHUNKS]
     f32x4 *const lds_b = lds + T::STAGES * T::A_CHUNKS;      // [STAGES][B_CHUNKS]
 
@@ -752,6 +752,13 @@ __global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_kernel(GemmArgs g)
         for (int nb = 0; nb < T::NB; ++nb) acc[mb][nb] = f32x16{};
     dma_range<T, B_COL, A_COL>(g, lds_a, lds_b, ra, rb, row0, col0, 0, g.k_tiles, tid, wave, wr, wc, l32, half, acc);
     dma_store_c<T, B_COL, A_COL, EPI, WIDE_C>(g, rc, row0, col0, wr, wc, l32, half, acc);
+}
+
+template <class T, bool B_COL, bool A_COL = false, bool EPI = false, bool WIDE_C = false>
+__global__ __launch_bounds__(T::THREADS) void gemm_mfma_dma_kernel(GemmArgs g)
+{
+    __shared__ f32x4 lds[T::STAGES * (T::A_CHUNKS + T::B_CHUNKS)];
+    dma_whole_tile<T, B_COL, A_COL, EPI, WIDE_C>(g, lds);
 }
 
 // Stream-K ("GEMM 性能优化", Wave 模型: a last, partly filled wave of tiles

@@ -181,8 +181,9 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
     // tile's arrival counter as soon as thread 0's wavefront has issued its
     // last loads, so the count's round trip overlaps the stream; the last to
     // count in adds the splits.  Every workgroup counted in is resident and
-    // has only its last loads, the sums and its stores left, so the last
-    // one's wait for their words is short (and bounded in any case).  A
+    // in its last pass (its other wavefronts stream alongside thread 0's),
+    // with only the sums and its stores after it, so the last one's wait for
+    // their words is short (and bounded in any case).  A
     // word-tagged launch (captured in a graph) reads its tag first, so that
     // when the run's last split tile advances the epoch word every workgroup
     // has read it.

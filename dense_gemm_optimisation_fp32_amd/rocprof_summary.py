@@ -46,18 +46,20 @@ def short_name(kernel: str) -> str:
         base = f"dma_{m.group(1)}x{m.group(2)}x{m.group(3)}{waves}_s{m.group(6)}"
         if "sk_kernel" in k:
             return "sk_" + base + ("_bcol" if re.search(r"EEELb1EEEv|>, true>", k) else "")
+        sliver = "_sliver" if "sliver_kernel" in k else ""
         flags = re.search(r">, (true|false), (true|false), (true|false), (true|false)>", k)
         if flags:
             tags = [t for t, f in zip(("bcol", "acol", "epi", "wide"), flags.groups()) if f == "true"]
-            return base + "".join("_" + t for t in tags)
-        return base
+            return base + "".join("_" + t for t in tags) + sliver
+        return base + sliver
     m = re.search(r"SkinnyTile<(\d+), (\d+), (\d+)>", k) or re.search(r"SkinnyTileILi(\d+)ELi(\d+)ELi(\d+)", k)
     if m:
         return f"skinny_16x{m.group(3)}_w{m.group(1)}_d{m.group(2)}"
     m = re.search(r"MfmaTile<(\d+), (\d+), (\d+), \d+, \d+>", k) or re.search(r"MfmaTileILi(\d+)ELi(\d+)ELi(\d+)", k)
     if m and "gemm_mfma_kernel" in k:
         return f"mfma_{m.group(1)}x{m.group(2)}x{m.group(3)}"
-    m = re.search(r"FewColTile<(\d+)>, (true|false)", k) or re.search(r"FewColTileILi(\d+)EEELb([01])", k)
+    m = (re.search(r"FewColTile<(\d+)(?:, \d+, \d+)?>, (true|false)", k)
+         or re.search(r"FewColTileILi(\d+)E(?:Li\d+ELi\d+E)?EELb([01])", k))
     if m:
         return f"fewcol_r{m.group(1)}" + ("_bcol" if m.group(2) in ("true", "1") else "")
     if "gemm_valu_kernel" in k:

@@ -126,13 +126,17 @@ struct gemm_f32_info {
     int waves_per_simd;     /* plan only: workgroups_per_cu * wavefronts per workgroup / 4 */
     /* Column sliver (plan only): when the tile the dispatch picks would leave
      * a last tile-column at most an eighth full, the plan covers the first
-     * n - sliver_cols columns (tiles_n, grid, ... describe that launch) and
-     * runs the last sliver_cols columns as a second launch on the same stream,
-     * with a plan of its own (variant sliver_variant, stream-K over
-     * sliver_stream_k workgroups).  0: one launch. */
+     * n - sliver_cols columns (tiles_n, ... describe those tiles) and runs the
+     * last sliver_cols columns with the few-column method: as a second launch
+     * on the same stream, with a plan of its own (variant sliver_variant,
+     * stream-K over sliver_stream_k workgroups), or, with sliver_fused = 1, as
+     * further workgroups of the tiles' launch (grid counts them; they take the
+     * slots a partly filled last wave of tiles leaves idle).  The two give
+     * bitwise the same C.  sliver_cols = 0: one launch, no sliver. */
     int64_t sliver_cols;
     int sliver_variant;
     int sliver_stream_k;
+    int sliver_fused;
 };
 
 /*
@@ -165,6 +169,8 @@ int gemm_f32_validate(int64_t m, int64_t n, int64_t k, int layout_b,
  *   GEMM_F32_STREAMK=0        never choose stream-K automatically;
  *   GEMM_F32_SLIVER=0         never split off a column sliver (see
  *                             gemm_f32_info.sliver_cols);
+ *   GEMM_F32_SLIVER_FUSE=0    run a sliver as a second launch, never in
+ *                             the tiles' launch (gemm_f32_info.sliver_fused);
  *   GEMM_F32_NUM_XCD=<count>  the XCD count the rasterisation undoes
  *                             (default: the device's; 1 turns the XCD
  *                             remap off, for measuring it);

@@ -637,6 +637,38 @@ def test_few_columns_vs_oracle(shape, layout_b):
     assert np.array_equal(C.astype(np.float64), Cref)
 
 
+SLIVER_SHAPES = [(5003, 4097, 2049), (3001, 2049, 1500), (1500, 1025, 3000), (4400, 4097, 1024),
+                 (2500, 3073, 777), (6000, 8193, 520), (700, 2049, 4100)]
+
+
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+@pytest.mark.parametrize("shape", SLIVER_SHAPES)
+def test_fused_sliver_matches_second_launch(shape, layout_b, monkeypatch):
+    """A column sliver carried by the tiles' launch gives bitwise the C of
+    the same plan with the sliver as a second launch (GEMM_F32_SLIVER_FUSE=0),
+    and matches the oracle on every element (integer inputs bit for bit)."""
+    m, n, k = shape
+    print(f"\n[case] fused sliver {shape} layout_b={layout_b}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=2100 + m + k)
+    C1, info1 = run_gemm(A, B, m, n, k, layout_b)
+    monkeypatch.setenv("GEMM_F32_SLIVER_FUSE", "0")
+    C0, info0 = run_gemm(A, B, m, n, k, layout_b)
+    monkeypatch.delenv("GEMM_F32_SLIVER_FUSE")
+    print(f"  {info1['name']} sliver {info1['sliver_cols']} fused {info1['sliver_fused']} "
+          f"grid {info1['grid']} / {info0['grid']}", flush=True)
+    assert info0["sliver_fused"] == 0 and info1["sliver_cols"] == info0["sliver_cols"]
+    if info1["sliver_fused"]:
+        rows = info1["threads"] // 64
+        assert info1["grid"] == info0["grid"] + -(-m // rows) * info1["sliver_cols"]
+    assert np.array_equal(C1, C0)
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    check_close(C1, Cref, S, f"fused sliver {shape}")
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=2200 + m + k)
+    C, _ = run_gemm(A, B, m, n, k, layout_b)
+    Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    assert np.array_equal(C.astype(np.float64), Cref)
+
+
 def test_few_columns_padded_strides():
     """NaN padding of A's and B's rows never reaches C; C's padding is kept."""
     m, n, k = 700, 3, 2100
@@ -651,9 +683,9 @@ def test_few_columns_padded_strides():
 
 @pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
 def test_column_sliver_plan(layout_b):
-    """A shape whose last tile-column would hold one column runs it as a
-    second launch on the few-column kernel: every element matches the oracle
-    (integer inputs bit for bit) and repeats bit for bit."""
+    """A shape whose last tile-column would hold one column runs it with
+    the few-column method, in the tiles' launch: every element matches the
+    oracle (integer inputs bit for bit) and repeats bit for bit."""
     import dense_gemm_optimisation_fp32_amd as g
 
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
@@ -664,6 +696,9 @@ def test_column_sliver_plan(layout_b):
     C, info, outs = run_gemm(A, B, m, n, k, layout_b, repeat=2)
     assert info["sliver_cols"] == 1 and info["sliver_variant"] == [
         v for v in range(g.gemm_f32_num_variants()) if g.gemm_f32_variant_info(v)["name"] == "fewcol_8x1_k2048"][0]
+    # 1280 tiles of 128 x 128 in 768 slots: the sliver's 1251 one-row
+    # workgroups ride in the idle slots of the second wave.
+    assert info["sliver_fused"] == 1 and info["grid"] == info["tiles_m"] * info["tiles_n"] + (m + 3) // 4
     assert np.array_equal(outs[0], outs[1])
     Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
     check_close(C, Cref, S, "column sliver")
