@@ -114,8 +114,7 @@ VariantDesc dma_ex_variant(const char *name)
     return d;
 }
 
-// A dispatch candidate's tile of 128 x 128 or more: also the kernels that
-// carry a column sliver.
+// The 128 x 128 candidate: also the kernels that carry a column sliver.
 template <class T>
 VariantDesc with_sliver(VariantDesc d)
 {
@@ -206,7 +205,7 @@ const VariantDesc &variant(int v)
         dma_variant<DmaTile<256, 256, 32, 2, 2, 2>>("dma_256x256x32_w2x2_s2"),
         with_sliver<DmaTile<128, 128, 16, 2, 2, 3, false>>(dma_ex_variant<DmaTile<128, 128, 16, 2, 2, 3, false>>("dma_128x128x16_w2x2_s3")),
         dma_variant<DmaTile<128, 128, 32, 2, 2, 3, false>>("dma_128x128x32_w2x2_s3"),
-        with_sliver<DmaTile<256, 128, 16, 2, 2, 3>>(dma_ex_variant<DmaTile<256, 128, 16, 2, 2, 3>>("dma_256x128x16_w2x2_s3")),
+        dma_ex_variant<DmaTile<256, 128, 16, 2, 2, 3>>("dma_256x128x16_w2x2_s3"),
         skinny_variant<SkinnyTile<4, 4, 64>>("skinny_16x64_w4_d4"),
         skinny_variant<SkinnyTile<8, 4, 64>>("skinny_16x64_w8_d4"),
         dma_ex_variant<DmaTile<64, 64, 16, 2, 2, 3>>("dma_64x64x16_w2x2_s3"),
@@ -221,7 +220,7 @@ const VariantDesc &variant(int v)
         fewcol_variant<gemmf32::FewColR4>("fewcol_8x4_k2048"),
         fewcol_variant<gemmf32::FewColR8>("fewcol_8x8_k1024"),
         dma_variant<DmaTile<256, 256, 16, 2, 4, 4>>("dma_256x256x16_w2x4_s4"),
-        with_sliver<DmaTile<256, 256, 16, 4, 2, 4>>(dma_ex_variant<DmaTile<256, 256, 16, 4, 2, 4>>("dma_256x256x16_w4x2_s4")),
+        dma_ex_variant<DmaTile<256, 256, 16, 4, 2, 4>>("dma_256x256x16_w4x2_s4"),
         dma_variant<DmaTile<256, 256, 16, 4, 2, 2>>("dma_256x256x16_w4x2_s2"),
         dma_variant<DmaTile<256, 256, 16, 4, 4, 4>>("dma_256x256x16_w4x4_s4"),
     };

@@ -79,9 +79,10 @@ using Skinny16W16D4 = SkinnyTile<16, 4, 16>;
     X5(gemm_mfma_dma_kernel, T, true, false, true, false)         \
     X5(gemm_mfma_dma_kernel, T, false, true, true, false)         \
     X5(gemm_mfma_dma_kernel, T, true, true, true, false)
-// Whole-tile kernels that carry a column sliver (the shape dispatch's
-// candidate tiles of 128 x 128 and larger: the few-column path fits their
-// register budget); _WIDE: with the 8/16-byte C stores.
+// Whole-tile kernels that carry a column sliver (the 128 x 128 tile: the
+// dispatch's larger candidates pick shapes whose tiles fill whole waves, and
+// the few-column path does not fit the 64-row tiles' register budget);
+// _WIDE: with the 8/16-byte C stores.
 #define GEMMF32_DMA_SLIVER(X5, T)                                 \
     X5(gemm_mfma_dma_sliver_kernel, T, false, false, false, false) \
     X5(gemm_mfma_dma_sliver_kernel, T, true, false, false, false)
@@ -101,8 +102,7 @@ using Skinny16W16D4 = SkinnyTile<16, 4, 16>;
     GEMMF32_DMA_EX(X5, Dma256x256x16S4) GEMMF32_DMA_EX_WIDE(X5, Dma256x256x16S4)
 #define GEMMF32_UNIT_DMA256x128(X5, X2, X1)                       \
     GEMMF32_DMA_BASE(X5, X2, Dma256x128x16S3) GEMMF32_DMA_WIDE(X5, Dma256x128x16S3) \
-    GEMMF32_DMA_EX(X5, Dma256x128x16S3) GEMMF32_DMA_EX_WIDE(X5, Dma256x128x16S3) \
-    GEMMF32_DMA_SLIVER(X5, Dma256x128x16S3) GEMMF32_DMA_SLIVER_WIDE(X5, Dma256x128x16S3)
+    GEMMF32_DMA_EX(X5, Dma256x128x16S3) GEMMF32_DMA_EX_WIDE(X5, Dma256x128x16S3)
 #define GEMMF32_UNIT_DMA128(X5, X2, X1)                           \
     GEMMF32_DMA_BASE(X5, X2, Dma128x128x16S3) GEMMF32_DMA_WIDE(X5, Dma128x128x16S3) \
     GEMMF32_DMA_EX(X5, Dma128x128x16S3) GEMMF32_DMA_EX_WIDE(X5, Dma128x128x16S3) \
@@ -120,7 +120,6 @@ using Skinny16W16D4 = SkinnyTile<16, 4, 16>;
     GEMMF32_DMA_BASE(X5, X2, Dma256x256x16W24S4) GEMMF32_DMA_WIDE(X5, Dma256x256x16W24S4) \
     GEMMF32_DMA_BASE(X5, X2, Dma256x256x16W42S4) GEMMF32_DMA_WIDE(X5, Dma256x256x16W42S4) \
     GEMMF32_DMA_EX(X5, Dma256x256x16W42S4) GEMMF32_DMA_EX_WIDE(X5, Dma256x256x16W42S4) \
-    GEMMF32_DMA_SLIVER(X5, Dma256x256x16W42S4) GEMMF32_DMA_SLIVER_WIDE(X5, Dma256x256x16W42S4) \
     GEMMF32_DMA_BASE(X5, X2, Dma256x256x16W42S2) GEMMF32_DMA_WIDE(X5, Dma256x256x16W42S2) \
     GEMMF32_DMA_BASE(X5, X2, Dma256x256x16W44S4) GEMMF32_DMA_WIDE(X5, Dma256x256x16W44S4)
 #define GEMMF32_UNIT_OTHER(X5, X2, X1)                            \
