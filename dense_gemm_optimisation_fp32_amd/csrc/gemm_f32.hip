@@ -870,13 +870,18 @@ const float *sliver_b(const gemm_f32_plan_impl *p, const float *B)
 // as the plan's own kernel, and the idle slot time of the last wave (idle
 // slots x one tile's time at that occupancy) is at least twice the sliver's
 // estimated work (per workgroup: 3 us plus its rows of A at 40 GB/s).
-// At 5003 x 4097 x 2049 (1280 tiles of 128 x 128 in 768 slots) the 626
-// few-column workgroups run in the 256 slots the second wave leaves idle.
-// GEMM_F32_SLIVER_FUSE=0 keeps the second launch.
+// Slivers of one or two columns only: the fused workgroups take one column
+// each and read A once per column, where the second launch reads it once for
+// up to 8 columns.  At 5003 x (4096 + r) x 2049 (1280 tiles of 128 x 128 in
+// 768 slots; the sliver's workgroups run in the 256 slots the second wave
+// leaves idle), fused against two launches, in alternation on one GPU:
+// r = 1 594.3-594.5 against 606.7-608.4 us, r = 2 604.1-604.9 against
+// 611.1, r = 4 630.1-630.8 against 604.9-609.8, r = 8 683.9 against
+// 613.3-613.9.  GEMM_F32_SLIVER_FUSE=0 keeps the second launch.
 void fuse_sliver(gemm_f32_plan p, const DeviceFacts &f)
 {
-    if (!p->sliver || p->workspace || p->args.sk_wgs || p->args.split_k != 1 || p->epilogue ||
-        p->layout_a != GEMM_F32_ROW_MAJOR || env_int("GEMM_F32_SLIVER_FUSE", 1) == 0)
+    if (!p->sliver || p->sliver->n > 2 || p->workspace || p->args.sk_wgs || p->args.split_k != 1 ||
+        p->epilogue || p->layout_a != GEMM_F32_ROW_MAJOR || env_int("GEMM_F32_SLIVER_FUSE", 1) == 0)
         return;
     const VariantDesc &d = variant(p->variant);
     const int col = p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0;

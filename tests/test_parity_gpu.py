@@ -637,10 +637,12 @@ def test_few_columns_vs_oracle(shape, layout_b):
     assert np.array_equal(C.astype(np.float64), Cref)
 
 
-# Shapes whose default plan has a one-column sliver: on 128 x 128 tiles in
-# the tiles' launch (the first three), or as a second launch (the rest).
+# Shapes whose default plan has a one-column sliver, on 128 x 128 tiles in
+# the tiles' launch (the first three) or as a second launch (the next four);
+# then slivers of 2 columns (fused) and 4 columns (second launch).
 SLIVER_SHAPES = [(5003, 4097, 2049), (8000, 1025, 520), (5003, 1537, 1024), (8000, 1537, 520),
-                 (3001, 2049, 1500), (8000, 2049, 520), (4000, 1025, 1024)]
+                 (3001, 2049, 1500), (8000, 2049, 520), (4000, 1025, 1024), (5003, 4098, 2049),
+                 (5003, 4100, 2049)]
 
 
 @pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
@@ -660,7 +662,8 @@ def test_fused_sliver_matches_second_launch(shape, layout_b, monkeypatch):
           f"grid {info1['grid']} / {info0['grid']}", flush=True)
     assert info0["sliver_fused"] == 0 and info1["sliver_cols"] == info0["sliver_cols"]
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:   # the plans above were seen there
-        assert info1["sliver_cols"] == 1 and info1["sliver_fused"] == (shape in SLIVER_SHAPES[:3])
+        assert info1["sliver_cols"] == (n - 4096 if m == 5003 and n > 4097 else 1)
+        assert info1["sliver_fused"] == (shape in SLIVER_SHAPES[:3] + SLIVER_SHAPES[7:8])
     if info1["sliver_fused"]:
         rows = info1["threads"] // 64
         assert info1["grid"] == info0["grid"] + -(-m // rows) * info1["sliver_cols"]
