@@ -316,6 +316,14 @@ FEW_TILE_CASES = [
     ((768, 768, 1024), ("skinny_16x64_w8_d4", 1), None),
     ((512, 512, 8192), ("skinny_16x64_w8_d4", 1), None),
     ((1024, 1024, 1024), None, None),
+    # Few rows and a large B: the few-row plan reads B once per 16 rows and
+    # keeps it only while that is estimated faster than stream-K over 64 x 64
+    # tiles.
+    ((48, 4096, 4096), ("skinny_16x64_w8_d4", 1), None),
+    ((96, 2048, 4096), ("skinny_16x64_w8_d4", 1), None),
+    ((128, 4096, 4096), None, None),
+    ((112, 4096, 2048), None, None),
+    ((48, 8192, 4096), None, None),
 ]
 
 
@@ -334,6 +342,8 @@ def test_few_tile_rows_plan(shape, row_plan, col_plan, layout_b):
     C, info, outs = run_gemm(A, B, m, n, k, layout_b, repeat=2)
     if want is None:
         assert info["kind"] == 0 and info["name"].startswith("dma_")
+        if k >= 2048 and m < 256:
+            assert info["name"] == "dma_64x64x16_w2x2_s2" and info["stream_k"] > 0
     else:
         assert (info["name"], info["split_k"]) == want
         assert info["grid"] == info["tiles_m"] * info["tiles_n"] * want[1]
