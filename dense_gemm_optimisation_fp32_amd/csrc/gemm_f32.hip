@@ -478,50 +478,29 @@ double estimate_seconds(const Candidate &cand, int per_cu, int per_cu_sk, int64_
 // workgroups that bring the grid to one workgroup per CU; at most 3072 k per
 // tile otherwise); then 16 x 64 tiles with 16 wavefronts and the same k
 // split; then 16 x 64 tiles with 8 wavefronts while T64 is within one
-// workgroup per CU, or two for k in [512, 4096], or three for k in [512,
-// 2048] (row-major B; column-major B, whose columns the few-row kernel reads
-// less evenly, up to one, and only to k = 2048 unless T64 <= CUs / 2).  Measured on one MI355X (us, this rule's plan / the tiled
-// or stream-K plan it replaces): 256x256x256 5.5 / 7.6, 128x512x1024 5.6 /
-// 21.2, 64x256x4096 6.8 / 25.4, 128x512x4096 10.2 / 26.6, 256x256x16384
-// 23.9 / 80.7, 300x700x1500 12.0 / 42.3, 640x320x1024 7.7 / 21.3,
-// 512x512x8192 39.9 / 54.0, 800x600x3000 33.8 / 44.7, 768x768x1024 17.7 /
-// 28.3; the tiled plans stay ahead from 1024x1024 (1024 tiles of 16 x 64)
-// and on 768x768x4096 (57.1 / 61.4 on 16 x 64 tiles).  Returns the variant
-// and *split, its k-split count, or -1.
+// workgroup per CU, or three for k in [512, 4096] (row-major B; column-major
+// B, whose columns the few-row kernel reads less evenly, up to one, and only
+// to k = 2048 unless T64 <= CUs / 2).  The row tiles of a column of tiles
+// run side by side on one XCD (gemm_skinny_kernel), so B, read once per 16
+// rows, comes from that XCD's L2 after the first.  Measured on one MI355X
+// (us, this rule's plan / the tiled or stream-K plan it replaces):
+// 256x256x256 5.5 / 7.6, 128x512x1024 5.6 / 21.2, 64x256x4096 6.8 / 25.4,
+// 128x512x4096 10.2 / 26.6, 256x256x16384 23.9 / 80.7, 300x700x1500 12.0 /
+// 42.3, 640x320x1024 7.7 / 21.3, 512x512x8192 39.9 / 54.0, 800x600x3000
+// 33.8 / 44.7, 768x768x1024 17.7 / 28.3; row-major B, k in (2048, 4096]:
+// 128x4096x4096 42.4 / 55.5, 160x4096x4096 57.2 / 70.4, 96x8192x4096 73.7 /
+// 87.5, 768x768x4096 57.7 / 62.9, 192x4096x3000 45.4 / 51.0, 1000x600x4000
+// 61.9 / 59.4 (the one loss); the tiled plans stay ahead from 1024x1024
+// (1024 tiles of 16 x 64).  Returns the variant and *split, its k-split
+// count, or -1.
 // The few-tile, long-k rule of the shape dispatch (below).
 bool few_tile_stream_k(int64_t m, int64_t n, int64_t k, const DeviceFacts &f, bool tail_ok)
 {
     return tail_ok && 2 * ceil_div(m, 64) * ceil_div(n, 64) < 5 * (int64_t)f.cu_count && k >= 2048;
 }
 
-// Whether the few-row plan on 16-row tiles is estimated faster than the
-// stream-K plan over 64 x 64 tiles (for shapes where the latter applies).
-// The few-row plan reads B once per 16 rows of A: from the L2s and the
-// last-level cache at ~12 TB/s while B is at most 24 MiB, ~6 TB/s beyond
-// (the last-level cache alone), plus 2 us.  The stream-K plan runs
-// 2 M' N' K (M', N' rounded up to 64) at a rate that grows with its tile
-// count and with k: 105 TFLOP/s x (1 - exp(-tiles / T0)), T0 = 97 x
-// (4096 / k)^0.55.  Fitted on one MI355X to M x N x K with M from 48 to 160
-// and N, K from 2048 to 14336 (row-major B; within ~10 % of the measured
-// times of both plans), and it keeps the few-row plan on the shapes
-// measured below.  Measured at M x 4096 x 4096 (us, few-row / stream-K):
-// M = 48 33.0 / 42.6, 64 41.7 / 42.6, 80 60.0 / 54.6, 128 92.3 / 55.4;
-// 48 x 8192 x 4096 63.0 / 56.6; 64 x 4096 x 14336 135.9 / 93.3;
-// 112 x 4096 x 2048 43.4 / 31.8; 96 x 2048 x 4096 31.5 / 38.4.
-bool few_rows_beat_stream_k(int64_t m, int64_t n, int64_t k)
-{
-    const double b_bytes = 4.0 * (double)k * (double)n;
-    const double t_rows = (double)ceil_div(m, 16) * b_bytes / (b_bytes <= 24.0 * 1048576.0 ? 12e12 : 6e12) + 2e-6;
-    const double tiles = (double)(ceil_div(m, 64) * ceil_div(n, 64));
-    const double t0 = 97.0 * std::pow(4096.0 / (double)k, 0.55);
-    const double rate = 105e12 * (1.0 - std::exp(-tiles / t0));
-    const double t_sk = 2.0 * tiles * 64.0 * 64.0 * (double)k / rate;
-    return t_rows <= t_sk;
-}
-
 int few_tile_rows(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFacts &f, int *split)
 {
-    if (few_tile_stream_k(m, n, k, f, true) && !few_rows_beat_stream_k(m, n, k)) return -1;
     const int64_t cus = f.cu_count;
     const int64_t t16 = ceil_div(m, 16) * ceil_div(n, 16);
     const int64_t t64 = ceil_div(m, 16) * ceil_div(n, 64);
@@ -538,10 +517,8 @@ int few_tile_rows(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFac
         *split = fill(t64);
         return V_SKINNY_W16_D4;
     }
-    const bool w8 = layout_b == GEMM_F32_ROW_MAJOR
-                        ? t64 <= cus || (t64 <= 2 * cus && k >= 512 && k <= 4096) ||
-                              (t64 <= 3 * cus && k >= 512 && k <= 2048)
-                        : 2 * t64 <= cus || (t64 <= cus && k <= 2048);
+    const bool w8 = layout_b == GEMM_F32_ROW_MAJOR ? t64 <= cus || (t64 <= 3 * cus && k >= 512 && k <= 4096)
+                                                   : 2 * t64 <= cus || (t64 <= cus && k <= 2048);
     if (w8) {
         *split = k < 2048 ? 1 : fill(t64);
         return V_SKINNY_W8_D4;

@@ -150,14 +150,14 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, h = lane >> 4;
 
-    // Workgroups on one XCD take neighbouring tiles of one split, so they
-    // share that XCD's L2 for A and for the cache lines of B that straddle
-    // two tiles.
+    // Workgroups on one XCD take neighbouring tiles of one split, row tiles
+    // first: the row tiles of one column of tiles read the same B at about
+    // the same time, through that XCD's L2.
     const int per_split = g.tiles_m * g.tiles_n;
     const int wg = xcd_contiguous(blockIdx.x, per_split * g.split_k, g.num_xcd);
     const int split = wg / per_split;
     const int rest = wg - split * per_split;
-    const int tm = rest / g.tiles_n, tn = rest - (rest / g.tiles_n) * g.tiles_n;
+    const int tn = rest / g.tiles_m, tm = rest - (rest / g.tiles_m) * g.tiles_m;
     const int row0 = tm * T::BM, col0 = tn * T::BN;
 
     // This wavefront's k-range: the split's range cut into WAVES shares of

@@ -316,14 +316,14 @@ FEW_TILE_CASES = [
     ((768, 768, 1024), ("skinny_16x64_w8_d4", 1), None),
     ((512, 512, 8192), ("skinny_16x64_w8_d4", 1), None),
     ((1024, 1024, 1024), None, None),
-    # Few rows and a large B: the few-row plan reads B once per 16 rows and
-    # keeps it only while that is estimated faster than stream-K over 64 x 64
-    # tiles.
+    # A few dozen rows against a large B (row-major: the few-row plan up to
+    # three 16 x 64 tiles per CU for k <= 4096; column-major: stream-K).
     ((48, 4096, 4096), ("skinny_16x64_w8_d4", 1), None),
     ((96, 2048, 4096), ("skinny_16x64_w8_d4", 1), None),
-    ((128, 4096, 4096), None, None),
-    ((112, 4096, 2048), None, None),
-    ((48, 8192, 4096), None, None),
+    ((128, 4096, 4096), ("skinny_16x64_w8_d4", 1), None),
+    ((112, 4096, 2048), ("skinny_16x64_w8_d4", 1), None),
+    ((48, 8192, 4096), ("skinny_16x64_w8_d4", 1), None),
+    ((160, 4096, 4096), ("skinny_16x64_w8_d4", 1), None),
 ]
 
 
