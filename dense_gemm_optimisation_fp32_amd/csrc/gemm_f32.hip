@@ -185,6 +185,7 @@ enum VariantId {
     V_DMA_256x256x16_W42_S4,
     V_DMA_256x256x16_W42_S2,
     V_DMA_256x256x16_W44_S4,
+    V_SKINNY32_W8_D4,
     V_COUNT
 };
 
@@ -224,6 +225,7 @@ const VariantDesc &variant(int v)
         dma_ex_variant<DmaTile<256, 256, 16, 4, 2, 4>>("dma_256x256x16_w4x2_s4"),
         dma_variant<DmaTile<256, 256, 16, 4, 2, 2>>("dma_256x256x16_w4x2_s2"),
         dma_variant<DmaTile<256, 256, 16, 4, 4, 4>>("dma_256x256x16_w4x4_s4"),
+        skinny_variant<SkinnyTile<8, 4, 64, 2>>("skinny_32x64_w8_d4"),
     };
     return table[v];
 }
@@ -555,7 +557,22 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
     *tail_tiles = 0;
     if (estimate) *estimate = 0.0;   // (not estimated for the few-row and few-tile plans)
     if (split) *split = 0;           // few-row plans: their k-split count (0: the automatic count)
-    if (m <= 32) return V_SKINNY_W16_D4;
+    if (m <= 32) {
+        // 17 to 32 rows: 32-row tiles (8 wavefronts, one workgroup per CU)
+        // read B once where two 16-row tiles read it twice, with as many k
+        // splits as bring the grid to one workgroup per CU.  Taken where
+        // measured ahead on one MI355X (us, 32-row / 16-row, M = 32):
+        // column-major B 4096x4096 25.8 / 27.3, 14336x4096 73.6 / 90.6,
+        // 4096x14336 65.6 / 86.1; row-major B with B of 2^25 elements or more
+        // 14336x4096 61.3 / 69.6, 4096x14336 52.5 / 60.5 (at 4096x4096 it
+        // trails by 2-3 %: 21.1 / 20.7).
+        if (m > 16 && n >= 1024 && (layout_b == GEMM_F32_COL_MAJOR || n * k >= (int64_t(1) << 25))) {
+            if (split)
+                *split = (int)std::min<int64_t>(8, std::max<int64_t>(1, ceil_div(f.cu_count, ceil_div(n, 64))));
+            return V_SKINNY32_W8_D4;
+        }
+        return V_SKINNY_W16_D4;
+    }
     if (tail_ok && n <= 8) return n == 1 ? V_FEWCOL_R1 : n <= 4 ? V_FEWCOL_R4 : V_FEWCOL_R8;
     if (tail_ok) {
         int s = 0;

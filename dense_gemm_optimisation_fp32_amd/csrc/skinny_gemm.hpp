@@ -38,19 +38,23 @@
 
 namespace gemmf32 {
 
-template <int WAVES_, int DEPTH_, int BN_>
+template <int WAVES_, int DEPTH_, int BN_, int RT_ = 1>
 struct SkinnyTile {
     static_assert(BN_ == 16 || BN_ == 64, "one MFMA block or four interleaved ones");
+    static_assert(RT_ == 1 || RT_ == 2, "16 or 32 rows");
     static constexpr int WAVES = WAVES_;
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int BM = 16, BN = BN_, KQ = 16;  // rows, columns, k per load group
-    static constexpr int NB = BN / 16;                // MFMA blocks per tile
+    static constexpr int RT = RT_;                    // 16-row MFMA blocks per tile (rows of A per lane)
+    static constexpr int BM = 16 * RT, BN = BN_, KQ = 16;  // rows, columns, k per load group
+    static constexpr int NB = BN / 16;                // MFMA blocks per tile row
     static constexpr int DEPTH = DEPTH_;              // k groups in flight per wavefront
-    static constexpr int RED = BN == 64 ? 1046 : 304;   // LDS floats per wavefront in the reduction
+    // LDS floats per wavefront in the reduction (one past red_index's largest value).
+    static constexpr int RED = BN == 64 ? (BM - 1) * 65 + 64 + 2 * ((BM - 1) >> 2) + 1
+                                        : (BM - 1) * 16 + 16 + 16 * ((BM - 1) >> 2);
 };
 
-// LDS position of element (r, c) of a wavefront's 16 x BN share in the
-// reduction.  An accumulator write puts lanes (h, j) = (l / 16, l % 16) at
+// LDS position of element (r, c) of a wavefront's BM x BN share in the
+// reduction (each 16-row block placed as the first).  An accumulator write puts lanes (h, j) = (l / 16, l % 16) at
 // row 4h + v, column NB*j + nb, and LDS serves 32 lanes per cycle from 32
 // banks: for BN = 16 the 16 columns of two row groups land 16 banks apart;
 // for BN = 64 (rows 65 floats apart) the columns 4j (8 banks, twice) are
@@ -77,8 +81,8 @@ constexpr bool red_index_one_to_one()
     return true;
 }
 
-// Loads of one 16-k group for lane (j, h): A[row][kq+4h .. +3] and the B
-// values of the 4 k-steps.  NB = 4: b[t][nb] (row-major B) or b[nb][t]
+// Loads of one 16-k group for lane (j, h): A[row + 16r][kq+4h .. +3] for
+// each 16-row block r of the tile and the B values of the 4 k-steps.  NB = 4: b[t][nb] (row-major B) or b[nb][t]
 // (column-major B) is column 4j + nb; NB = 1: b[0][t] is column j.  Element
 // checks only when the group is not whole (tail of a range, or k past K).
 // Columns at or past N may read other elements of B: they only feed columns
@@ -86,12 +90,14 @@ constexpr bool red_index_one_to_one()
 template <class T, bool B_COL>
 __device__ __forceinline__ void skinny_load(const GemmArgs &g, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                             int row, int col0, int j, int h, int kq, int kend, bool whole,
-                                            bool live, f32x4 &a, f32x4 (&b)[T::NB])
+                                            bool live, f32x4 (&a)[T::RT], f32x4 (&b)[T::NB])
 {
     const int ka = kq + 4 * h;
     if (whole) {
         // A group that is not live reads zeros (out-of-range offsets).
-        a = buf_load_x4(ra, elem_off(live && row < g.m, row, g.lda, ka));
+#pragma unroll
+        for (int r = 0; r < T::RT; ++r)
+            a[r] = buf_load_x4(ra, elem_off(live && row + 16 * r < g.m, row + 16 * r, g.lda, ka));
         if constexpr (T::NB == 4 && !B_COL) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) b[t] = buf_load_x4(rb, elem_off(live, ka + t, g.ldb, col0 + 4 * j));
@@ -109,7 +115,10 @@ __device__ __forceinline__ void skinny_load(const GemmArgs &g, __amdgpu_buffer_r
         }
     } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) a[q] = buf_load_x1(ra, elem_off(row < g.m && ka + q < kend, row, g.lda, ka + q));
+        for (int r = 0; r < T::RT; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                a[r][q] = buf_load_x1(ra, elem_off(row + 16 * r < g.m && ka + q < kend, row + 16 * r, g.lda, ka + q));
 #pragma unroll
         for (int x = 0; x < T::NB; ++x)
 #pragma unroll
@@ -126,14 +135,17 @@ __device__ __forceinline__ void skinny_load(const GemmArgs &g, __amdgpu_buffer_r
 }
 
 template <class T, bool B_COL>
-__device__ __forceinline__ void skinny_mfma(const f32x4 &a, const f32x4 (&b)[T::NB], f32x4 (&acc)[T::NB])
+__device__ __forceinline__ void skinny_mfma(const f32x4 (&a)[T::RT], const f32x4 (&b)[T::NB],
+                                            f32x4 (&acc)[T::RT][T::NB])
 {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int nb = 0; nb < T::NB; ++nb) {
             const float bv = (T::NB == 4 && !B_COL) ? b[t][nb] : b[nb][t];
-            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], bv, acc[nb], 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < T::RT; ++r)
+                acc[r][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r][t], bv, acc[r][nb], 0, 0, 0);
         }
 }
 
@@ -172,10 +184,12 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, g.b_bytes);
 
-    const int row = row0 + j;    // A row this lane supplies
-    f32x4 acc[T::NB];
+    const int row = row0 + j;    // A row this lane supplies (and row + 16r for block r)
+    f32x4 acc[T::RT][T::NB];
 #pragma unroll
-    for (int nb = 0; nb < T::NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < T::RT; ++r)
+#pragma unroll
+        for (int nb = 0; nb < T::NB; ++nb) acc[r][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Split plans: the workgroups of a tile count themselves in on the
     // tile's arrival counter as soon as thread 0's wavefront has issued its
@@ -221,7 +235,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
     const int G = kspan / T::KQ;
     const int passes = (G + D - 1) / D;
     if (passes > 0) {
-        f32x4 a[D], b[D][T::NB];
+        f32x4 a[D][T::RT], b[D][T::NB];
 #pragma unroll
         for (int u = 0; u < D; ++u) {
             skinny_load<T, B_COL>(g, ra, rb, row, col0, j, h, kw0 + u * T::KQ, kw1, true, u < G, a[u], b[u]);
@@ -253,18 +267,21 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
     }
     // The partial group at the end of the range, element by element.
     if (G * T::KQ < kspan) {
-        f32x4 at, bt[T::NB];
+        f32x4 at[T::RT], bt[T::NB];
         skinny_load<T, B_COL>(g, ra, rb, row, col0, j, h, kw0 + G * T::KQ, kw1, false, true, at, bt);
         skinny_mfma<T, B_COL>(at, bt, acc);
     }
 
     // Add the wavefronts' shares in wavefront order (element (r, c) of the
-    // 16 x BN tile: r = 4*h + v, c = NB*j + nb; LDS positions by red_index,
-    // free of bank conflicts).
+    // BM x BN tile: r = 16*rt + 4*h + v, c = NB*j + nb; LDS positions by
+    // red_index, free of bank conflicts).
 #pragma unroll
-    for (int nb = 0; nb < T::NB; ++nb)
+    for (int rt = 0; rt < T::RT; ++rt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[wave][red_index<T>(4 * h + v, T::NB * j + nb)] = acc[nb][v];
+        for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                red[wave][red_index<T>(16 * rt + 4 * h + v, T::NB * j + nb)] = acc[rt][nb][v];
     __shared__ int last;
     if (g.split_k > 1 && tid == 0) {
         last = before == (unsigned)(g.split_k - 1);

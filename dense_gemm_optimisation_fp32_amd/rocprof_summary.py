@@ -52,9 +52,10 @@ def short_name(kernel: str) -> str:
             tags = [t for t, f in zip(("bcol", "acol", "epi", "wide"), flags.groups()) if f == "true"]
             return base + "".join("_" + t for t in tags) + sliver
         return base + sliver
-    m = re.search(r"SkinnyTile<(\d+), (\d+), (\d+)>", k) or re.search(r"SkinnyTileILi(\d+)ELi(\d+)ELi(\d+)", k)
+    m = (re.search(r"SkinnyTile<(\d+), (\d+), (\d+)(?:, (\d+))?>", k)
+         or re.search(r"SkinnyTileILi(\d+)ELi(\d+)ELi(\d+)E(?:Li(\d+)E)?", k))
     if m:
-        return f"skinny_16x{m.group(3)}_w{m.group(1)}_d{m.group(2)}"
+        return f"skinny_{16 * int(m.group(4) or 1)}x{m.group(3)}_w{m.group(1)}_d{m.group(2)}"
     m = re.search(r"MfmaTile<(\d+), (\d+), (\d+), \d+, \d+>", k) or re.search(r"MfmaTileILi(\d+)ELi(\d+)ELi(\d+)", k)
     if m and "gemm_mfma_kernel" in k:
         return f"mfma_{m.group(1)}x{m.group(2)}x{m.group(3)}"

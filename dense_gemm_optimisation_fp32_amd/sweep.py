@@ -51,8 +51,9 @@ def kernel_tag(info: dict, layout_b: int) -> str:
     if info["kind"] == 1:
         return f"gemm_valu_kernelI{b}"
     if info["kind"] == 2:
-        m = re.match(r"skinny_16x(\d+)_w(\d+)_d(\d+)", info["name"])
-        return f"SkinnyTileILi{m.group(2)}ELi{m.group(3)}ELi{m.group(1)}EEE{b}"
+        m = re.match(r"skinny_(\d+)x(\d+)_w(\d+)_d(\d+)", info["name"])
+        rt = int(m.group(1)) // 16
+        return f"SkinnyTileILi{m.group(3)}ELi{m.group(4)}ELi{m.group(2)}ELi{rt}EEE{b}"
     dims = (f"ILi{info['bm']}ELi{info['bn']}ELi{info['bk']}ELi{info['waves_m']}ELi{info['waves_n']}")
     if info["name"].startswith("dma_"):
         # DmaTile<..., STAGES, PRIO>, then B_COL, A_COL = false, EPI = false,

@@ -116,5 +116,11 @@ def test_profile_kernel_short_names():
                       "false>(gemmf32::GemmArgs)") == "sk_dma_64x128x16_s2"
     assert short_name("void gemmf32::gemm_skinny_kernel<gemmf32::SkinnyTile<16, 4, 16>, false>"
                       "(gemmf32::GemmArgs)") == "skinny_16x16_w16_d4"
+    assert short_name("void gemmf32::gemm_skinny_kernel<gemmf32::SkinnyTile<8, 4, 64, 2>, true>"
+                      "(gemmf32::GemmArgs)") == "skinny_32x64_w8_d4"
+    assert short_name("void gemmf32::gemm_mfma_dma_sliver_kernel<gemmf32::DmaTile<128, 128, 16, 2, 2, 3, false>, "
+                      "false, false, false, true>(gemmf32::GemmArgs)") == "dma_128x128x16_s3_wide_sliver"
+    assert short_name("void gemmf32::gemm_fewcol_kernel<gemmf32::FewColTile<1, 4, 2>, false>"
+                      "(gemmf32::GemmArgs)") == "fewcol_r1"
     assert short_name("void gemmf32::gemm_fewcol_kernel<gemmf32::FewColTile<1>, true>"
                       "(gemmf32::GemmArgs)") == "fewcol_r1_bcol"

@@ -725,6 +725,37 @@ def test_column_sliver_plan(layout_b):
     assert np.array_equal(C.astype(np.float64), Cref)
 
 
+# 17 to 32 rows: 32-row tiles where measured ahead (column-major B, or a B of
+# 2^25 elements or more, N >= 1024), with the k split that fills the CUs.
+ROWS32_CASES = [((32, 4096, 4096), COL_MAJOR, "skinny_32x64_w8_d4", 4),
+                ((17, 14336, 4096), ROW_MAJOR, "skinny_32x64_w8_d4", 2),
+                ((24, 4096, 14336), ROW_MAJOR, "skinny_32x64_w8_d4", 4),
+                ((32, 4096, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 2),
+                ((20, 512, 4096), COL_MAJOR, "skinny_16x64_w16_d4", None)]
+
+
+@pytest.mark.parametrize("shape,layout_b,name,split", ROWS32_CASES)
+def test_few_rows_32_row_tiles(shape, layout_b, name, split):
+    """The dispatch's plan for 17 to 32 rows; every element against the
+    oracle (integer inputs bit for bit) and runs repeat bit for bit."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the choices were measured on a 256-CU MI355X")
+    m, n, k = shape
+    print(f"\n[case] 32-row tiles {shape} layout_b={layout_b}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=2500 + m + n)
+    C, info, outs = run_gemm(A, B, m, n, k, layout_b, repeat=2)
+    assert info["name"] == name
+    if split is not None:
+        assert info["split_k"] == split and info["grid"] == info["tiles_m"] * info["tiles_n"] * split
+    assert np.array_equal(outs[0], outs[1])
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    check_close(C, Cref, S, f"{name} {shape}")
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=2600 + m + n)
+    C, _ = run_gemm(A, B, m, n, k, layout_b)
+    Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    assert np.array_equal(C.astype(np.float64), Cref)
+
+
 # Seeded random shapes through the default dispatch (every path the shape
 # classes select: few rows, few columns, few tiles with stream-K, column
 # slivers, the whole-tile candidates), both B layouts, every element.

@@ -44,6 +44,7 @@ def _both(m, n, k, layout_b, seed):
 @pytest.mark.parametrize("first,second,kind", [
     ((16, 4096, 4096), (16, 300, 2000), "split_k"),       # few rows: split-k partial sums
     ((64, 256, 4096), (64, 200, 3000), "split_k"),        # few tiles on 16x16 tiles, k split 4 ways
+    ((32, 4096, 4096), (24, 2048, 3000), "split_k"),      # 17-32 rows (32-row tiles with column-major B)
     ((1024, 1024, 8192), (1200, 700, 3000), "stream_k"),  # few tiles, long k: stream-K
     ((513, 257, 1000), (300, 520, 77), "tiles"),          # whole tiles, no scratch
 ])
