@@ -186,6 +186,7 @@ enum VariantId {
     V_DMA_256x256x16_W42_S2,
     V_DMA_256x256x16_W44_S4,
     V_SKINNY32_W8_D4,
+    V_SKINNY_16x32_W16_D4,
     V_COUNT
 };
 
@@ -226,6 +227,7 @@ const VariantDesc &variant(int v)
         dma_variant<DmaTile<256, 256, 16, 4, 2, 2>>("dma_256x256x16_w4x2_s2"),
         dma_variant<DmaTile<256, 256, 16, 4, 4, 4>>("dma_256x256x16_w4x4_s4"),
         skinny_variant<SkinnyTile<8, 4, 64, 2>>("skinny_32x64_w8_d4"),
+        skinny_variant<SkinnyTile<16, 4, 32>>("skinny_16x32_w16_d4"),
     };
     return table[v];
 }
@@ -570,6 +572,26 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
             if (split)
                 *split = (int)std::min<int64_t>(8, std::max<int64_t>(1, ceil_div(f.cu_count, ceil_div(n, 64))));
             return V_SKINNY32_W8_D4;
+        }
+        // Up to 16 rows: 32-column tiles with half the k splits of 64-column
+        // tiles (the same number of workgroups, each over twice the k) where
+        // the 64-column plan splits k at least twice.  Each split past the
+        // first adds a partial tile to write and to sum, and halving them
+        // paid wherever A, which every column tile reads again, is light:
+        // up to 4 rows, or k per split up to 1024, or column-major B up to 8
+        // rows.  Measured on one MI355X (us, 32-column / 64-column, best of
+        // two): 16x2048x2048 7.56 / 9.40 (col. B), 7.21 / 8.52 (row B);
+        // 16x4096x2048 10.28 / 11.57, 8.79 / 10.05; 1x4096x4096 16.40 /
+        // 18.27, 14.84 / 15.55; 8x4096x4096 col. B 17.67 / 18.95; 1x8192x4096
+        // 28.49 / 31.72, 26.03 / 27.39.  Where it did not pay: 16 rows and
+        // 2048 k per split (16x4096x4096 row B 17.50 / 16.50), or one split
+        // (16x8192x4096 row B 31.53 / 27.98).
+        const int64_t s64 = std::max<int64_t>(1, f.cu_count / ceil_div(n, 64));
+        const int64_t s32 = std::max<int64_t>(1, f.cu_count / ceil_div(n, 32));
+        if (m <= 16 && n >= 2048 && s64 >= 2 &&
+            (m <= 4 || ceil_div(k, s32) <= 1024 || (layout_b == GEMM_F32_COL_MAJOR && m <= 8))) {
+            if (split) *split = (int)s32;
+            return V_SKINNY_16x32_W16_D4;
         }
         return V_SKINNY_W16_D4;
     }

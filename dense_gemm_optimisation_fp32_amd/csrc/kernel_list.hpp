@@ -57,6 +57,7 @@ using SkinnyW8D4 = SkinnyTile<8, 4, 64>;
 using SkinnyW16D4 = SkinnyTile<16, 4, 64>;
 using Skinny16W16D4 = SkinnyTile<16, 4, 16>;
 using Skinny32W8D4 = SkinnyTile<8, 4, 64, 2>;     // 32-row tiles
+using Skinny16x32W16D4 = SkinnyTile<16, 4, 32>;   // 32-column tiles
 
 }  // namespace gemmf32
 
@@ -135,6 +136,7 @@ using Skinny32W8D4 = SkinnyTile<8, 4, 64, 2>;     // 32-row tiles
     X2(gemm_skinny_kernel, SkinnyW16D4, false) X2(gemm_skinny_kernel, SkinnyW16D4, true)     \
     X2(gemm_skinny_kernel, Skinny16W16D4, false) X2(gemm_skinny_kernel, Skinny16W16D4, true)     \
     X2(gemm_skinny_kernel, Skinny32W8D4, false) X2(gemm_skinny_kernel, Skinny32W8D4, true)       \
+    X2(gemm_skinny_kernel, Skinny16x32W16D4, false) X2(gemm_skinny_kernel, Skinny16x32W16D4, true) \
     X2(gemm_fewcol_kernel, FewColR1, false) X2(gemm_fewcol_kernel, FewColR1, true)             \
     X2(gemm_fewcol_kernel, FewColR4, false) X2(gemm_fewcol_kernel, FewColR4, true)             \
     X2(gemm_fewcol_kernel, FewColR8, false) X2(gemm_fewcol_kernel, FewColR8, true)

@@ -19,7 +19,8 @@
 // Tile widths.  BN = 64: four MFMA blocks with interleaved columns (lane
 // column j stands for column 4*j + nb of block nb), so one 16-byte load of
 // row-major B feeds all 4 blocks of a k-step; column-major B is loaded as 16
-// bytes along k of one column.  BN = 16: one block; row-major B is loaded one
+// bytes along k of one column.  BN = 32: two interleaved blocks, 8-byte
+// loads of row-major B.  BN = 16: one block; row-major B is loaded one
 // element per k-step (16 lanes still read 64 contiguous bytes of a row),
 // column-major B as 16 bytes along k.  The narrow tile gives N/16 workgroups,
 // enough to cover the CUs without splitting k across workgroups.
@@ -40,7 +41,7 @@ namespace gemmf32 {
 
 template <int WAVES_, int DEPTH_, int BN_, int RT_ = 1>
 struct SkinnyTile {
-    static_assert(BN_ == 16 || BN_ == 64, "one MFMA block or four interleaved ones");
+    static_assert(BN_ == 16 || BN_ == 32 || BN_ == 64, "one MFMA block, or two or four interleaved ones");
     static_assert(RT_ == 1 || RT_ == 2, "16 or 32 rows");
     static constexpr int WAVES = WAVES_;
     static constexpr int THREADS = 64 * WAVES;
@@ -49,8 +50,9 @@ struct SkinnyTile {
     static constexpr int NB = BN / 16;                // MFMA blocks per tile row
     static constexpr int DEPTH = DEPTH_;              // k groups in flight per wavefront
     // LDS floats per wavefront in the reduction (one past red_index's largest value).
-    static constexpr int RED = BN == 64 ? (BM - 1) * 65 + 64 + 2 * ((BM - 1) >> 2) + 1
-                                        : (BM - 1) * 16 + 16 + 16 * ((BM - 1) >> 2);
+    static constexpr int RED = BN == 64   ? (BM - 1) * 65 + 64 + 2 * ((BM - 1) >> 2) + 1
+                               : BN == 32 ? 33 * BM
+                                          : (BM - 1) * 16 + 16 + 16 * ((BM - 1) >> 2);
 };
 
 // LDS position of element (r, c) of a wavefront's BM x BN share in the
@@ -64,6 +66,7 @@ template <class T>
 constexpr __host__ __device__ int red_index(int r, int c)
 {
     if constexpr (T::BN == 64) return r * 65 + c + (c >> 5) + 2 * (r >> 2);
+    else if constexpr (T::BN == 32) return r * 33 + c + ((r >> 2) & 1);
     else return r * 16 + c + 16 * (r >> 2);
 }
 
@@ -83,7 +86,7 @@ constexpr bool red_index_one_to_one()
 
 // Loads of one 16-k group for lane (j, h): A[row + 16r][kq+4h .. +3] for
 // each 16-row block r of the tile and the B values of the 4 k-steps.  NB = 4: b[t][nb] (row-major B) or b[nb][t]
-// (column-major B) is column 4j + nb; NB = 1: b[0][t] is column j.  Element
+// (column-major B) is column 4j + nb; NB = 2: b[nb][t] is column 2j + nb; NB = 1: b[0][t] is column j.  Element
 // checks only when the group is not whole (tail of a range, or k past K).
 // Columns at or past N may read other elements of B: they only feed columns
 // of C that are never stored.
@@ -101,17 +104,22 @@ __device__ __forceinline__ void skinny_load(const GemmArgs &g, __amdgpu_buffer_r
         if constexpr (T::NB == 4 && !B_COL) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) b[t] = buf_load_x4(rb, elem_off(live, ka + t, g.ldb, col0 + 4 * j));
-        } else if constexpr (T::NB == 4) {
+        } else if constexpr (T::NB == 2 && !B_COL) {
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                const int col = col0 + 4 * j + nb;
-                b[nb] = buf_load_x4(rb, elem_off(live && col < g.n, col, g.ldb, ka));
+            for (int t = 0; t < 4; ++t) {
+                const f32x2 v = buf_load_x2(rb, elem_off(live, ka + t, g.ldb, col0 + 2 * j));
+                b[0][t] = v[0];
+                b[1][t] = v[1];
             }
         } else if constexpr (!B_COL) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) b[0][t] = buf_load_x1(rb, elem_off(live, ka + t, g.ldb, col0 + j));
         } else {
-            b[0] = buf_load_x4(rb, elem_off(live && col0 + j < g.n, col0 + j, g.ldb, ka));
+#pragma unroll
+            for (int nb = 0; nb < T::NB; ++nb) {
+                const int col = col0 + T::NB * j + nb;
+                b[nb] = buf_load_x4(rb, elem_off(live && col < g.n, col, g.ldb, ka));
+            }
         }
     } else {
 #pragma unroll

@@ -756,6 +756,43 @@ def test_few_rows_32_row_tiles(shape, layout_b, name, split):
     assert np.array_equal(C.astype(np.float64), Cref)
 
 
+# Up to 16 rows: 32-column tiles with half the k splits of 64-column tiles
+# where A is light (up to 4 rows, k per split up to 1024, or column-major B
+# up to 8 rows), 64-column tiles otherwise.  n = 3000 and 2050 end in a
+# ragged 32-column tile; k = 1999 and 777 end in a partial 16-k group.
+COLS32_CASES = [((16, 2048, 2048), ROW_MAJOR, "skinny_16x32_w16_d4", 4),
+                ((1, 4096, 4096), COL_MAJOR, "skinny_16x32_w16_d4", 2),
+                ((8, 4096, 4096), COL_MAJOR, "skinny_16x32_w16_d4", 2),
+                ((3, 8192, 4096), ROW_MAJOR, "skinny_16x32_w16_d4", 1),
+                ((13, 3000, 1999), COL_MAJOR, "skinny_16x32_w16_d4", 2),
+                ((5, 2050, 777), ROW_MAJOR, "skinny_16x32_w16_d4", 3),
+                ((8, 4096, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
+                ((16, 4096, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
+                ((16, 8192, 4096), COL_MAJOR, "skinny_16x64_w16_d4", 2),
+                ((4, 1024, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 16)]
+
+
+@pytest.mark.parametrize("shape,layout_b,name,split", COLS32_CASES)
+def test_few_rows_32_column_tiles(shape, layout_b, name, split):
+    """The dispatch's tile width for up to 16 rows; every element against
+    the oracle (integer inputs bit for bit) and runs repeat bit for bit."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the choices were measured on a 256-CU MI355X")
+    m, n, k = shape
+    print(f"\n[case] 32-column tiles {shape} layout_b={layout_b}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=2700 + m + n)
+    C, info, outs = run_gemm(A, B, m, n, k, layout_b, repeat=2)
+    assert info["name"] == name
+    assert info["split_k"] == split and info["grid"] == info["tiles_m"] * info["tiles_n"] * split
+    assert np.array_equal(outs[0], outs[1])
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    check_close(C, Cref, S, f"{name} {shape}")
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=2800 + m + n)
+    C, _ = run_gemm(A, B, m, n, k, layout_b)
+    Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    assert np.array_equal(C.astype(np.float64), Cref)
+
+
 # Seeded random shapes through the default dispatch (every path the shape
 # classes select: few rows, few columns, few tiles with stream-K, column
 # slivers, the whole-tile candidates), both B layouts, every element.
