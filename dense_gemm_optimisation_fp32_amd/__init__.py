@@ -68,6 +68,7 @@ class gemm_f32_info(ctypes.Structure):
         ("workgroups_per_cu", ctypes.c_int), ("waves_per_simd", ctypes.c_int),
         ("sliver_cols", ctypes.c_int64), ("sliver_variant", ctypes.c_int), ("sliver_stream_k", ctypes.c_int),
         ("sliver_fused", ctypes.c_int),
+        ("transposed", ctypes.c_int),
     ]
 
     def as_dict(self):

@@ -106,7 +106,9 @@ __device__ __forceinline__ void fewcol_copy_b(const GemmArgs &g, __amdgpu_buffer
 // column groups (row block fastest).  `bs`: LDS for the B chunk
 // (T::LDS_BYTES).  Every row is computed the same way whatever the number of
 // wavefronts, so a tile with more wavefronts gives bitwise the same C.
-template <class T, bool B_COL>
+// C_T: the product is the transpose of the caller's (see gemm_fewcol_t_kernel),
+// so result (row, j) is stored at C[j * ldc + row].
+template <class T, bool B_COL, bool C_T = false>
 __device__ __forceinline__ void fewcol_body(const GemmArgs &g, int block, f32x4 *bs)
 {
     const int tid = threadIdx.x;
@@ -186,7 +188,12 @@ __device__ __forceinline__ void fewcol_body(const GemmArgs &g, int block, f32x4 
 #pragma unroll
         for (int j = 0; j < T::R; ++j) {
             const float v = wave_sum(acc[t][j]);
-            if (lane == 0 && row < g.m && j0 + j < g.n) g.C[(size_t)row * g.ldc + j0 + j] = v;
+            if (lane == 0 && row < g.m && j0 + j < g.n) {
+                if constexpr (C_T)
+                    g.C[(size_t)(j0 + j) * g.ldc + row] = v;
+                else
+                    g.C[(size_t)row * g.ldc + j0 + j] = v;
+            }
         }
     }
 }
@@ -198,6 +205,20 @@ __global__ __launch_bounds__(T::THREADS, 4) void gemm_fewcol_kernel(GemmArgs g)
 {
     __shared__ f32x4 bs[T::R * T::LD / 4];   // [column][k] chunk of B, k-contiguous
     fewcol_body<T, B_COL>(g, (int)blockIdx.x, bs);
+}
+
+// The transposed product C^T = B^T . A^T for one row of C and column-major B
+// (y = W x with the weight W stored one output per row).  The kernel's A is
+// the caller's B read as a row-major N x K matrix (its columns are contiguous
+// along k, so every load instruction covers 1 KiB of one of them, where the
+// few-row kernel's operand layout reads 64 bytes of each of 16 columns); its
+// B is the caller's A read as a column-major K x M matrix; result (row, j) is
+// element (j, row) of the caller's C.
+template <class T, bool B_COL>
+__global__ __launch_bounds__(T::THREADS, 4) void gemm_fewcol_t_kernel(GemmArgs g)
+{
+    __shared__ f32x4 bs[T::R * T::LD / 4];
+    fewcol_body<T, B_COL, true>(g, (int)blockIdx.x, bs);
 }
 
 }  // namespace gemmf32

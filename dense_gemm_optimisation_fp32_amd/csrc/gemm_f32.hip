@@ -67,6 +67,8 @@ struct VariantDesc {
                                 // at a time (N a multiple of NB), or NULL
     const void *fn_sliver[2];   // [column-major B]: whole tiles carrying a column sliver, or NULL
     const void *fn_sliver_wide; // the same with the wide C stores, or NULL
+    const void *fn_t;           // few-column: the transposed product C^T = B^T A^T for
+                                // column-major B (gemm_fewcol_t_kernel), or NULL
 };
 
 template <class T>
@@ -130,10 +132,12 @@ VariantDesc with_sliver(VariantDesc d)
 template <class T>
 VariantDesc fewcol_variant(const char *name)
 {
-    return VariantDesc{
+    VariantDesc d{
         name, GEMM_F32_KIND_FEWCOL, T::ROWS, T::R, T::KC, T::WAVES, 1, T::THREADS, T::LDS_BYTES, 1,
         {reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_kernel<T, false>),
          reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_kernel<T, true>)}};
+    if constexpr (T::R == 1) d.fn_t = reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_t_kernel<T, true>);
+    return d;
 }
 
 template <class T>
@@ -400,6 +404,9 @@ struct gemm_f32_plan_impl {
     gemm_f32_plan_impl *sliver = nullptr;
     int64_t sliver_col0 = 0;
     bool sliver_fused = false;
+    // The kernel computes C^T = B^T A^T: its A is the caller's B and its B
+    // the caller's A (args describe the product the kernel computes).
+    bool swap_ab = false;
 };
 
 namespace {
@@ -528,6 +535,24 @@ int few_tile_rows(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFac
         return V_SKINNY_W8_D4;
     }
     return -1;
+}
+
+// One row of C and column-major B (y = W x with W stored one output per
+// row): the transposed product C^T = B^T A^T is a one-column product whose
+// rows are B's columns, and the few-column kernel reads each of them in
+// whole 1 KiB runs along k, where the few-row kernel's operand layout reads
+// 64 bytes of each of 16 columns per load instruction; there is no k split
+// to sum.  Measured on one MI355X (us, transposed / few-row plan, 8 rotating
+// B sets, best of two): 1x2048x2048 5.07 / 6.91, 1x4096x2048 7.61 / 8.58,
+// 1x4096x4096 14.42 / 16.43, 1x8192x4096 25.37 / 28.45, 1x4096x8192 26.44 /
+// 29.92, 1x11008x4096 32.87 / 46.15, 1x14336x4096 41.50 / 51.08,
+// 1x4096x14336 40.90 / 47.40.  (With 2 to 8 rows the 4- and 8-column
+// kernels, whose every workgroup copies all of A^T through LDS, were 1.04 to
+// 1.7 times slower except at N >= 11008.)  GEMM_F32_TRANSPOSE=0 turns it off.
+bool transposed_few_column(int64_t m, int64_t n, int64_t k, int layout_b)
+{
+    return m == 1 && layout_b == GEMM_F32_COL_MAJOR && n >= 2048 && k >= 2048 &&
+           env_int("GEMM_F32_TRANSPOSE", 1) != 0;
 }
 
 // Shape dispatch.  Few rows: the bandwidth-bound split-k path.  Few tiles:
@@ -709,11 +734,15 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
     bool auto_stream_k = false;
     int64_t auto_tail = 0;
     int auto_split = 0;
+    bool swap_ab = false;
     if (v < 0) {
         v = env_int("GEMM_F32_VARIANT", -1);
-        if (v < 0 || v >= V_COUNT)
-            v = choose_variant(m, n, k, layout_b, facts, !ex, epilogue != 0, &auto_stream_k, &auto_tail, nullptr,
-                               &auto_split);
+        if (v < 0 || v >= V_COUNT) {
+            swap_ab = !ex && transposed_few_column(m, n, k, layout_b);
+            v = swap_ab ? V_FEWCOL_R1
+                        : choose_variant(m, n, k, layout_b, facts, !ex, epilogue != 0, &auto_stream_k, &auto_tail,
+                                         nullptr, &auto_split);
+        }
         if (ex && !variant(v).fn_ex[0][0][0]) v = V_DMA_64x64x16_S2;
     }
     const VariantDesc &d = variant(v);
@@ -729,6 +758,18 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
     p->layout_b = layout_b;
     p->epilogue = epilogue;
     p->fn = ex ? d.fn_ex[layout_a][layout_b][epilogue] : d.fn[layout_b];
+    // C's extent before the transposed plan exchanges the operands' roles.
+    const uint32_t c_bytes = (uint32_t)(((m - 1) * ldc + n) * 4);
+    p->swap_ab = swap_ab;
+    if (swap_ab) {
+        // C^T = B^T A^T: B^T is the caller's column-major B read as a
+        // row-major n x k matrix (leading dimension ldb), A^T the caller's
+        // row-major A read as a column-major k x m matrix (leading dimension
+        // lda); the kernel stores its result (i, j) at C[j * ldc + i].
+        p->fn = d.fn_t;
+        std::swap(m, n);
+        std::swap(lda, ldb);
+    }
     // Row-major B: 8- or 16-byte C stores (and C loads of the epilogue)
     // when N is a multiple of the columns a lane holds per row
     // (bn / waves_n / 32).
@@ -760,7 +801,7 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
     a.alpha = 1.0f;
     a.beta = 0.0f;
     a.b_bytes = (uint32_t)((layout_b == GEMM_F32_ROW_MAJOR ? (k - 1) * ldb + n : (n - 1) * ldb + k) * 4);
-    a.c_bytes = (uint32_t)(((m - 1) * ldc + n) * 4);
+    a.c_bytes = c_bytes;
     a.split_k = 1;
     a.k_per_split = (int)k;
     // The whole-chunk loads of row-major B may run up to 3 elements past the
@@ -1038,6 +1079,7 @@ void for_each_kernel(const VariantDesc &d, F f)
             for (int e = 0; e < 2; ++e) f(d.fn_ex[a][b][e]);
     for (int a = 0; a < 2; ++a)
         for (int e = 0; e < 2; ++e) f(d.fn_wide[a][e]);
+    f(d.fn_t);
 }
 
 void fill_static_info(int v, gemm_f32_info *info)
@@ -1201,8 +1243,8 @@ int gemm_f32_run(gemm_f32_plan p, const float *A, const float *B, float *C, void
 {
     if (!p || !pointers_ok(A, B, C)) return GEMM_F32_ERR_INVALID_VALUE;
     GemmArgs a = p->args;
-    a.A = A;
-    a.B = B;
+    a.A = p->swap_ab ? B : A;
+    a.B = p->swap_ab ? A : B;
     a.C = C;
     if (p->sliver_fused) {
         a.sliver_B = sliver_b(p, B);
@@ -1237,8 +1279,8 @@ int gemm_f32_run_noalloc(int64_t m, int64_t n, int64_t k, int layout_b, int64_t 
         // share the scratch area.
         gemm_f32_plan_impl &p = parts[i];
         GemmArgs a = p.args;
-        a.A = A;
-        a.B = i ? sliver_b(&parts[0], B) : B;
+        a.A = p.swap_ab ? B : A;
+        a.B = p.swap_ab ? A : i ? sliver_b(&parts[0], B) : B;
         a.C = i ? C + parts[0].sliver_col0 : C;
         if (words[i]) {
             void *base = nullptr;
@@ -1282,8 +1324,8 @@ int gemm_f32_run_ex(gemm_f32_plan p, const float *A, const float *B, float *C, f
     const bool plain = alpha == 1.0f && beta == 0.0f && !bias && activation == GEMM_F32_ACT_NONE;
     if (!plain && !p->epilogue) return GEMM_F32_ERR_INVALID_VALUE;
     GemmArgs a = p->args;
-    a.A = A;
-    a.B = B;
+    a.A = p->swap_ab ? B : A;
+    a.B = p->swap_ab ? A : B;
     a.C = C;
     a.alpha = alpha;
     a.beta = beta;
@@ -1350,6 +1392,7 @@ int gemm_f32_describe(gemm_f32_plan p, gemm_f32_info *info)
         info->sliver_stream_k = p->sliver->args.sk_wgs;
         info->sliver_fused = p->sliver_fused ? 1 : 0;
     }
+    info->transposed = p->swap_ab ? 1 : 0;
     return GEMM_F32_SUCCESS;
 }
 

@@ -761,7 +761,7 @@ def test_few_rows_32_row_tiles(shape, layout_b, name, split):
 # up to 8 rows), 64-column tiles otherwise.  n = 3000 and 2050 end in a
 # ragged 32-column tile; k = 1999 and 777 end in a partial 16-k group.
 COLS32_CASES = [((16, 2048, 2048), ROW_MAJOR, "skinny_16x32_w16_d4", 4),
-                ((1, 4096, 4096), COL_MAJOR, "skinny_16x32_w16_d4", 2),
+                ((2, 4096, 4096), COL_MAJOR, "skinny_16x32_w16_d4", 2),
                 ((8, 4096, 4096), COL_MAJOR, "skinny_16x32_w16_d4", 2),
                 ((3, 8192, 4096), ROW_MAJOR, "skinny_16x32_w16_d4", 1),
                 ((13, 3000, 1999), COL_MAJOR, "skinny_16x32_w16_d4", 2),
@@ -791,6 +791,58 @@ def test_few_rows_32_column_tiles(shape, layout_b, name, split):
     C, _ = run_gemm(A, B, m, n, k, layout_b)
     Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
     assert np.array_equal(C.astype(np.float64), Cref)
+
+
+# One row of C with column-major B: the transposed product C^T = B^T A^T on
+# the one-column few-column kernel (N >= 2048, K >= 2048); every other
+# one-row or column-major case keeps the few-row plan.  Padded leading
+# dimensions (lda, ldb, ldc past the matrix) and ragged N and K included.
+TRANSPOSED_CASES = [((1, 4096, 4096), COL_MAJOR, 0, 1),
+                    ((1, 2050, 2049), COL_MAJOR, 0, 1),
+                    ((1, 3001, 5003), COL_MAJOR, 7, 1),
+                    ((1, 14336, 4096), COL_MAJOR, 0, 1),
+                    ((1, 4096, 4096), ROW_MAJOR, 0, 0),
+                    ((2, 4096, 4096), COL_MAJOR, 0, 0),
+                    ((1, 1024, 4096), COL_MAJOR, 0, 0),
+                    ((1, 4096, 1024), COL_MAJOR, 0, 0)]
+
+
+@pytest.mark.parametrize("shape,layout_b,pad,transposed", TRANSPOSED_CASES)
+def test_one_row_transposed_product(shape, layout_b, pad, transposed):
+    """The dispatch's plan for one row; every element against the oracle
+    (integer inputs bit for bit), runs repeat bit for bit, and the padding
+    of C's row is never written."""
+    m, n, k = shape
+    print(f"\n[case] one row {shape} layout_b={layout_b} pad={pad}", flush=True)
+    lda, ldb, ldc = k + pad, (n if layout_b == ROW_MAJOR else k) + pad, n + pad
+    for dist, seed in (("normal1", 2900 + n), ("int8range", 2950 + n)):
+        A, B = random_operands(m, n, k, layout_b, dist, seed=seed, lda=lda, ldb=ldb)
+        C, info, outs = run_gemm(A, B, m, n, k, layout_b, lda, ldb, ldc, c_fill=-7.25, repeat=2)
+        assert info["transposed"] == transposed
+        if transposed:
+            assert info["name"] == "fewcol_8x1_k2048" and info["split_k"] == 1
+        assert np.array_equal(outs[0], outs[1])
+        assert np.all(C[:, n:] == np.float32(-7.25)), "C row padding was written"
+        Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b, lda, ldb)
+        if dist == "int8range":
+            assert np.array_equal(C[:, :n].astype(np.float64), Cref)
+        else:
+            check_close(C[:, :n], Cref, S, f"one row {shape}")
+
+
+def test_one_row_transposed_product_switch(monkeypatch):
+    """GEMM_F32_TRANSPOSE=0 keeps the few-row plan, and both plans agree
+    with the oracle on the same inputs."""
+    import dense_gemm_optimisation_fp32_amd as g
+    m, n, k = 1, 4096, 4096
+    A, B = random_operands(m, n, k, COL_MAJOR, "normal1", seed=2990)
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, COL_MAJOR)
+    C1, info1 = run_gemm(A, B, m, n, k, COL_MAJOR)
+    monkeypatch.setenv("GEMM_F32_TRANSPOSE", "0")
+    C0, info0 = run_gemm(A, B, m, n, k, COL_MAJOR)
+    assert info1["transposed"] == 1 and info0["transposed"] == 0 and info0["kind"] == g.GEMM_F32_KIND_SKINNY
+    check_close(C1, Cref, S, "transposed")
+    check_close(C0, Cref, S, "few-row")
 
 
 # Seeded random shapes through the default dispatch (every path the shape

@@ -47,6 +47,7 @@ def _both(m, n, k, layout_b, seed):
     ((32, 4096, 4096), (24, 2048, 3000), "split_k"),      # 17-32 rows (32-row tiles with column-major B)
     ((1024, 1024, 8192), (1200, 700, 3000), "stream_k"),  # few tiles, long k: stream-K
     ((513, 257, 1000), (300, 520, 77), "tiles"),          # whole tiles, no scratch
+    ((1, 4096, 4096), (1, 2050, 2049), "one_row"),        # column-major B: the transposed product
 ])
 def test_noalloc_matches_the_plan_entry_point(first, second, kind, layout_b):
     for shape, seed in ((first, 1600), (second, 1601)):
@@ -57,6 +58,8 @@ def test_noalloc_matches_the_plan_entry_point(first, second, kind, layout_b):
             assert info["split_k"] > 1
         elif kind == "stream_k":
             assert info["stream_k"] > 0
+        elif kind == "one_row":
+            assert info["transposed"] == (1 if layout_b == COL_MAJOR else 0)
         ok, ratio = oracle.within_tolerance(c_static, Cref, S, REL, ABS)
         assert ok, f"{shape}: max error ratio {ratio:.3g}"
         assert np.array_equal(c_static, c_plan), f"{shape}: differs from gemm_f32_run"
