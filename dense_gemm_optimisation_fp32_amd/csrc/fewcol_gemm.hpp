@@ -24,15 +24,16 @@
 
 namespace gemmf32 {
 
-template <int R_, int WAVES_ = 4, int ROWS_PER_WAVE_ = 2>
+template <int R_, int WAVES_ = 4, int ROWS_PER_WAVE_ = 2, int KC_ = (R_ == 8 ? 1024 : 2048)>
 struct FewColTile {
     static_assert(R_ == 1 || R_ == 4 || R_ == 8, "columns per workgroup");
+    static_assert(KC_ % 256 == 0 && R_ * (KC_ + 4) * 4 <= 33 * 1024, "k chunk: whole 256-k groups, at most ~32 KiB of B");
     static constexpr int R = R_;                 // columns of C per workgroup
     static constexpr int WAVES = WAVES_;
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int ROWS_PER_WAVE = ROWS_PER_WAVE_;
     static constexpr int ROWS = WAVES * ROWS_PER_WAVE;   // rows of C per workgroup
-    static constexpr int KC = R_ == 8 ? 1024 : 2048;   // k per LDS chunk (at most 32 KiB of B)
+    static constexpr int KC = KC_;               // k per LDS chunk
     static constexpr int GROUPS = KC / 256;      // 16-byte loads per lane per row and chunk
     static constexpr int LD = KC + 4;             // LDS floats per column (padded: conflict-free copies)
     static constexpr int LDS_BYTES = R * LD * 4;
@@ -64,6 +65,24 @@ __device__ __forceinline__ float wave_sum(float v)
 // writes (the padded column stride spreads them over the banks).  One
 // column of row-major B: 4-byte loads.  Partial groups (at K, or at N)
 // element by element.
+//
+// Two ways to order it against the chunk's loads of A.  fewcol_copy_b loads
+// and writes in one pass after A's loads are issued; memory loads complete in
+// issue order, so its LDS writes wait for A's loads from memory as well.
+// With 4 or 8 columns, a copy of 8 to 16 KiB per workgroup, that wait cost
+// up to a fifth of the time: there fewcol_load_b issues the copy's loads into
+// registers (FewColStage) before A's and fewcol_store_b writes them after,
+// waiting for the B loads only (B is small and read from the L2).  Measured
+// on one MI355X (us, staged / one pass): 4096x4x4096 14.8 / 18.0,
+// 8192x4x8192 53.6 / 56.5, 8192x8x8192 68.1 / 79.8; the 8-column kernel on
+// the transposed product of 8x4096x4096 with column-major B 21.2 / 26.4.
+// Staged: the 8-column tile and the 4-column tile with 1024-k chunks.  Not
+// staged: one column (no gain: 4096-row transposed products 1 % slower
+// staged) and the 4-column tile with 2048-k chunks, whose staged copy does
+// not fit the registers beside A's chunk (it spilled).  The two 4-column
+// tiles split the shapes by k: the 1024-k staged tile took 4096x4x4096 from
+// 18.0 to 14.6 us and 16384x3x4096 from 56.1 to 50.9, but 8192x4x8192 from
+// 56.4 to 62.3 (twice the chunks, each a round trip of A's loads).
 template <class T, bool B_COL>
 __device__ __forceinline__ void fewcol_copy_b(const GemmArgs &g, __amdgpu_buffer_rsrc_t rb, f32x4 *bs, float *bsf,
                                               int kc, int klen, int j0, int tid)
@@ -102,6 +121,76 @@ __device__ __forceinline__ void fewcol_copy_b(const GemmArgs &g, __amdgpu_buffer
     }
 }
 
+template <class T, bool B_COL>
+constexpr bool fewcol_staged() { return T::R == 8 || (T::R == 4 && T::KC == 1024); }
+
+template <class T, bool B_COL>
+struct FewColStage {
+    static constexpr bool ONE = !B_COL && T::R == 1;   // one column of row-major B: 4-byte elements
+    static constexpr int TOTAL = B_COL ? T::R * T::KC / 4 : ONE ? T::KC : T::KC * (T::R / 4);
+    static constexpr int CP = (TOTAL + T::THREADS - 1) / T::THREADS;   // elements per thread
+    f32x4 v[ONE ? 1 : CP];
+    float s[ONE ? CP : 1];
+};
+
+template <class T, bool B_COL>
+__device__ __forceinline__ void fewcol_load_b(const GemmArgs &g, __amdgpu_buffer_rsrc_t rb, FewColStage<T, B_COL> &st,
+                                              int kc, int klen, int j0, int tid)
+{
+    using S = FewColStage<T, B_COL>;
+#pragma unroll
+    for (int i = 0; i < S::CP; ++i) {
+        const int e = tid + i * T::THREADS;
+        const bool live = S::TOTAL % T::THREADS == 0 || e < S::TOTAL;
+        if constexpr (B_COL) {
+            const int j = e / (T::KC / 4), kk = 4 * (e % (T::KC / 4));
+            const bool col_ok = live && j0 + j < g.n;
+            if (col_ok && kk + 4 <= klen) {
+                st.v[i] = buf_load_x4(rb, elem_off(true, j0 + j, g.ldb, kc + kk));
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    st.v[i][u] = buf_load_x1(rb, elem_off(col_ok && kk + u < klen, j0 + j, g.ldb, kc + kk + u));
+            }
+        } else if constexpr (!S::ONE) {
+            constexpr int Q = T::R / 4;
+            const int kk = e / Q, c = e % Q;
+            const int col = j0 + 4 * c;
+            if (live && kk < klen && col + 4 <= g.n) {
+                st.v[i] = buf_load_x4(rb, elem_off(true, kc + kk, g.ldb, col));
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    st.v[i][u] = buf_load_x1(rb, elem_off(live && kk < klen && col + u < g.n, kc + kk, g.ldb, col + u));
+            }
+        } else {
+            st.s[i] = buf_load_x1(rb, elem_off(live && e < klen && j0 < g.n, kc + e, g.ldb, j0));
+        }
+    }
+}
+
+template <class T, bool B_COL>
+__device__ __forceinline__ void fewcol_store_b(const FewColStage<T, B_COL> &st, f32x4 *bs, float *bsf, int tid)
+{
+    using S = FewColStage<T, B_COL>;
+#pragma unroll
+    for (int i = 0; i < S::CP; ++i) {
+        const int e = tid + i * T::THREADS;
+        if (S::TOTAL % T::THREADS != 0 && e >= S::TOTAL) break;
+        if constexpr (B_COL) {
+            const int j = e / (T::KC / 4), kk = 4 * (e % (T::KC / 4));
+            bs[(j * T::LD + kk) / 4] = st.v[i];
+        } else if constexpr (!S::ONE) {
+            constexpr int Q = T::R / 4;
+            const int kk = e / Q, c = e % Q;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) bsf[(4 * c + u) * T::LD + kk] = st.v[i][u];
+        } else {
+            bsf[e] = st.s[i];
+        }
+    }
+}
+
 // Workgroup `block` of the grid: ceil(m / ROWS) row blocks x ceil(n / R)
 // column groups (row block fastest).  `bs`: LDS for the B chunk
 // (T::LDS_BYTES).  Every row is computed the same way whatever the number of
@@ -131,8 +220,11 @@ __device__ __forceinline__ void fewcol_body(const GemmArgs &g, int block, f32x4 
 
     for (int kc = 0; kc < g.k; kc += T::KC) {
         const int klen = min(T::KC, g.k - kc);
-        // This chunk's A loads first (ROWS_PER_WAVE * GROUPS 16-byte loads
-        // per lane), so that they are in flight with the B chunk's.
+        // This chunk's A loads (ROWS_PER_WAVE * GROUPS 16-byte loads per
+        // lane), for a staged copy after the B chunk's loads.
+        constexpr bool STAGED = fewcol_staged<T, B_COL>();
+        FewColStage<T, B_COL> st;
+        if constexpr (STAGED) fewcol_load_b<T, B_COL>(g, rb_, st, kc, klen, j0, tid);
         f32x4 a[T::ROWS_PER_WAVE][T::GROUPS];
         if (klen == T::KC) {
             // A whole chunk: every group is whole (uniform branch).
@@ -159,13 +251,14 @@ __device__ __forceinline__ void fewcol_body(const GemmArgs &g, int block, f32x4 
                     }
                 }
         }
-        // The B chunk: element (k, column j0 + j) for k < klen and j0 + j < n,
-        // zero elsewhere.  Column-major B is read along k; row-major B along
-        // its few columns.  The barriers wait for LDS only: the A loads stay
-        // in flight (the compiler waits for each load where its value is
-        // used).
+        // The B chunk into LDS.  The barriers wait for LDS only: the A loads
+        // stay in flight (the compiler waits for each load where its value
+        // is used, and for the B loads before their LDS writes).
         fewcol_barrier();   // the previous chunk's LDS reads are done
-        fewcol_copy_b<T, B_COL>(g, rb_, bs, bsf, kc, klen, j0, tid);
+        if constexpr (STAGED)
+            fewcol_store_b<T, B_COL>(st, bs, bsf, tid);
+        else
+            fewcol_copy_b<T, B_COL>(g, rb_, bs, bsf, kc, klen, j0, tid);
         fewcol_barrier();
 
 #pragma unroll

@@ -136,7 +136,8 @@ VariantDesc fewcol_variant(const char *name)
         name, GEMM_F32_KIND_FEWCOL, T::ROWS, T::R, T::KC, T::WAVES, 1, T::THREADS, T::LDS_BYTES, 1,
         {reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_kernel<T, false>),
          reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_kernel<T, true>)}};
-    if constexpr (T::R == 1) d.fn_t = reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_t_kernel<T, true>);
+    if constexpr (T::R == 1 || (T::R == 4 && T::KC == 1024))
+        d.fn_t = reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_t_kernel<T, true>);
     return d;
 }
 
@@ -191,6 +192,7 @@ enum VariantId {
     V_DMA_256x256x16_W44_S4,
     V_SKINNY32_W8_D4,
     V_SKINNY_16x32_W16_D4,
+    V_FEWCOL_R4_K1024,
     V_COUNT
 };
 
@@ -232,6 +234,7 @@ const VariantDesc &variant(int v)
         dma_variant<DmaTile<256, 256, 16, 4, 4, 4>>("dma_256x256x16_w4x4_s4"),
         skinny_variant<SkinnyTile<8, 4, 64, 2>>("skinny_32x64_w8_d4"),
         skinny_variant<SkinnyTile<16, 4, 32>>("skinny_16x32_w16_d4"),
+        fewcol_variant<gemmf32::FewColR4K1024>("fewcol_8x4_k1024"),
     };
     return table[v];
 }
@@ -537,22 +540,39 @@ int few_tile_rows(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFac
     return -1;
 }
 
-// One row of C and column-major B (y = W x with W stored one output per
-// row): the transposed product C^T = B^T A^T is a one-column product whose
-// rows are B's columns, and the few-column kernel reads each of them in
-// whole 1 KiB runs along k, where the few-row kernel's operand layout reads
-// 64 bytes of each of 16 columns per load instruction; there is no k split
-// to sum.  Measured on one MI355X (us, transposed / few-row plan, 8 rotating
-// B sets, best of two): 1x2048x2048 5.07 / 6.91, 1x4096x2048 7.61 / 8.58,
-// 1x4096x4096 14.42 / 16.43, 1x8192x4096 25.37 / 28.45, 1x4096x8192 26.44 /
-// 29.92, 1x11008x4096 32.87 / 46.15, 1x14336x4096 41.50 / 51.08,
-// 1x4096x14336 40.90 / 47.40.  (With 2 to 8 rows the 4- and 8-column
-// kernels, whose every workgroup copies all of A^T through LDS, were 1.04 to
-// 1.7 times slower except at N >= 11008.)  GEMM_F32_TRANSPOSE=0 turns it off.
-bool transposed_few_column(int64_t m, int64_t n, int64_t k, int layout_b)
+// Up to four rows of C and column-major B (y = W x for a few vectors x, with
+// W stored one output per row): the transposed product C^T = B^T A^T is a
+// product with one to four columns whose N rows are B's columns, and the
+// few-column kernels read each of them in whole 1 KiB runs along k, where
+// the few-row kernel's operand layout reads 64 bytes of each of 16 columns
+// per load instruction; no k split is summed.  The few-column kernels do not
+// split k either, so the plan needs enough rows of B^T (8 per workgroup) to
+// fill the CUs when k is long.  Measured on one MI355X (us, transposed /
+// few-row plan, rotating B sets, best of two):
+//   one row (one-column kernel): 1x2048x2048 5.07 / 6.91, 1x4096x4096 14.42
+//   / 16.43, 1x11008x4096 32.87 / 46.15, 1x14336x4096 41.50 / 51.08,
+//   1x4096x14336 40.90 / 47.40, 1x1024x1024 3.53 / 8.29, 1x256x4096 4.50 /
+//   15.78, 1x512x8192 7.36 / 13.66; long k with few columns of B lost:
+//   1x2048x65536 118.9 / 109.9, 1x1024x65536 77.5 / 59.6, 1x512x32768
+//   36.5 / 23.1;
+//   2 to 4 rows (the staged four-column kernel, 1024-k chunks; M = 4):
+//   4x6144x4096 21.75 / 27.21, 4x8192x3000 20.85 / 23.97, 4x11008x4096 36.78
+//   / 48.14, 4x14336x4096 44.07 / 53.55, 4x14336x2048 23.72 / 28.50,
+//   4x13824x5120 52.45 / 66.34, 4x28672x4096 80.97 / 99.97; with N up to
+//   4096 or k = 8192 it lost or tied: 4x4096x4096 16.89 / 16.69,
+//   4x4096x2048 9.47 / 8.39, 4x4096x8192 36.34 / 31.34, 4x8192x8192 61.45
+//   / 58.33, 4x14336x8192 97.14 / 98.03.
+// Returns the few-column variant of the transposed plan, or -1.
+// GEMM_F32_TRANSPOSE=0 turns it off; =2 (measurement) takes it for every
+// shape it serves (up to four rows, column-major B).
+int transposed_few_column(int64_t m, int64_t n, int64_t k, int layout_b)
 {
-    return m == 1 && layout_b == GEMM_F32_COL_MAJOR && n >= 2048 && k >= 2048 &&
-           env_int("GEMM_F32_TRANSPOSE", 1) != 0;
+    const int mode = env_int("GEMM_F32_TRANSPOSE", 1);
+    if (mode == 0 || layout_b != GEMM_F32_COL_MAJOR || m > 4) return -1;
+    const int v = m == 1 ? V_FEWCOL_R1 : V_FEWCOL_R4_K1024;
+    if (mode == 2) return v;
+    if (m == 1) return k <= 16384 && (n >= 1024 || n * k <= (int64_t(1) << 22)) ? v : -1;
+    return n >= 6144 && k >= 2048 && k <= 5120 ? v : -1;
 }
 
 // Shape dispatch.  Few rows: the bandwidth-bound split-k path.  Few tiles:
@@ -620,7 +640,10 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
         }
         return V_SKINNY_W16_D4;
     }
-    if (tail_ok && n <= 8) return n == 1 ? V_FEWCOL_R1 : n <= 4 ? V_FEWCOL_R4 : V_FEWCOL_R8;
+    // (2 to 4 columns: the staged 1024-k chunks up to k = 4096, the 2048-k
+    // chunks beyond; fewcol_gemm.hpp has the measurements.)
+    if (tail_ok && n <= 8)
+        return n == 1 ? V_FEWCOL_R1 : n <= 4 ? (k <= 4096 ? V_FEWCOL_R4_K1024 : V_FEWCOL_R4) : V_FEWCOL_R8;
     if (tail_ok) {
         int s = 0;
         const int v = few_tile_rows(m, n, k, layout_b, f, &s);
@@ -738,8 +761,9 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
     if (v < 0) {
         v = env_int("GEMM_F32_VARIANT", -1);
         if (v < 0 || v >= V_COUNT) {
-            swap_ab = !ex && transposed_few_column(m, n, k, layout_b);
-            v = swap_ab ? V_FEWCOL_R1
+            const int tv = ex ? -1 : transposed_few_column(m, n, k, layout_b);
+            swap_ab = tv >= 0;
+            v = swap_ab ? tv
                         : choose_variant(m, n, k, layout_b, facts, !ex, epilogue != 0, &auto_stream_k, &auto_tail,
                                          nullptr, &auto_split);
         }

@@ -49,6 +49,7 @@ __global__ void zero_words_kernel(unsigned *p, int n);
 // Few-column tiles (columns per workgroup).
 using FewColR1 = FewColTile<1>;
 using FewColR4 = FewColTile<4>;
+using FewColR4K1024 = FewColTile<4, 4, 2, 1024>;
 using FewColR8 = FewColTile<8>;
 
 // Few-row tiles (wavefronts, k groups in flight, columns).
@@ -140,7 +141,9 @@ using Skinny16x32W16D4 = SkinnyTile<16, 4, 32>;   // 32-column tiles
     X2(gemm_fewcol_kernel, FewColR1, false) X2(gemm_fewcol_kernel, FewColR1, true)             \
     X2(gemm_fewcol_t_kernel, FewColR1, true)                                                     \
     X2(gemm_fewcol_kernel, FewColR4, false) X2(gemm_fewcol_kernel, FewColR4, true)             \
-    X2(gemm_fewcol_kernel, FewColR8, false) X2(gemm_fewcol_kernel, FewColR8, true)
+    X2(gemm_fewcol_kernel, FewColR8, false) X2(gemm_fewcol_kernel, FewColR8, true)             \
+    X2(gemm_fewcol_kernel, FewColR4K1024, false) X2(gemm_fewcol_kernel, FewColR4K1024, true)   \
+    X2(gemm_fewcol_t_kernel, FewColR4K1024, true)
 
 #define GEMMF32_ALL_UNITS(X5, X2, X1)                                                     \
     GEMMF32_UNIT_DMA256(X5, X2, X1) GEMMF32_UNIT_DMA256S4(X5, X2, X1)                     \

@@ -138,9 +138,9 @@ struct gemm_f32_info {
     int sliver_stream_k;
     int sliver_fused;
     /* Plan only: 1 when the plan computes the transposed product
-     * C^T = B^T . A^T (one row of C, column-major B: the caller's B read as
-     * a row-major N x K matrix on the one-column few-column kernel, whose
-     * loads run along each column of B; "PMPP Chapter 06", section 1: the
+     * C^T = B^T . A^T (up to four rows of C, column-major B: the caller's B
+     * read as a row-major N x K matrix on a few-column kernel, whose loads
+     * run along each column of B; "PMPP Chapter 06", section 1: the
      * corner-turning layout read along its contiguous direction).  The
      * tile fields then describe that product (tiles_m counts blocks of
      * columns of C).  0 otherwise. */
@@ -179,8 +179,9 @@ int gemm_f32_validate(int64_t m, int64_t n, int64_t k, int layout_b,
  *                             gemm_f32_info.sliver_cols);
  *   GEMM_F32_SLIVER_FUSE=0    run a sliver as a second launch, never in
  *                             the tiles' launch (gemm_f32_info.sliver_fused);
- *   GEMM_F32_TRANSPOSE=0      never compute one row of C with column-major B
- *                             as the transposed product (gemm_f32_info.transposed);
+ *   GEMM_F32_TRANSPOSE=0      never compute a few rows of C with column-major
+ *                             B as the transposed product (gemm_f32_info.transposed);
+ *                             =2 (measurement) always, for up to four rows;
  *   GEMM_F32_NUM_XCD=<count>  the XCD count the rasterisation undoes
  *                             (default: the device's; 1 turns the XCD
  *                             remap off, for measuring it);

@@ -24,7 +24,8 @@ CASES = [
     ((64, 256, 4096), COL_MAJOR, "split_k"),           # few tiles: 16x16 tiles, k split 4 ways
     ((24, 4096, 4096), COL_MAJOR, "split_k"),          # 32-row tiles, k split 4 ways
     ((4, 4096, 2048), COL_MAJOR, "split_k"),           # 16x32 tiles, k split 2 ways
-    ((1, 4096, 2048), COL_MAJOR, "tiles"),             # one row: the transposed few-column product
+    ((1, 4096, 2048), COL_MAJOR, "tiles"),             # one row: the transposed one-column product
+    ((4, 8192, 3000), COL_MAJOR, "tiles"),             # four rows: the transposed four-column product
     ((1024, 1024, 8192), ROW_MAJOR, "stream_k"),       # few tiles, long k: stream-K over all tiles
     ((2304, 9216, 4096), ROW_MAJOR, "stream_k_tail"),  # the partial last wave split by stream-K
     ((5003, 4097, 2049), ROW_MAJOR, "sliver"),         # tiles and a one-column sliver

@@ -625,7 +625,7 @@ def test_binding_matmul_matches_oracle_both_layouts():
 # Few columns (N <= 8): the matrix-vector-like path, chosen by the shape
 # dispatch; k beyond one LDS chunk (2048) and with a tail, both B layouts.
 FEWCOL_SHAPES = [(5003, 1, 2049), (300, 3, 77), (1000, 4, 4096), (777, 5, 2500), (4096, 8, 4096), (64, 2, 1),
-                 (33, 7, 6000)]
+                 (33, 7, 6000), (700, 3, 9000)]
 
 
 @pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
@@ -793,41 +793,47 @@ def test_few_rows_32_column_tiles(shape, layout_b, name, split):
     assert np.array_equal(C.astype(np.float64), Cref)
 
 
-# One row of C with column-major B: the transposed product C^T = B^T A^T on
-# the one-column few-column kernel (N >= 2048, K >= 2048); every other
-# one-row or column-major case keeps the few-row plan.  Padded leading
-# dimensions (lda, ldb, ldc past the matrix) and ragged N and K included.
-TRANSPOSED_CASES = [((1, 4096, 4096), COL_MAJOR, 0, 1),
-                    ((1, 2050, 2049), COL_MAJOR, 0, 1),
-                    ((1, 3001, 5003), COL_MAJOR, 7, 1),
-                    ((1, 14336, 4096), COL_MAJOR, 0, 1),
-                    ((1, 4096, 4096), ROW_MAJOR, 0, 0),
-                    ((2, 4096, 4096), COL_MAJOR, 0, 0),
-                    ((1, 1024, 4096), COL_MAJOR, 0, 0),
-                    ((1, 4096, 1024), COL_MAJOR, 0, 0)]
+# Up to four rows of C with column-major B: the transposed product
+# C^T = B^T A^T on a few-column kernel (one row: k <= 16384 and N >= 1024 or
+# N * K <= 2^22; 2 to 4 rows: N >= 6144 and 2048 <= K <= 5120); every other
+# case keeps the few-row plan.  Padded leading dimensions (lda, ldb, ldc past
+# the matrix), ragged N and K, and 3 rows on the four-column kernel included.
+TRANSPOSED_CASES = [((1, 4096, 4096), COL_MAJOR, 0, "fewcol_8x1_k2048"),
+                    ((1, 2050, 2049), COL_MAJOR, 0, "fewcol_8x1_k2048"),
+                    ((1, 3001, 5003), COL_MAJOR, 7, "fewcol_8x1_k2048"),
+                    ((1, 14336, 4096), COL_MAJOR, 0, "fewcol_8x1_k2048"),
+                    ((1, 300, 1000), COL_MAJOR, 3, "fewcol_8x1_k2048"),
+                    ((3, 8192, 3000), COL_MAJOR, 0, "fewcol_8x4_k1024"),
+                    ((4, 6144, 4096), COL_MAJOR, 5, "fewcol_8x4_k1024"),
+                    ((2, 11009, 2049), COL_MAJOR, 0, "fewcol_8x4_k1024"),
+                    ((1, 600, 20000), COL_MAJOR, 0, None),
+                    ((1, 4096, 4096), ROW_MAJOR, 0, None),
+                    ((2, 4096, 4096), COL_MAJOR, 0, None),
+                    ((4, 6144, 8192), COL_MAJOR, 0, None),
+                    ((5, 8192, 4096), COL_MAJOR, 0, None)]
 
 
-@pytest.mark.parametrize("shape,layout_b,pad,transposed", TRANSPOSED_CASES)
-def test_one_row_transposed_product(shape, layout_b, pad, transposed):
-    """The dispatch's plan for one row; every element against the oracle
-    (integer inputs bit for bit), runs repeat bit for bit, and the padding
-    of C's row is never written."""
+@pytest.mark.parametrize("shape,layout_b,pad,name", TRANSPOSED_CASES)
+def test_few_rows_transposed_product(shape, layout_b, pad, name):
+    """The dispatch's plan for up to five rows; every element against the
+    oracle (integer inputs bit for bit), runs repeat bit for bit, and the
+    padding of C's rows is never written."""
     m, n, k = shape
-    print(f"\n[case] one row {shape} layout_b={layout_b} pad={pad}", flush=True)
+    print(f"\n[case] transposed product {shape} layout_b={layout_b} pad={pad}", flush=True)
     lda, ldb, ldc = k + pad, (n if layout_b == ROW_MAJOR else k) + pad, n + pad
     for dist, seed in (("normal1", 2900 + n), ("int8range", 2950 + n)):
         A, B = random_operands(m, n, k, layout_b, dist, seed=seed, lda=lda, ldb=ldb)
         C, info, outs = run_gemm(A, B, m, n, k, layout_b, lda, ldb, ldc, c_fill=-7.25, repeat=2)
-        assert info["transposed"] == transposed
-        if transposed:
-            assert info["name"] == "fewcol_8x1_k2048" and info["split_k"] == 1
+        assert info["transposed"] == (name is not None)
+        if name is not None:
+            assert info["name"] == name and info["split_k"] == 1
         assert np.array_equal(outs[0], outs[1])
         assert np.all(C[:, n:] == np.float32(-7.25)), "C row padding was written"
         Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b, lda, ldb)
         if dist == "int8range":
             assert np.array_equal(C[:, :n].astype(np.float64), Cref)
         else:
-            check_close(C[:, :n], Cref, S, f"one row {shape}")
+            check_close(C[:, :n], Cref, S, f"transposed product {shape}")
 
 
 def test_one_row_transposed_product_switch(monkeypatch):
