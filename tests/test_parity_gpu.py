@@ -552,7 +552,7 @@ def test_operand_extent_near_limit(name):
 # Full workload shapes, in the plan the benchmark times (gemm_f32_create).
 # ---------------------------------------------------------------------------
 
-FULL = ["sq256", "sq4096", "sq4096t", "ragged", "ffn", "skinny", "longk"]
+FULL = ["sq256", "sq4096", "sq4096t", "ragged", "ffn", "skinny", "longk", "gemv_t", "decode4_t", "fewcol8"]
 
 
 def record_ratio(what, ratio, oracle_s=None):

@@ -60,6 +60,9 @@ WORKLOADS = {
         Workload("ffn", 8192, 14336, 4096, ROW_MAJOR, "normal002", 4, "FFN linear layer"),
         Workload("skinny", 16, 4096, 4096, ROW_MAJOR, "normal002", 4, "memory-bound, few rows"),
         Workload("longk", 1024, 1024, 8192, ROW_MAJOR, "uniform", 5, "few tiles, long k (stream-K)"),
+        Workload("gemv_t", 1, 4096, 4096, COL_MAJOR, "normal002", 6, "one row, B column-major (y = W x)"),
+        Workload("decode4_t", 4, 14336, 4096, COL_MAJOR, "normal002", 7, "four rows, B column-major, FFN-sized"),
+        Workload("fewcol8", 8192, 8, 8192, ROW_MAJOR, "normal002", 8, "few columns: A streamed once"),
     )
 }
 
