@@ -653,6 +653,18 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
         }
     }
     if (few_tile_stream_k(m, n, k, f, tail_ok)) {
+        // Column-major B whose 64 x 128 tiles make one nearly full wave (7/8
+        // of the CUs to all of them, one workgroup each): those tiles,
+        // data-parallel.  Measured on one MI355X (us, 64x128 / stream-K over
+        // 64x64): 512x4096x4096 128.0 / 144.2, 128x14336x4096 129.9 / 146.7,
+        // 2048x1024x4096 127.9 / 142.5, 256x7168x4096 137.0 / 142.9,
+        // 960x2048x3000 99.7 / 116.5, 1024x2048x8192 253.4 / 273.2,
+        // 512x4096x2048 69.5 / 77.4; at 192 tiles stream-K stayed ahead
+        // (384x4096x4096 127.6 / 109.0).  With row-major B the two came out
+        // even (0.95-1.06) and stream-K stays.
+        const int64_t t128 = ceil_div(m, 64) * ceil_div(n, 128);
+        if (layout_b == GEMM_F32_COL_MAJOR && 8 * t128 >= 7 * (int64_t)f.cu_count && t128 <= f.cu_count)
+            return V_DMA_64x128x16_S2;
         *stream_k = true;
         return V_DMA_64x64x16_S2;
     }

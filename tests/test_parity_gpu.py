@@ -300,6 +300,36 @@ def test_stream_k_chosen_for_few_tiles_long_k(layout_b):
         assert np.array_equal(C.astype(np.float64), Cref)
 
 
+# Column-major B with one nearly full wave of 64x128 tiles (224 to 256 on
+# 256 CUs): those tiles, data-parallel, where row-major B keeps stream-K.
+ONE_WAVE_CASES = [((512, 4096, 4096), COL_MAJOR, "dma_64x128x16_w2x2_s2", 0),
+                  ((960, 2048, 3000), COL_MAJOR, "dma_64x128x16_w2x2_s2", 0),
+                  ((128, 14336, 2049), COL_MAJOR, "dma_64x128x16_w2x2_s2", 0),
+                  ((500, 4000, 3001), COL_MAJOR, "dma_64x128x16_w2x2_s2", 0),
+                  ((384, 4096, 4096), COL_MAJOR, "dma_64x64x16_w2x2_s2", 1),
+                  ((512, 4096, 4096), ROW_MAJOR, "dma_64x64x16_w2x2_s2", 1)]
+
+
+@pytest.mark.parametrize("shape,layout_b,name,stream_k", ONE_WAVE_CASES)
+def test_one_wave_of_64x128_tiles(shape, layout_b, name, stream_k):
+    """The dispatch's plan where 64x128 tiles make one nearly full wave;
+    every element against the oracle (integer inputs bit for bit)."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the choices were measured on a 256-CU MI355X")
+    m, n, k = shape
+    print(f"\n[case] one wave of 64x128 tiles {shape} layout_b={layout_b}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=3100 + m)
+    C, info, outs = run_gemm(A, B, m, n, k, layout_b, repeat=2)
+    assert info["name"] == name and (info["stream_k"] > 0) == bool(stream_k)
+    assert np.array_equal(outs[0], outs[1])
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    check_close(C, Cref, S, f"{name} {shape}")
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=3200 + m)
+    C, _ = run_gemm(A, B, m, n, k, layout_b)
+    Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    assert np.array_equal(C.astype(np.float64), Cref)
+
+
 # Few tiles on the few-row kernel: (shape, the plan with row-major B, with
 # column-major B), a plan being (variant, k-split count), or None for a tiled
 # plan.  Measured on one MI355X, 256 CUs.
