@@ -660,11 +660,17 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
         // 2048x1024x4096 127.9 / 142.5, 256x7168x4096 137.0 / 142.9,
         // 960x2048x3000 99.7 / 116.5, 1024x2048x8192 253.4 / 273.2,
         // 512x4096x2048 69.5 / 77.4; at 192 tiles stream-K stayed ahead
-        // (384x4096x4096 127.6 / 109.0).  With row-major B the two came out
-        // even (0.95-1.06) and stream-K stays.
-        const int64_t t128 = ceil_div(m, 64) * ceil_div(n, 128);
-        if (layout_b == GEMM_F32_COL_MAJOR && 8 * t128 >= 7 * (int64_t)f.cu_count && t128 <= f.cu_count)
-            return V_DMA_64x128x16_S2;
+        // (384x4096x4096 127.6 / 109.0).  Row-major B: the three-stage
+        // 64 x 128 tile where they fill 15/16 of the CUs or more and k is at
+        // most 6144 (us, 64x128 s3 / stream-K): 512x4096x4096 138.2 / 142.9,
+        // 1024x2048x4096 137.7 / 143.2, 128x16384x4096 138.4 / 163.2,
+        // 512x4096x2048 70.8 / 78.1, 960x2048x3000 102.2 / 109.3,
+        // 1000x2000x5000 167.8 / 172.1; not at 224 tiles (448x4096x4096 137.5
+        // / 130.2) or k = 8192 (512x4096x8192 271.6 / 269.6).
+        const int64_t t128 = ceil_div(m, 64) * ceil_div(n, 128), cus = f.cu_count;
+        if (layout_b == GEMM_F32_COL_MAJOR && 8 * t128 >= 7 * cus && t128 <= cus) return V_DMA_64x128x16_S2;
+        if (layout_b == GEMM_F32_ROW_MAJOR && 16 * t128 >= 15 * cus && t128 <= cus && k <= 6144)
+            return V_DMA_64x128x16_S3;
         *stream_k = true;
         return V_DMA_64x64x16_S2;
     }
@@ -811,7 +817,8 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
     // (bn / waves_n / 32).
     const int lane_cols = d.kind == GEMM_F32_KIND_MFMA ? d.bn / d.waves_n / 32 : 0;
     p->c_store_width = 1;
-    if (layout_b == GEMM_F32_ROW_MAJOR && d.fn_wide[layout_a][epilogue] && lane_cols > 0 && n % lane_cols == 0) {
+    if (layout_b == GEMM_F32_ROW_MAJOR && d.fn_wide[layout_a][epilogue] && lane_cols > 0 && n % lane_cols == 0 &&
+        env_int("GEMM_F32_WIDE_C", 1) != 0) {
         p->fn = d.fn_wide[layout_a][epilogue];
         p->c_store_width = lane_cols;
     }

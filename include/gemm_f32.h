@@ -182,6 +182,9 @@ int gemm_f32_validate(int64_t m, int64_t n, int64_t k, int layout_b,
  *   GEMM_F32_TRANSPOSE=0      never compute a few rows of C with column-major
  *                             B as the transposed product (gemm_f32_info.transposed);
  *                             =2 (measurement) always, for up to four rows;
+ *   GEMM_F32_WIDE_C=0         store C one element at a time even where the
+ *                             whole-tile kernel could store 2 or 4 (for measuring
+ *                             gemm_f32_info.c_store_width);
  *   GEMM_F32_NUM_XCD=<count>  the XCD count the rasterisation undoes
  *                             (default: the device's; 1 turns the XCD
  *                             remap off, for measuring it);

@@ -300,14 +300,18 @@ def test_stream_k_chosen_for_few_tiles_long_k(layout_b):
         assert np.array_equal(C.astype(np.float64), Cref)
 
 
-# Column-major B with one nearly full wave of 64x128 tiles (224 to 256 on
-# 256 CUs): those tiles, data-parallel, where row-major B keeps stream-K.
+# One nearly full wave of 64x128 tiles: column-major B from 224 tiles on 256
+# CUs (two-stage tiles), row-major B from 240 tiles with k up to 6144
+# (three-stage tiles), data-parallel; stream-K over 64x64 tiles otherwise.
 ONE_WAVE_CASES = [((512, 4096, 4096), COL_MAJOR, "dma_64x128x16_w2x2_s2", 0),
                   ((960, 2048, 3000), COL_MAJOR, "dma_64x128x16_w2x2_s2", 0),
                   ((128, 14336, 2049), COL_MAJOR, "dma_64x128x16_w2x2_s2", 0),
                   ((500, 4000, 3001), COL_MAJOR, "dma_64x128x16_w2x2_s2", 0),
                   ((384, 4096, 4096), COL_MAJOR, "dma_64x64x16_w2x2_s2", 1),
-                  ((512, 4096, 4096), ROW_MAJOR, "dma_64x64x16_w2x2_s2", 1)]
+                  ((512, 4096, 4096), ROW_MAJOR, "dma_64x128x16_w2x2_s3", 0),
+                  ((961, 2047, 3001), ROW_MAJOR, "dma_64x128x16_w2x2_s3", 0),
+                  ((448, 4096, 4096), ROW_MAJOR, "dma_64x64x16_w2x2_s2", 1),
+                  ((512, 4096, 8192), ROW_MAJOR, "dma_64x64x16_w2x2_s2", 1)]
 
 
 @pytest.mark.parametrize("shape,layout_b,name,stream_k", ONE_WAVE_CASES)
