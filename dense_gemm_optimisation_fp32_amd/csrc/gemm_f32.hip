@@ -144,10 +144,14 @@ VariantDesc fewcol_variant(const char *name)
 template <class T>
 VariantDesc skinny_variant(const char *name)
 {
-    return VariantDesc{
+    VariantDesc d{
         name, GEMM_F32_KIND_SKINNY, T::BM, T::BN, T::KQ, 1, T::WAVES, T::THREADS, T::WAVES * T::BM * T::BN * 4, 1,
         {reinterpret_cast<const void *>(&gemmf32::gemm_skinny_kernel<T, false>),
          reinterpret_cast<const void *>(&gemmf32::gemm_skinny_kernel<T, true>)}};
+    // The linear-layer epilogue with row-major A (no column-major A kernels).
+    d.fn_ex[0][0][1] = reinterpret_cast<const void *>(&gemmf32::gemm_skinny_epi_kernel<T, false>);
+    d.fn_ex[0][1][1] = reinterpret_cast<const void *>(&gemmf32::gemm_skinny_epi_kernel<T, true>);
+    return d;
 }
 
 VariantDesc valu_variant(const char *name)
@@ -785,10 +789,10 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
                         : choose_variant(m, n, k, layout_b, facts, !ex, epilogue != 0, &auto_stream_k, &auto_tail,
                                          nullptr, &auto_split);
         }
-        if (ex && !variant(v).fn_ex[0][0][0]) v = V_DMA_64x64x16_S2;
+        if (ex && !variant(v).fn_ex[layout_a][layout_b][epilogue]) v = V_DMA_64x64x16_S2;
     }
     const VariantDesc &d = variant(v);
-    if (ex && !d.fn_ex[0][0][0]) return GEMM_F32_ERR_INVALID_VALUE;
+    if (ex && !d.fn_ex[layout_a][layout_b][epilogue]) return GEMM_F32_ERR_INVALID_VALUE;
     if (ex) {
         auto_stream_k = false;
         auto_tail = 0;

@@ -157,11 +157,23 @@ __device__ __forceinline__ void skinny_mfma(const f32x4 (&a)[T::RT], const f32x4
         }
 }
 
+// The linear-layer epilogue on one element of C, with the whole-tile
+// kernels' arithmetic: act(alpha * x + beta * C[r][c] + bias[c]); C is read
+// only when beta != 0 and the bias only when there is one.
+__device__ __forceinline__ float skinny_epilogue(const GemmArgs &g, float x, int r, int c)
+{
+    const float cold = g.use_beta ? g.C[(size_t)r * g.ldc + c] : 0.0f;
+    const float bias = g.bias ? g.bias[c] : 0.0f;
+    const float y = fmaxf(g.alpha * x + g.beta * cold + bias, g.act == 1 ? 0.0f : -__builtin_inff());
+    return g.act == 2 ? gelu_erf(y) : y;
+}
+
 // Grid: tiles_m * tiles_n * split_k workgroups.  With one split the
 // workgroup writes its tile of C; otherwise the splits meet through
 // g.partial[split][m][n] (epoch-tagged words) and g.arrivals[tile].
-template <class T, bool B_COL>
-__global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
+// EPI: C gets the linear-layer epilogue (skinny_epilogue) where it is written.
+template <class T, bool B_COL, bool EPI>
+__device__ __forceinline__ void skinny_body(const GemmArgs &g)
 {
     static_assert(red_index_one_to_one<T>(), "reduction layout");
     __shared__ float red[T::WAVES][T::RED];
@@ -325,7 +337,8 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
         for (int q = 0; q < EPT; ++q) {
             const int e = tid + q * T::THREADS;
             const int r = row0 + e / T::BN, c = col0 + e % T::BN;
-            if (e < ELEMS && r < g.m && c < g.n) g.C[(size_t)r * g.ldc + c] = own[q];
+            if (e < ELEMS && r < g.m && c < g.n)
+                g.C[(size_t)r * g.ldc + c] = EPI ? skinny_epilogue(g, own[q], r, c) : own[q];
         }
         return;
     }
@@ -373,9 +386,22 @@ __global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
                 sum = sp == 0 ? v : sum + v;
             }
         }
-        g.C[(size_t)r * g.ldc + c] = sum;
+        g.C[(size_t)r * g.ldc + c] = EPI ? skinny_epilogue(g, sum, r, c) : sum;
     }
     record_give_up(budget, g.status);
+}
+
+template <class T, bool B_COL>
+__global__ __launch_bounds__(T::THREADS) void gemm_skinny_kernel(GemmArgs g)
+{
+    skinny_body<T, B_COL, false>(g);
+}
+
+// The same with the linear-layer epilogue (row-major A).
+template <class T, bool B_COL>
+__global__ __launch_bounds__(T::THREADS) void gemm_skinny_epi_kernel(GemmArgs g)
+{
+    skinny_body<T, B_COL, true>(g);
 }
 
 }  // namespace gemmf32

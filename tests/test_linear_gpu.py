@@ -227,3 +227,62 @@ def test_group_m_default_per_tile():
     assert g.Plan(4096, 4096, 4096, ROW_MAJOR, 4096, 4096, 4096).info["group_m"] == 4
     assert g.Plan(4096, 4096, 4096, COL_MAJOR, 4096, 4096, 4096).info["group_m"] == 4
     assert g.Plan(6144, 6144, 6144, ROW_MAJOR, 6144, 6144, 6144).info["group_m"] == 8
+
+
+# Few rows with the epilogue: the few-row kernel applies it where it writes C
+# (one k split, or the last split of a tile to finish); column-major A keeps
+# the tiled 64x64 plan.  (shape, B layout, plan name, k splits.)
+FEW_ROW_EX = [((16, 4096, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
+              ((16, 4096, 4096), COL_MAJOR, "skinny_16x64_w16_d4", 4),
+              ((1, 4096, 4096), COL_MAJOR, "skinny_16x32_w16_d4", 2),
+              ((24, 2048, 3000), COL_MAJOR, "skinny_32x64_w8_d4", 8),
+              ((5, 2050, 777), ROW_MAJOR, "skinny_16x32_w16_d4", 3),
+              ((1, 300, 17), ROW_MAJOR, "skinny_16x64_w16_d4", 1)]
+
+
+@pytest.mark.parametrize("shape,layout_b,name,split", FEW_ROW_EX)
+def test_few_rows_epilogue(shape, layout_b, name, split):
+    """The fused epilogue on the few-row plans against the oracle's epilogue,
+    runs repeating bit for bit; integer operands with alpha = beta = 1 exact,
+    and C's row padding never written."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the plans were chosen for a 256-CU MI355X")
+    m, n, k = shape
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=500 + m + n)
+    c_in, bias = epilogue_operands(m, n, seed=600 + m)
+    AB, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    for act in ACTS:
+        for alpha, beta, with_bias in [(0.5, -1.5, True), (1.0, 0.0, False)]:
+            print(f"\n[case] few-row epilogue {shape} layout_b={layout_b} act={act} alpha={alpha} beta={beta}",
+                  flush=True)
+            C, info, outs = run_ex(A, B, m, n, k, ROW_MAJOR, layout_b, epilogue=1, alpha=alpha, beta=beta,
+                                   c_in=c_in, bias=bias if with_bias else None, act=act, repeat=2)
+            assert info["name"] == name and info["epilogue"] == 1 and info["split_k"] == split
+            ref, scale = oracle.epilogue_f64(AB, S, c_in, alpha, beta, bias if with_bias else None, act)
+            check(C[:, :n], ref, scale, f"{name} {shape} act={act} alpha={alpha} beta={beta}")
+            assert np.array_equal(outs[0], outs[1])
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=700 + m)
+    rng = np.random.default_rng(701)
+    c_in = rng.integers(-50, 51, (m, n)).astype(np.float32)
+    bias = rng.integers(-9, 10, n).astype(np.float32)
+    AB, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    for act in (g.GEMM_F32_ACT_NONE, g.GEMM_F32_ACT_RELU):
+        C, _, _ = run_ex(A, B, m, n, k, ROW_MAJOR, layout_b, ldc=n + 3, epilogue=1, alpha=1.0, beta=1.0,
+                         c_in=c_in, bias=bias, act=act, c_fill=-3.5)
+        ref, _ = oracle.epilogue_f64(AB, S, c_in, 1.0, 1.0, bias, act)
+        assert np.array_equal(C[:, :n].astype(np.float64), ref)
+        assert np.all(C[:, n:] == np.float32(-3.5))
+
+
+def test_few_rows_epilogue_column_major_a():
+    """Column-major A with few rows has no few-row kernel: the 64x64 tiled
+    plan, against the oracle."""
+    m, n, k = 16, 1000, 700
+    A, B = random_operands(m, n, k, ROW_MAJOR, "normal1", seed=800, layout_a=COL_MAJOR)
+    c_in, bias = epilogue_operands(m, n, seed=801)
+    C, info, _ = run_ex(A, B, m, n, k, COL_MAJOR, ROW_MAJOR, epilogue=1, alpha=0.5, beta=2.0, c_in=c_in,
+                        bias=bias, act=g.GEMM_F32_ACT_GELU)
+    assert info["name"] == "dma_64x64x16_w2x2_s2"
+    AB, S = oracle.gemm_f64(A, B, m, n, k, ROW_MAJOR, layout_a=COL_MAJOR)
+    ref, scale = oracle.epilogue_f64(AB, S, c_in, 0.5, 2.0, bias, g.GEMM_F32_ACT_GELU)
+    check(C[:, :n], ref, scale, "column-major A, few rows")
