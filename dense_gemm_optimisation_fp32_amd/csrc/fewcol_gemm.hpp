@@ -21,6 +21,7 @@
 #pragma once
 
 #include "device_common.hpp"
+#include "epilogue.hpp"
 
 namespace gemmf32 {
 
@@ -196,8 +197,9 @@ __device__ __forceinline__ void fewcol_store_b(const FewColStage<T, B_COL> &st, 
 // (T::LDS_BYTES).  Every row is computed the same way whatever the number of
 // wavefronts, so a tile with more wavefronts gives bitwise the same C.
 // C_T: the product is the transpose of the caller's (see gemm_fewcol_t_kernel),
-// so result (row, j) is stored at C[j * ldc + row].
-template <class T, bool B_COL, bool C_T = false>
+// so result (row, j) is stored at C[j * ldc + row].  EPI: with the
+// linear-layer epilogue (linear_epilogue) on C's element.
+template <class T, bool B_COL, bool C_T = false, bool EPI = false>
 __device__ __forceinline__ void fewcol_body(const GemmArgs &g, int block, f32x4 *bs)
 {
     const int tid = threadIdx.x;
@@ -282,10 +284,8 @@ __device__ __forceinline__ void fewcol_body(const GemmArgs &g, int block, f32x4 
         for (int j = 0; j < T::R; ++j) {
             const float v = wave_sum(acc[t][j]);
             if (lane == 0 && row < g.m && j0 + j < g.n) {
-                if constexpr (C_T)
-                    g.C[(size_t)(j0 + j) * g.ldc + row] = v;
-                else
-                    g.C[(size_t)row * g.ldc + j0 + j] = v;
+                const int cr = C_T ? j0 + j : row, cc = C_T ? row : j0 + j;   // C's row and column
+                g.C[(size_t)cr * g.ldc + cc] = EPI ? linear_epilogue(g, v, cr, cc) : v;
             }
         }
     }
@@ -312,6 +312,14 @@ __global__ __launch_bounds__(T::THREADS, 4) void gemm_fewcol_t_kernel(GemmArgs g
 {
     __shared__ f32x4 bs[T::R * T::LD / 4];
     fewcol_body<T, B_COL, true>(g, (int)blockIdx.x, bs);
+}
+
+// The same with the linear-layer epilogue.
+template <class T, bool B_COL>
+__global__ __launch_bounds__(T::THREADS, 4) void gemm_fewcol_t_epi_kernel(GemmArgs g)
+{
+    __shared__ f32x4 bs[T::R * T::LD / 4];
+    fewcol_body<T, B_COL, true, true>(g, (int)blockIdx.x, bs);
 }
 
 }  // namespace gemmf32

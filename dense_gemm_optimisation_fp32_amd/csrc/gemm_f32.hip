@@ -69,6 +69,7 @@ struct VariantDesc {
     const void *fn_sliver_wide; // the same with the wide C stores, or NULL
     const void *fn_t;           // few-column: the transposed product C^T = B^T A^T for
                                 // column-major B (gemm_fewcol_t_kernel), or NULL
+    const void *fn_t_epi;       // the same with the linear-layer epilogue, or NULL
 };
 
 template <class T>
@@ -136,8 +137,10 @@ VariantDesc fewcol_variant(const char *name)
         name, GEMM_F32_KIND_FEWCOL, T::ROWS, T::R, T::KC, T::WAVES, 1, T::THREADS, T::LDS_BYTES, 1,
         {reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_kernel<T, false>),
          reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_kernel<T, true>)}};
-    if constexpr (T::R == 1 || (T::R == 4 && T::KC == 1024))
+    if constexpr (T::R == 1 || (T::R == 4 && T::KC == 1024)) {
         d.fn_t = reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_t_kernel<T, true>);
+        d.fn_t_epi = reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_t_epi_kernel<T, true>);
+    }
     return d;
 }
 
@@ -783,16 +786,18 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
     if (v < 0) {
         v = env_int("GEMM_F32_VARIANT", -1);
         if (v < 0 || v >= V_COUNT) {
-            const int tv = ex ? -1 : transposed_few_column(m, n, k, layout_b);
+            // (The transposed plan serves row-major A, with or without the
+            // epilogue.)
+            const int tv = layout_a == GEMM_F32_COL_MAJOR ? -1 : transposed_few_column(m, n, k, layout_b);
             swap_ab = tv >= 0;
             v = swap_ab ? tv
                         : choose_variant(m, n, k, layout_b, facts, !ex, epilogue != 0, &auto_stream_k, &auto_tail,
                                          nullptr, &auto_split);
         }
-        if (ex && !variant(v).fn_ex[layout_a][layout_b][epilogue]) v = V_DMA_64x64x16_S2;
+        if (ex && !swap_ab && !variant(v).fn_ex[layout_a][layout_b][epilogue]) v = V_DMA_64x64x16_S2;
     }
     const VariantDesc &d = variant(v);
-    if (ex && !d.fn_ex[layout_a][layout_b][epilogue]) return GEMM_F32_ERR_INVALID_VALUE;
+    if (ex && !swap_ab && !d.fn_ex[layout_a][layout_b][epilogue]) return GEMM_F32_ERR_INVALID_VALUE;
     if (ex) {
         auto_stream_k = false;
         auto_tail = 0;
@@ -803,7 +808,7 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
     p->layout_a = layout_a;
     p->layout_b = layout_b;
     p->epilogue = epilogue;
-    p->fn = ex ? d.fn_ex[layout_a][layout_b][epilogue] : d.fn[layout_b];
+    p->fn = swap_ab ? nullptr : ex ? d.fn_ex[layout_a][layout_b][epilogue] : d.fn[layout_b];
     // C's extent before the transposed plan exchanges the operands' roles.
     const uint32_t c_bytes = (uint32_t)(((m - 1) * ldc + n) * 4);
     p->swap_ab = swap_ab;
@@ -812,7 +817,7 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
         // row-major n x k matrix (leading dimension ldb), A^T the caller's
         // row-major A read as a column-major k x m matrix (leading dimension
         // lda); the kernel stores its result (i, j) at C[j * ldc + i].
-        p->fn = d.fn_t;
+        p->fn = epilogue ? d.fn_t_epi : d.fn_t;
         std::swap(m, n);
         std::swap(lda, ldb);
     }
@@ -1127,6 +1132,7 @@ void for_each_kernel(const VariantDesc &d, F f)
     for (int a = 0; a < 2; ++a)
         for (int e = 0; e < 2; ++e) f(d.fn_wide[a][e]);
     f(d.fn_t);
+    f(d.fn_t_epi);
 }
 
 void fill_static_info(int v, gemm_f32_info *info)

@@ -36,6 +36,7 @@
 #pragma once
 
 #include "device_common.hpp"
+#include "epilogue.hpp"
 
 namespace gemmf32 {
 
@@ -157,21 +158,10 @@ __device__ __forceinline__ void skinny_mfma(const f32x4 (&a)[T::RT], const f32x4
         }
 }
 
-// The linear-layer epilogue on one element of C, with the whole-tile
-// kernels' arithmetic: act(alpha * x + beta * C[r][c] + bias[c]); C is read
-// only when beta != 0 and the bias only when there is one.
-__device__ __forceinline__ float skinny_epilogue(const GemmArgs &g, float x, int r, int c)
-{
-    const float cold = g.use_beta ? g.C[(size_t)r * g.ldc + c] : 0.0f;
-    const float bias = g.bias ? g.bias[c] : 0.0f;
-    const float y = fmaxf(g.alpha * x + g.beta * cold + bias, g.act == 1 ? 0.0f : -__builtin_inff());
-    return g.act == 2 ? gelu_erf(y) : y;
-}
-
 // Grid: tiles_m * tiles_n * split_k workgroups.  With one split the
 // workgroup writes its tile of C; otherwise the splits meet through
 // g.partial[split][m][n] (epoch-tagged words) and g.arrivals[tile].
-// EPI: C gets the linear-layer epilogue (skinny_epilogue) where it is written.
+// EPI: C gets the linear-layer epilogue (linear_epilogue) where it is written.
 template <class T, bool B_COL, bool EPI>
 __device__ __forceinline__ void skinny_body(const GemmArgs &g)
 {
@@ -338,7 +328,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs &g)
             const int e = tid + q * T::THREADS;
             const int r = row0 + e / T::BN, c = col0 + e % T::BN;
             if (e < ELEMS && r < g.m && c < g.n)
-                g.C[(size_t)r * g.ldc + c] = EPI ? skinny_epilogue(g, own[q], r, c) : own[q];
+                g.C[(size_t)r * g.ldc + c] = EPI ? linear_epilogue(g, own[q], r, c) : own[q];
         }
         return;
     }
@@ -386,7 +376,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs &g)
                 sum = sp == 0 ? v : sum + v;
             }
         }
-        g.C[(size_t)r * g.ldc + c] = EPI ? skinny_epilogue(g, sum, r, c) : sum;
+        g.C[(size_t)r * g.ldc + c] = EPI ? linear_epilogue(g, sum, r, c) : sum;
     }
     record_give_up(budget, g.status);
 }

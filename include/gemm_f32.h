@@ -141,9 +141,10 @@ struct gemm_f32_info {
      * C^T = B^T . A^T (up to four rows of C, column-major B: the caller's B
      * read as a row-major N x K matrix on a few-column kernel, whose loads
      * run along each column of B; "PMPP Chapter 06", section 1: the
-     * corner-turning layout read along its contiguous direction).  The
-     * tile fields then describe that product (tiles_m counts blocks of
-     * columns of C).  0 otherwise. */
+     * corner-turning layout read along its contiguous direction), with or
+     * without the linear-layer epilogue (row-major A).  The tile fields
+     * then describe that product (tiles_m counts blocks of columns of C).
+     * 0 otherwise. */
     int transposed;
 };
 

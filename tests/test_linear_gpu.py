@@ -230,14 +230,19 @@ def test_group_m_default_per_tile():
 
 
 # Few rows with the epilogue: the few-row kernel applies it where it writes C
-# (one k split, or the last split of a tile to finish); column-major A keeps
-# the tiled 64x64 plan.  (shape, B layout, plan name, k splits.)
+# (one k split, or the last split of a tile to finish), the transposed
+# few-column plans (up to four rows, column-major B) where they store C's
+# element; column-major A keeps the tiled 64x64 plan.  (shape, B layout,
+# plan name, k splits.)
 FEW_ROW_EX = [((16, 4096, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
               ((16, 4096, 4096), COL_MAJOR, "skinny_16x64_w16_d4", 4),
-              ((1, 4096, 4096), COL_MAJOR, "skinny_16x32_w16_d4", 2),
+              ((2, 4096, 4096), COL_MAJOR, "skinny_16x32_w16_d4", 2),
               ((24, 2048, 3000), COL_MAJOR, "skinny_32x64_w8_d4", 8),
               ((5, 2050, 777), ROW_MAJOR, "skinny_16x32_w16_d4", 3),
-              ((1, 300, 17), ROW_MAJOR, "skinny_16x64_w16_d4", 1)]
+              ((1, 300, 17), ROW_MAJOR, "skinny_16x64_w16_d4", 1),
+              ((1, 4096, 4096), COL_MAJOR, "fewcol_8x1_k2048", 1),
+              ((1, 3001, 2049), COL_MAJOR, "fewcol_8x1_k2048", 1),
+              ((3, 8192, 3000), COL_MAJOR, "fewcol_8x4_k1024", 1)]
 
 
 @pytest.mark.parametrize("shape,layout_b,name,split", FEW_ROW_EX)
@@ -258,6 +263,7 @@ def test_few_rows_epilogue(shape, layout_b, name, split):
             C, info, outs = run_ex(A, B, m, n, k, ROW_MAJOR, layout_b, epilogue=1, alpha=alpha, beta=beta,
                                    c_in=c_in, bias=bias if with_bias else None, act=act, repeat=2)
             assert info["name"] == name and info["epilogue"] == 1 and info["split_k"] == split
+            assert info["transposed"] == (1 if name.startswith("fewcol") else 0)
             ref, scale = oracle.epilogue_f64(AB, S, c_in, alpha, beta, bias if with_bias else None, act)
             check(C[:, :n], ref, scale, f"{name} {shape} act={act} alpha={alpha} beta={beta}")
             assert np.array_equal(outs[0], outs[1])
