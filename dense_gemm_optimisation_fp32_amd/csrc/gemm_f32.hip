@@ -602,10 +602,13 @@ int transposed_few_column(int64_t m, int64_t n, int64_t k, int layout_b)
 // Otherwise the direct-to-LDS tile whose estimated time is least, and with
 // it *tail_tiles > 0 when its partial last wave goes to stream-K.  tail_ok:
 // the plan can run the stream-K kernel (row-major A, no epilogue); when it
-// cannot, few-tile shapes take the best data-parallel tile instead.
-// epilogue: the plan fuses the linear-layer epilogue.
+// cannot, few-tile long-k shapes take the best data-parallel tile instead.
+// epilogue: the plan fuses the linear-layer epilogue.  row_a: A is
+// row-major, so the few-row kernel (which carries the epilogue) can run the
+// few-tile shapes.
 int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFacts &f, bool tail_ok, bool epilogue,
-                   bool *stream_k, int64_t *tail_tiles, double *estimate = nullptr, int *split = nullptr)
+                   bool *stream_k, int64_t *tail_tiles, double *estimate = nullptr, int *split = nullptr,
+                   bool row_a = true)
 {
     *stream_k = false;
     *tail_tiles = 0;
@@ -651,7 +654,8 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
     // chunks beyond; fewcol_gemm.hpp has the measurements.)
     if (tail_ok && n <= 8)
         return n == 1 ? V_FEWCOL_R1 : n <= 4 ? (k <= 4096 ? V_FEWCOL_R4_K1024 : V_FEWCOL_R4) : V_FEWCOL_R8;
-    if (tail_ok) {
+    if (row_a) {
+        // (The few-row kernel also carries the epilogue, for row-major A.)
         int s = 0;
         const int v = few_tile_rows(m, n, k, layout_b, f, &s);
         if (v >= 0) {
@@ -792,7 +796,7 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
             swap_ab = tv >= 0;
             v = swap_ab ? tv
                         : choose_variant(m, n, k, layout_b, facts, !ex, epilogue != 0, &auto_stream_k, &auto_tail,
-                                         nullptr, &auto_split);
+                                         nullptr, &auto_split, layout_a == GEMM_F32_ROW_MAJOR);
         }
         if (ex && !swap_ab && !variant(v).fn_ex[layout_a][layout_b][epilogue]) v = V_DMA_64x64x16_S2;
     }

@@ -229,8 +229,8 @@ def test_group_m_default_per_tile():
     assert g.Plan(6144, 6144, 6144, ROW_MAJOR, 6144, 6144, 6144).info["group_m"] == 8
 
 
-# Few rows with the epilogue: the few-row kernel applies it where it writes C
-# (one k split, or the last split of a tile to finish), the transposed
+# Few rows (and few tiles) with the epilogue: the few-row kernel applies it
+# where it writes C (one k split, or the last split of a tile to finish), the transposed
 # few-column plans (up to four rows, column-major B) where they store C's
 # element; column-major A keeps the tiled 64x64 plan.  (shape, B layout,
 # plan name, k splits.)
@@ -242,7 +242,9 @@ FEW_ROW_EX = [((16, 4096, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
               ((1, 300, 17), ROW_MAJOR, "skinny_16x64_w16_d4", 1),
               ((1, 4096, 4096), COL_MAJOR, "fewcol_8x1_k2048", 1),
               ((1, 3001, 2049), COL_MAJOR, "fewcol_8x1_k2048", 1),
-              ((3, 8192, 3000), COL_MAJOR, "fewcol_8x4_k1024", 1)]
+              ((3, 8192, 3000), COL_MAJOR, "fewcol_8x4_k1024", 1),
+              ((256, 256, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
+              ((300, 700, 1500), COL_MAJOR, "skinny_16x64_w8_d4", 1)]
 
 
 @pytest.mark.parametrize("shape,layout_b,name,split", FEW_ROW_EX)
