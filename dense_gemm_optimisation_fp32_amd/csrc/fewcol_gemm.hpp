@@ -300,6 +300,14 @@ __global__ __launch_bounds__(T::THREADS, 4) void gemm_fewcol_kernel(GemmArgs g)
     fewcol_body<T, B_COL>(g, (int)blockIdx.x, bs);
 }
 
+// The same with the linear-layer epilogue.
+template <class T, bool B_COL>
+__global__ __launch_bounds__(T::THREADS, 4) void gemm_fewcol_epi_kernel(GemmArgs g)
+{
+    __shared__ f32x4 bs[T::R * T::LD / 4];
+    fewcol_body<T, B_COL, false, true>(g, (int)blockIdx.x, bs);
+}
+
 // The transposed product C^T = B^T . A^T for one row of C and column-major B
 // (y = W x with the weight W stored one output per row).  The kernel's A is
 // the caller's B read as a row-major N x K matrix (its columns are contiguous

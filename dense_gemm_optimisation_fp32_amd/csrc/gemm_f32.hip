@@ -137,6 +137,9 @@ VariantDesc fewcol_variant(const char *name)
         name, GEMM_F32_KIND_FEWCOL, T::ROWS, T::R, T::KC, T::WAVES, 1, T::THREADS, T::LDS_BYTES, 1,
         {reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_kernel<T, false>),
          reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_kernel<T, true>)}};
+    // The linear-layer epilogue with row-major A.
+    d.fn_ex[0][0][1] = reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_epi_kernel<T, false>);
+    d.fn_ex[0][1][1] = reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_epi_kernel<T, true>);
     if constexpr (T::R == 1 || (T::R == 4 && T::KC == 1024)) {
         d.fn_t = reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_t_kernel<T, true>);
         d.fn_t_epi = reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_t_epi_kernel<T, true>);
@@ -604,8 +607,8 @@ int transposed_few_column(int64_t m, int64_t n, int64_t k, int layout_b)
 // the plan can run the stream-K kernel (row-major A, no epilogue); when it
 // cannot, few-tile long-k shapes take the best data-parallel tile instead.
 // epilogue: the plan fuses the linear-layer epilogue.  row_a: A is
-// row-major, so the few-row kernel (which carries the epilogue) can run the
-// few-tile shapes.
+// row-major, so the few-column kernels and the few-row kernel (which carry
+// the epilogue) can run the few-column and few-tile shapes.
 int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFacts &f, bool tail_ok, bool epilogue,
                    bool *stream_k, int64_t *tail_tiles, double *estimate = nullptr, int *split = nullptr,
                    bool row_a = true)
@@ -652,7 +655,7 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
     }
     // (2 to 4 columns: the staged 1024-k chunks up to k = 4096, the 2048-k
     // chunks beyond; fewcol_gemm.hpp has the measurements.)
-    if (tail_ok && n <= 8)
+    if (row_a && n <= 8)
         return n == 1 ? V_FEWCOL_R1 : n <= 4 ? (k <= 4096 ? V_FEWCOL_R4_K1024 : V_FEWCOL_R4) : V_FEWCOL_R8;
     if (row_a) {
         // (The few-row kernel also carries the epilogue, for row-major A.)

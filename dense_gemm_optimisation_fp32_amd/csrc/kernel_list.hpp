@@ -138,11 +138,11 @@ using Skinny16x32W16D4 = SkinnyTile<16, 4, 32>;   // 32-column tiles
     X2(gemm_skinny_kernel, Skinny16W16D4, false) X2(gemm_skinny_kernel, Skinny16W16D4, true) X2(gemm_skinny_epi_kernel, Skinny16W16D4, false) X2(gemm_skinny_epi_kernel, Skinny16W16D4, true)     \
     X2(gemm_skinny_kernel, Skinny32W8D4, false) X2(gemm_skinny_kernel, Skinny32W8D4, true) X2(gemm_skinny_epi_kernel, Skinny32W8D4, false) X2(gemm_skinny_epi_kernel, Skinny32W8D4, true)       \
     X2(gemm_skinny_kernel, Skinny16x32W16D4, false) X2(gemm_skinny_kernel, Skinny16x32W16D4, true) X2(gemm_skinny_epi_kernel, Skinny16x32W16D4, false) X2(gemm_skinny_epi_kernel, Skinny16x32W16D4, true) \
-    X2(gemm_fewcol_kernel, FewColR1, false) X2(gemm_fewcol_kernel, FewColR1, true)             \
+    X2(gemm_fewcol_kernel, FewColR1, false) X2(gemm_fewcol_kernel, FewColR1, true) X2(gemm_fewcol_epi_kernel, FewColR1, false) X2(gemm_fewcol_epi_kernel, FewColR1, true)             \
     X2(gemm_fewcol_t_kernel, FewColR1, true) X2(gemm_fewcol_t_epi_kernel, FewColR1, true)          \
-    X2(gemm_fewcol_kernel, FewColR4, false) X2(gemm_fewcol_kernel, FewColR4, true)             \
-    X2(gemm_fewcol_kernel, FewColR8, false) X2(gemm_fewcol_kernel, FewColR8, true)             \
-    X2(gemm_fewcol_kernel, FewColR4K1024, false) X2(gemm_fewcol_kernel, FewColR4K1024, true)   \
+    X2(gemm_fewcol_kernel, FewColR4, false) X2(gemm_fewcol_kernel, FewColR4, true) X2(gemm_fewcol_epi_kernel, FewColR4, false) X2(gemm_fewcol_epi_kernel, FewColR4, true)             \
+    X2(gemm_fewcol_kernel, FewColR8, false) X2(gemm_fewcol_kernel, FewColR8, true) X2(gemm_fewcol_epi_kernel, FewColR8, false) X2(gemm_fewcol_epi_kernel, FewColR8, true)             \
+    X2(gemm_fewcol_kernel, FewColR4K1024, false) X2(gemm_fewcol_kernel, FewColR4K1024, true) X2(gemm_fewcol_epi_kernel, FewColR4K1024, false) X2(gemm_fewcol_epi_kernel, FewColR4K1024, true)   \
     X2(gemm_fewcol_t_kernel, FewColR4K1024, true) X2(gemm_fewcol_t_epi_kernel, FewColR4K1024, true)
 
 #define GEMMF32_ALL_UNITS(X5, X2, X1)                                                     \

@@ -229,10 +229,11 @@ def test_group_m_default_per_tile():
     assert g.Plan(6144, 6144, 6144, ROW_MAJOR, 6144, 6144, 6144).info["group_m"] == 8
 
 
-# Few rows (and few tiles) with the epilogue: the few-row kernel applies it
+# Few rows (few tiles, few columns) with the epilogue: the few-row kernel applies it
 # where it writes C (one k split, or the last split of a tile to finish), the transposed
-# few-column plans (up to four rows, column-major B) where they store C's
-# element; column-major A keeps the tiled 64x64 plan.  (shape, B layout,
+# few-column plans (up to four rows, column-major B) and the few-column
+# kernels (N <= 8) where they store C's element; column-major A keeps the
+# tiled 64x64 plan.  (shape, B layout,
 # plan name, k splits.)
 FEW_ROW_EX = [((16, 4096, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
               ((16, 4096, 4096), COL_MAJOR, "skinny_16x64_w16_d4", 4),
@@ -244,7 +245,11 @@ FEW_ROW_EX = [((16, 4096, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
               ((1, 3001, 2049), COL_MAJOR, "fewcol_8x1_k2048", 1),
               ((3, 8192, 3000), COL_MAJOR, "fewcol_8x4_k1024", 1),
               ((256, 256, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
-              ((300, 700, 1500), COL_MAJOR, "skinny_16x64_w8_d4", 1)]
+              ((300, 700, 1500), COL_MAJOR, "skinny_16x64_w8_d4", 1),
+              ((1000, 1, 4096), ROW_MAJOR, "fewcol_8x1_k2048", 1),
+              ((777, 3, 2500), COL_MAJOR, "fewcol_8x4_k1024", 1),
+              ((700, 4, 9000), ROW_MAJOR, "fewcol_8x4_k2048", 1),
+              ((513, 7, 1000), COL_MAJOR, "fewcol_8x8_k1024", 1)]
 
 
 @pytest.mark.parametrize("shape,layout_b,name,split", FEW_ROW_EX)
@@ -265,7 +270,7 @@ def test_few_rows_epilogue(shape, layout_b, name, split):
             C, info, outs = run_ex(A, B, m, n, k, ROW_MAJOR, layout_b, epilogue=1, alpha=alpha, beta=beta,
                                    c_in=c_in, bias=bias if with_bias else None, act=act, repeat=2)
             assert info["name"] == name and info["epilogue"] == 1 and info["split_k"] == split
-            assert info["transposed"] == (1 if name.startswith("fewcol") else 0)
+            assert info["transposed"] == (1 if name.startswith("fewcol") and n > 8 else 0)
             ref, scale = oracle.epilogue_f64(AB, S, c_in, alpha, beta, bias if with_bias else None, act)
             check(C[:, :n], ref, scale, f"{name} {shape} act={act} alpha={alpha} beta={beta}")
             assert np.array_equal(outs[0], outs[1])
