@@ -54,8 +54,8 @@ METRIC = "FP32 GEMM TFLOPS (2MNK/t) and % of MI355X FP32 matrix peak at 4096^3"
 TRAFFIC_SOURCES = ("device_common.hpp", "mfma_gemm.hpp", "mfma_dma_gemm.hpp")
 TRAFFIC_COUNTERS = {
     "sq4096": {"kernel": "dma_256x256x16_w4x2_s4",
-               "sources_sha1": "83e50de05f66627c18ccf652009ae9bd3252e9ff",
-               "fetch_kib": 196678.9, "write_kib": 65536.0,
+               "sources_sha1": "72a0065f3a3f4f9925b330e49eea83347ac410e9",
+               "fetch_kib": 196677.8, "write_kib": 65536.0,
                "fetch_factor": 2.000, "write_factor": 1.000},
 }
 

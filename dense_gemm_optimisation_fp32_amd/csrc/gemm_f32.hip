@@ -70,6 +70,8 @@ struct VariantDesc {
     const void *fn_t;           // few-column: the transposed product C^T = B^T A^T for
                                 // column-major B (gemm_fewcol_t_kernel), or NULL
     const void *fn_t_epi;       // the same with the linear-layer epilogue, or NULL
+    const void *fn_sk_epi[2];   // [column-major B]: stream-K with the linear-layer epilogue
+                                // (row-major A), or NULL
 };
 
 template <class T>
@@ -115,6 +117,16 @@ VariantDesc dma_ex_variant(const char *name)
         d.fn_wide[0][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, false, false, true, true>);
         d.fn_wide[1][1] = reinterpret_cast<const void *>(&gemm_mfma_dma_kernel<T, false, true, true, true>);
     }
+    return d;
+}
+
+// The two-stage 64 x 64 tile: also stream-K with the linear-layer epilogue
+// (the few-tile long-k plans of epilogue plans with row-major A).
+template <class T>
+VariantDesc with_sk_epi(VariantDesc d)
+{
+    d.fn_sk_epi[0] = reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_sk_epi_kernel<T, false>);
+    d.fn_sk_epi[1] = reinterpret_cast<const void *>(&gemmf32::gemm_mfma_dma_sk_epi_kernel<T, true>);
     return d;
 }
 
@@ -230,7 +242,7 @@ const VariantDesc &variant(int v)
         dma_ex_variant<DmaTile<64, 64, 16, 2, 2, 3>>("dma_64x64x16_w2x2_s3"),
         skinny_variant<SkinnyTile<16, 4, 64>>("skinny_16x64_w16_d4"),
         skinny_variant<SkinnyTile<16, 4, 16>>("skinny_16x16_w16_d4"),
-        dma_ex_variant<DmaTile<64, 64, 16, 2, 2, 2>>("dma_64x64x16_w2x2_s2"),
+        with_sk_epi<DmaTile<64, 64, 16, 2, 2, 2>>(dma_ex_variant<DmaTile<64, 64, 16, 2, 2, 2>>("dma_64x64x16_w2x2_s2")),
         dma_variant<DmaTile<128, 64, 16, 2, 2, 2>>("dma_128x64x16_w2x2_s2"),
         dma_variant<DmaTile<128, 64, 16, 2, 2, 3>>("dma_128x64x16_w2x2_s3"),
         dma_ex_variant<DmaTile<64, 128, 16, 2, 2, 2>>("dma_64x128x16_w2x2_s2"),
@@ -666,7 +678,9 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
             return v;
         }
     }
-    if (few_tile_stream_k(m, n, k, f, tail_ok)) {
+    // (Epilogue plans with row-major A have the two-stage 64 x 64 tile's
+    // stream-K kernel.)
+    if (few_tile_stream_k(m, n, k, f, tail_ok || (epilogue && row_a))) {
         // Column-major B whose 64 x 128 tiles make one nearly full wave (7/8
         // of the CUs to all of them, one workgroup each): those tiles,
         // data-parallel.  Measured on one MI355X (us, 64x128 / stream-K over
@@ -683,8 +697,8 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
         // / 130.2) or k = 8192 (512x4096x8192 271.6 / 269.6).
         const int64_t t128 = ceil_div(m, 64) * ceil_div(n, 128), cus = f.cu_count;
         if (layout_b == GEMM_F32_COL_MAJOR && 8 * t128 >= 7 * cus && t128 <= cus) return V_DMA_64x128x16_S2;
-        if (layout_b == GEMM_F32_ROW_MAJOR && 16 * t128 >= 15 * cus && t128 <= cus && k <= 6144)
-            return V_DMA_64x128x16_S3;
+        if (layout_b == GEMM_F32_ROW_MAJOR && tail_ok && 16 * t128 >= 15 * cus && t128 <= cus && k <= 6144)
+            return V_DMA_64x128x16_S3;   // (no epilogue kernels)
         *stream_k = true;
         return V_DMA_64x64x16_S2;
     }
@@ -805,7 +819,10 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
     }
     const VariantDesc &d = variant(v);
     if (ex && !swap_ab && !d.fn_ex[layout_a][layout_b][epilogue]) return GEMM_F32_ERR_INVALID_VALUE;
-    if (ex) {
+    // Stream-K for the linear-layer epilogue with row-major A where the
+    // variant has its kernels; none for column-major A.
+    const void *const *fn_sk = epilogue ? d.fn_sk_epi : d.fn_sk;
+    if (layout_a == GEMM_F32_COL_MAJOR || !fn_sk[0]) {
         auto_stream_k = false;
         auto_tail = 0;
     }
@@ -905,7 +922,7 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
         }
     }
 
-    if (d.fn_sk[0]) {
+    if (fn_sk[0]) {
         // Stream-K, chosen by the shape dispatch: either up to three
         // workgroups per CU share the k-slabs of all tiles evenly, or one
         // workgroup per CU shares those of the partial last wave's tiles
@@ -914,7 +931,7 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
         // the other tiles get a workgroup each); GEMM_F32_STREAMK=0 disables
         // the automatic choice.
         const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
-        int64_t wgs = ex ? 0 : env_int("GEMM_F32_SK_WGS", 0);
+        int64_t wgs = layout_a == GEMM_F32_COL_MAJOR ? 0 : env_int("GEMM_F32_SK_WGS", 0);
         int64_t shared = wgs > 0 ? env_int("GEMM_F32_SK_TILES", (int)tiles) : tiles;
         if (wgs <= 0 && auto_tail > 0 && env_int("GEMM_F32_STREAMK", 1) != 0) {
             // The partial last wave's tiles (the first ones in raster order)
@@ -924,7 +941,7 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
             shared = auto_tail;
         } else if (wgs <= 0 && auto_stream_k && env_int("GEMM_F32_STREAMK", 1) != 0) {
             int per_cu = 0;
-            hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, d.fn_sk[layout_b], d.threads, 0);
+            hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn_sk[layout_b], d.threads, 0);
             if (e != hipSuccess) return hip_fail(e);
             // Three workgroups per CU (fewer if fewer fit), at most 8
             // segments per tile (the last one to arrive reads all the
@@ -945,6 +962,7 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
         if (wgs > 0) {
             a.sk_wgs = (int)wgs;
             a.sk_tiles = (int)shared;
+            p->fn = fn_sk[layout_b];
             p->c_store_width = 1;   // the stream-K kernel stores one element at a time
             p->grid = (unsigned)(wgs + tiles - shared);
             const size_t words = (size_t)2 * wgs * d.bm * d.bn * sizeof(unsigned long long);
@@ -1133,6 +1151,7 @@ void for_each_kernel(const VariantDesc &d, F f)
 {
     for (const void *fn : d.fn) f(fn);
     for (const void *fn : d.fn_sk) f(fn);
+    for (const void *fn : d.fn_sk_epi) f(fn);
     for (int a = 0; a < 2; ++a)
         for (int b = 0; b < 2; ++b)
             for (int e = 0; e < 2; ++e) f(d.fn_ex[a][b][e]);
@@ -1227,9 +1246,7 @@ int launch_kernel(const gemm_f32_plan_impl *p, GemmArgs &a, void *stream)
 {
     void *kargs[] = {&a};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const int col = p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0;
-    const void *fn = p->args.sk_wgs ? variant(p->variant).fn_sk[col] : p->fn;
-    hipError_t e = hipLaunchKernel(fn, dim3(p->grid), dim3(p->block), kargs, 0, s);
+    hipError_t e = hipLaunchKernel(p->fn, dim3(p->grid), dim3(p->block), kargs, 0, s);
     if (e != hipSuccess) return hip_fail(e);
     return GEMM_F32_SUCCESS;
 }
@@ -1435,8 +1452,7 @@ int gemm_f32_describe(gemm_f32_plan p, gemm_f32_info *info)
     info->layout_a = p->layout_a;
     info->epilogue = p->epilogue;
     // The kernel this plan launches, its resources and its occupancy.
-    const int col = p->layout_b == GEMM_F32_COL_MAJOR ? 1 : 0;
-    const void *fn = p->args.sk_wgs ? variant(p->variant).fn_sk[col] : p->fn;
+    const void *fn = p->fn;
     info->vgprs = info->agprs = info->sgprs = info->scratch_bytes = info->compiler_waves_per_simd = 0;
     fill_resources(fn, info);
     int wgs = 0;

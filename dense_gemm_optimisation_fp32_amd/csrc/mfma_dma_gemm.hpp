@@ -41,6 +41,7 @@
 // its extent and already zero).
 #pragma once
 
+#include "epilogue.hpp"
 #include "mfma_gemm.hpp"
 
 namespace gemmf32 {
@@ -630,7 +631,7 @@ struct StreamK {
 // device-scope cache policy, with the lane's offset in one register and the
 // slot and block in the scalar offset, and are read back eight per lane at
 // a time, so the fix-up needs few registers beyond the main loop's.
-template <class T, bool B_COL>
+template <class T, bool B_COL, bool EPI = false>
 __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsrc_t rc, const StreamK &sk, int t,
                                           int p, int tid, int row0, int col0, int wr, int wc, int l32, int half,
                                           int *last_flag, unsigned epoch, const f32x16 (&acc)[T::MB][T::NB])
@@ -710,7 +711,12 @@ __device__ __forceinline__ void dma_fixup(const GemmArgs &g, __amdgpu_buffer_rsr
                     const int e = v0 + v;
                     const int r = row0 + wr * T::WM + mb * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
                     const int c = B_COL ? col0 + wc * T::WN + nb * 32 + l32 : col0 + wc * T::WN + T::NB * l32 + nb;
-                    buf_store_x1(sum[v], rc, elem_off(r < g.m && c < g.n, r, g.ldc, c));
+                    const bool in = r < g.m && c < g.n;
+                    float y = sum[v];
+                    if constexpr (EPI) {
+                        if (in) y = linear_epilogue(g, y, r, c);
+                    }
+                    buf_store_x1(y, rc, elem_off(in, r, g.ldc, c));
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -783,8 +789,10 @@ constexpr int sk_waves_per_simd()
     return lds_cap < reg_cap ? lds_cap : reg_cap;
 }
 
-template <class T, bool B_COL>
-__global__ __launch_bounds__(T::THREADS, sk_waves_per_simd<T>()) void gemm_mfma_dma_sk_kernel(GemmArgs g)
+// EPI: C gets the linear-layer epilogue, in the whole tiles' stores and in
+// the fix-up's (linear_epilogue, per element).
+template <class T, bool B_COL, bool EPI>
+__device__ __forceinline__ void dma_sk_body(const GemmArgs &g)
 {
     // The fix-up's flag lives in one extra chunk of the ring's array: with a
     // second LDS variable the compiler can no longer tell the ring's copies
@@ -818,7 +826,7 @@ __global__ __launch_bounds__(T::THREADS, sk_waves_per_simd<T>()) void gemm_mfma_
 #pragma unroll
             for (int nb = 0; nb < T::NB; ++nb) acc[mb][nb] = f32x16{};
         dma_range<T, B_COL>(g, lds_a, lds_b, ra, rb, row0, col0, 0, KT, tid, wave, wr, wc, l32, half, acc);
-        dma_store_c<T, B_COL>(g, rc, row0, col0, wr, wc, l32, half, acc);
+        dma_store_c<T, B_COL, false, EPI>(g, rc, row0, col0, wr, wc, l32, half, acc);
         return;
     }
 
@@ -864,9 +872,10 @@ __global__ __launch_bounds__(T::THREADS, sk_waves_per_simd<T>()) void gemm_mfma_
             for (int nb = 0; nb < T::NB; ++nb) acc[mb][nb] = f32x16{};
         dma_range<T, B_COL>(g, lds_a, lds_b, ra, rb, row0, col0, kt0, kt1, tid_i, wave, wr, wc, l32_i, half_i, acc);
         if (kt0 == 0 && kt1 == KT)
-            dma_store_c<T, B_COL>(g, rc, row0, col0, wr, wc, l32_i, half_i, acc);
+            dma_store_c<T, B_COL, false, EPI>(g, rc, row0, col0, wr, wc, l32_i, half_i, acc);
         else
-            dma_fixup<T, B_COL>(g, rc, sk, t, p, tid_i, row0, col0, wr, wc, l32_i, half_i, last_flag, epoch, acc);
+            dma_fixup<T, B_COL, EPI>(g, rc, sk, t, p, tid_i, row0, col0, wr, wc, l32_i, half_i, last_flag, epoch,
+                                     acc);
     }
     // A word-tagged launch counts the split tiles this workgroup finished
     // (here, where the registers are free, rather than in the fix-up).
@@ -874,6 +883,22 @@ __global__ __launch_bounds__(T::THREADS, sk_waves_per_simd<T>()) void gemm_mfma_
         const int finished = last_flag[1];
         advance_epoch(g, count_split_tiles(g, finished), epoch, finished);
     }
+}
+
+template <class T, bool B_COL>
+__global__ __launch_bounds__(T::THREADS, sk_waves_per_simd<T>()) void gemm_mfma_dma_sk_kernel(GemmArgs g)
+{
+    dma_sk_body<T, B_COL, false>(g);
+}
+
+// The same with the linear-layer epilogue (row-major A).  Held to four
+// wavefronts per SIMD (the epilogue's registers spilled at eight; the
+// stream-K plans run at most three workgroups per CU).
+template <class T, bool B_COL>
+__global__ __launch_bounds__(T::THREADS, sk_waves_per_simd<T>() < 4 ? sk_waves_per_simd<T>() : 4) void
+gemm_mfma_dma_sk_epi_kernel(GemmArgs g)
+{
+    dma_sk_body<T, B_COL, true>(g);
 }
 
 }  // namespace gemmf32

@@ -299,3 +299,62 @@ def test_few_rows_epilogue_column_major_a():
     AB, S = oracle.gemm_f64(A, B, m, n, k, ROW_MAJOR, layout_a=COL_MAJOR)
     ref, scale = oracle.epilogue_f64(AB, S, c_in, 0.5, 2.0, bias, g.GEMM_F32_ACT_GELU)
     check(C[:, :n], ref, scale, "column-major A, few rows")
+
+
+@pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])
+def test_stream_k_epilogue_default_plan(layout_b):
+    """Few tiles and long k with the epilogue and row-major A: stream-K over
+    64x64 tiles, the epilogue applied by the last segment of each split tile;
+    against the oracle's epilogue, runs repeating bit for bit, and integer
+    operands exact."""
+    m, n, k = 1024, 1024, 8192
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=900)
+    c_in, bias = epilogue_operands(m, n, seed=901)
+    AB, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    for act, alpha, beta in ((g.GEMM_F32_ACT_GELU, 0.5, -1.5), (g.GEMM_F32_ACT_NONE, 1.0, 0.0)):
+        print(f"\n[case] stream-K epilogue layout_b={layout_b} act={act}", flush=True)
+        C, info, outs = run_ex(A, B, m, n, k, ROW_MAJOR, layout_b, epilogue=1, alpha=alpha, beta=beta,
+                               c_in=c_in, bias=bias, act=act, repeat=2)
+        assert info["name"] == "dma_64x64x16_w2x2_s2" and info["stream_k"] > 1 and info["epilogue"] == 1
+        ref, scale = oracle.epilogue_f64(AB, S, c_in, alpha, beta, bias, act)
+        check(C[:, :n], ref, scale, f"stream-K epilogue act={act}")
+        assert np.array_equal(outs[0], outs[1])
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=902)
+    rng = np.random.default_rng(903)
+    c_in = rng.integers(-50, 51, (m, n)).astype(np.float32)
+    bias = rng.integers(-9, 10, n).astype(np.float32)
+    AB, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    C, _, _ = run_ex(A, B, m, n, k, ROW_MAJOR, layout_b, epilogue=1, alpha=1.0, beta=1.0, c_in=c_in, bias=bias,
+                     act=g.GEMM_F32_ACT_RELU)
+    ref, _ = oracle.epilogue_f64(AB, S, c_in, 1.0, 1.0, bias, g.GEMM_F32_ACT_RELU)
+    assert np.array_equal(C[:, :n].astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("wgs,shared", [(3, None), (40, None), (7, 5)])
+def test_stream_k_epilogue_forced(wgs, shared, monkeypatch):
+    """Forced stream-K with the epilogue on ragged 64x64 tiles: segments
+    shorter than a tile, tiles shared by many segments, and (with a subset of
+    shared tiles) whole tiles stored by the stream-K kernel itself."""
+    monkeypatch.setenv("GEMM_F32_VARIANT", str(variant_index("dma_64x64x16_w2x2_s2")))
+    monkeypatch.setenv("GEMM_F32_SK_WGS", str(wgs))
+    if shared is not None:
+        monkeypatch.setenv("GEMM_F32_SK_TILES", str(shared))
+    m, n, k = 300, 200, 999
+    A, B = random_operands(m, n, k, ROW_MAJOR, "normal1", seed=910 + wgs)
+    c_in, bias = epilogue_operands(m, n, seed=911)
+    AB, S = oracle.gemm_f64(A, B, m, n, k, ROW_MAJOR)
+    C, info, outs = run_ex(A, B, m, n, k, ROW_MAJOR, ROW_MAJOR, ldc=n + 3, epilogue=1, alpha=2.0, beta=0.5,
+                           c_in=c_in, bias=bias, act=g.GEMM_F32_ACT_GELU, c_fill=-3.5, repeat=2)
+    assert info["stream_k"] == wgs and info["stream_k_tiles"] == (shared or info["tiles_m"] * info["tiles_n"])
+    ref, scale = oracle.epilogue_f64(AB, S, c_in, 2.0, 0.5, bias, g.GEMM_F32_ACT_GELU)
+    check(C[:, :n], ref, scale, f"forced stream-K epilogue wgs={wgs}")
+    assert np.array_equal(outs[0], outs[1])
+    assert np.all(C[:, n:] == np.float32(-3.5))
+
+
+def test_stream_k_epilogue_column_major_a_stays_data_parallel():
+    """Column-major A has no stream-K kernels: the few-tile long-k epilogue
+    plan runs whole tiles."""
+    m, n, k = 1024, 1024, 8192
+    plan = g.Plan(m, n, k, ROW_MAJOR, m, n, n, layout_a=COL_MAJOR, epilogue=1)
+    assert plan.info["stream_k"] == 0

@@ -444,14 +444,18 @@ def test_dispatch_choice(shape, name, tail):
 
 
 def test_linear_plan_for_few_tiles_long_k():
-    """A few-tile long-k shape gets stream-K as a plain product; with the
-    epilogue (no stream-K kernel) it gets the data-parallel tile with the most
-    tiles rather than the stream-K tile run whole."""
+    """A few-tile long-k shape gets stream-K as a plain product and with the
+    epilogue and row-major A (the two-stage 64x64 tile's stream-K kernel
+    carries it); with column-major A (no stream-K kernel) it gets the
+    data-parallel tile with the most tiles rather than the stream-K tile run
+    whole."""
     import dense_gemm_optimisation_fp32_amd as g
 
     m, n, k = 1024, 1024, 8192
     assert g.Plan(m, n, k, ROW_MAJOR, k, n, n).info["stream_k"] > 0
     info = g.Plan(m, n, k, ROW_MAJOR, k, n, n, epilogue=1).info
+    assert info["stream_k"] > 0 and info["name"] == "dma_64x64x16_w2x2_s2"
+    info = g.Plan(m, n, k, ROW_MAJOR, m, n, n, layout_a=COL_MAJOR, epilogue=1).info
     assert info["stream_k"] == 0 and info["name"] == "dma_64x64x16_w2x2_s2"
 
 
