@@ -138,3 +138,55 @@ def test_noalloc_replayed_from_a_graph(shape, layout_b, kind):
         torch.cuda.synchronize()
         assert np.array_equal(C.cpu().numpy(), want)
     del graph
+
+
+# Epilogue plans whose kernels split tiles along k: stream-K over 64x64 tiles
+# and the few-row kernel's k splits, each with bias + GELU (beta = 0, so every
+# replay computes the same function of the new inputs).
+EPI_CASES = [((1024, 1024, 8192), ROW_MAJOR, "stream_k"),
+             ((16, 4096, 4096), COL_MAJOR, "split_k"),
+             ((4, 8192, 3000), COL_MAJOR, "transposed")]
+
+
+@pytest.mark.parametrize("shape,layout_b,kind", EPI_CASES)
+def test_epilogue_plan_replayed_from_a_graph(shape, layout_b, kind):
+    m, n, k = shape
+    ldb = n if layout_b == ROW_MAJOR else k
+    print(f"\n[case] graph replay epilogue {kind} shape={shape} layout_b={layout_b}", flush=True)
+    plan = g.Plan(m, n, k, layout_b, k, ldb, n, epilogue=1)
+    info = plan.info
+    if kind == "stream_k":
+        assert info["stream_k"] > 1
+    elif kind == "split_k":
+        assert info["split_k"] > 1
+    else:
+        assert info["transposed"] == 1
+    stream = lambda: torch.cuda.current_stream().cuda_stream
+    dA, dB = _device_operands(m, n, k, layout_b, seed=2500)
+    bias = torch.linspace(-1.0, 1.0, n, device="cuda")
+    C = torch.full((m, n), float("nan"), device="cuda")
+    run = lambda: plan.run_ex(dA.data_ptr(), dB.data_ptr(), C.data_ptr(), 1.0, 0.0, bias.data_ptr(),
+                              g.GEMM_F32_ACT_GELU, stream())
+    run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        nA, nB = _device_operands(m, n, k, layout_b, seed=2600 + rep)
+        dA.copy_(nA)
+        dB.copy_(nB)
+        C.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = C.cpu().numpy()
+        C.fill_(float("nan"))
+        run()                                   # the eager run of the same plan and inputs
+        torch.cuda.synchronize()
+        want = C.cpu().numpy()
+        assert np.isfinite(got).all(), f"replay {rep}: NaN in C"
+        assert np.array_equal(got, want), f"replay {rep} differs from the eager run"
+    assert g.gemm_f32_plan_check(plan.handle) is False
+    del graph
