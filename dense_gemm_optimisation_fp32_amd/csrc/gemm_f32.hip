@@ -166,9 +166,13 @@ VariantDesc skinny_variant(const char *name)
         name, GEMM_F32_KIND_SKINNY, T::BM, T::BN, T::KQ, 1, T::WAVES, T::THREADS, T::WAVES * T::BM * T::BN * 4, 1,
         {reinterpret_cast<const void *>(&gemmf32::gemm_skinny_kernel<T, false>),
          reinterpret_cast<const void *>(&gemmf32::gemm_skinny_kernel<T, true>)}};
-    // The linear-layer epilogue with row-major A (no column-major A kernels).
+    // Column-major A and the linear-layer epilogue.
     d.fn_ex[0][0][1] = reinterpret_cast<const void *>(&gemmf32::gemm_skinny_epi_kernel<T, false>);
     d.fn_ex[0][1][1] = reinterpret_cast<const void *>(&gemmf32::gemm_skinny_epi_kernel<T, true>);
+    d.fn_ex[1][0][0] = reinterpret_cast<const void *>(&gemmf32::gemm_skinny_acol_kernel<T, false>);
+    d.fn_ex[1][1][0] = reinterpret_cast<const void *>(&gemmf32::gemm_skinny_acol_kernel<T, true>);
+    d.fn_ex[1][0][1] = reinterpret_cast<const void *>(&gemmf32::gemm_skinny_acol_epi_kernel<T, false>);
+    d.fn_ex[1][1][1] = reinterpret_cast<const void *>(&gemmf32::gemm_skinny_acol_epi_kernel<T, true>);
     return d;
 }
 
@@ -619,8 +623,8 @@ int transposed_few_column(int64_t m, int64_t n, int64_t k, int layout_b)
 // the plan can run the stream-K kernel (row-major A, no epilogue); when it
 // cannot, few-tile long-k shapes take the best data-parallel tile instead.
 // epilogue: the plan fuses the linear-layer epilogue.  row_a: A is
-// row-major, so the few-column kernels and the few-row kernel (which carry
-// the epilogue) can run the few-column and few-tile shapes.
+// row-major, so the few-column kernels (which carry the epilogue) can run
+// the few-column shapes; the few-row kernel serves both A layouts.
 int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFacts &f, bool tail_ok, bool epilogue,
                    bool *stream_k, int64_t *tail_tiles, double *estimate = nullptr, int *split = nullptr,
                    bool row_a = true)
@@ -669,8 +673,8 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
     // chunks beyond; fewcol_gemm.hpp has the measurements.)
     if (row_a && n <= 8)
         return n == 1 ? V_FEWCOL_R1 : n <= 4 ? (k <= 4096 ? V_FEWCOL_R4_K1024 : V_FEWCOL_R4) : V_FEWCOL_R8;
-    if (row_a) {
-        // (The few-row kernel also carries the epilogue, for row-major A.)
+    {
+        // (The few-row kernel carries the epilogue and column-major A too.)
         int s = 0;
         const int v = few_tile_rows(m, n, k, layout_b, f, &s);
         if (v >= 0) {

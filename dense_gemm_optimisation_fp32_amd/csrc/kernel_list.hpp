@@ -133,12 +133,18 @@ using Skinny16x32W16D4 = SkinnyTile<16, 4, 32>;   // 32-column tiles
     X2(gemm_mfma_kernel, Reg256x128x32, false) X2(gemm_mfma_kernel, Reg256x128x32, true) \
     X2(gemm_mfma_kernel, Reg128x128x32, false) X2(gemm_mfma_kernel, Reg128x128x32, true) \
     X1(gemm_valu_kernel, false) X1(gemm_valu_kernel, true)                                   \
-    X2(gemm_skinny_kernel, SkinnyW4D4, false) X2(gemm_skinny_kernel, SkinnyW4D4, true) X2(gemm_skinny_epi_kernel, SkinnyW4D4, false) X2(gemm_skinny_epi_kernel, SkinnyW4D4, true)       \
-    X2(gemm_skinny_kernel, SkinnyW8D4, false) X2(gemm_skinny_kernel, SkinnyW8D4, true) X2(gemm_skinny_epi_kernel, SkinnyW8D4, false) X2(gemm_skinny_epi_kernel, SkinnyW8D4, true)       \
-    X2(gemm_skinny_kernel, SkinnyW16D4, false) X2(gemm_skinny_kernel, SkinnyW16D4, true) X2(gemm_skinny_epi_kernel, SkinnyW16D4, false) X2(gemm_skinny_epi_kernel, SkinnyW16D4, true)     \
-    X2(gemm_skinny_kernel, Skinny16W16D4, false) X2(gemm_skinny_kernel, Skinny16W16D4, true) X2(gemm_skinny_epi_kernel, Skinny16W16D4, false) X2(gemm_skinny_epi_kernel, Skinny16W16D4, true)     \
-    X2(gemm_skinny_kernel, Skinny32W8D4, false) X2(gemm_skinny_kernel, Skinny32W8D4, true) X2(gemm_skinny_epi_kernel, Skinny32W8D4, false) X2(gemm_skinny_epi_kernel, Skinny32W8D4, true)       \
+    X2(gemm_skinny_kernel, SkinnyW4D4, false) X2(gemm_skinny_kernel, SkinnyW4D4, true) X2(gemm_skinny_epi_kernel, SkinnyW4D4, false) X2(gemm_skinny_epi_kernel, SkinnyW4D4, true) \
+    X2(gemm_skinny_acol_kernel, SkinnyW4D4, false) X2(gemm_skinny_acol_kernel, SkinnyW4D4, true) X2(gemm_skinny_acol_epi_kernel, SkinnyW4D4, false) X2(gemm_skinny_acol_epi_kernel, SkinnyW4D4, true)       \
+    X2(gemm_skinny_kernel, SkinnyW8D4, false) X2(gemm_skinny_kernel, SkinnyW8D4, true) X2(gemm_skinny_epi_kernel, SkinnyW8D4, false) X2(gemm_skinny_epi_kernel, SkinnyW8D4, true) \
+    X2(gemm_skinny_acol_kernel, SkinnyW8D4, false) X2(gemm_skinny_acol_kernel, SkinnyW8D4, true) X2(gemm_skinny_acol_epi_kernel, SkinnyW8D4, false) X2(gemm_skinny_acol_epi_kernel, SkinnyW8D4, true)       \
+    X2(gemm_skinny_kernel, SkinnyW16D4, false) X2(gemm_skinny_kernel, SkinnyW16D4, true) X2(gemm_skinny_epi_kernel, SkinnyW16D4, false) X2(gemm_skinny_epi_kernel, SkinnyW16D4, true) \
+    X2(gemm_skinny_acol_kernel, SkinnyW16D4, false) X2(gemm_skinny_acol_kernel, SkinnyW16D4, true) X2(gemm_skinny_acol_epi_kernel, SkinnyW16D4, false) X2(gemm_skinny_acol_epi_kernel, SkinnyW16D4, true)     \
+    X2(gemm_skinny_kernel, Skinny16W16D4, false) X2(gemm_skinny_kernel, Skinny16W16D4, true) X2(gemm_skinny_epi_kernel, Skinny16W16D4, false) X2(gemm_skinny_epi_kernel, Skinny16W16D4, true) \
+    X2(gemm_skinny_acol_kernel, Skinny16W16D4, false) X2(gemm_skinny_acol_kernel, Skinny16W16D4, true) X2(gemm_skinny_acol_epi_kernel, Skinny16W16D4, false) X2(gemm_skinny_acol_epi_kernel, Skinny16W16D4, true)     \
+    X2(gemm_skinny_kernel, Skinny32W8D4, false) X2(gemm_skinny_kernel, Skinny32W8D4, true) X2(gemm_skinny_epi_kernel, Skinny32W8D4, false) X2(gemm_skinny_epi_kernel, Skinny32W8D4, true) \
+    X2(gemm_skinny_acol_kernel, Skinny32W8D4, false) X2(gemm_skinny_acol_kernel, Skinny32W8D4, true) X2(gemm_skinny_acol_epi_kernel, Skinny32W8D4, false) X2(gemm_skinny_acol_epi_kernel, Skinny32W8D4, true)       \
     X2(gemm_skinny_kernel, Skinny16x32W16D4, false) X2(gemm_skinny_kernel, Skinny16x32W16D4, true) X2(gemm_skinny_epi_kernel, Skinny16x32W16D4, false) X2(gemm_skinny_epi_kernel, Skinny16x32W16D4, true) \
+    X2(gemm_skinny_acol_kernel, Skinny16x32W16D4, false) X2(gemm_skinny_acol_kernel, Skinny16x32W16D4, true) X2(gemm_skinny_acol_epi_kernel, Skinny16x32W16D4, false) X2(gemm_skinny_acol_epi_kernel, Skinny16x32W16D4, true) \
     X2(gemm_fewcol_kernel, FewColR1, false) X2(gemm_fewcol_kernel, FewColR1, true) X2(gemm_fewcol_epi_kernel, FewColR1, false) X2(gemm_fewcol_epi_kernel, FewColR1, true)             \
     X2(gemm_fewcol_t_kernel, FewColR1, true) X2(gemm_fewcol_t_epi_kernel, FewColR1, true)          \
     X2(gemm_fewcol_kernel, FewColR4, false) X2(gemm_fewcol_kernel, FewColR4, true) X2(gemm_fewcol_epi_kernel, FewColR4, false) X2(gemm_fewcol_epi_kernel, FewColR4, true)             \

@@ -90,8 +90,10 @@ constexpr bool red_index_one_to_one()
 // (column-major B) is column 4j + nb; NB = 2: b[nb][t] is column 2j + nb; NB = 1: b[0][t] is column j.  Element
 // checks only when the group is not whole (tail of a range, or k past K).
 // Columns at or past N may read other elements of B: they only feed columns
-// of C that are never stored.
-template <class T, bool B_COL>
+// of C that are never stored.  A_COL: column-major A, read one element per
+// k-step (16 lanes read 64 contiguous bytes of a column; A is small and read
+// from the L2).
+template <class T, bool B_COL, bool A_COL = false>
 __device__ __forceinline__ void skinny_load(const GemmArgs &g, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                             int row, int col0, int j, int h, int kq, int kend, bool whole,
                                             bool live, f32x4 (&a)[T::RT], f32x4 (&b)[T::NB])
@@ -100,8 +102,18 @@ __device__ __forceinline__ void skinny_load(const GemmArgs &g, __amdgpu_buffer_r
     if (whole) {
         // A group that is not live reads zeros (out-of-range offsets).
 #pragma unroll
-        for (int r = 0; r < T::RT; ++r)
-            a[r] = buf_load_x4(ra, elem_off(live && row + 16 * r < g.m, row + 16 * r, g.lda, ka));
+        for (int r = 0; r < T::RT; ++r) {
+            if constexpr (A_COL) {
+                // One lane offset for the 4 k-steps; the steps' distance,
+                // lda elements, is uniform and goes in the scalar offset.
+                const uint32_t off = elem_off(live && row + 16 * r < g.m, ka, g.lda, row + 16 * r);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    a[r][q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, (int)off, q * g.lda * 4, 0));
+            } else {
+                a[r] = buf_load_x4(ra, elem_off(live && row + 16 * r < g.m, row + 16 * r, g.lda, ka));
+            }
+        }
         if constexpr (T::NB == 4 && !B_COL) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) b[t] = buf_load_x4(rb, elem_off(live, ka + t, g.ldb, col0 + 4 * j));
@@ -127,7 +139,8 @@ __device__ __forceinline__ void skinny_load(const GemmArgs &g, __amdgpu_buffer_r
         for (int r = 0; r < T::RT; ++r)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                a[r][q] = buf_load_x1(ra, elem_off(row + 16 * r < g.m && ka + q < kend, row + 16 * r, g.lda, ka + q));
+                a[r][q] = buf_load_x1(ra, A_COL ? elem_off(row + 16 * r < g.m && ka + q < kend, ka + q, g.lda, row + 16 * r)
+                                                : elem_off(row + 16 * r < g.m && ka + q < kend, row + 16 * r, g.lda, ka + q));
 #pragma unroll
         for (int x = 0; x < T::NB; ++x)
 #pragma unroll
@@ -162,7 +175,8 @@ __device__ __forceinline__ void skinny_mfma(const f32x4 (&a)[T::RT], const f32x4
 // workgroup writes its tile of C; otherwise the splits meet through
 // g.partial[split][m][n] (epoch-tagged words) and g.arrivals[tile].
 // EPI: C gets the linear-layer epilogue (linear_epilogue) where it is written.
-template <class T, bool B_COL, bool EPI>
+// A_COL: column-major A.
+template <class T, bool B_COL, bool EPI, bool A_COL = false>
 __device__ __forceinline__ void skinny_body(const GemmArgs &g)
 {
     static_assert(red_index_one_to_one<T>(), "reduction layout");
@@ -248,7 +262,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs &g)
         f32x4 a[D][T::RT], b[D][T::NB];
 #pragma unroll
         for (int u = 0; u < D; ++u) {
-            skinny_load<T, B_COL>(g, ra, rb, row, col0, j, h, kw0 + u * T::KQ, kw1, true, u < G, a[u], b[u]);
+            skinny_load<T, B_COL, A_COL>(g, ra, rb, row, col0, j, h, kw0 + u * T::KQ, kw1, true, u < G, a[u], b[u]);
             __builtin_amdgcn_sched_barrier(0);
         }
         for (int p = 1; p < passes; ++p) {
@@ -257,7 +271,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs &g)
                 const int q = p * D + u;
                 skinny_mfma<T, B_COL>(a[u], b[u], acc);
                 __builtin_amdgcn_sched_barrier(0);
-                skinny_load<T, B_COL>(g, ra, rb, row, col0, j, h, kw0 + q * T::KQ, kw1, true, q < G, a[u], b[u]);
+                skinny_load<T, B_COL, A_COL>(g, ra, rb, row, col0, j, h, kw0 + q * T::KQ, kw1, true, q < G, a[u], b[u]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -278,7 +292,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs &g)
     // The partial group at the end of the range, element by element.
     if (G * T::KQ < kspan) {
         f32x4 at[T::RT], bt[T::NB];
-        skinny_load<T, B_COL>(g, ra, rb, row, col0, j, h, kw0 + G * T::KQ, kw1, false, true, at, bt);
+        skinny_load<T, B_COL, A_COL>(g, ra, rb, row, col0, j, h, kw0 + G * T::KQ, kw1, false, true, at, bt);
         skinny_mfma<T, B_COL>(at, bt, acc);
     }
 
@@ -392,6 +406,19 @@ template <class T, bool B_COL>
 __global__ __launch_bounds__(T::THREADS) void gemm_skinny_epi_kernel(GemmArgs g)
 {
     skinny_body<T, B_COL, true>(g);
+}
+
+// Column-major A, without and with the epilogue.
+template <class T, bool B_COL>
+__global__ __launch_bounds__(T::THREADS) void gemm_skinny_acol_kernel(GemmArgs g)
+{
+    skinny_body<T, B_COL, false, true>(g);
+}
+
+template <class T, bool B_COL>
+__global__ __launch_bounds__(T::THREADS) void gemm_skinny_acol_epi_kernel(GemmArgs g)
+{
+    skinny_body<T, B_COL, true, true>(g);
 }
 
 }  // namespace gemmf32

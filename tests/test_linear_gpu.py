@@ -232,8 +232,7 @@ def test_group_m_default_per_tile():
 # Few rows (few tiles, few columns) with the epilogue: the few-row kernel applies it
 # where it writes C (one k split, or the last split of a tile to finish), the transposed
 # few-column plans (up to four rows, column-major B) and the few-column
-# kernels (N <= 8) where they store C's element; column-major A keeps the
-# tiled 64x64 plan.  (shape, B layout,
+# kernels (N <= 8) where they store C's element.  (shape, B layout,
 # plan name, k splits.)
 FEW_ROW_EX = [((16, 4096, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
               ((16, 4096, 4096), COL_MAJOR, "skinny_16x64_w16_d4", 4),
@@ -287,18 +286,42 @@ def test_few_rows_epilogue(shape, layout_b, name, split):
         assert np.all(C[:, n:] == np.float32(-3.5))
 
 
-def test_few_rows_epilogue_column_major_a():
-    """Column-major A with few rows has no few-row kernel: the 64x64 tiled
-    plan, against the oracle."""
-    m, n, k = 16, 1000, 700
-    A, B = random_operands(m, n, k, ROW_MAJOR, "normal1", seed=800, layout_a=COL_MAJOR)
-    c_in, bias = epilogue_operands(m, n, seed=801)
-    C, info, _ = run_ex(A, B, m, n, k, COL_MAJOR, ROW_MAJOR, epilogue=1, alpha=0.5, beta=2.0, c_in=c_in,
-                        bias=bias, act=g.GEMM_F32_ACT_GELU)
-    assert info["name"] == "dma_64x64x16_w2x2_s2"
-    AB, S = oracle.gemm_f64(A, B, m, n, k, ROW_MAJOR, layout_a=COL_MAJOR)
-    ref, scale = oracle.epilogue_f64(AB, S, c_in, 0.5, 2.0, bias, g.GEMM_F32_ACT_GELU)
-    check(C[:, :n], ref, scale, "column-major A, few rows")
+# Column-major A on the few-row kernel (16 rows of a column per 64-byte
+# read), plain and with the epilogue: (shape, B layout, plan name, k splits
+# or None).
+COL_A_FEW = [((16, 4096, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
+             ((24, 2048, 3000), COL_MAJOR, "skinny_32x64_w8_d4", 8),
+             ((16, 1000, 700), ROW_MAJOR, "skinny_16x64_w16_d4", None),
+             ((5, 2050, 777), COL_MAJOR, "skinny_16x32_w16_d4", 3),
+             ((200, 190, 70), ROW_MAJOR, "skinny_16x16_w16_d4", 1)]
+
+
+@pytest.mark.parametrize("shape,layout_b,name,split", COL_A_FEW)
+def test_few_rows_column_major_a(shape, layout_b, name, split):
+    """Column-major A (lda padded, NaN in the padding) on the few-row plans:
+    the plain product (integer operands bit for bit) and the epilogue against
+    the oracle."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the plans were chosen for a 256-CU MI355X")
+    m, n, k = shape
+    lda = m + 3
+    print(f"\n[case] few rows, column-major A {shape} layout_b={layout_b}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=820 + m, layout_a=COL_MAJOR, lda=lda)
+    C, info, outs = run_ex(A, B, m, n, k, COL_MAJOR, layout_b, lda=lda, repeat=2)
+    assert info["name"] == name and info["layout_a"] == COL_MAJOR
+    if split is not None:
+        assert info["split_k"] == split
+    Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b, lda=lda, layout_a=COL_MAJOR)
+    assert np.array_equal(C[:, :n].astype(np.float64), Cref)
+    assert np.array_equal(outs[0], outs[1])
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=830 + m, layout_a=COL_MAJOR, lda=lda)
+    c_in, bias = epilogue_operands(m, n, seed=831)
+    C, info, _ = run_ex(A, B, m, n, k, COL_MAJOR, layout_b, lda=lda, epilogue=1, alpha=0.5, beta=1.5,
+                        c_in=c_in, bias=bias, act=g.GEMM_F32_ACT_GELU)
+    assert info["name"] == name and info["epilogue"] == 1
+    AB, S = oracle.gemm_f64(A, B, m, n, k, layout_b, lda=lda, layout_a=COL_MAJOR)
+    ref, scale = oracle.epilogue_f64(AB, S, c_in, 0.5, 1.5, bias, g.GEMM_F32_ACT_GELU)
+    check(C[:, :n], ref, scale, f"{name} column-major A {shape}")
 
 
 @pytest.mark.parametrize("layout_b", [ROW_MAJOR, COL_MAJOR])

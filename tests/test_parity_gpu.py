@@ -390,10 +390,15 @@ def test_few_tile_rows_plan(shape, row_plan, col_plan, layout_b):
     C, _ = run_gemm(A, B, m, n, k, layout_b)
     Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
     assert np.array_equal(C.astype(np.float64), Cref)
-    # the linear-layer plans (no few-row kernel for them) stay tiled
+    # the linear-layer plans take the same plan (the few-row kernel carries
+    # the epilogue)
     import dense_gemm_optimisation_fp32_amd as g
     ldb = n if layout_b == ROW_MAJOR else k
-    assert g.Plan(m, n, k, layout_b, k, ldb, n, epilogue=1).info["name"].startswith("dma_")
+    info_ex = g.Plan(m, n, k, layout_b, k, ldb, n, epilogue=1).info
+    if want is None:
+        assert info_ex["name"].startswith("dma_")
+    else:
+        assert (info_ex["name"], info_ex["split_k"]) == want
 
 
 # The shape dispatch's choice on the shapes it was measured on (one MI355X,
