@@ -219,6 +219,7 @@ enum VariantId {
     V_SKINNY32_W8_D4,
     V_SKINNY_16x32_W16_D4,
     V_FEWCOL_R4_K1024,
+    V_SKINNY16_W4_D4,
     V_COUNT
 };
 
@@ -261,6 +262,7 @@ const VariantDesc &variant(int v)
         skinny_variant<SkinnyTile<8, 4, 64, 2>>("skinny_32x64_w8_d4"),
         skinny_variant<SkinnyTile<16, 4, 32>>("skinny_16x32_w16_d4"),
         fewcol_variant<gemmf32::FewColR4K1024>("fewcol_8x4_k1024"),
+        skinny_variant<SkinnyTile<4, 4, 16>>("skinny_16x16_w4_d4"),
     };
     return table[v];
 }
@@ -545,13 +547,24 @@ int few_tile_rows(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFac
     const int64_t t16 = ceil_div(m, 16) * ceil_div(n, 16);
     const int64_t t64 = ceil_div(m, 16) * ceil_div(n, 64);
     auto fill = [&](int64_t tiles) { return (int)std::max<int64_t>(1, std::min<int64_t>(8, cus / tiles)); };
+    // (16 x 16 tiles without a k split across workgroups run four
+    // wavefronts: fewer waves to launch on these latency-bound shapes.
+    // Measured on one MI355X, us, four / sixteen wavefronts, row-major then
+    // column-major B: 256x256x256 3.04 / 3.57, 3.18 / 3.78; 200x300x256
+    // 3.19 / 3.60; 128x256x512 3.26 / 3.76, 3.93 / 4.41; 128x128x1536 5.45 /
+    // 6.15; 256x256x1024 4.38 / 4.52; 256x256x2048 6.49 / 6.77, 9.05 / 9.14;
+    // 256x256x64 3.23 / 3.19.)
     if (2 * t16 <= cus) {
-        *split = k < 2048 ? 1 : fill(t16);
+        if (k < 2048) {
+            *split = 1;
+            return V_SKINNY16_W4_D4;
+        }
+        *split = fill(t16);
         return V_SKINNY16_W16_D4;
     }
     if (t16 <= cus && k <= 3072) {
         *split = 1;
-        return V_SKINNY16_W16_D4;
+        return V_SKINNY16_W4_D4;
     }
     if (t16 <= cus) {
         *split = fill(t64);

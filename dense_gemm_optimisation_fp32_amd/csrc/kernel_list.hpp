@@ -57,6 +57,7 @@ using SkinnyW4D4 = SkinnyTile<4, 4, 64>;
 using SkinnyW8D4 = SkinnyTile<8, 4, 64>;
 using SkinnyW16D4 = SkinnyTile<16, 4, 64>;
 using Skinny16W16D4 = SkinnyTile<16, 4, 16>;
+using Skinny16W4D4 = SkinnyTile<4, 4, 16>;       // 16x16 tiles, 4 wavefronts
 using Skinny32W8D4 = SkinnyTile<8, 4, 64, 2>;     // 32-row tiles
 using Skinny16x32W16D4 = SkinnyTile<16, 4, 32>;   // 32-column tiles
 
@@ -141,6 +142,8 @@ using Skinny16x32W16D4 = SkinnyTile<16, 4, 32>;   // 32-column tiles
     X2(gemm_skinny_acol_kernel, SkinnyW16D4, false) X2(gemm_skinny_acol_kernel, SkinnyW16D4, true) X2(gemm_skinny_acol_epi_kernel, SkinnyW16D4, false) X2(gemm_skinny_acol_epi_kernel, SkinnyW16D4, true)     \
     X2(gemm_skinny_kernel, Skinny16W16D4, false) X2(gemm_skinny_kernel, Skinny16W16D4, true) X2(gemm_skinny_epi_kernel, Skinny16W16D4, false) X2(gemm_skinny_epi_kernel, Skinny16W16D4, true) \
     X2(gemm_skinny_acol_kernel, Skinny16W16D4, false) X2(gemm_skinny_acol_kernel, Skinny16W16D4, true) X2(gemm_skinny_acol_epi_kernel, Skinny16W16D4, false) X2(gemm_skinny_acol_epi_kernel, Skinny16W16D4, true)     \
+    X2(gemm_skinny_kernel, Skinny16W4D4, false) X2(gemm_skinny_kernel, Skinny16W4D4, true) X2(gemm_skinny_epi_kernel, Skinny16W4D4, false) X2(gemm_skinny_epi_kernel, Skinny16W4D4, true) \
+    X2(gemm_skinny_acol_kernel, Skinny16W4D4, false) X2(gemm_skinny_acol_kernel, Skinny16W4D4, true) X2(gemm_skinny_acol_epi_kernel, Skinny16W4D4, false) X2(gemm_skinny_acol_epi_kernel, Skinny16W4D4, true)     \
     X2(gemm_skinny_kernel, Skinny32W8D4, false) X2(gemm_skinny_kernel, Skinny32W8D4, true) X2(gemm_skinny_epi_kernel, Skinny32W8D4, false) X2(gemm_skinny_epi_kernel, Skinny32W8D4, true) \
     X2(gemm_skinny_acol_kernel, Skinny32W8D4, false) X2(gemm_skinny_acol_kernel, Skinny32W8D4, true) X2(gemm_skinny_acol_epi_kernel, Skinny32W8D4, false) X2(gemm_skinny_acol_epi_kernel, Skinny32W8D4, true)       \
     X2(gemm_skinny_kernel, Skinny16x32W16D4, false) X2(gemm_skinny_kernel, Skinny16x32W16D4, true) X2(gemm_skinny_epi_kernel, Skinny16x32W16D4, false) X2(gemm_skinny_epi_kernel, Skinny16x32W16D4, true) \

@@ -293,7 +293,7 @@ COL_A_FEW = [((16, 4096, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
              ((24, 2048, 3000), COL_MAJOR, "skinny_32x64_w8_d4", 8),
              ((16, 1000, 700), ROW_MAJOR, "skinny_16x64_w16_d4", None),
              ((5, 2050, 777), COL_MAJOR, "skinny_16x32_w16_d4", 3),
-             ((200, 190, 70), ROW_MAJOR, "skinny_16x16_w16_d4", 1)]
+             ((200, 190, 70), ROW_MAJOR, "skinny_16x16_w4_d4", 1)]
 
 
 @pytest.mark.parametrize("shape,layout_b,name,split", COL_A_FEW)

@@ -338,10 +338,11 @@ def test_one_wave_of_64x128_tiles(shape, layout_b, name, stream_k):
 # column-major B), a plan being (variant, k-split count), or None for a tiled
 # plan.  Measured on one MI355X, 256 CUs.
 FEW_TILE_CASES = [
-    ((256, 256, 256), ("skinny_16x16_w16_d4", 1), ("skinny_16x16_w16_d4", 1)),
+    ((256, 256, 256), ("skinny_16x16_w4_d4", 1), ("skinny_16x16_w4_d4", 1)),
     ((64, 256, 4096), ("skinny_16x16_w16_d4", 4), ("skinny_16x16_w16_d4", 4)),
     ((64, 128, 8192), ("skinny_16x16_w16_d4", 8), ("skinny_16x16_w16_d4", 8)),
-    ((200, 200, 3000), ("skinny_16x16_w16_d4", 1), ("skinny_16x16_w16_d4", 1)),
+    ((200, 200, 3000), ("skinny_16x16_w4_d4", 1), ("skinny_16x16_w4_d4", 1)),
+    ((100, 100, 800), ("skinny_16x16_w4_d4", 1), ("skinny_16x16_w4_d4", 1)),
     ((128, 512, 4096), ("skinny_16x64_w16_d4", 4), ("skinny_16x64_w16_d4", 4)),
     ((40, 1000, 5000), ("skinny_16x64_w16_d4", 5), ("skinny_16x64_w16_d4", 5)),
     ((300, 700, 1500), ("skinny_16x64_w8_d4", 1), ("skinny_16x64_w8_d4", 1)),
