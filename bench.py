@@ -223,10 +223,12 @@ def time_workload(name, steps, warmup, variant=None, rotate=1, layout_a=0, epilo
     # Average launch duration: one pair of HIP events on the launch stream
     # around `steps` back-to-back launches (an event pair per launch would
     # add its own overhead to microsecond kernels).  The engine clock is
-    # sampled meanwhile only for launches of 50 us or more: the sampler's
-    # thread slows the launch loop of microsecond kernels, whose events would
-    # then time the gaps between launches (256^3: 4.25 us against 3.2 us per
-    # step by the wall clock and 3.21 us in a kernel trace).
+    # sampled meanwhile only for launches of 50 us or more (the clock-adjusted
+    # fraction is reported for the compute-bound workloads; the sampler's
+    # thread competes with the launch loop).  For microsecond kernels the
+    # pair still times the gaps between launches as well: 256^3 reads about
+    # 4.0 us here against 3.2 us per step by the wall clock and 3.21 us in a
+    # kernel trace.
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     clock = ClockSampler() if wall / steps >= 50e-6 else None
