@@ -83,7 +83,14 @@ __device__ __forceinline__ float wave_sum(float v)
 // not fit the registers beside A's chunk (it spilled).  The two 4-column
 // tiles split the shapes by k: the 1024-k staged tile took 4096x4x4096 from
 // 18.0 to 14.6 us and 16384x3x4096 from 56.1 to 50.9, but 8192x4x8192 from
-// 56.4 to 62.3 (twice the chunks, each a round trip of A's loads).
+// 56.4 to 62.3 (twice the chunks, each a round trip of A's loads).  The
+// staged 4-column tile runs eight wavefronts of one row each (the same 8 rows
+// per workgroup, twice the wavefronts to cover the loads' latency):
+// 4096x4x4096 13.61 against 14.57 us with four wavefronts of two rows,
+// 16384x3x4096 49.63 / 50.86, the transposed 4x6144x4096 21.10 / 21.57
+// (4x14336x4096 level).  The same change lost on the 8-column tile at
+// 8192x8x8192 (70.95 / 67.77) and on the one-column tile at 8192x1x8192
+// (51.50 / 49.70).
 template <class T, bool B_COL>
 __device__ __forceinline__ void fewcol_copy_b(const GemmArgs &g, __amdgpu_buffer_rsrc_t rb, f32x4 *bs, float *bsf,
                                               int kc, int klen, int j0, int tid)

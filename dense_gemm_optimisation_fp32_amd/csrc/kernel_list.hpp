@@ -49,7 +49,7 @@ __global__ void zero_words_kernel(unsigned *p, int n);
 // Few-column tiles (columns per workgroup).
 using FewColR1 = FewColTile<1>;
 using FewColR4 = FewColTile<4>;
-using FewColR4K1024 = FewColTile<4, 4, 2, 1024>;
+using FewColR4K1024 = FewColTile<4, 8, 1, 1024>;   // eight wavefronts of one row
 using FewColR8 = FewColTile<8>;
 
 // Few-row tiles (wavefronts, k groups in flight, columns).
