@@ -220,6 +220,7 @@ enum VariantId {
     V_SKINNY_16x32_W16_D4,
     V_FEWCOL_R4_K1024,
     V_SKINNY16_W4_D4,
+    V_FEWCOL_R1_W8,
     V_COUNT
 };
 
@@ -263,6 +264,7 @@ const VariantDesc &variant(int v)
         skinny_variant<SkinnyTile<16, 4, 32>>("skinny_16x32_w16_d4"),
         fewcol_variant<gemmf32::FewColR4K1024>("fewcol_8x4_k1024"),
         skinny_variant<SkinnyTile<4, 4, 16>>("skinny_16x16_w4_d4"),
+        fewcol_variant<gemmf32::FewColR1W8>("fewcol_8x1_k2048_w8"),
     };
     return table[v];
 }
@@ -588,7 +590,10 @@ int few_tile_rows(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFac
 // split k either, so the plan needs enough rows of B^T (8 per workgroup) to
 // fill the CUs when k is long.  Measured on one MI355X (us, transposed /
 // few-row plan, rotating B sets, best of two):
-//   one row (one-column kernel): 1x2048x2048 5.07 / 6.91, 1x4096x4096 14.42
+//   one row (one-column kernel, four wavefronts of two rows; the plan now
+//   runs eight wavefronts of one row, 0.89-0.97 of these times: 1x2048x2048
+//   4.71, 1x4096x4096 13.77, 1x14336x4096 40.14, 1x4096x8192 25.57,
+//   1x2048x8192 14.76 against 16.62): 1x2048x2048 5.07 / 6.91, 1x4096x4096 14.42
 //   / 16.43, 1x11008x4096 32.87 / 46.15, 1x14336x4096 41.50 / 51.08,
 //   1x4096x14336 40.90 / 47.40, 1x1024x1024 3.53 / 8.29, 1x256x4096 4.50 /
 //   15.78, 1x512x8192 7.36 / 13.66; long k with few columns of B lost:
@@ -608,7 +613,7 @@ int transposed_few_column(int64_t m, int64_t n, int64_t k, int layout_b)
 {
     const int mode = env_int("GEMM_F32_TRANSPOSE", 1);
     if (mode == 0 || layout_b != GEMM_F32_COL_MAJOR || m > 4) return -1;
-    const int v = m == 1 ? V_FEWCOL_R1 : V_FEWCOL_R4_K1024;
+    const int v = m == 1 ? V_FEWCOL_R1_W8 : V_FEWCOL_R4_K1024;
     if (mode == 2) return v;
     if (m == 1) return k <= 16384 && (n >= 1024 || n * k <= (int64_t(1) << 22)) ? v : -1;
     return n >= 6144 && k >= 2048 && k <= 5120 ? v : -1;

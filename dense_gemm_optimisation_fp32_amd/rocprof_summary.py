@@ -59,13 +59,14 @@ def short_name(kernel: str) -> str:
     m = re.search(r"MfmaTile<(\d+), (\d+), (\d+), \d+, \d+>", k) or re.search(r"MfmaTileILi(\d+)ELi(\d+)ELi(\d+)", k)
     if m and "gemm_mfma_kernel" in k:
         return f"mfma_{m.group(1)}x{m.group(2)}x{m.group(3)}"
-    m = (re.search(r"FewColTile<(\d+)(?:, \d+, \d+(?:, (\d+))?)?>, (true|false)", k)
-         or re.search(r"FewColTileILi(\d+)E(?:Li\d+ELi\d+E(?:Li(\d+)E)?)?EELb([01])", k))
+    m = (re.search(r"FewColTile<(\d+)(?:, (\d+), \d+(?:, (\d+))?)?>, (true|false)", k)
+         or re.search(r"FewColTileILi(\d+)E(?:Li(\d+)ELi\d+E(?:Li(\d+)E)?)?EELb([01])", k))
     if m:
-        r, kc = int(m.group(1)), m.group(2)
+        r, waves, kc = int(m.group(1)), m.group(2), m.group(3)
         default_kc = 1024 if r == 8 else 2048
         return (f"fewcol_r{r}" + (f"_k{kc}" if kc and int(kc) != default_kc else "")
-                + ("_t" if "fewcol_t_kernel" in k else "") + ("_bcol" if m.group(3) in ("true", "1") else ""))
+                + (f"_w{waves}" if waves and int(waves) != 4 else "")
+                + ("_t" if "fewcol_t_" in k else "") + ("_bcol" if m.group(4) in ("true", "1") else ""))
     if "gemm_valu_kernel" in k:
         return "valu_128x128x8"
     if "zero_words_kernel" in k:

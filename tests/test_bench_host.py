@@ -126,11 +126,15 @@ def test_profile_kernel_short_names():
                       "(gemmf32::GemmArgs)") == "fewcol_r1_bcol"
     assert short_name("void gemmf32::gemm_fewcol_kernel<gemmf32::FewColTile<4, 4, 2, 1024>, false>"
                       "(gemmf32::GemmArgs)") == "fewcol_r4_k1024"
+    assert short_name("void gemmf32::gemm_fewcol_t_kernel<gemmf32::FewColTile<1, 8, 1, 2048>, true>"
+                      "(gemmf32::GemmArgs)") == "fewcol_r1_w8_t_bcol"
+    assert short_name("_ZN7gemmf3220gemm_fewcol_t_kernelINS_10FewColTileILi4ELi8ELi1ELi1024EEELb1EEEvNS_8GemmArgsE"
+                      ) == "fewcol_r4_k1024_w8_t_bcol"
     assert short_name("void gemmf32::gemm_fewcol_kernel<gemmf32::FewColTile<8, 4, 2, 1024>, false>"
                       "(gemmf32::GemmArgs)") == "fewcol_r8"
     assert short_name("void gemmf32::gemm_fewcol_t_kernel<gemmf32::FewColTile<1, 4, 2, 2048>, true>"
                       "(gemmf32::GemmArgs)") == "fewcol_r1_t_bcol"
-    assert short_name("_ZN7gemmf3220gemm_fewcol_t_kernelINS_10FewColTileILi4ELi4ELi2ELi1024EEELb1EEEvNS_8GemmArgsE"
+    assert short_name("_ZN7gemmf3220gemm_fewcol_t_epi_kernelINS_10FewColTileILi4ELi4ELi2ELi1024EEELb1EEEvNS_8GemmArgsE"
                       ) == "fewcol_r4_k1024_t_bcol"
     assert short_name("_ZN7gemmf3218gemm_fewcol_kernelINS_10FewColTileILi1ELi4ELi2ELi2048EEELb0EEEvNS_8GemmArgsE"
                       ) == "fewcol_r1"

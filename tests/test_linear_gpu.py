@@ -240,8 +240,8 @@ FEW_ROW_EX = [((16, 4096, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
               ((24, 2048, 3000), COL_MAJOR, "skinny_32x64_w8_d4", 8),
               ((5, 2050, 777), ROW_MAJOR, "skinny_16x32_w16_d4", 3),
               ((1, 300, 17), ROW_MAJOR, "skinny_16x64_w16_d4", 1),
-              ((1, 4096, 4096), COL_MAJOR, "fewcol_8x1_k2048", 1),
-              ((1, 3001, 2049), COL_MAJOR, "fewcol_8x1_k2048", 1),
+              ((1, 4096, 4096), COL_MAJOR, "fewcol_8x1_k2048_w8", 1),
+              ((1, 3001, 2049), COL_MAJOR, "fewcol_8x1_k2048_w8", 1),
               ((3, 8192, 3000), COL_MAJOR, "fewcol_8x4_k1024", 1),
               ((256, 256, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
               ((300, 700, 1500), COL_MAJOR, "skinny_16x64_w8_d4", 1),

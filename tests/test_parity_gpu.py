@@ -842,11 +842,11 @@ def test_few_rows_32_column_tiles(shape, layout_b, name, split):
 # N * K <= 2^22; 2 to 4 rows: N >= 6144 and 2048 <= K <= 5120); every other
 # case keeps the few-row plan.  Padded leading dimensions (lda, ldb, ldc past
 # the matrix), ragged N and K, and 3 rows on the four-column kernel included.
-TRANSPOSED_CASES = [((1, 4096, 4096), COL_MAJOR, 0, "fewcol_8x1_k2048"),
-                    ((1, 2050, 2049), COL_MAJOR, 0, "fewcol_8x1_k2048"),
-                    ((1, 3001, 5003), COL_MAJOR, 7, "fewcol_8x1_k2048"),
-                    ((1, 14336, 4096), COL_MAJOR, 0, "fewcol_8x1_k2048"),
-                    ((1, 300, 1000), COL_MAJOR, 3, "fewcol_8x1_k2048"),
+TRANSPOSED_CASES = [((1, 4096, 4096), COL_MAJOR, 0, "fewcol_8x1_k2048_w8"),
+                    ((1, 2050, 2049), COL_MAJOR, 0, "fewcol_8x1_k2048_w8"),
+                    ((1, 3001, 5003), COL_MAJOR, 7, "fewcol_8x1_k2048_w8"),
+                    ((1, 14336, 4096), COL_MAJOR, 0, "fewcol_8x1_k2048_w8"),
+                    ((1, 300, 1000), COL_MAJOR, 3, "fewcol_8x1_k2048_w8"),
                     ((3, 8192, 3000), COL_MAJOR, 0, "fewcol_8x4_k1024"),
                     ((4, 6144, 4096), COL_MAJOR, 5, "fewcol_8x4_k1024"),
                     ((2, 11009, 2049), COL_MAJOR, 0, "fewcol_8x4_k1024"),
