@@ -152,7 +152,7 @@ VariantDesc fewcol_variant(const char *name)
     // The linear-layer epilogue with row-major A.
     d.fn_ex[0][0][1] = reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_epi_kernel<T, false>);
     d.fn_ex[0][1][1] = reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_epi_kernel<T, true>);
-    if constexpr (T::R == 1 || (T::R == 4 && T::KC == 1024)) {
+    if constexpr (T::R == 1 || (T::R == 4 && T::KC == 1024) || T::ROWS_PER_WAVE == 1) {
         d.fn_t = reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_t_kernel<T, true>);
         d.fn_t_epi = reinterpret_cast<const void *>(&gemmf32::gemm_fewcol_t_epi_kernel<T, true>);
     }
@@ -221,6 +221,7 @@ enum VariantId {
     V_FEWCOL_R4_K1024,
     V_SKINNY16_W4_D4,
     V_FEWCOL_R1_W8,
+    V_FEWCOL_R8_W8,
     V_COUNT
 };
 
@@ -265,6 +266,7 @@ const VariantDesc &variant(int v)
         fewcol_variant<gemmf32::FewColR4K1024>("fewcol_8x4_k1024"),
         skinny_variant<SkinnyTile<4, 4, 16>>("skinny_16x16_w4_d4"),
         fewcol_variant<gemmf32::FewColR1W8>("fewcol_8x1_k2048_w8"),
+        fewcol_variant<gemmf32::FewColR8W8>("fewcol_8x8_k1024_w8"),
     };
     return table[v];
 }
@@ -606,17 +608,25 @@ int few_tile_rows(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFac
 //   4096 or k = 8192 it lost or tied: 4x4096x4096 16.89 / 16.69,
 //   4x4096x2048 9.47 / 8.39, 4x4096x8192 36.34 / 31.34, 4x8192x8192 61.45
 //   / 58.33, 4x14336x8192 97.14 / 98.03.
+//   5 to 8 rows (an eight-column tile of eight wavefronts of one row): only
+//   where the few-row plan's one split of 64-column tiles leaves CUs idle
+//   (CUs / 2 < N / 64 < CUs): 5x11008x4096 39.79 / 48.13, 8x11008x4096
+//   41.18 / 49.92, 8x14336x4096 52.90 / 54.02; with the CUs filled it lost:
+//   8x4096x4096 18.53 / 17.63, 8x8192x4096 34.23 / 31.66, 5x4096x8192
+//   37.77 / 31.53.
 // Returns the few-column variant of the transposed plan, or -1.
 // GEMM_F32_TRANSPOSE=0 turns it off; =2 (measurement) takes it for every
-// shape it serves (up to four rows, column-major B).
-int transposed_few_column(int64_t m, int64_t n, int64_t k, int layout_b)
+// shape it serves (up to eight rows, column-major B).
+int transposed_few_column(int64_t m, int64_t n, int64_t k, int layout_b, int64_t cus)
 {
     const int mode = env_int("GEMM_F32_TRANSPOSE", 1);
-    if (mode == 0 || layout_b != GEMM_F32_COL_MAJOR || m > 4) return -1;
-    const int v = m == 1 ? V_FEWCOL_R1_W8 : V_FEWCOL_R4_K1024;
+    if (mode == 0 || layout_b != GEMM_F32_COL_MAJOR || m > 8) return -1;
+    const int v = m == 1 ? V_FEWCOL_R1_W8 : m <= 4 ? V_FEWCOL_R4_K1024 : V_FEWCOL_R8_W8;
     if (mode == 2) return v;
     if (m == 1) return k <= 16384 && (n >= 1024 || n * k <= (int64_t(1) << 22)) ? v : -1;
-    return n >= 6144 && k >= 2048 && k <= 5120 ? v : -1;
+    if (m <= 4) return n >= 6144 && k >= 2048 && k <= 5120 ? v : -1;
+    const int64_t t64 = ceil_div(n, 64);
+    return 2 * t64 > cus && t64 < cus && k >= 2048 && k <= 4096 ? v : -1;
 }
 
 // Shape dispatch.  Few rows: the bandwidth-bound split-k path.  Few tiles:
@@ -831,7 +841,8 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
         if (v < 0 || v >= V_COUNT) {
             // (The transposed plan serves row-major A, with or without the
             // epilogue.)
-            const int tv = layout_a == GEMM_F32_COL_MAJOR ? -1 : transposed_few_column(m, n, k, layout_b);
+            const int tv =
+                layout_a == GEMM_F32_COL_MAJOR ? -1 : transposed_few_column(m, n, k, layout_b, facts.cu_count);
             swap_ab = tv >= 0;
             v = swap_ab ? tv
                         : choose_variant(m, n, k, layout_b, facts, !ex, epilogue != 0, &auto_stream_k, &auto_tail,

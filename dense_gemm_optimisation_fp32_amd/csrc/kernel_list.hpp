@@ -51,6 +51,7 @@ using FewColR1 = FewColTile<1>;
 using FewColR4 = FewColTile<4>;
 using FewColR4K1024 = FewColTile<4, 8, 1, 1024>;   // eight wavefronts of one row
 using FewColR1W8 = FewColTile<1, 8, 1, 2048>;      // the transposed one-row product's tile
+using FewColR8W8 = FewColTile<8, 8, 1, 1024>;      // the transposed 5- to 8-row product's tile
 using FewColR8 = FewColTile<8>;
 
 // Few-row tiles (wavefronts, k groups in flight, columns).
@@ -154,6 +155,8 @@ using Skinny16x32W16D4 = SkinnyTile<16, 4, 32>;   // 32-column tiles
     X2(gemm_fewcol_kernel, FewColR4, false) X2(gemm_fewcol_kernel, FewColR4, true) X2(gemm_fewcol_epi_kernel, FewColR4, false) X2(gemm_fewcol_epi_kernel, FewColR4, true)             \
     X2(gemm_fewcol_kernel, FewColR1W8, false) X2(gemm_fewcol_kernel, FewColR1W8, true) X2(gemm_fewcol_epi_kernel, FewColR1W8, false) X2(gemm_fewcol_epi_kernel, FewColR1W8, true) \
     X2(gemm_fewcol_t_kernel, FewColR1W8, true) X2(gemm_fewcol_t_epi_kernel, FewColR1W8, true) \
+    X2(gemm_fewcol_kernel, FewColR8W8, false) X2(gemm_fewcol_kernel, FewColR8W8, true) X2(gemm_fewcol_epi_kernel, FewColR8W8, false) X2(gemm_fewcol_epi_kernel, FewColR8W8, true) \
+    X2(gemm_fewcol_t_kernel, FewColR8W8, true) X2(gemm_fewcol_t_epi_kernel, FewColR8W8, true) \
     X2(gemm_fewcol_kernel, FewColR8, false) X2(gemm_fewcol_kernel, FewColR8, true) X2(gemm_fewcol_epi_kernel, FewColR8, false) X2(gemm_fewcol_epi_kernel, FewColR8, true)             \
     X2(gemm_fewcol_kernel, FewColR4K1024, false) X2(gemm_fewcol_kernel, FewColR4K1024, true) X2(gemm_fewcol_epi_kernel, FewColR4K1024, false) X2(gemm_fewcol_epi_kernel, FewColR4K1024, true)   \
     X2(gemm_fewcol_t_kernel, FewColR4K1024, true) X2(gemm_fewcol_t_epi_kernel, FewColR4K1024, true)

@@ -138,7 +138,7 @@ struct gemm_f32_info {
     int sliver_stream_k;
     int sliver_fused;
     /* Plan only: 1 when the plan computes the transposed product
-     * C^T = B^T . A^T (up to four rows of C, column-major B: the caller's B
+     * C^T = B^T . A^T (up to eight rows of C, column-major B: the caller's B
      * read as a row-major N x K matrix on a few-column kernel, whose loads
      * run along each column of B; "PMPP Chapter 06", section 1: the
      * corner-turning layout read along its contiguous direction), with or
@@ -182,7 +182,7 @@ int gemm_f32_validate(int64_t m, int64_t n, int64_t k, int layout_b,
  *                             the tiles' launch (gemm_f32_info.sliver_fused);
  *   GEMM_F32_TRANSPOSE=0      never compute a few rows of C with column-major
  *                             B as the transposed product (gemm_f32_info.transposed);
- *                             =2 (measurement) always, for up to four rows;
+ *                             =2 (measurement) always, for up to eight rows;
  *   GEMM_F32_WIDE_C=0         store C one element at a time even where the
  *                             whole-tile kernel could store 2 or 4 (for measuring
  *                             gemm_f32_info.c_store_width);

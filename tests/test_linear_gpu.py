@@ -243,6 +243,7 @@ FEW_ROW_EX = [((16, 4096, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
               ((1, 4096, 4096), COL_MAJOR, "fewcol_8x1_k2048_w8", 1),
               ((1, 3001, 2049), COL_MAJOR, "fewcol_8x1_k2048_w8", 1),
               ((3, 8192, 3000), COL_MAJOR, "fewcol_8x4_k1024", 1),
+              ((6, 11008, 3000), COL_MAJOR, "fewcol_8x8_k1024_w8", 1),
               ((256, 256, 4096), ROW_MAJOR, "skinny_16x64_w16_d4", 4),
               ((300, 700, 1500), COL_MAJOR, "skinny_16x64_w8_d4", 1),
               ((1000, 1, 4096), ROW_MAJOR, "fewcol_8x1_k2048", 1),
