@@ -269,8 +269,11 @@ int gemm_f32_run_noalloc(int64_t m, int64_t n, int64_t k, int layout_b, int64_t 
  * epilogue is evaluated in float32 (alpha*acc + beta*C + bias, multiply-adds
  * may be fused), then act; GELU's erf is the Abramowitz-Stegun 7.1.26
  * approximation (|error| <= 1.5e-7).  These plans run on the direct-to-LDS tiled kernels
- * (256x256 for column-major A without the epilogue, else 256x128, 128x128, 64x128 or 64x64);
- * the few-row path and stream-K are not used.
+ * (256x256, 256x128, 128x128, 64x128 or 64x64 tiles), on the few-row kernel (up to 32 rows,
+ * and shapes with few tiles; either A layout), on the few-column kernels (N <= 8, row-major
+ * A), as the transposed product C^T = B^T . A^T for up to eight rows with column-major B
+ * (row-major A), and, for few tiles with a long k and row-major A, on stream-K over 64x64
+ * tiles; the epilogue is applied where each kernel writes C.
  */
 
 /* gemm_f32_validate_ex: gemm_f32_validate with A's layout: lda >= k (row-major
