@@ -607,7 +607,10 @@ int few_tile_rows(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFac
 //   4x13824x5120 52.45 / 66.34, 4x28672x4096 80.97 / 99.97; with N up to
 //   4096 or k = 8192 it lost or tied: 4x4096x4096 16.89 / 16.69,
 //   4x4096x2048 9.47 / 8.39, 4x4096x8192 36.34 / 31.34, 4x8192x8192 61.45
-//   / 58.33, 4x14336x8192 97.14 / 98.03.
+//   / 58.33, 4x14336x8192 97.14 / 98.03; ahead again at k from 10240 (the
+//   eight-wavefront four-column tile): 2x4096x11008 37.79 / 41.17,
+//   4x4096x11008 38.11 / 42.42, 4x4096x14336 46.08 / 49.81 (four-wavefront
+//   tile).
 //   5 to 8 rows (an eight-column tile of eight wavefronts of one row): only
 //   where the few-row plan's one split of 64-column tiles leaves CUs idle
 //   (CUs / 2 < N / 64 < CUs): 5x11008x4096 39.79 / 48.13, 8x11008x4096
@@ -624,7 +627,7 @@ int transposed_few_column(int64_t m, int64_t n, int64_t k, int layout_b, int64_t
     const int v = m == 1 ? V_FEWCOL_R1_W8 : m <= 4 ? V_FEWCOL_R4_K1024 : V_FEWCOL_R8_W8;
     if (mode == 2) return v;
     if (m == 1) return k <= 16384 && (n >= 1024 || n * k <= (int64_t(1) << 22)) ? v : -1;
-    if (m <= 4) return n >= 6144 && k >= 2048 && k <= 5120 ? v : -1;
+    if (m <= 4) return (n >= 6144 && k >= 2048 && k <= 5120) || (n >= 4096 && k >= 10240 && k <= 16384) ? v : -1;
     const int64_t t64 = ceil_div(n, 64);
     return 2 * t64 > cus && t64 < cus && k >= 2048 && k <= 4096 ? v : -1;
 }

@@ -839,7 +839,8 @@ def test_few_rows_32_column_tiles(shape, layout_b, name, split):
 
 # Up to eight rows of C with column-major B: the transposed product
 # C^T = B^T A^T on a few-column kernel (one row: k <= 16384 and N >= 1024 or
-# N * K <= 2^22; 2 to 4 rows: N >= 6144 and 2048 <= K <= 5120; 5 to 8 rows:
+# N * K <= 2^22; 2 to 4 rows: N >= 6144 and 2048 <= K <= 5120, or N >= 4096
+# and 10240 <= K <= 16384; 5 to 8 rows:
 # 128 < N / 64 < 256 and 2048 <= K <= 4096); every other
 # case keeps the few-row plan.  Padded leading dimensions (lda, ldb, ldc past
 # the matrix), ragged N and K, and 3 rows on the four-column kernel included.
@@ -856,6 +857,7 @@ TRANSPOSED_CASES = [((1, 4096, 4096), COL_MAJOR, 0, "fewcol_8x1_k2048_w8"),
                     ((2, 4096, 4096), COL_MAJOR, 0, None),
                     ((4, 6144, 8192), COL_MAJOR, 0, None),
                     ((5, 8192, 4096), COL_MAJOR, 0, None),
+                    ((3, 4096, 11008), COL_MAJOR, 0, "fewcol_8x4_k1024"),
                     ((5, 11008, 4096), COL_MAJOR, 0, "fewcol_8x8_k1024_w8"),
                     ((8, 14336, 2049), COL_MAJOR, 5, "fewcol_8x8_k1024_w8"),
                     ((8, 11008, 8192), COL_MAJOR, 0, None),
