@@ -526,7 +526,7 @@ double estimate_seconds(const Candidate &cand, int per_cu, int per_cu_sk, int64_
 // split; then 16 x 64 tiles with 8 wavefronts while T64 is within one
 // workgroup per CU, or three for k in [512, 4096] (row-major B; column-major
 // B, whose columns the few-row kernel reads less evenly, up to one, and only
-// to k = 2048 unless T64 <= CUs / 2).  The row tiles of a column of tiles
+// to k = 3584 unless T64 <= CUs / 2).  The row tiles of a column of tiles
 // run side by side on one XCD (gemm_skinny_kernel), so B, read once per 16
 // rows, comes from that XCD's L2 after the first.  Measured on one MI355X
 // (us, this rule's plan / the tiled or stream-K plan it replaces):
@@ -574,8 +574,14 @@ int few_tile_rows(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFac
         *split = fill(t64);
         return V_SKINNY_W16_D4;
     }
+    // (Column-major B with CUs / 2 < T64 <= CUs: up to k = 3584, where the
+    // few-row plan with one split was measured ahead of stream-K over 64 x 64
+    // tiles, us: 250x600x2500 18.9 / 28.6, 240x1000x2200 19.9 / 29.2,
+    // 160x1536x3000 26.3 / 36.5, 128x2048x3000 26.6 / 32.5, 200x700x3000
+    // 26.9 / 30.9, 180x900x3500 31.2 / 33.6; at k = 4096 stream-K kept its
+    // lead or tied: 256x1024x4096 37.1 / 35.3, 300x500x4096 37.2 / 34.8.)
     const bool w8 = layout_b == GEMM_F32_ROW_MAJOR ? t64 <= cus || (t64 <= 3 * cus && k >= 512 && k <= 4096)
-                                                   : 2 * t64 <= cus || (t64 <= cus && k <= 2048);
+                                                   : 2 * t64 <= cus || (t64 <= cus && k <= 3584);
     if (w8) {
         *split = k < 2048 ? 1 : fill(t64);
         return V_SKINNY_W8_D4;

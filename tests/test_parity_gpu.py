@@ -348,6 +348,8 @@ FEW_TILE_CASES = [
     ((300, 700, 1500), ("skinny_16x64_w8_d4", 1), ("skinny_16x64_w8_d4", 1)),
     ((300, 300, 3000), ("skinny_16x64_w8_d4", 2), ("skinny_16x64_w8_d4", 2)),
     ((800, 600, 3000), ("skinny_16x64_w8_d4", 1), None),
+    ((250, 600, 2500), ("skinny_16x64_w8_d4", 1), ("skinny_16x64_w8_d4", 1)),
+    ((256, 1024, 4096), ("skinny_16x64_w8_d4", 1), None),
     ((768, 768, 1024), ("skinny_16x64_w8_d4", 1), None),
     ((512, 512, 8192), ("skinny_16x64_w8_d4", 1), None),
     ((1024, 1024, 1024), None, None),
