@@ -743,6 +743,27 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
         *stream_k = true;
         return V_DMA_64x64x16_S2;
     }
+    {
+        // Column-major B whose 128 x 128 tiles number more than two and at
+        // most two and a half per CU, with k from 2048: stream-K over those
+        // tiles with three workgroups per CU.  One data-parallel wave of
+        // three per CU would leave a sixth to a third of its slots idle, and
+        // the smaller tiles read B in shorter runs along its columns.
+        // Measured on one MI355X (us, stream-K over 128x128 / the
+        // data-parallel plan): 1536x5632x4096 545.0 / 593.7, 2048x4608x4096
+        // 572.9 / 649.1, 2432x4096x4096 630.3 / 693.8, 2048x5120x5120 780.4 /
+        // 867.2, 2000x5000x4000 622.1 / 678.0, 2048x5120x16384 2582.9 /
+        // 2976.2, 2048x4608x2048 305.9 / 318.3; it lost at 512 tiles
+        // (2048x4096x4096 498.9 / 484.3), 672 tiles (1792x6144x4096 682.0 /
+        // 641.3) and k = 1024 (2048x4608x1024 171.4 / 156.8).  Row-major B
+        // was level (2048x4608x4096 570.0 / 569.0).
+        const int64_t t128 = ceil_div(m, 128) * ceil_div(n, 128), cus = f.cu_count;
+        if (layout_b == GEMM_F32_COL_MAJOR && tail_ok && !epilogue && row_a && t128 > 2 * cus &&
+            2 * t128 <= 5 * cus && k >= 2048) {
+            *stream_k = true;
+            return V_DMA_128x128x16_S3;
+        }
+    }
     int best = -1;
     double best_t = 0.0;
     const bool log = env_int("GEMM_F32_LOG", 0) >= 2;

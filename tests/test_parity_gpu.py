@@ -334,6 +334,36 @@ def test_one_wave_of_64x128_tiles(shape, layout_b, name, stream_k):
     assert np.array_equal(C.astype(np.float64), Cref)
 
 
+# Column-major B with more than two and at most two and a half 128x128 tiles
+# per CU and k from 2048: stream-K over 128x128 tiles; (shape, layout of B,
+# whether the plan is that one).
+SUB_WAVE_128_CASES = [((1536, 5632, 2100), COL_MAJOR, True),
+                      ((2000, 5000, 2049), COL_MAJOR, True),
+                      ((2048, 4608, 1024), COL_MAJOR, False),
+                      ((2048, 4096, 2048), COL_MAJOR, False),
+                      ((1536, 5632, 2100), ROW_MAJOR, False)]
+
+
+@pytest.mark.parametrize("shape,layout_b,taken", SUB_WAVE_128_CASES)
+def test_stream_k_over_128x128_tiles(shape, layout_b, taken):
+    """The dispatch's stream-K plan over 128x128 tiles short of three per CU;
+    every element against the oracle (integer inputs bit for bit)."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the choices were measured on a 256-CU MI355X")
+    m, n, k = shape
+    print(f"\n[case] stream-K over 128x128 tiles {shape} layout_b={layout_b}", flush=True)
+    A, B = random_operands(m, n, k, layout_b, "normal1", seed=3300 + m)
+    C, info, outs = run_gemm(A, B, m, n, k, layout_b, repeat=2)
+    assert (info["name"] == "dma_128x128x16_w2x2_s3" and info["stream_k"] == 768) == taken, info
+    assert np.array_equal(outs[0], outs[1])
+    Cref, S = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    check_close(C, Cref, S, f"{info['name']} {shape}")
+    A, B = random_operands(m, n, k, layout_b, "int8range", seed=3400 + m)
+    C, _ = run_gemm(A, B, m, n, k, layout_b)
+    Cref, _ = oracle.gemm_f64(A, B, m, n, k, layout_b)
+    assert np.array_equal(C.astype(np.float64), Cref)
+
+
 # Few tiles on the few-row kernel: (shape, the plan with row-major B, with
 # column-major B), a plan being (variant, k-split count), or None for a tiled
 # plan.  Measured on one MI355X, 256 CUs.
