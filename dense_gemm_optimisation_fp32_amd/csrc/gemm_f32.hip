@@ -662,9 +662,12 @@ int transposed_few_column(int64_t m, int64_t n, int64_t k, int layout_b, int64_t
 // epilogue: the plan fuses the linear-layer epilogue.  row_a: A is
 // row-major, so the few-column kernels (which carry the epilogue) can run
 // the few-column shapes; the few-row kernel serves both A layouts.
+// small_scratch: the plan keeps its partial sums in the allocation-free
+// entry point's 64 MiB scratch area, too small for stream-K over 128 x 128
+// tiles (about 192 MiB at 768 workgroups), so that rule is skipped.
 int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFacts &f, bool tail_ok, bool epilogue,
                    bool *stream_k, int64_t *tail_tiles, double *estimate = nullptr, int *split = nullptr,
-                   bool row_a = true)
+                   bool row_a = true, bool small_scratch = false)
 {
     *stream_k = false;
     *tail_tiles = 0;
@@ -758,7 +761,7 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
         // 641.3) and k = 1024 (2048x4608x1024 171.4 / 156.8).  Row-major B
         // was level (2048x4608x4096 570.0 / 569.0).
         const int64_t t128 = ceil_div(m, 128) * ceil_div(n, 128), cus = f.cu_count;
-        if (layout_b == GEMM_F32_COL_MAJOR && tail_ok && !epilogue && row_a && t128 > 2 * cus &&
+        if (layout_b == GEMM_F32_COL_MAJOR && tail_ok && !epilogue && row_a && !small_scratch && t128 > 2 * cus &&
             2 * t128 <= 5 * cus && k >= 2048) {
             *stream_k = true;
             return V_DMA_128x128x16_S3;
@@ -804,19 +807,19 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
 // few-column kernel, which reads A once more: estimated at 4 m k bytes at
 // 5 TB/s plus 3 us of launch.  Returns r, or 0 when one launch is estimated
 // faster.  GEMM_F32_SLIVER=0 turns it off.
-int64_t choose_sliver(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFacts &f)
+int64_t choose_sliver(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFacts &f, bool small_scratch = false)
 {
     if (env_int("GEMM_F32_SLIVER", 1) == 0 || m <= 32 || n < 512) return 0;
     bool sk = false;
     int64_t tail = 0;
     double t_full = 0.0;
-    const int v = choose_variant(m, n, k, layout_b, f, true, false, &sk, &tail, &t_full);
+    const int v = choose_variant(m, n, k, layout_b, f, true, false, &sk, &tail, &t_full, nullptr, true, small_scratch);
     if (sk || t_full <= 0.0) return 0;
     const int bn = variant(v).bn;
     const int64_t r = n % bn;
     if (r == 0 || r * 8 > bn || r > 8) return 0;
     double t_main = 0.0;
-    choose_variant(m, n - r, k, layout_b, f, true, false, &sk, &tail, &t_main);
+    choose_variant(m, n - r, k, layout_b, f, true, false, &sk, &tail, &t_main, nullptr, true, small_scratch);
     if (sk || t_main <= 0.0) return 0;
     const double t_sliver = 4.0 * (double)m * (double)k / 5e12 + 3e-6;
     if (env_int("GEMM_F32_LOG", 0) >= 2)
@@ -845,7 +848,7 @@ int64_t stream_k_split_tiles(int64_t shared, int64_t k_tiles, int64_t wgs)
 // word; zero for plans that split no tile along k).  No allocation.
 int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, int64_t k, int layout_a,
               int layout_b, int64_t lda, int64_t ldb, int64_t ldc, int epilogue, size_t *ws_words,
-              size_t *ws_counters)
+              size_t *ws_counters, bool small_scratch = false)
 {
     *ws_words = 0;
     *ws_counters = 0;
@@ -876,7 +879,7 @@ int plan_fill(gemm_f32_plan_impl *p, int forced_variant, int64_t m, int64_t n, i
             swap_ab = tv >= 0;
             v = swap_ab ? tv
                         : choose_variant(m, n, k, layout_b, facts, !ex, epilogue != 0, &auto_stream_k, &auto_tail,
-                                         nullptr, &auto_split, layout_a == GEMM_F32_ROW_MAJOR);
+                                         nullptr, &auto_split, layout_a == GEMM_F32_ROW_MAJOR, small_scratch);
         }
         if (ex && !swap_ab && !variant(v).fn_ex[layout_a][layout_b][epilogue]) v = V_DMA_64x64x16_S2;
     }
@@ -1065,7 +1068,7 @@ void plan_attach(gemm_f32_plan_impl *p, void *words, unsigned *counters, size_t 
 // Columns of a column sliver for a plan (0: none): plain products with the
 // shape dispatch's own choices only (no forced variant, stream-K or split).
 int64_t plan_sliver(int forced_variant, int64_t m, int64_t n, int64_t k, int layout_a, int layout_b, int64_t lda,
-                    int64_t ldb, int64_t ldc, int epilogue)
+                    int64_t ldb, int64_t ldc, int epilogue, bool small_scratch = false)
 {
     if (forced_variant >= 0 || layout_a != GEMM_F32_ROW_MAJOR || epilogue) return 0;
     if (env_int("GEMM_F32_VARIANT", -1) >= 0 || env_int("GEMM_F32_SK_WGS", 0) > 0 ||
@@ -1075,7 +1078,7 @@ int64_t plan_sliver(int forced_variant, int64_t m, int64_t n, int64_t k, int lay
     int dev = 0;
     DeviceFacts facts;
     if (device_facts(&dev, &facts) != GEMM_F32_SUCCESS) return 0;
-    return choose_sliver(m, n, k, layout_b, facts);
+    return choose_sliver(m, n, k, layout_b, facts, small_scratch);
 }
 
 // B and C of a plan's sliver: column sliver_col0 of B (row-major: the next
@@ -1400,15 +1403,16 @@ int gemm_f32_run_noalloc(int64_t m, int64_t n, int64_t k, int layout_b, int64_t 
 {
     if (!pointers_ok(A, B, C)) return GEMM_F32_ERR_INVALID_VALUE;
     // Host state on the stack, nothing allocated: the plan and, when the
-    // dispatch splits off a column sliver, the sliver's plan.
-    const int64_t r = plan_sliver(-1, m, n, k, GEMM_F32_ROW_MAJOR, layout_b, lda, ldb, ldc, 0);
+    // dispatch splits off a column sliver, the sliver's plan; both without
+    // the stream-K plans whose partial sums outgrow the scratch area.
+    const int64_t r = plan_sliver(-1, m, n, k, GEMM_F32_ROW_MAJOR, layout_b, lda, ldb, ldc, 0, true);
     gemm_f32_plan_impl parts[2];
     size_t words[2] = {0, 0}, counters[2] = {0, 0};
     int st = plan_fill(&parts[0], -1, m, n - r, k, GEMM_F32_ROW_MAJOR, layout_b, lda, ldb, ldc, 0, &words[0],
-                       &counters[0]);
+                       &counters[0], true);
     if (st == GEMM_F32_SUCCESS && r)
         st = plan_fill(&parts[1], -1, m, r, k, GEMM_F32_ROW_MAJOR, layout_b, lda, ldb, ldc, 0, &words[1],
-                       &counters[1]);
+                       &counters[1], true);
     if (st != GEMM_F32_SUCCESS) return st;
     for (int i = 0; i < (r ? 2 : 1); ++i)
         if (words[i] > kScratchWordBytes || counters[i] + kExtraCounters > kScratchCounters)

@@ -228,7 +228,12 @@ int gemm_f32_run(gemm_f32_plan plan, const float *A, const float *B, float *C, v
  * gemm_f32_run_noalloc: C = A.B on `stream`, as gemm_f32_create, gemm_f32_run
  * and gemm_f32_destroy with the same arguments would compute it (the same
  * plan and kernels), for callers that cannot allocate: code under HIP graph
- * capture, tight serving loops, harnesses that forbid allocation.  It calls
+ * capture, tight serving loops, harnesses that forbid allocation.  One
+ * exception: column-major B with more than two and at most two and a half
+ * 128 x 128 tiles per CU and k >= 2048, where gemm_f32_create plans stream-K
+ * over 128 x 128 tiles (about 192 MiB of partial sums), runs the plan the
+ * dispatch takes without that rule (equal within the tolerance, not bit for
+ * bit).  It calls
  * no hipMalloc, hipFree or other allocating routine, host or device; the
  * plan lives on the call's stack.  Plans that split tiles along k (the
  * few-row path's split-k, stream-K) keep their partial sums in a scratch
