@@ -120,8 +120,9 @@ VariantDesc dma_ex_variant(const char *name)
     return d;
 }
 
-// The two-stage 64 x 64 tile: also stream-K with the linear-layer epilogue
-// (the few-tile long-k plans of epilogue plans with row-major A).
+// Stream-K with the linear-layer epilogue: the two-stage 64 x 64 tile (the
+// few-tile long-k plans of epilogue plans with row-major A) and the 128 x
+// 128 tile (column-major B short of three tiles per CU).
 template <class T>
 VariantDesc with_sk_epi(VariantDesc d)
 {
@@ -241,7 +242,8 @@ const VariantDesc &variant(int v)
         dma_variant<DmaTile<256, 256, 16, 2, 2, 3>>("dma_256x256x16_w2x2_s3"),
         dma_ex_variant<DmaTile<256, 256, 16, 2, 2, 4>>("dma_256x256x16_w2x2_s4"),
         dma_variant<DmaTile<256, 256, 32, 2, 2, 2>>("dma_256x256x32_w2x2_s2"),
-        with_sliver<DmaTile<128, 128, 16, 2, 2, 3, false>>(dma_ex_variant<DmaTile<128, 128, 16, 2, 2, 3, false>>("dma_128x128x16_w2x2_s3")),
+        with_sk_epi<DmaTile<128, 128, 16, 2, 2, 3, false>>(with_sliver<DmaTile<128, 128, 16, 2, 2, 3, false>>(
+            dma_ex_variant<DmaTile<128, 128, 16, 2, 2, 3, false>>("dma_128x128x16_w2x2_s3"))),
         dma_variant<DmaTile<128, 128, 32, 2, 2, 3, false>>("dma_128x128x32_w2x2_s3"),
         dma_ex_variant<DmaTile<256, 128, 16, 2, 2, 3>>("dma_256x128x16_w2x2_s3"),
         skinny_variant<SkinnyTile<4, 4, 64>>("skinny_16x64_w4_d4"),
@@ -759,10 +761,16 @@ int choose_variant(int64_t m, int64_t n, int64_t k, int layout_b, const DeviceFa
         // 2976.2, 2048x4608x2048 305.9 / 318.3; it lost at 512 tiles
         // (2048x4096x4096 498.9 / 484.3), 672 tiles (1792x6144x4096 682.0 /
         // 641.3) and k = 1024 (2048x4608x1024 171.4 / 156.8).  Row-major B
-        // was level (2048x4608x4096 570.0 / 569.0).
+        // was level (2048x4608x4096 570.0 / 569.0).  With the linear-layer
+        // epilogue (bias + GELU; us, stream-K / the data-parallel epilogue
+        // plan): 2432x4096x4096 645.1 / 708.4, 2048x5120x5120 809.4 / 880.7,
+        // 2000x5000x4000 642.5 / 691.3, 1536x5632x4096 565.1 / 579.8,
+        // 2048x4608x4096 593.0 / 603.7; level at k = 2048 (2048x4608x2048
+        // 315.3 / 312.2), so epilogue plans take it from k = 3072.
         const int64_t t128 = ceil_div(m, 128) * ceil_div(n, 128), cus = f.cu_count;
-        if (layout_b == GEMM_F32_COL_MAJOR && tail_ok && !epilogue && row_a && !small_scratch && t128 > 2 * cus &&
-            2 * t128 <= 5 * cus && k >= 2048) {
+        const bool kernels = epilogue ? row_a && k >= 3072 : tail_ok;
+        if (layout_b == GEMM_F32_COL_MAJOR && kernels && !small_scratch && t128 > 2 * cus && 2 * t128 <= 5 * cus &&
+            k >= 2048) {
             *stream_k = true;
             return V_DMA_128x128x16_S3;
         }

@@ -113,6 +113,7 @@ using Skinny16x32W16D4 = SkinnyTile<16, 4, 32>;   // 32-column tiles
     GEMMF32_DMA_BASE(X5, X2, Dma128x128x16S3) GEMMF32_DMA_WIDE(X5, Dma128x128x16S3) \
     GEMMF32_DMA_EX(X5, Dma128x128x16S3) GEMMF32_DMA_EX_WIDE(X5, Dma128x128x16S3) \
     GEMMF32_DMA_SLIVER(X5, Dma128x128x16S3) GEMMF32_DMA_SLIVER_WIDE(X5, Dma128x128x16S3) \
+    X2(gemm_mfma_dma_sk_epi_kernel, Dma128x128x16S3, false) X2(gemm_mfma_dma_sk_epi_kernel, Dma128x128x16S3, true) \
     GEMMF32_DMA_BASE(X5, X2, Dma128x128x32S3) GEMMF32_DMA_WIDE(X5, Dma128x128x32S3)
 #define GEMMF32_UNIT_DMA64(X5, X2, X1)                            \
     GEMMF32_DMA_BASE(X5, X2, Dma64x64x16S3) GEMMF32_DMA_EX(X5, Dma64x64x16S3) \

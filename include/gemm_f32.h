@@ -278,7 +278,9 @@ int gemm_f32_run_noalloc(int64_t m, int64_t n, int64_t k, int layout_b, int64_t 
  * and shapes with few tiles; either A layout), on the few-column kernels (N <= 8, row-major
  * A), as the transposed product C^T = B^T . A^T for up to eight rows with column-major B
  * (row-major A), and, for few tiles with a long k and row-major A, on stream-K over 64x64
- * tiles; the epilogue is applied where each kernel writes C.
+ * tiles, and with column-major B, row-major A and k >= 3072 where 128x128 tiles number
+ * two to two and a half per CU, on stream-K over those tiles; the epilogue is applied where
+ * each kernel writes C.
  */
 
 /* gemm_f32_validate_ex: gemm_f32_validate with A's layout: lda >= k (row-major

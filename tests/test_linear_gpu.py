@@ -376,6 +376,42 @@ def test_stream_k_epilogue_forced(wgs, shared, monkeypatch):
     assert np.all(C[:, n:] == np.float32(-3.5))
 
 
+
+# Column-major B with more than two and at most two and a half 128x128 tiles
+# per CU: stream-K over 128x128 tiles with the epilogue from k = 3072;
+# (shape, whether the plan is that one).
+SUB_WAVE_EPI = [((1536, 5632, 3100), True), ((2048, 4608, 2048), False)]
+
+
+@pytest.mark.parametrize("shape,taken", SUB_WAVE_EPI)
+def test_stream_k_epilogue_over_128x128_tiles(shape, taken):
+    """The epilogue on stream-K over 128x128 tiles (the last segment of each
+    split tile applies it): every element against the oracle's epilogue,
+    runs repeating bit for bit, integer operands exact."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the choice was measured on a 256-CU MI355X")
+    m, n, k = shape
+    print(f"\n[case] stream-K epilogue over 128x128 tiles {shape}", flush=True)
+    A, B = random_operands(m, n, k, COL_MAJOR, "normal1", seed=920)
+    c_in, bias = epilogue_operands(m, n, seed=921)
+    AB, S = oracle.gemm_f64(A, B, m, n, k, COL_MAJOR)
+    C, info, outs = run_ex(A, B, m, n, k, ROW_MAJOR, COL_MAJOR, epilogue=1, alpha=0.5, beta=-1.5, c_in=c_in,
+                           bias=bias, act=g.GEMM_F32_ACT_GELU, repeat=2)
+    assert (info["name"] == "dma_128x128x16_w2x2_s3" and info["stream_k"] == 768) == taken, info
+    assert info["epilogue"] == 1
+    ref, scale = oracle.epilogue_f64(AB, S, c_in, 0.5, -1.5, bias, g.GEMM_F32_ACT_GELU)
+    check(C[:, :n], ref, scale, f"{info['name']} epilogue {shape}")
+    assert np.array_equal(outs[0], outs[1])
+    A, B = random_operands(m, n, k, COL_MAJOR, "int8range", seed=922)
+    rng = np.random.default_rng(923)
+    c_in = rng.integers(-50, 51, (m, n)).astype(np.float32)
+    bias = rng.integers(-9, 10, n).astype(np.float32)
+    AB, S = oracle.gemm_f64(A, B, m, n, k, COL_MAJOR)
+    C, _, _ = run_ex(A, B, m, n, k, ROW_MAJOR, COL_MAJOR, epilogue=1, alpha=1.0, beta=1.0, c_in=c_in, bias=bias,
+                     act=g.GEMM_F32_ACT_RELU)
+    ref, _ = oracle.epilogue_f64(AB, S, c_in, 1.0, 1.0, bias, g.GEMM_F32_ACT_RELU)
+    assert np.array_equal(C[:, :n].astype(np.float64), ref)
+
 def test_stream_k_epilogue_column_major_a_stays_data_parallel():
     """Column-major A has no stream-K kernels: the few-tile long-k epilogue
     plan runs whole tiles."""
